@@ -1,0 +1,341 @@
+"""Pins of the oracle's whole forward: an independent library model, closed
+forms, path invariants, error behaviour and planted mistakes (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.talker as ot
+from oracle import TalkerOracle
+from synth import TalkerShape, make_weights, prefill_embeddings, step_embedding
+
+
+def small_shape(**kw):
+    """A Talker-like geometry with q_dim != hidden (as in the Talker)."""
+    base = dict(name="pin", n_layers=2, hidden=64, n_heads=4, n_kv_heads=2,
+                head_dim=32, intermediate=96, vocab=40, rms_eps=1e-6,
+                rope_theta=1e6, weight_dtype="f32", kv_dtype="f32", cap=48,
+                n_seqs=3, seed=77, emb_seed=78)
+    base.update(kw)
+    return TalkerShape(**base)
+
+
+def scaled_weights(shape, wscale=0.15):
+    """Weights with larger spread than 0.02 so every term matters in the pins."""
+    w = make_weights(shape)
+    f = np.float32(wscale / 0.02)
+    for lw in w["layers"]:
+        for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            lw[k] = lw[k] * f
+    w["w_head"] = w["w_head"] * f
+    return w
+
+
+# -- independent library model ---------------------------------------------------
+
+def _transformers_logits(shape, w, emb):
+    from transformers import Qwen3Config
+    from transformers.models.qwen3.modeling_qwen3 import Qwen3Model
+    cfg = Qwen3Config(
+        vocab_size=8, hidden_size=shape.hidden,
+        intermediate_size=shape.intermediate,
+        num_hidden_layers=shape.n_layers, num_attention_heads=shape.n_heads,
+        num_key_value_heads=shape.n_kv_heads, head_dim=shape.head_dim,
+        rms_norm_eps=shape.rms_eps, attention_bias=False,
+        rope_parameters={"rope_type": "default",
+                         "rope_theta": shape.rope_theta})
+    cfg._attn_implementation = "eager"
+    m = Qwen3Model(cfg).double().eval()
+    names = {"wq": "self_attn.q_proj.weight", "wk": "self_attn.k_proj.weight",
+             "wv": "self_attn.v_proj.weight", "wo": "self_attn.o_proj.weight",
+             "wg": "mlp.gate_proj.weight", "wu": "mlp.up_proj.weight",
+             "wd": "mlp.down_proj.weight",
+             "g_in": "input_layernorm.weight",
+             "g_post": "post_attention_layernorm.weight",
+             "g_q": "self_attn.q_norm.weight", "g_k": "self_attn.k_norm.weight"}
+    sd = {}
+    for l, lw in enumerate(w["layers"]):
+        for k, n in names.items():
+            sd[f"layers.{l}.{n}"] = torch.from_numpy(lw[k].astype(np.float64))
+    sd["norm.weight"] = torch.from_numpy(w["g_final"].astype(np.float64))
+    missing, unexpected = m.load_state_dict(sd, strict=False)
+    assert set(missing) == {"embed_tokens.weight"} and not unexpected
+    with torch.no_grad():
+        hs = m(inputs_embeds=torch.from_numpy(emb.astype(np.float64))[None],
+               use_cache=False).last_hidden_state[0].numpy()
+    return hs @ w["w_head"].astype(np.float64).T
+
+
+def test_oracle_matches_transformers_qwen3_all_rows():
+    # transformers' Qwen3 decoder (pre-norm, QK-norm, rotate-half RoPE, GQA,
+    # SwiGLU) is an independent implementation of the same block; it keeps
+    # RMSNorm and RoPE tables in float32 internally, hence the tolerance.
+    shape = small_shape()
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 20)
+    ref = _transformers_logits(shape, w, emb)
+    orc = TalkerOracle(shape, w)
+    logits, _ = orc.prefill(0, emb, all_rows=True)
+    err = np.abs(logits - ref).max() / np.abs(ref).max()
+    assert err < 2e-5, err
+
+
+def test_oracle_decode_path_matches_transformers():
+    # prefill 12 rows, then 8 one-row decodes at positions 12..19: every
+    # decode's logits equal the library model's row at that position
+    shape = small_shape()
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 20)
+    ref = _transformers_logits(shape, w, emb)
+    orc = TalkerOracle(shape, w)
+    orc.prefill(1, emb[:12])
+    for t in range(12, 20):
+        lg, _ = orc.decode(1, emb[t])
+        err = np.abs(lg - ref[t]).max() / np.abs(ref[t]).max()
+        assert err < 2e-5, (t, err)
+    assert orc.kv_len(1) == 20
+
+
+# -- closed forms ------------------------------------------------------------------
+
+def test_residual_path_closed_form():
+    # with o_proj = down = 0 every layer returns its input, so the logits are
+    # codec_head applied to the final RMSNorm of the embedding row
+    shape = small_shape(n_layers=3)
+    w = scaled_weights(shape)
+    for lw in w["layers"]:
+        lw["wo"][:] = 0
+        lw["wd"][:] = 0
+    emb = prefill_embeddings(shape, 5)
+    lg, hid = TalkerOracle(shape, w).prefill(0, emb)
+    x = emb[-1].astype(np.float64)
+    hn = x / math.sqrt(np.mean(x * x) + shape.rms_eps) * w["g_final"]
+    np.testing.assert_allclose(hid, hn, rtol=1e-12)
+    np.testing.assert_allclose(lg, w["w_head"].astype(np.float64) @ hn,
+                               rtol=1e-11, atol=1e-13)
+
+
+def test_first_position_attention_is_v_projection():
+    # at position 0 the attention output is the (cache-rounded) V of that row;
+    # one layer with zero MLP: x1 = x + Wo @ repeat(V) exactly
+    shape = small_shape(n_layers=1, kv_dtype="f16")
+    w = scaled_weights(shape)
+    lw = w["layers"][0]
+    lw["wd"][:] = 0
+    emb = prefill_embeddings(shape, 1)
+    taps = []
+    orc = TalkerOracle(shape, w)
+    orc.extend(0, emb, taps=taps)
+    x = emb[0].astype(np.float64)
+    h = x / math.sqrt(np.mean(x * x) + shape.rms_eps) * lw["g_in"]
+    v = (lw["wv"].astype(np.float64) @ h).astype(np.float32).astype(np.float16)
+    v = v.astype(np.float64).reshape(shape.n_kv_heads, shape.head_dim)
+    o = np.repeat(v, shape.n_heads // shape.n_kv_heads, axis=0).reshape(-1)
+    np.testing.assert_allclose(taps[0][0], x + lw["wo"].astype(np.float64) @ o,
+                               rtol=1e-12)
+
+
+# -- path invariants -------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_prefill_equals_prefill_then_decode(kv):
+    shape = small_shape(kv_dtype=kv)
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 17)
+    a = TalkerOracle(shape, w)
+    la, ha = a.prefill(0, emb)
+    b = TalkerOracle(shape, w)
+    b.prefill(0, emb[:16])
+    lb, hb = b.decode(0, emb[16])
+    np.testing.assert_allclose(lb, la, rtol=1e-11, atol=1e-12)
+    for l in range(shape.n_layers):
+        for which in (0, 1):
+            np.testing.assert_allclose(b.kv(0, l, which), a.kv(0, l, which),
+                                       rtol=1e-11, atol=1e-12)
+
+
+def test_chunked_extend_equals_one_shot_and_batched_equals_serial():
+    shape = small_shape(kv_dtype="f16")
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 30)
+    a = TalkerOracle(shape, w)
+    la, _ = a.prefill(0, emb)
+    b = TalkerOracle(shape, w)
+    b.prefill(0, emb[:7])
+    b.extend(0, emb[7:19])
+    lb, _ = b.extend(0, emb[19:])
+    np.testing.assert_allclose(lb, la, rtol=1e-11, atol=1e-12)
+    # batched decode over three sequences equals three serial decodes
+    c = TalkerOracle(shape, w)
+    d = TalkerOracle(shape, w)
+    for sq, n in ((0, 5), (1, 9), (2, 2)):
+        e = prefill_embeddings(shape, n, seq=sq)
+        c.prefill(sq, e)
+        d.prefill(sq, e)
+    steps = np.stack([step_embedding(shape, 0, seq=s) for s in (2, 0, 1)])
+    lc, hc = c.decode_batch([2, 0, 1], steps)
+    for i, sq in enumerate((2, 0, 1)):
+        ld, hd_ = d.decode(sq, steps[i])
+        np.testing.assert_array_equal(lc[i], ld)
+    assert [c.kv_len(s) for s in range(3)] == [6, 10, 3]
+
+
+def test_causality_later_rows_do_not_change_earlier_logits():
+    shape = small_shape()
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 12)
+    la, _ = TalkerOracle(shape, w).prefill(0, emb, all_rows=True)
+    emb2 = emb.copy()
+    emb2[8:] += 5.0
+    lb, _ = TalkerOracle(shape, w).prefill(0, emb2, all_rows=True)
+    np.testing.assert_array_equal(la[:8], lb[:8])
+    assert np.abs(la[8:] - lb[8:]).max() > 1e-3
+
+
+def test_stale_cache_tail_is_never_read():
+    shape = small_shape(kv_dtype="f16")
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 20)
+    a = TalkerOracle(shape, w)
+    a.prefill(0, emb)
+    a.kv_rewind(0, 11)
+    for c in (a.kc[0], a.vc[0]):
+        c[:, :, 11:, :] = np.nan
+    la, _ = a.decode(0, emb[11])
+    assert np.isfinite(la).all()
+    b = TalkerOracle(shape, w)
+    b.prefill(0, emb[:11])
+    lb, _ = b.decode(0, emb[11])
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_errors_leave_state_unchanged():
+    shape = small_shape(cap=10)
+    w = scaled_weights(shape)
+    o = TalkerOracle(shape, w)
+    o.prefill(0, prefill_embeddings(shape, 9))
+    k_before = o.kv(0, 0, 0)
+    o.decode(0, step_embedding(shape, 0))
+    assert o.kv_len(0) == 10
+    with pytest.raises(OverflowError):
+        o.decode(0, step_embedding(shape, 1))
+    with pytest.raises(OverflowError):
+        o.prefill(1, prefill_embeddings(shape, 11))
+    with pytest.raises(ValueError):
+        o.kv_rewind(0, 11)
+    with pytest.raises(ValueError):
+        o.extend(0, np.zeros((0, shape.hidden)))
+    assert o.kv_len(0) == 10 and o.kv_len(1) == 0
+    np.testing.assert_array_equal(o.kv(0, 0, 0)[:, :9], k_before)
+
+
+def test_precision_floor_f32_vs_f64():
+    # the same forward in float32 stays within 1e-5 of float64 relative to the
+    # logit scale: the floor under the kernel tolerances
+    shape = small_shape(kv_dtype="f16", hidden=128, intermediate=384,
+                        n_heads=8, n_kv_heads=4)
+    w = make_weights(shape)
+    emb = prefill_embeddings(shape, 24)
+    l64, _ = TalkerOracle(shape, w).prefill(0, emb, all_rows=True)
+    l32, _ = TalkerOracle(shape, w, dtype=np.float32).prefill(0, emb,
+                                                               all_rows=True)
+    err = np.abs(l32 - l64).max() / np.abs(l64).max()
+    assert err < 1e-5, err
+
+
+# -- planted mistakes: each must be caught by a pin above ------------------------
+
+def _interleaved_rope(x, pos, theta):
+    hd = x.shape[-1]
+    inv = ot.rope_inv_freq(hd, theta)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def _sign_flipped_rope(x, pos, theta):
+    return ot.rope_neox(x, -np.asarray(pos), theta)
+
+
+def _modulo_gqa(q, kc, vc, positions, scale):
+    # wrong group map: h % n_kv instead of h // G
+    nkv = kc.shape[0]
+    perm = [h % nkv for h in range(q.shape[1])]
+    return ot.causal_gqa_attention(q, kc[perm], vc[perm], positions, scale)
+
+
+def _fresh_kv_in_prefill(self, l, x, seq, p0):
+    # reads fresh float64 K/V for the rows just computed (not the f16 cache)
+    s, w = self.s, self.layers[l]
+    T = x.shape[0]
+    pos = p0 + np.arange(T)
+    h = ot.rms_norm(x, w["g_in"], s.rms_eps)
+    q = (h @ w["wq"].T).reshape(T, s.n_heads, s.head_dim)
+    k = (h @ w["wk"].T).reshape(T, s.n_kv_heads, s.head_dim)
+    v = (h @ w["wv"].T).reshape(T, s.n_kv_heads, s.head_dim)
+    q = ot.rope_neox(ot.rms_norm(q, w["g_q"], s.rms_eps), pos[:, None],
+                     s.rope_theta)
+    k = ot.rope_neox(ot.rms_norm(k, w["g_k"], s.rms_eps), pos[:, None],
+                     s.rope_theta)
+    kc = self.kc[seq][l].copy()
+    vc = self.vc[seq][l].copy()
+    kc[:, p0:p0 + T] = k.transpose(1, 0, 2)
+    vc[:, p0:p0 + T] = v.transpose(1, 0, 2)
+    self.kc[seq][l, :, p0:p0 + T] = ot.round_kv(k.transpose(1, 0, 2),
+                                                s.kv_dtype, self.dtype)
+    self.vc[seq][l, :, p0:p0 + T] = ot.round_kv(v.transpose(1, 0, 2),
+                                                s.kv_dtype, self.dtype)
+    o = ot.causal_gqa_attention(q, kc, vc, pos, self.scale)
+    x = x + o.reshape(T, s.q_dim) @ w["wo"].T
+    h2 = ot.rms_norm(x, w["g_post"], s.rms_eps)
+    return x + ot.swiglu(h2 @ w["wg"].T, h2 @ w["wu"].T) @ w["wd"].T
+
+
+def test_planted_rope_mistakes_are_caught(monkeypatch):
+    import tests.test_oracle_steps as steps
+    for bad in (_interleaved_rope, _sign_flipped_rope):
+        monkeypatch.setattr(steps, "rope_neox", bad)
+        with pytest.raises(AssertionError):
+            steps.test_rope_hand_worked_examples("rope_neox_hd4_pos2_mixed.txt")
+    monkeypatch.setattr(ot, "rope_neox", _interleaved_rope)
+    with pytest.raises(AssertionError):
+        test_oracle_matches_transformers_qwen3_all_rows()
+
+
+def test_planted_gqa_mistake_is_caught(monkeypatch):
+    import tests.test_oracle_steps as steps
+    monkeypatch.setattr(steps, "causal_gqa_attention", _modulo_gqa)
+    with pytest.raises(AssertionError):
+        steps.test_attention_matches_torch_sdpa_gqa()
+
+
+def test_planted_fresh_kv_reading_is_caught(monkeypatch):
+    # the read-after-write reading makes prefill(T) equal prefill(T-1) + decode
+    # to rounding; reading fresh values in prefill breaks it for an f16 cache
+    monkeypatch.setattr(TalkerOracle, "layer", _fresh_kv_in_prefill)
+    with pytest.raises(AssertionError):
+        test_prefill_equals_prefill_then_decode("f16")
+
+
+def test_planted_missing_eps_and_gain_are_caught(monkeypatch):
+    import tests.test_oracle_steps as steps
+    monkeypatch.setattr(steps, "rms_norm",
+                        lambda x, g, eps: x / np.sqrt(np.mean(x * x, -1,
+                                                              keepdims=True)) * g)
+    with pytest.raises(AssertionError):
+        steps.test_rms_norm_constant_vector_closed_form()
+    monkeypatch.setattr(steps, "rms_norm",
+                        lambda x, g, eps: ot.rms_norm(x, 1.0 + g, eps))
+    with pytest.raises(AssertionError):
+        steps.test_rms_norm_matches_torch_rms_norm()
+
+
+def test_planted_swapped_gate_up_is_caught(monkeypatch):
+    monkeypatch.setattr(ot, "swiglu", lambda g, u: ot.silu(u) * g)
+    with pytest.raises(AssertionError):
+        test_oracle_matches_transformers_qwen3_all_rows()
