@@ -1,0 +1,200 @@
+"""Benchmark of the KV-cached Talker forward on one MI355X.
+
+Headline: batch-1 decode of the 28-layer Talker (bf16 weights, f16 KV cache)
+at context 1921..2048, after a 1920-row prefill on the same weights.  A step
+is one decode token through the whole stack (every layer plus the final norm
+and codec head).  Prefill tok/s of the 1920-row prefill is reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Inputs are synthetic (seeded N(0, 1) embeddings, N(0, 0.02) bf16 weights) and
+resident in device memory before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Talker decode tok/s (bs1, KV 2k) + prefill tok/s; % HBM BW / % MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def kv_bytes_per_position(s) -> int:
+    return s.n_layers * 2 * s.n_kv_heads * s.head_dim * (2 if s.kv_dtype == "f16" else 4)
+
+
+def weight_bytes(s) -> int:
+    per = s.params_per_layer() * s.n_layers + s.vocab * s.hidden
+    return per * (2 if s.weight_dtype == "bf16" else 4)
+
+
+def decode_bytes(s, keys: int) -> int:
+    """Algorithmic HBM bytes of one decode token attending `keys` positions:
+    every weight once, K and V of every attended position once, plus the
+    new position's K and V written."""
+    kvp = kv_bytes_per_position(s)
+    return weight_bytes(s) + kvp * keys + kvp
+
+
+def prefill_flops(s, T: int, p0: int = 0) -> float:
+    """Matrix flops of a T-row prefill at offset p0: projections on every row,
+    causal attention (QK^T and PV) over each row's context, head on the last
+    row."""
+    proj = 2.0 * (s.params_per_layer()) * T * s.n_layers
+    ctx = sum(p0 + t + 1 for t in range(T))
+    attn = 4.0 * s.q_dim * ctx * s.n_layers
+    return proj + attn + 2.0 * s.vocab * s.hidden
+
+
+def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
+    """The oracle (float64 NumPy) on this host: a bounded sample of the same
+    workload — the 1920-row prefill, then `n_steps` decode steps."""
+    from oracle import TalkerOracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    orc = TalkerOracle(shape, weights)
+    t0 = time.perf_counter()
+    orc.prefill(0, emb)
+    t1 = time.perf_counter()
+    for k in range(n_steps):
+        orc.decode(0, steps_emb[k])
+    t2 = time.perf_counter()
+    return {
+        "value": n_steps / (t2 - t1), "unit": "tok/s",
+        "cores": blas_threads or cores,
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle on {cores} host cores (BLAS threads "
+                   f"{blas_threads}): {n_steps} decode steps at context "
+                   f"{emb.shape[0] + 1}..{emb.shape[0] + n_steps} after its own "
+                   f"{emb.shape[0]}-row prefill; value = decode tok/s"),
+        "prefill_tok_s": emb.shape[0] / (t1 - t0),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--workload", default="talker_28l_kv2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=8)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(it would shard independent utterances, one process per GPU)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from qwen3_tts_talker_amd import Talker, qtalk
+    from synth import make_weights, prefill_embeddings, step_embedding, workload
+
+    shape = workload(args.workload)
+    T = shape.prefill_len
+    K = args.steps
+    if T + K > shape.cap:
+        K = shape.cap - T
+    torch.cuda.set_device(0)
+    weights = make_weights(shape)
+    emb_h = prefill_embeddings(shape, T)
+    steps_h = np.stack([step_embedding(shape, k) for k in range(max(K, args.cpu_steps))])
+    tk = Talker(shape, weights)
+    lib = qtalk.load_library()
+    ctx = tk.ctx
+    emb = torch.from_numpy(emb_h).cuda()
+    steps = torch.from_numpy(steps_h).cuda()
+    logits = torch.empty(shape.vocab, device="cuda")
+    st = torch.cuda.current_stream()
+
+    # prefill: warm once, then time reps (events on the library's stream)
+    def prefill_once():
+        s = lib.qtalk_prefill(ctx, 0, emb.data_ptr(), T, logits.data_ptr(), None)
+        assert s == 0, qtalk.qtalk_last_error(ctx)
+
+    prefill_once()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.prefill_reps)]
+    for r in range(args.prefill_reps):
+        ev[2 * r].record(st)
+        prefill_once()
+        ev[2 * r + 1].record(st)
+    torch.cuda.synchronize()
+    pre_ms = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(args.prefill_reps))
+    pre_med = pre_ms[len(pre_ms) // 2]
+
+    # decode warmup from context T, then rewind and time K steps
+    for k in range(args.warmup):
+        s = lib.qtalk_decode(ctx, 0, steps[k % K].data_ptr(), logits.data_ptr(), None)
+        assert s == 0, qtalk.qtalk_last_error(ctx)
+    torch.cuda.synchronize()
+    lib.qtalk_kv_rewind(ctx, 0, T)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(st)
+    for k in range(K):
+        lib.qtalk_decode(ctx, 0, steps[k].data_ptr(), logits.data_ptr(), None)
+        evs[k + 1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert tk.kv_len(0) == T + K
+    step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(K)])
+    total_ms = evs[0].elapsed_time(evs[K])
+    tok_s = K / (total_ms / 1e3)
+
+    alg_bytes = sum(decode_bytes(shape, T + k + 1) for k in range(K))
+    achieved = alg_bytes / (total_ms / 1e3) / 1e9
+    roof = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "kernel": ("k_decode_fused (one persistent launch per token)"
+                   if os.environ.get("QTALK_FUSED_DECODE", "1") != "0"
+                   else "decode step (all launches of one token)"),
+        "bytes_per_step": int(alg_bytes / K),
+    }
+    pf = prefill_flops(shape, T)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": shape.name, "layers": shape.n_layers,
+                   "hidden": shape.hidden, "heads": f"{shape.n_heads}q/{shape.n_kv_heads}kv",
+                   "head_dim": shape.head_dim, "intermediate": shape.intermediate,
+                   "vocab": shape.vocab, "batch": 1, "prefill_len": T,
+                   "decode_ctx": [T + 1, T + K], "weights": shape.weight_dtype,
+                   "kv_cache": shape.kv_dtype},
+        "p50_step_us": round(float(np.percentile(step_ms, 50)) * 1e3, 1),
+        "p99_step_us": round(float(np.percentile(step_ms, 99)) * 1e3, 1),
+        "wall_s": round(wall, 3),
+        "prefill_tok_s": round(T / (pre_med / 1e3), 1),
+        "prefill_ms": round(pre_med, 3),
+        "prefill_tflops": round(pf / (pre_med / 1e3) / 1e12, 2),
+        "prefill_mfma_frac": round(pf / (pre_med / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof,
+    }
+    tk.close()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+/*
+ * qtalk.h - C ABI of the KV-cached Talker forward on MI355X (gfx950).
+ *
+ * The library computes the Qwen3-lineage Talker decoder stack used by
+ * Qwen3-TTS: per layer a pre-norm RMSNorm, bias-free Q/K/V projections,
+ * per-head QK-RMSNorm, 1-D NEOX rotary embedding, a write of K and V into a
+ * per-sequence KV cache, causal grouped-query attention that reads the cache
+ * back, o_proj plus residual, a post-attention RMSNorm and a SwiGLU MLP plus
+ * residual; then a final RMSNorm and the codec_head projection to codebook-0
+ * logits.  Sources: "qwentts.cpp src/talker-forward.h" (file header,
+ * talker_layer_forward, talker_forward_core, talker_forward_prefill,
+ * talker_forward_decode), "transcribe.cpp src/causal_lm/causal_lm.cpp"
+ * (block_prefill, block_step, mul_mat_f32acc) and "rightkit-qts 0.2.3
+ * src/pipeline/tts_transformer.rs" (TtsTransformerConfig defaults,
+ * forward_prefill_cached, forward_step_cached).
+ *
+ * General conventions
+ *  - All compute runs as HIP kernels on the stream given to qtalk_create.
+ *    Every call validates its arguments on the host first; on any error it
+ *    launches nothing, leaves every cache length unchanged, records a message
+ *    (qtalk_last_error) and returns a negative qtalk_status.
+ *  - Calls that take activations (emb, logits, hidden_out, kv_read dst) take
+ *    DEVICE pointers owned by the caller, in float32, row-major.  They return
+ *    once the work is enqueued; results are ready when the stream reaches
+ *    that point (synchronise the stream, or order later work on it).
+ *  - Accumulation is float32 everywhere (dot products, sums of squares,
+ *    softmax), as the pages require to keep large residual channels from
+ *    overflowing ("transcribe.cpp src/causal_lm/causal_lm.cpp",
+ *    mul_mat_f32acc).
+ *  - A context is not thread-safe; use one per host thread, or serialise.
+ */
+#ifndef QTALK_H
+#define QTALK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QTALK_OK = 0,
+  QTALK_E_INVAL = -1,    /* bad argument: null pointer, bad id, T < 1, shape */
+  QTALK_E_OVERFLOW = -2, /* the write would pass the KV capacity            */
+  QTALK_E_NOMEM = -3,    /* device allocation failed                         */
+  QTALK_E_DEVICE = -4    /* a HIP call or kernel launch failed               */
+} qtalk_status;
+
+typedef enum { QTALK_F32 = 0, QTALK_BF16 = 1, QTALK_F16 = 2 } qtalk_dtype;
+
+/* Model geometry and cache sizes.  The Talker defaults are hidden 1024,
+ * 28 layers, 16 query heads, 8 KV heads, head_dim 128, intermediate 3072,
+ * vocab 3072, eps 1e-6, theta 1e6 ("rightkit-qts 0.2.3
+ * src/pipeline/tts_transformer.rs", TtsTransformerConfig::default).
+ * Requirements (else QTALK_E_INVAL): every size >= 1; head_dim is 64 or 128;
+ * n_heads % n_kv_heads == 0; hidden, intermediate and n_heads*head_dim are
+ * multiples of 64; intermediate is a multiple of 16; weight_dtype is F32 or
+ * BF16; kv_dtype is F32 or F16.  q_dim = n_heads*head_dim need not equal
+ * hidden (it does not for the Talker: 2048 vs 1024). */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t vocab;
+  float rms_eps;
+  float rope_theta;
+  int32_t max_seq_len;  /* KV capacity per sequence                    */
+  int32_t max_seqs;     /* number of independent sequences (KV sets)   */
+  int32_t weight_dtype; /* qtalk_dtype: F32 or BF16 (projections, head) */
+  int32_t kv_dtype;     /* qtalk_dtype: F32 or F16 (cache storage)      */
+} qtalk_config;
+
+/* One layer's weights.  Projections are row-major [out][in] in weight_dtype,
+ * as ggml's mul_mat(W, x) stores them ("qwentts.cpp
+ * src/talker-forward.h", talker_layer_forward):
+ *   q_proj [n_heads*head_dim][hidden], k_proj and v_proj
+ *   [n_kv_heads*head_dim][hidden], o_proj [hidden][n_heads*head_dim],
+ *   gate_proj and up_proj [intermediate][hidden], down_proj
+ *   [hidden][intermediate].
+ * Norm gains are float32: input_norm and post_attn_norm [hidden], q_norm and
+ * k_norm [head_dim] (one gain shared by every head).
+ * Pointers may be host or device memory; qtalk_create copies (and repacks)
+ * them into library-owned device memory, so the caller may free them
+ * afterwards. */
+typedef struct {
+  const void *q_proj, *k_proj, *v_proj, *o_proj;
+  const void *gate_proj, *up_proj, *down_proj;
+  const float *input_norm, *post_attn_norm, *q_norm, *k_norm;
+} qtalk_layer_weights;
+
+typedef struct {
+  const qtalk_layer_weights *layers; /* host array [n_layers]              */
+  const float *final_norm;           /* [hidden] float32                    */
+  const void *codec_head;            /* [vocab][hidden] in weight_dtype     */
+} qtalk_weights;
+
+typedef struct qtalk_ctx qtalk_ctx;
+
+/* Create a context on the current HIP device: copy the weights, allocate the
+ * zero-initialised KV cache ([n_layers][max_seqs][n_kv_heads][max_seq_len]
+ * [head_dim] for K and for V) and scratch buffers.  `hip_stream` is a
+ * hipStream_t (NULL: the default stream).  On success *out owns everything
+ * until qtalk_destroy.  Errors: QTALK_E_INVAL (config, null pointer),
+ * QTALK_E_NOMEM, QTALK_E_DEVICE; *out is then NULL. */
+qtalk_status qtalk_create(const qtalk_config *config,
+                          const qtalk_weights *weights, void *hip_stream,
+                          qtalk_ctx **out);
+
+/* Wait for the context's stream, then free everything it owns.  NULL is a
+ * no-op. */
+void qtalk_destroy(qtalk_ctx *ctx);
+
+/* Prefill: rewind sequence `seq` to 0 and write T positions from
+ * emb [T][hidden]; logits [vocab] receive the codebook-0 logits of the last
+ * row; hidden_out [hidden] (nullable) receives that row's hidden state after
+ * the final RMSNorm.  ("qwentts.cpp src/talker-forward.h",
+ * talker_forward_prefill.)  Errors: QTALK_E_INVAL (seq out of range, T < 1,
+ * null emb/logits), QTALK_E_OVERFLOW (T > max_seq_len). */
+qtalk_status qtalk_prefill(qtalk_ctx *ctx, int32_t seq, const float *emb,
+                           int32_t T, float *logits, float *hidden_out);
+
+/* Extend: append T positions at cur_len(seq) (chunked prefill: the rows
+ * attend to everything before them), same outputs as qtalk_prefill.
+ * ("qwentts.cpp src/talker-forward.h", talker_forward_core with n_past.)
+ * Errors as qtalk_prefill; QTALK_E_OVERFLOW when cur_len + T > max_seq_len. */
+qtalk_status qtalk_extend(qtalk_ctx *ctx, int32_t seq, const float *emb,
+                          int32_t T, float *logits, float *hidden_out);
+
+/* Decode: one position at cur_len(seq) from emb [hidden]; attends to
+ * [0, cur_len + 1); cur_len advances by one.  ("qwentts.cpp
+ * src/talker-forward.h", talker_forward_decode.)  Errors: QTALK_E_INVAL,
+ * QTALK_E_OVERFLOW when cur_len + 1 > max_seq_len. */
+qtalk_status qtalk_decode(qtalk_ctx *ctx, int32_t seq, const float *emb,
+                          float *logits, float *hidden_out);
+
+/* Batched decode: one position for each of n distinct sequences seqs[0..n)
+ * (a HOST array), emb [n][hidden], logits [n][vocab], hidden_out [n][hidden]
+ * (nullable).  Row i is exactly the single-sequence decode of seqs[i]; the
+ * sequences may have different lengths.  ("qwentts.cpp
+ * src/talker-forward.h", talker_forward_decode and
+ * talker_layer_forward_batch.)  Errors: QTALK_E_INVAL (n < 1, n > max_seqs,
+ * repeated or out-of-range id), QTALK_E_OVERFLOW if any sequence is full;
+ * then no sequence advances. */
+qtalk_status qtalk_decode_batch(qtalk_ctx *ctx, int32_t n, const int32_t *seqs,
+                                const float *emb, float *logits,
+                                float *hidden_out);
+
+/* Truncate sequence `seq` to its first n_keep positions (0 <= n_keep <=
+ * cur_len); slots at and above n_keep are never read again.  Rewind to 0 is
+ * the pages' kv_cache_reset.  Errors: QTALK_E_INVAL. */
+qtalk_status qtalk_kv_rewind(qtalk_ctx *ctx, int32_t seq, int32_t n_keep);
+
+/* Current length of sequence `seq`, or -1 for a bad context or id. */
+int32_t qtalk_kv_len(const qtalk_ctx *ctx, int32_t seq);
+
+/* Test hook: copy the cached K (kv = 0) or V (kv = 1) of (seq, layer),
+ * converted to float32, into the device buffer dst
+ * [n_kv_heads][cur_len][head_dim].  Errors: QTALK_E_INVAL. */
+qtalk_status qtalk_kv_read(qtalk_ctx *ctx, int32_t seq, int32_t layer,
+                           int32_t kv, float *dst);
+
+/* Block until the context's stream has finished all enqueued work.
+ * Errors: QTALK_E_DEVICE if a kernel failed. */
+qtalk_status qtalk_sync(qtalk_ctx *ctx);
+
+/* Message of the last error on this context ("" if none).  The string lives
+ * until the next call on the context. */
+const char *qtalk_last_error(const qtalk_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QTALK_H */

@@ -1,0 +1,363 @@
+// Attention-side kernels: per-head QK RMSNorm + NEOX RoPE + KV append, and
+// split-KV causal GQA attention over the cache with a log-sum-exp merge.
+//
+// Semantics: "qwentts.cpp src/talker-forward.h", talker_layer_forward (QK
+// norm over head_dim with one [head_dim] gain, NEOX rotate-half RoPE at the
+// absolute position, set_rows of K/V into the cache, then attention over the
+// cache window with scale 1/sqrt(head_dim) and the causal mask key <= pos);
+// "transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill (query head h
+// reads KV head h / (n_heads / n_kv_heads)).  The attention reads the cache
+// after the write, so K/V pass through the cache's storage type.
+#include "kernels.h"
+
+namespace qtalk {
+
+template <typename KVT>
+struct KVIO;
+template <>
+struct KVIO<float> {
+  template <int N>
+  static __device__ __forceinline__ void load(const float* p, float* f) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + i);
+      f[i] = v.x;
+      f[i + 1] = v.y;
+      f[i + 2] = v.z;
+      f[i + 3] = v.w;
+    }
+  }
+  static __device__ __forceinline__ float cvt(float v) { return v; }
+};
+template <>
+struct KVIO<f16_t> {
+  template <int N>
+  static __device__ __forceinline__ void load(const f16_t* p, float* f) {
+    if constexpr (N == 8) {
+      const f16x8_t v = *reinterpret_cast<const f16x8_t*>(p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
+        const h4 v = *reinterpret_cast<const h4*>(p + i);
+        f[i] = (float)v[0];
+        f[i + 1] = (float)v[1];
+        f[i + 2] = (float)v[2];
+        f[i + 3] = (float)v[3];
+      }
+    }
+  }
+  static __device__ __forceinline__ f16_t cvt(float v) { return (f16_t)v; }
+};
+
+// ---------------------------------------------------------------------------
+// QK-norm + RoPE + append.  grid (rows, n_heads + 2 n_kv), one wave per head.
+// Lane i < hd/2 holds the NEOX pair (x_i, x_{i+hd/2}).
+
+template <int HD, typename KVT>
+__global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
+  constexpr int HALF = HD / 2;
+  const int t = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int nq = a.n_heads, nkv = a.n_kv_heads;
+  float* row = a.qkv + (size_t)t * a.ldqkv;
+  const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
+  int kind, kvh = 0;
+  float* x;
+  const float* g = nullptr;
+  if (hh < nq) {
+    kind = 0;
+    x = row + hh * HD;
+    g = a.g_q;
+  } else if (hh < nq + nkv) {
+    kind = 1;
+    kvh = hh - nq;
+    x = row + (nq + kvh) * HD;
+    g = a.g_k;
+  } else {
+    kind = 2;
+    kvh = hh - nq - nkv;
+    x = row + (nq + nkv + kvh) * HD;
+  }
+  const bool act = lane < HALF;
+  float x1 = act ? x[lane] : 0.f;
+  float x2 = act ? x[lane + HALF] : 0.f;
+  if (kind < 2) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float inv = rsqrtf(ss / (float)HD + a.eps);
+    if (act) {
+      x1 = x1 * inv * g[lane];
+      x2 = x2 * inv * g[lane + HALF];
+      const float2 cs = a.rope[(size_t)pos * HALF + lane];
+      const float y1 = x1 * cs.x - x2 * cs.y;
+      const float y2 = x2 * cs.x + x1 * cs.y;
+      x1 = y1;
+      x2 = y2;
+    }
+  }
+  if (!act) return;
+  if (kind == 0) {
+    x[lane] = x1;
+    x[lane + HALF] = x2;
+  } else {
+    KVT* c = reinterpret_cast<KVT*>(kind == 1 ? a.kc : a.vc) +
+             ((size_t)(seq * nkv + kvh) * a.cap + pos) * HD;
+    c[lane] = KVIO<KVT>::cvt(x1);
+    c[lane + HALF] = KVIO<KVT>::cvt(x2);
+  }
+}
+
+void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st) {
+  const dim3 grid(a.rows.n, a.n_heads + 2 * a.n_kv_heads);
+  if (a.head_dim == 128) {
+    if (kv_f16) hipLaunchKernelGGL((k_qk_rope_append<128, f16_t>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((k_qk_rope_append<128, float>), grid, dim3(64), 0, st, a);
+  } else {
+    if (kv_f16) hipLaunchKernelGGL((k_qk_rope_append<64, f16_t>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((k_qk_rope_append<64, float>), grid, dim3(64), 0, st, a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV attention.  grid (n_splits, n_kv, rows), 256 threads.  A block owns
+// keys [c*kps, min((c+1)*kps, pos+1)) of KV head g for row t and serves all G
+// query heads of that group from one read of K and V (the group shares the KV
+// head).  Keys are walked in chunks of 64 with an online softmax.
+//   score phase: 16 lanes per key (hd/16 dims each), 16 keys per block pass
+//   value phase: 16 lanes per key row, 16 key slots, per-thread accumulators
+
+template <int HD, int G, typename KVT, int OUT>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
+  constexpr int DPL = HD / 16;
+  constexpr int KC = 64;
+  __shared__ float s_p[G][KC];
+  __shared__ float s_m[G], s_l[G], s_alpha[G];
+  __shared__ float s_red[16][HD];
+
+  const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq = a.n_heads, nkv = a.n_kv_heads;
+  const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
+  const int n_ctx = pos + 1;
+  const int k_begin = c * a.keys_per_split;
+  const int k_end = min(n_ctx, k_begin + a.keys_per_split);
+
+  if (k_begin >= k_end) {  // this split lies past the row's context
+    if (OUT == ATT_PARTIAL && tid < G) {
+      float* ml = a.part_ml + ((size_t)(t * nq + g * G + tid) * a.n_splits + c) * 2;
+      ml[0] = -INFINITY;
+      ml[1] = 0.f;
+    }
+    return;
+  }
+
+  const size_t head_off = (size_t)(seq * nkv + g) * a.cap * HD;
+  const KVT* Kp = reinterpret_cast<const KVT*>(a.kc) + head_off;
+  const KVT* Vp = reinterpret_cast<const KVT*>(a.vc) + head_off;
+
+  // score-phase lane roles
+  const int sub = lane & 15;  // dims sub*DPL .. +DPL
+  const int kq = lane >> 4;   // key within the wave's group of 4
+  float qr[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qp = a.q + (size_t)t * a.ldq + (size_t)(g * G + h) * HD + sub * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qr[h][e] = qp[e] * a.scale;
+  }
+  // value-phase roles
+  const int vs = tid >> 4;  // key slot 0..15
+  const int vd = tid & 15;  // dims vd*DPL .. +DPL
+  float acc[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+  if (tid < G) {
+    s_m[tid] = -INFINITY;
+    s_l[tid] = 0.f;
+  }
+
+  for (int kb = k_begin; kb < k_end; kb += KC) {
+    // scores
+#pragma unroll
+    for (int p = 0; p < KC / 16; ++p) {
+      const int jl = p * 16 + wave * 4 + kq;
+      const int j = kb + jl;
+      float kf[DPL];
+      const bool ok = j < k_end;
+      if (ok) KVIO<KVT>::template load<DPL>(Kp + (size_t)j * HD + sub * DPL, kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+        if (ok) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) d = fmaf(qr[h][e], kf[e], d);
+        }
+        d = group_sum<16>(d);
+        if (sub == 0) s_p[h][jl] = ok ? d : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // softmax bookkeeping, one wave per head
+    for (int h = wave; h < G; h += 4) {
+      const float s = s_p[h][lane];
+      const float mold = s_m[h];
+      const float mnew = fmaxf(mold, wave_max(s));
+      const float pv = (s == -INFINITY) ? 0.f : __expf(s - mnew);
+      s_p[h][lane] = pv;
+      const float ps = wave_sum(pv);
+      if (lane == 0) {
+        const float alpha = (mold == -INFINITY) ? 0.f : __expf(mold - mnew);
+        s_alpha[h] = alpha;
+        s_l[h] = s_l[h] * alpha + ps;
+        s_m[h] = mnew;
+      }
+    }
+    __syncthreads();
+    // values
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = s_alpha[h];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
+    }
+#pragma unroll
+    for (int r = 0; r < KC / 16; ++r) {
+      const int jl = r * 16 + vs;
+      const int j = kb + jl;
+      if (j < k_end) {
+        float vf[DPL];
+        KVIO<KVT>::template load<DPL>(Vp + (size_t)j * HD + vd * DPL, vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pv = s_p[h][jl];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // reduce the 16 key slots and write
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s_red[vs][vd * DPL + e] = acc[h][e];
+    __syncthreads();
+    if (tid < HD) {
+      float o = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o += s_red[i][tid];
+      const int qh = g * G + h;
+      if (OUT == ATT_PARTIAL) {
+        const size_t base = (size_t)(t * nq + qh) * a.n_splits + c;
+        a.part_o[base * HD + tid] = o;
+        if (tid == 0) {
+          a.part_ml[base * 2] = s_m[h];
+          a.part_ml[base * 2 + 1] = s_l[h];
+        }
+      } else {
+        const float v = o / s_l[h];
+        const size_t oi = (size_t)t * a.ldo + (size_t)qh * HD + tid;
+        if (OUT == ATT_F32) reinterpret_cast<float*>(a.out)[oi] = v;
+        else reinterpret_cast<bf16_t*>(a.out)[oi] = (bf16_t)f32_to_bf16(v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// grid (n_heads, rows), hd threads: combine the splits' (m, l, o)
+__global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
+  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
+  const int ns = a.n_splits, HD = a.head_dim;
+  const size_t base = (size_t)(t * a.n_heads + h) * ns;
+  const float* ml = a.part_ml + base * 2;
+  float M = -INFINITY;
+  for (int c = 0; c < ns; ++c) M = fmaxf(M, ml[2 * c]);
+  float L = 0.f, o = 0.f;
+  for (int c = 0; c < ns; ++c) {
+    const float l = ml[2 * c + 1];
+    if (l > 0.f) {
+      const float w = __expf(ml[2 * c] - M);
+      L = fmaf(w, l, L);
+      o = fmaf(w, a.part_o[(base + c) * HD + d], o);
+    }
+  }
+  reinterpret_cast<float*>(a.out)[(size_t)t * a.ldo + (size_t)h * HD + d] = o / L;
+}
+
+template <int HD, typename KVT, int OUT>
+static void launch_g(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.n_splits, a.n_kv_heads, a.rows.n);
+  switch (a.n_heads / a.n_kv_heads) {
+    case 1: hipLaunchKernelGGL((k_attn_decode<HD, 1, KVT, OUT>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_decode<HD, 2, KVT, OUT>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_decode<HD, 4, KVT, OUT>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_attn_decode<HD, 8, KVT, OUT>), grid, dim3(256), 0, st, a); break;
+  }
+}
+
+template <int HD, typename KVT>
+static void launch_o(AttnOut mode, const AttnArgs& a, hipStream_t st) {
+  if (mode == ATT_PARTIAL) launch_g<HD, KVT, ATT_PARTIAL>(a, st);
+  else if (mode == ATT_F32) launch_g<HD, KVT, ATT_F32>(a, st);
+  else launch_g<HD, KVT, ATT_BF16>(a, st);
+}
+
+void launch_attn_decode(bool kv_f16, AttnOut mode, AttnArgs a, hipStream_t st) {
+  if (a.head_dim == 128) {
+    if (kv_f16) launch_o<128, f16_t>(mode, a, st);
+    else launch_o<128, float>(mode, a, st);
+  } else {
+    if (kv_f16) launch_o<64, f16_t>(mode, a, st);
+    else launch_o<64, float>(mode, a, st);
+  }
+}
+
+void launch_attn_merge(AttnArgs a, hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_merge, dim3(a.n_heads, a.rows.n), dim3(a.head_dim), 0, st, a);
+}
+
+// ---------------------------------------------------------------------------
+// small helpers
+
+__global__ void k_rope_table(float2* tab, int cap, int half, int hd, double theta) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)cap * half) return;
+  const int pos = (int)(idx / half), i = (int)(idx % half);
+  const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+  const double ang = (double)pos * inv;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+void launch_rope_table(float2* tab, int cap, int head_dim, double theta, hipStream_t st) {
+  const int half = head_dim / 2;
+  const size_t n = (size_t)cap * half;
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, cap,
+                     half, head_dim, theta);
+}
+
+template <typename KVT>
+__global__ void k_kv_to_f32(const KVT* src, int cap, int len, int hd, float* dst) {
+  const int t = blockIdx.x, h = blockIdx.y;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x)
+    dst[((size_t)h * len + t) * hd + d] = (float)src[((size_t)h * cap + t) * hd + d];
+}
+
+void launch_kv_to_f32(bool kv_f16, const void* src, int n_kv, int cap, int len, int hd, float* dst,
+                      hipStream_t st) {
+  if (len <= 0) return;
+  const dim3 grid(len, n_kv);
+  if (kv_f16)
+    hipLaunchKernelGGL(k_kv_to_f32<f16_t>, grid, dim3(128), 0, st,
+                       reinterpret_cast<const f16_t*>(src), cap, len, hd, dst);
+  else
+    hipLaunchKernelGGL(k_kv_to_f32<float>, grid, dim3(128), 0, st,
+                       reinterpret_cast<const float*>(src), cap, len, hd, dst);
+}
+
+}  // namespace qtalk

@@ -1,0 +1,236 @@
+// Prefill projections on the matrix cores: C[M][N] = A[M][K] * B[N][K]^T with
+// A the (normalised) activations in bf16 and B a weight matrix stored
+// [out][in] in bf16, float32 accumulation ("transcribe.cpp
+// src/causal_lm/causal_lm.cpp", mul_mat_f32acc).  Both operands are
+// K-contiguous, so every lane feeds v_mfma_f32_16x16x32_bf16 with one 16-byte
+// LDS read per operand.
+//
+// Tiles: BM x 128 per 256-thread block (4 waves as 2 x 2, each BM/2 x 64),
+// BK = 64, rows padded to 72 elements in LDS.  Global loads for the next K
+// tile are issued before the MFMAs of the current one.  Small-M shapes split
+// K over blockIdx.z into a float32 workspace that a second kernel sums in a
+// fixed order (deterministic), applying the epilogue there.
+#include "kernels.h"
+
+namespace qtalk {
+
+constexpr int GB_N = 128;
+constexpr int GB_K = 64;
+constexpr int G_STRIDE = GB_K + 8;  // bf16 elements per LDS row
+
+template <int BM, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) {
+  constexpr int BN = GB_N;
+  constexpr int TM = BM / 32;  // 16-row MFMA tiles per wave (M)
+  constexpr int TN = BN / 32;  // 16-col MFMA tiles per wave (N)
+  constexpr int AR = BM / 32;  // 16-byte A chunks per thread per K tile
+  constexpr int BR = BN / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t As[BM * G_STRIDE];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * G_STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int nkt = k_per_split / GB_K;
+  const int M = a.M, K = a.K;
+
+  // global -> register staging roles
+  const int lrow = tid >> 3, lchunk = (tid & 7) * 8;
+  const bf16_t* Ag[AR];
+  const bf16_t* Bg[BR];
+#pragma unroll
+  for (int i = 0; i < AR; ++i) {
+    int r = m0 + lrow + 32 * i;
+    r = r < M ? r : M - 1;
+    Ag[i] = a.A + (size_t)r * a.lda + kbeg + lchunk;
+  }
+#pragma unroll
+  for (int i = 0; i < BR; ++i) Bg[i] = a.B + (size_t)(n0 + lrow + 32 * i) * K + kbeg + lchunk;
+
+  uint4 ra[AR], rb[BR];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < AR; ++i) ra[i] = *reinterpret_cast<const uint4*>(Ag[i] + kt * GB_K);
+#pragma unroll
+    for (int i = 0; i < BR; ++i)
+      rb[i] = ld_stream16(Bg[i] + kt * GB_K);
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < AR; ++i)
+      *reinterpret_cast<uint4*>(&As[(lrow + 32 * i) * G_STRIDE + lchunk]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BR; ++i)
+      *reinterpret_cast<uint4*>(&Bs[(lrow + 32 * i) * G_STRIDE + lchunk]) = rb[i];
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < GB_K; ks += 32) {
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(
+            &As[(wm * (BM / 2) + i * 16 + fr) * G_STRIDE + ks + fk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+            &Bs[(wn * (BN / 2) + j * 16 + fr) * G_STRIDE + ks + fk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      lstore();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds C[rbase + r][cbase + (lane & 15)], r = 0..3
+  const int rq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int rbase = m0 + wm * (BM / 2) + i * 16 + rq;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * (BN / 2) + j * 16 + fr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rbase + r;
+        if (row >= M) continue;
+        const float v = acc[i][j][r];
+        if (SPLIT) {
+          a.work[((size_t)blockIdx.z * M + row) * a.N + col] = v;
+        } else if (EPI == EPI_STORE) {
+          reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = v;
+        } else if (EPI == EPI_ADD) {
+          reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] += v;
+        } else if ((j & 1) == 0) {  // SwiGLU: tile j = gate block, j+1 = up block
+          const float u = acc[i][j + 1 < TN ? j + 1 : j][r];
+          const int oc = (n0 + wn * (BN / 2) + j * 16) / 2 + fr;
+          reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + oc] =
+              (bf16_t)f32_to_bf16(silu_f(v) * u);
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a, int ks) {
+  const size_t MN = (size_t)a.M * a.N;
+  const size_t n_out = (EPI == EPI_SWIGLU) ? MN / 2 : MN;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_out;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    if (EPI == EPI_SWIGLU) {
+      const int half = a.N / 2;
+      const int row = (int)(idx / half), r = (int)(idx % half);
+      const size_t p = (size_t)row * a.N + (size_t)(r >> 4) * 32 + (r & 15);
+      float gsum = 0.f, usum = 0.f;
+      for (int z = 0; z < ks; ++z) {
+        gsum += a.work[z * MN + p];
+        usum += a.work[z * MN + p + 16];
+      }
+      reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + r] =
+          (bf16_t)f32_to_bf16(silu_f(gsum) * usum);
+    } else {
+      const int row = (int)(idx / a.N), col = (int)(idx % a.N);
+      float s = 0.f;
+      for (int z = 0; z < ks; ++z) s += a.work[z * MN + idx];
+      float* c = reinterpret_cast<float*>(a.C) + (size_t)row * a.ldc + col;
+      if (EPI == EPI_ADD) *c += s;
+      else *c = s;
+    }
+  }
+}
+
+bool gemm_shape_ok(int M, int N, int K) {
+  return M >= 1 && N % GB_N == 0 && K % GB_K == 0;
+}
+
+template <int BM, int EPI>
+static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
+  const dim3 grid(a.N / GB_N, (a.M + BM - 1) / BM, ks);
+  const int kps = a.K / ks;
+  if (ks == 1) {
+    hipLaunchKernelGGL((k_gemm_bf16<BM, EPI, false>), grid, dim3(256), 0, st, a, kps);
+  } else {
+    hipLaunchKernelGGL((k_gemm_bf16<BM, EPI, true>), grid, dim3(256), 0, st, a, kps);
+    const size_t n_out = (size_t)a.M * a.N / (EPI == EPI_SWIGLU ? 2 : 1);
+    const unsigned blocks = (unsigned)((n_out + 255) / 256 < 4096 ? (n_out + 255) / 256 : 4096);
+    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3(blocks), dim3(256), 0, st, a, ks);
+  }
+}
+
+void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
+  const int BM = a.M > 64 ? 128 : 64;
+  const int tiles = (a.N / GB_N) * ((a.M + BM - 1) / BM);
+  const int nkt = a.K / GB_K;
+  int ks = 1;
+  // split K while the grid is short of the 256 CUs and each split keeps >= 4
+  // K tiles; ks divides the K tile count
+  while (tiles * ks < 256 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 &&
+         (size_t)(ks * 2) * a.M * a.N <= a.work_elems)
+    ks *= 2;
+  if (BM == 128) {
+    switch (epi) {
+      case EPI_STORE: launch_bm<128, EPI_STORE>(a, ks, st); break;
+      case EPI_ADD: launch_bm<128, EPI_ADD>(a, ks, st); break;
+      case EPI_SWIGLU: launch_bm<128, EPI_SWIGLU>(a, ks, st); break;
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE: launch_bm<64, EPI_STORE>(a, ks, st); break;
+      case EPI_ADD: launch_bm<64, EPI_ADD>(a, ks, st); break;
+      case EPI_SWIGLU: launch_bm<64, EPI_SWIGLU>(a, ks, st); break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm to bf16 rows (the A operand of the next projection)
+
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* x, int ldx, int K,
+                                                      const float* g, float eps, bf16_t* out,
+                                                      int ldo) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)t * ldx;
+  float ss = 0.f;
+  for (int k = tid * 4; k < K; k += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + k);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum<256>(ss, red);
+  const float inv = rsqrtf(ss / (float)K + eps);
+  for (int k = tid * 4; k < K; k += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + k);
+    const float4 gg = *reinterpret_cast<const float4*>(g + k);
+    uint2 o;
+    o.x = f32_to_bf16(v.x * inv * gg.x) | (f32_to_bf16(v.y * inv * gg.y) << 16);
+    o.y = f32_to_bf16(v.z * inv * gg.z) | (f32_to_bf16(v.w * inv * gg.w) << 16);
+    *reinterpret_cast<uint2*>(out + (size_t)t * ldo + k) = o;
+  }
+}
+
+void launch_rmsnorm_bf16(const float* x, int ldx, int T, int K, const float* g, float eps,
+                         bf16_t* out, int ldo, hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(T), dim3(256), 0, st, x, ldx, K, g, eps, out, ldo);
+}
+
+}  // namespace qtalk

@@ -1,0 +1,122 @@
+// Host-side launchers of the Talker kernels (internal to the library).
+#pragma once
+
+#include "common.h"
+
+namespace qtalk {
+
+enum Epilogue { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+
+// y[n][o] (=|+=) sum_k W[o][k] * xn[n][k], xn = RMSNorm(x[n]) * gain when
+// `gain` is set (else xn = x).  EPI_SWIGLU reads W as gate|up rows
+// interleaved in blocks of 16 (see pack order in the runtime) and writes
+// silu(gate) * up for O logical rows.  norm_out (nullable) receives xn.
+struct GemvArgs {
+  const void* W;
+  int O;
+  int K;
+  const float* X;
+  int ldx;
+  int nrows;
+  const float* gain;
+  float eps;
+  float* Y;
+  int ldy;
+  float* norm_out;
+  int ld_norm;
+};
+void launch_gemv(bool w_bf16, Epilogue epi, GemvArgs a, hipStream_t st);
+
+// QK RMSNorm + NEOX RoPE on q (in place) and k, then K/V append into the cache.
+struct QkArgs {
+  float* qkv;
+  int ldqkv;
+  int n_heads, n_kv_heads, head_dim;
+  const float* g_q;
+  const float* g_k;
+  float eps;
+  const float2* rope;  // [cap][head_dim/2] (cos, sin)
+  void* kc;
+  void* vc;  // cache base of this layer: [S][n_kv][cap][hd]
+  int cap;
+  RowMeta rows;
+};
+void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st);
+
+// Causal GQA attention of the listed rows over the cache (split over keys).
+enum AttnOut { ATT_PARTIAL = 0, ATT_F32 = 1, ATT_BF16 = 2 };
+struct AttnArgs {
+  const float* q;  // q of row t, head h at q + t*ldq + h*hd
+  int ldq;
+  const void* kc;
+  const void* vc;  // [S][n_kv][cap][hd] of this layer
+  int n_heads, n_kv_heads, head_dim, cap;
+  float scale;
+  int keys_per_split;
+  int n_splits;
+  float* part_o;   // [rows][n_heads][n_splits][hd]
+  float* part_ml;  // [rows][n_heads][n_splits][2]
+  void* out;       // final output row t at out + t*ldo (f32 or bf16)
+  int ldo;
+  RowMeta rows;
+};
+void launch_attn_decode(bool kv_f16, AttnOut mode, AttnArgs a, hipStream_t st);
+void launch_attn_merge(AttnArgs a, hipStream_t st);
+
+// C = A[M][K] (bf16) * B[N][K]^T (bf16) on MFMA, float32 accumulation.
+struct GemmArgs {
+  const bf16_t* A;
+  int lda;
+  const bf16_t* B;
+  int M, N, K;
+  void* C;  // f32 [M][ldc] for STORE/ADD; bf16 [M][ldc] for SWIGLU
+  int ldc;
+  float* work;  // split-K partials [ksplit][M][N]
+  size_t work_elems;
+};
+void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
+bool gemm_shape_ok(int M, int N, int K);
+
+// out[t][k] = bf16(RMSNorm(x[t]) * g)
+void launch_rmsnorm_bf16(const float* x, int ldx, int T, int K, const float* g,
+                         float eps, bf16_t* out, int ldo, hipStream_t st);
+
+// cos/sin table [cap][half], angle pos * theta^(-2i/hd), float64 math
+void launch_rope_table(float2* tab, int cap, int head_dim, double theta,
+                       hipStream_t st);
+
+// dst[h][t][d] = float(cache[h][t][d]) for t < len
+void launch_kv_to_f32(bool kv_f16, const void* src, int n_kv, int cap, int len,
+                      int hd, float* dst, hipStream_t st);
+
+// Batch-1 decode of the whole stack in one persistent launch (Talker
+// geometry, bf16 weights, f16 cache).  See k_decode_fused.hip.
+struct FusedDecodeArgs {
+  const bf16_t* w;  // layer l at w + l * layer_stride: [Wqkv | Wo | Wgu | Wd]
+  size_t layer_stride;
+  const float* norms;  // layer l at norms + l * norm_stride: g_in, g_post, g_q, g_k
+  size_t norm_stride;
+  const bf16_t* head;
+  const float* g_final;
+  f16_t* kc;
+  f16_t* vc;  // [L][S][NKV][cap][HD]
+  size_t layer_kv_elems;
+  int cap, seq, pos, n_layers;
+  float eps;
+  const float2* rope;
+  const float* emb;
+  float* logits;
+  float* hidden_out;
+  uint64_t* ll;    // [n_layers + 1][words per layer] exchange words
+  uint64_t* part;  // [n_layers][NKV][NCH][G][HD + 2] chunk partials, as words
+  int* err;
+  uint32_t epoch;
+};
+bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
+                            int n_kv_heads, int head_dim);
+bool fused_decode_fits();
+size_t fused_decode_ll_words(int n_layers);
+size_t fused_decode_part_words(int n_layers);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st);
+
+}  // namespace qtalk

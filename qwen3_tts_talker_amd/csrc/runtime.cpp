@@ -1,0 +1,573 @@
+// Host runtime of the C ABI in include/qtalk.h: weight repack, KV cache and
+// scratch ownership, argument validation and the per-layer launch sequence.
+//
+// Forward order per layer ("qwentts.cpp src/talker-forward.h",
+// talker_layer_forward): input RMSNorm -> QKV projection -> QK-norm + RoPE +
+// K/V append -> causal GQA attention over the cache -> o_proj + residual ->
+// post-attention RMSNorm -> gate|up projection + SwiGLU -> down + residual.
+// After the stack: final RMSNorm + codec_head on the last row
+// (talker_forward_core), or on every row of a batched decode
+// (talker_forward_decode).
+//
+// Two launch paths compute the same thing:
+//  - matrix-vector path (decode, short or float32 prefill): activations stay
+//    float32, weights are upcast in the kernels;
+//  - matrix-core path (bf16 prefill longer than 16 rows): activations are
+//    rounded to bf16 as the A operand of MFMA GEMMs, accumulation is float32.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/qtalk.h"
+#include "kernels.h"
+
+using namespace qtalk;
+
+namespace {
+
+constexpr int GEMV_ROWS = MAX_ROWS;  // rows per matrix-vector pass
+constexpr int MFMA_MIN_ROWS = 17;    // prefill rows that switch to the matrix cores
+constexpr int MAX_SPLITS = 128;      // key splits of the decode attention
+constexpr int MAX_CHUNK = 2048;      // rows per matrix-core pass
+constexpr size_t WORK_ELEMS = (size_t)4 << 20;  // split-K workspace (floats)
+
+struct LayerDev {
+  void* wqkv;  // [q_dim + 2 kv_dim][H]: q rows, then k rows, then v rows
+  void* wo;    // [H][q_dim]
+  void* wgu;   // [2 I][H]: 16 gate rows, 16 up rows, repeated
+  void* wd;    // [H][I]
+  float *g_in, *g_post, *g_q, *g_k;
+};
+
+}  // namespace
+
+struct qtalk_ctx {
+  qtalk_config cfg{};
+  hipStream_t stream = nullptr;
+  bool w_bf16 = true, kv_f16 = true;
+  size_t welem = 2;
+  int q_dim = 0, kv_dim = 0, qkv_dim = 0;
+  std::vector<LayerDev> layers;
+  void* wblob = nullptr;
+  float* nblob = nullptr;
+  void* head = nullptr;
+  float* g_final = nullptr;
+  void *kc = nullptr, *vc = nullptr;
+  size_t layer_kv_elems = 0;  // elements of one layer's cache (all sequences)
+  float2* rope = nullptr;
+  std::vector<int32_t> cur_len;
+  int tc = 0;  // rows per matrix-core pass
+  float *x = nullptr, *qkv = nullptr, *att = nullptr, *act = nullptr;
+  bf16_t* hn = nullptr;
+  float *part_o = nullptr, *part_ml = nullptr;
+  float* work = nullptr;
+  // persistent batch-1 decode (Talker geometry only)
+  bool fused = false;
+  uint64_t* ll = nullptr;
+  uint64_t* fpart = nullptr;
+  int* ferr = nullptr;
+  uint32_t epoch = 0;
+  size_t per_layer = 0, norms_per_layer = 0;
+  std::string err;
+};
+
+namespace {
+
+qtalk_status fail(qtalk_ctx* c, qtalk_status s, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return s;
+}
+
+bool dev_alloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  return hipMalloc(p, bytes) == hipSuccess;
+}
+
+void free_all(qtalk_ctx* c) {
+  void* ptrs[] = {c->wblob, c->nblob, c->head, c->kc,     c->vc,    c->rope,   c->x,
+                  c->qkv,   c->att,   c->act,  c->hn,     c->part_o, c->part_ml, c->work,
+                  c->ll,    c->fpart, c->ferr};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+}
+
+const char* check_config(const qtalk_config* g) {
+  if (g->n_layers < 1 || g->hidden < 1 || g->n_heads < 1 || g->n_kv_heads < 1 ||
+      g->intermediate < 1 || g->vocab < 1 || g->max_seq_len < 1 || g->max_seqs < 1)
+    return "every size must be >= 1";
+  if (g->head_dim != 64 && g->head_dim != 128) return "head_dim must be 64 or 128";
+  if (g->n_heads % g->n_kv_heads) return "n_heads must be a multiple of n_kv_heads";
+  const int G = g->n_heads / g->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return "n_heads / n_kv_heads must be 1, 2, 4 or 8";
+  if (g->hidden % 64 || g->intermediate % 64 || (g->n_heads * g->head_dim) % 64)
+    return "hidden, intermediate and n_heads*head_dim must be multiples of 64";
+  if (!(g->rms_eps >= 0.f) || !(g->rope_theta > 0.f)) return "bad rms_eps or rope_theta";
+  if (g->weight_dtype != QTALK_F32 && g->weight_dtype != QTALK_BF16)
+    return "weight_dtype must be F32 or BF16";
+  if (g->kv_dtype != QTALK_F32 && g->kv_dtype != QTALK_F16) return "kv_dtype must be F32 or F16";
+  return nullptr;
+}
+
+// ---------------------------------------------------------------------------
+
+struct Fwd {
+  qtalk_ctx* c;
+  hipStream_t st;
+  const qtalk_config& g;
+  explicit Fwd(qtalk_ctx* cc) : c(cc), st(cc->stream), g(cc->cfg) {}
+
+  char* kv_layer(void* base, int l) const {
+    return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_elems * (c->kv_f16 ? 2 : 4);
+  }
+
+  void qk_append(int l, const RowMeta& rows) {
+    QkArgs q{};
+    q.qkv = c->qkv;
+    q.ldqkv = c->qkv_dim;
+    q.n_heads = g.n_heads;
+    q.n_kv_heads = g.n_kv_heads;
+    q.head_dim = g.head_dim;
+    q.g_q = c->layers[l].g_q;
+    q.g_k = c->layers[l].g_k;
+    q.eps = g.rms_eps;
+    q.rope = c->rope;
+    q.kc = kv_layer(c->kc, l);
+    q.vc = kv_layer(c->vc, l);
+    q.cap = g.max_seq_len;
+    q.rows = rows;
+    launch_qk_rope_append(c->kv_f16, q, st);
+  }
+
+  AttnArgs attn_args(int l, const RowMeta& rows) const {
+    AttnArgs a{};
+    a.q = c->qkv;
+    a.ldq = c->qkv_dim;
+    a.kc = kv_layer(c->kc, l);
+    a.vc = kv_layer(c->vc, l);
+    a.n_heads = g.n_heads;
+    a.n_kv_heads = g.n_kv_heads;
+    a.head_dim = g.head_dim;
+    a.cap = g.max_seq_len;
+    a.scale = 1.0f / sqrtf((float)g.head_dim);
+    a.part_o = c->part_o;
+    a.part_ml = c->part_ml;
+    a.out = c->att;
+    a.ldo = c->q_dim;
+    a.rows = rows;
+    return a;
+  }
+
+  static int max_ctx(const RowMeta& r) {
+    if (r.uniform) return r.p0 + r.n;
+    int m = 0;
+    for (int i = 0; i < r.n; ++i) m = std::max(m, r.pos[i] + 1);
+    return m;
+  }
+
+  void gemv(const void* W, int O, int K, const float* X, int ldx, int n, const float* gain,
+            float* Y, int ldy, Epilogue epi, float* norm_out = nullptr, int ld_norm = 0) {
+    GemvArgs a{W, O, K, X, ldx, n, gain, g.rms_eps, Y, ldy, norm_out, ld_norm};
+    launch_gemv(c->w_bf16, epi, a, st);
+  }
+
+  // matrix-vector layer on rows.n <= GEMV_ROWS rows held in c->x
+  void layer_gemv(int l, const RowMeta& rows) {
+    const LayerDev& L = c->layers[l];
+    const int n = rows.n, H = g.hidden;
+    gemv(L.wqkv, c->qkv_dim, H, c->x, H, n, L.g_in, c->qkv, c->qkv_dim, EPI_STORE);
+    qk_append(l, rows);
+    AttnArgs a = attn_args(l, rows);
+    const int ctx = max_ctx(rows);
+    a.keys_per_split = 64 * ((ctx + 64 * MAX_SPLITS - 1) / (64 * MAX_SPLITS));
+    a.n_splits = (ctx + a.keys_per_split - 1) / a.keys_per_split;
+    launch_attn_decode(c->kv_f16, ATT_PARTIAL, a, st);
+    launch_attn_merge(a, st);
+    gemv(L.wo, H, c->q_dim, c->att, c->q_dim, n, nullptr, c->x, H, EPI_ADD);
+    gemv(L.wgu, g.intermediate, H, c->x, H, n, L.g_post, c->act, g.intermediate, EPI_SWIGLU);
+    gemv(L.wd, H, g.intermediate, c->act, g.intermediate, n, nullptr, c->x, H, EPI_ADD);
+  }
+
+  void gemm(const bf16_t* A, int lda, const void* B, int M, int N, int K, void* C, int ldc,
+            Epilogue epi) {
+    GemmArgs a{A, lda, reinterpret_cast<const bf16_t*>(B), M, N, K, C, ldc, c->work, WORK_ELEMS};
+    launch_gemm(epi, a, st);
+  }
+
+  // matrix-core layer on rows.n <= c->tc uniform rows held in c->x
+  void layer_mfma(int l, const RowMeta& rows) {
+    const LayerDev& L = c->layers[l];
+    const int T = rows.n, H = g.hidden, I = g.intermediate;
+    bf16_t* att_b = reinterpret_cast<bf16_t*>(c->att);
+    bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
+    launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
+    gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
+    qk_append(l, rows);
+    AttnArgs a = attn_args(l, rows);
+    a.keys_per_split = max_ctx(rows);
+    a.n_splits = 1;
+    launch_attn_decode(c->kv_f16, ATT_BF16, a, st);
+    gemm(att_b, c->q_dim, L.wo, T, H, c->q_dim, c->x, H, EPI_ADD);
+    launch_rmsnorm_bf16(c->x, H, T, H, L.g_post, g.rms_eps, c->hn, H, st);
+    gemm(c->hn, H, L.wgu, T, 2 * I, H, act_b, I, EPI_SWIGLU);
+    gemm(act_b, I, L.wd, T, H, I, c->x, H, EPI_ADD);
+  }
+
+  void head(const float* X, int n, float* logits, float* hidden_out) {
+    gemv(c->head, g.vocab, g.hidden, X, g.hidden, n, c->g_final, logits, g.vocab, EPI_STORE,
+         hidden_out, g.hidden);
+  }
+
+  // rows of one sequence at positions p0 .. p0+T-1 (prefill / extend)
+  void run_sequence(int seq, int p0, const float* emb, int T, float* logits, float* hidden_out) {
+    const bool mfma = c->w_bf16 && T >= MFMA_MIN_ROWS &&
+                      gemm_shape_ok(1, c->qkv_dim, g.hidden) && gemm_shape_ok(1, g.hidden, c->q_dim) &&
+                      gemm_shape_ok(1, 2 * g.intermediate, g.hidden) &&
+                      gemm_shape_ok(1, g.hidden, g.intermediate) && g.intermediate % 16 == 0;
+    const int chunk = mfma ? c->tc : GEMV_ROWS;
+    int done = 0;
+    while (done < T) {
+      const int n = std::min(chunk, T - done);
+      RowMeta rows{};
+      rows.n = n;
+      rows.uniform = 1;
+      rows.seq0 = seq;
+      rows.p0 = p0 + done;
+      (void)hipMemcpyAsync(c->x, emb + (size_t)done * g.hidden, (size_t)n * g.hidden * 4,
+                           hipMemcpyDeviceToDevice, st);
+      for (int l = 0; l < g.n_layers; ++l) {
+        if (mfma && n >= MFMA_MIN_ROWS) layer_mfma(l, rows);
+        else layer_gemv(l, rows);
+      }
+      done += n;
+      if (done == T) head(c->x + (size_t)(n - 1) * g.hidden, 1, logits, hidden_out);
+    }
+  }
+
+  // batch-1 decode as one persistent launch
+  qtalk_status run_fused(int seq, const float* emb, float* logits, float* hidden_out) {
+    FusedDecodeArgs a{};
+    a.w = reinterpret_cast<const bf16_t*>(c->wblob);
+    a.layer_stride = c->per_layer;
+    a.norms = c->nblob;
+    a.norm_stride = c->norms_per_layer;
+    a.head = reinterpret_cast<const bf16_t*>(c->head);
+    a.g_final = c->g_final;
+    a.kc = reinterpret_cast<f16_t*>(c->kc);
+    a.vc = reinterpret_cast<f16_t*>(c->vc);
+    a.layer_kv_elems = c->layer_kv_elems;
+    a.cap = g.max_seq_len;
+    a.seq = seq;
+    a.pos = c->cur_len[seq];
+    a.n_layers = g.n_layers;
+    a.eps = g.rms_eps;
+    a.rope = c->rope;
+    a.emb = emb;
+    a.logits = logits;
+    a.hidden_out = hidden_out;
+    a.ll = c->ll;
+    a.part = c->fpart;
+    a.err = c->ferr;
+    a.epoch = c->epoch + 1;
+    const hipError_t e = launch_decode_fused(a, st);
+    if (e != hipSuccess)
+      return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
+    c->epoch += 1;
+    return QTALK_OK;
+  }
+
+  // one row per listed sequence (batched decode)
+  void run_batch(const int32_t* seqs, int n, const float* emb, float* logits, float* hidden_out) {
+    for (int b0 = 0; b0 < n; b0 += GEMV_ROWS) {
+      const int nb = std::min(GEMV_ROWS, n - b0);
+      RowMeta rows{};
+      rows.n = nb;
+      rows.uniform = 0;
+      for (int i = 0; i < nb; ++i) {
+        rows.seq[i] = seqs[b0 + i];
+        rows.pos[i] = c->cur_len[seqs[b0 + i]];
+      }
+      (void)hipMemcpyAsync(c->x, emb + (size_t)b0 * g.hidden, (size_t)nb * g.hidden * 4,
+                           hipMemcpyDeviceToDevice, st);
+      for (int l = 0; l < g.n_layers; ++l) layer_gemv(l, rows);
+      head(c->x, nb, logits + (size_t)b0 * g.vocab,
+           hidden_out ? hidden_out + (size_t)b0 * g.hidden : nullptr);
+    }
+  }
+};
+
+qtalk_status launch_status(qtalk_ctx* c) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(c, QTALK_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  return QTALK_OK;
+}
+
+qtalk_status copy_in(void* dst, const void* src, size_t bytes) {
+  return hipMemcpy(dst, src, bytes, hipMemcpyDefault) == hipSuccess ? QTALK_OK : QTALK_E_DEVICE;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, void* hip_stream,
+                          qtalk_ctx** out) {
+  if (!out) return QTALK_E_INVAL;
+  *out = nullptr;
+  if (!config || !w || !w->layers || !w->final_norm || !w->codec_head) return QTALK_E_INVAL;
+  if (check_config(config)) return QTALK_E_INVAL;
+  const qtalk_config& g = *config;
+  for (int l = 0; l < g.n_layers; ++l) {
+    const qtalk_layer_weights& lw = w->layers[l];
+    if (!lw.q_proj || !lw.k_proj || !lw.v_proj || !lw.o_proj || !lw.gate_proj || !lw.up_proj ||
+        !lw.down_proj || !lw.input_norm || !lw.post_attn_norm || !lw.q_norm || !lw.k_norm)
+      return QTALK_E_INVAL;
+  }
+
+  qtalk_ctx* c = new qtalk_ctx();
+  c->cfg = g;
+  c->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  c->w_bf16 = g.weight_dtype == QTALK_BF16;
+  c->kv_f16 = g.kv_dtype == QTALK_F16;
+  c->welem = c->w_bf16 ? 2 : 4;
+  c->q_dim = g.n_heads * g.head_dim;
+  c->kv_dim = g.n_kv_heads * g.head_dim;
+  c->qkv_dim = c->q_dim + 2 * c->kv_dim;
+  const size_t H = g.hidden, I = g.intermediate, we = c->welem;
+  const size_t n_qkv = (size_t)c->qkv_dim * H, n_o = H * c->q_dim, n_gu = 2 * I * H, n_d = H * I;
+  const size_t per_layer = n_qkv + n_o + n_gu + n_d;
+  const size_t norms_per_layer = 2 * H + 2 * (size_t)g.head_dim;
+  c->layer_kv_elems = (size_t)g.max_seqs * g.n_kv_heads * g.max_seq_len * g.head_dim;
+  c->tc = std::min(g.max_seq_len, MAX_CHUNK);
+  const int part_rows = GEMV_ROWS;
+  const int rows = std::max(c->tc, GEMV_ROWS);
+  const size_t kvb = c->kv_f16 ? 2 : 4;
+
+  bool ok = dev_alloc(&c->wblob, per_layer * g.n_layers * we) &&
+            dev_alloc((void**)&c->nblob, (norms_per_layer * g.n_layers + H) * 4) &&
+            dev_alloc(&c->head, (size_t)g.vocab * H * we) &&
+            dev_alloc(&c->kc, c->layer_kv_elems * g.n_layers * kvb) &&
+            dev_alloc(&c->vc, c->layer_kv_elems * g.n_layers * kvb) &&
+            dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
+            dev_alloc((void**)&c->x, (size_t)rows * H * 4) &&
+            dev_alloc((void**)&c->qkv, (size_t)rows * c->qkv_dim * 4) &&
+            dev_alloc((void**)&c->att, (size_t)rows * c->q_dim * 4) &&
+            dev_alloc((void**)&c->act, (size_t)rows * I * 4) &&
+            dev_alloc((void**)&c->hn, (size_t)rows * H * 2) &&
+            dev_alloc((void**)&c->part_o, (size_t)part_rows * g.n_heads * MAX_SPLITS * g.head_dim * 4) &&
+            dev_alloc((void**)&c->part_ml, (size_t)part_rows * g.n_heads * MAX_SPLITS * 2 * 4) &&
+            dev_alloc((void**)&c->work, WORK_ELEMS * 4);
+  c->per_layer = per_layer;
+  c->norms_per_layer = norms_per_layer;
+  const char* env = getenv("QTALK_FUSED_DECODE");
+  c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') &&
+             fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
+                                    g.n_heads, g.n_kv_heads, g.head_dim) &&
+             fused_decode_fits();
+  if (c->fused) {
+    ok = dev_alloc((void**)&c->ll, fused_decode_ll_words(g.n_layers) * 8) &&
+         dev_alloc((void**)&c->fpart, fused_decode_part_words(g.n_layers) * 8) &&
+         dev_alloc((void**)&c->ferr, 4);
+  }
+  if (!ok) {
+    (void)hipGetLastError();
+    free_all(c);
+    delete c;
+    return QTALK_E_NOMEM;
+  }
+
+  qtalk_status s = QTALK_OK;
+  char* wb = reinterpret_cast<char*>(c->wblob);
+  c->layers.resize(g.n_layers);
+  for (int l = 0; l < g.n_layers && s == QTALK_OK; ++l) {
+    const qtalk_layer_weights& lw = w->layers[l];
+    LayerDev& L = c->layers[l];
+    char* base = wb + (size_t)l * per_layer * we;
+    L.wqkv = base;
+    L.wo = base + n_qkv * we;
+    L.wgu = base + (n_qkv + n_o) * we;
+    L.wd = base + (n_qkv + n_o + n_gu) * we;
+    float* nb = c->nblob + (size_t)l * norms_per_layer;
+    L.g_in = nb;
+    L.g_post = nb + H;
+    L.g_q = nb + 2 * H;
+    L.g_k = nb + 2 * H + g.head_dim;
+    char* qkv = reinterpret_cast<char*>(L.wqkv);
+    if (copy_in(qkv, lw.q_proj, (size_t)c->q_dim * H * we) ||
+        copy_in(qkv + (size_t)c->q_dim * H * we, lw.k_proj, (size_t)c->kv_dim * H * we) ||
+        copy_in(qkv + (size_t)(c->q_dim + c->kv_dim) * H * we, lw.v_proj, (size_t)c->kv_dim * H * we) ||
+        copy_in(L.wo, lw.o_proj, n_o * we) || copy_in(L.wd, lw.down_proj, n_d * we) ||
+        copy_in(L.g_in, lw.input_norm, H * 4) || copy_in(L.g_post, lw.post_attn_norm, H * 4) ||
+        copy_in(L.g_q, lw.q_norm, g.head_dim * 4) || copy_in(L.g_k, lw.k_norm, g.head_dim * 4))
+      s = QTALK_E_DEVICE;
+    // gate|up interleaved in blocks of 16 rows: [g0..g15, u0..u15, g16.., u16..]
+    const size_t blk = 16 * H * we;
+    if (s == QTALK_OK &&
+        (hipMemcpy2D(L.wgu, 2 * blk, lw.gate_proj, blk, blk, I / 16, hipMemcpyDefault) != hipSuccess ||
+         hipMemcpy2D(reinterpret_cast<char*>(L.wgu) + blk, 2 * blk, lw.up_proj, blk, blk, I / 16,
+                     hipMemcpyDefault) != hipSuccess))
+      s = QTALK_E_DEVICE;
+  }
+  c->g_final = c->nblob + (size_t)g.n_layers * norms_per_layer;
+  if (s == QTALK_OK && (copy_in(c->g_final, w->final_norm, H * 4) ||
+                        copy_in(c->head, w->codec_head, (size_t)g.vocab * H * we)))
+    s = QTALK_E_DEVICE;
+  if (s == QTALK_OK) {
+    const size_t kv_bytes = c->layer_kv_elems * g.n_layers * kvb;
+    if (hipMemsetAsync(c->kc, 0, kv_bytes, c->stream) != hipSuccess ||
+        hipMemsetAsync(c->vc, 0, kv_bytes, c->stream) != hipSuccess)
+      s = QTALK_E_DEVICE;
+    if (c->fused &&
+        (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, c->stream) != hipSuccess ||
+         hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, c->stream) != hipSuccess ||
+         hipMemsetAsync(c->ferr, 0, 4, c->stream) != hipSuccess))
+      s = QTALK_E_DEVICE;
+    launch_rope_table(c->rope, g.max_seq_len, g.head_dim, (double)g.rope_theta, c->stream);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess)
+      s = QTALK_E_DEVICE;
+  }
+  if (s != QTALK_OK) {
+    free_all(c);
+    delete c;
+    return s;
+  }
+  c->cur_len.assign(g.max_seqs, 0);
+  *out = c;
+  return QTALK_OK;
+}
+
+void qtalk_destroy(qtalk_ctx* c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->stream);
+  free_all(c);
+  delete c;
+}
+
+static qtalk_status seq_call(qtalk_ctx* c, int32_t seq, const float* emb, int32_t T, float* logits,
+                             float* hidden_out, bool rewind) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", seq);
+  if (T < 1) return fail(c, QTALK_E_INVAL, "T must be >= 1 (got %d)", T);
+  if (!emb || !logits) return fail(c, QTALK_E_INVAL, "emb and logits must not be null");
+  const int p0 = rewind ? 0 : c->cur_len[seq];
+  if ((long long)p0 + T > c->cfg.max_seq_len)
+    return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + %d > %d", p0, T, c->cfg.max_seq_len);
+  Fwd f(c);
+  f.run_sequence(seq, p0, emb, T, logits, hidden_out);
+  const qtalk_status s = launch_status(c);
+  if (s == QTALK_OK) c->cur_len[seq] = p0 + T;
+  return s;
+}
+
+qtalk_status qtalk_prefill(qtalk_ctx* c, int32_t seq, const float* emb, int32_t T, float* logits,
+                           float* hidden_out) {
+  return seq_call(c, seq, emb, T, logits, hidden_out, true);
+}
+
+qtalk_status qtalk_extend(qtalk_ctx* c, int32_t seq, const float* emb, int32_t T, float* logits,
+                          float* hidden_out) {
+  return seq_call(c, seq, emb, T, logits, hidden_out, false);
+}
+
+qtalk_status qtalk_decode(qtalk_ctx* c, int32_t seq, const float* emb, float* logits,
+                          float* hidden_out) {
+  if (!c || !c->fused) return seq_call(c, seq, emb, 1, logits, hidden_out, false);
+  c->err.clear();
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", seq);
+  if (!emb || !logits) return fail(c, QTALK_E_INVAL, "emb and logits must not be null");
+  if (c->cur_len[seq] + 1 > c->cfg.max_seq_len)
+    return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + 1 > %d", c->cur_len[seq],
+                c->cfg.max_seq_len);
+  Fwd f(c);
+  const qtalk_status s = f.run_fused(seq, emb, logits, hidden_out);
+  if (s == QTALK_OK) c->cur_len[seq] += 1;
+  return s;
+}
+
+qtalk_status qtalk_decode_batch(qtalk_ctx* c, int32_t n, const int32_t* seqs, const float* emb,
+                                float* logits, float* hidden_out) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (n < 1 || n > c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "n must be in [1, max_seqs]");
+  if (!seqs || !emb || !logits) return fail(c, QTALK_E_INVAL, "seqs, emb and logits must not be null");
+  std::vector<char> seen(c->cfg.max_seqs, 0);
+  for (int i = 0; i < n; ++i) {
+    const int s = seqs[i];
+    if (s < 0 || s >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", s);
+    if (seen[s]) return fail(c, QTALK_E_INVAL, "sequence %d listed twice", s);
+    seen[s] = 1;
+    if (c->cur_len[s] + 1 > c->cfg.max_seq_len)
+      return fail(c, QTALK_E_OVERFLOW, "cache overflow on sequence %d", s);
+  }
+  Fwd f(c);
+  f.run_batch(seqs, n, emb, logits, hidden_out);
+  const qtalk_status st = launch_status(c);
+  if (st == QTALK_OK)
+    for (int i = 0; i < n; ++i) c->cur_len[seqs[i]] += 1;
+  return st;
+}
+
+qtalk_status qtalk_kv_rewind(qtalk_ctx* c, int32_t seq, int32_t n_keep) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", seq);
+  if (n_keep < 0 || n_keep > c->cur_len[seq])
+    return fail(c, QTALK_E_INVAL, "n_keep %d outside [0, %d]", n_keep, c->cur_len[seq]);
+  c->cur_len[seq] = n_keep;
+  return QTALK_OK;
+}
+
+int32_t qtalk_kv_len(const qtalk_ctx* c, int32_t seq) {
+  if (!c || seq < 0 || seq >= c->cfg.max_seqs) return -1;
+  return c->cur_len[seq];
+}
+
+qtalk_status qtalk_kv_read(qtalk_ctx* c, int32_t seq, int32_t layer, int32_t kv, float* dst) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (seq < 0 || seq >= c->cfg.max_seqs || layer < 0 || layer >= c->cfg.n_layers ||
+      (kv != 0 && kv != 1) || !dst)
+    return fail(c, QTALK_E_INVAL, "bad kv_read arguments");
+  const qtalk_config& g = c->cfg;
+  const size_t eb = c->kv_f16 ? 2 : 4;
+  const char* base = reinterpret_cast<const char*>(kv ? c->vc : c->kc) +
+                     ((size_t)layer * c->layer_kv_elems +
+                      (size_t)seq * g.n_kv_heads * g.max_seq_len * g.head_dim) * eb;
+  launch_kv_to_f32(c->kv_f16, base, g.n_kv_heads, g.max_seq_len, c->cur_len[seq], g.head_dim, dst,
+                   c->stream);
+  return launch_status(c);
+}
+
+qtalk_status qtalk_sync(qtalk_ctx* c) {
+  if (!c) return QTALK_E_INVAL;
+  const hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return fail(c, QTALK_E_DEVICE, "stream failed: %s", hipGetErrorString(e));
+  if (c->fused) {
+    int code = 0;
+    if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(c, QTALK_E_DEVICE, "cannot read the decode status word");
+    if (code)
+      return fail(c, QTALK_E_DEVICE, "persistent decode gave up waiting (code %d)", code);
+  }
+  return QTALK_OK;
+}
+
+const char* qtalk_last_error(const qtalk_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+}  // extern "C"
+#pragma GCC visibility pop

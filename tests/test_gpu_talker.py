@@ -1,0 +1,338 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Tolerances: max |gpu - oracle| / max |oracle| per step <= 2e-3 for the float32
+workload and <= 2e-2 for bf16 weights; codebook-0 argmax exact except where
+the oracle's own top-2 gap is inside the tolerance band; the KV cache is
+compared per (layer, K or V) the same way, position by position.
+"""
+import numpy as np
+import pytest
+
+from oracle import TalkerOracle
+from synth import prefill_embeddings, step_embedding, workload, batch_lengths
+from tests.helpers import argmax_in_band, argmax_ok, dev, host, rel_err, say, weights_for
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 2e-3
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    from qwen3_tts_talker_amd import load_library
+    load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _talker(shape, w):
+    from qwen3_tts_talker_amd import Talker
+    return Talker(shape, w)
+
+
+def _check_kv(tk, orc, shape, tol, seq=0, layers=None):
+    worst = 0.0
+    for l in (range(len(orc.layers)) if layers is None else layers):
+        for which in (0, 1):
+            g = host(tk.kv_read(seq, l, which))
+            o = orc.kv(seq, l, which)
+            e = rel_err(g, o)
+            worst = max(worst, e)
+            assert e <= tol, (l, which, e)
+    return worst
+
+
+def _prefill_decode(name, T, steps, tol, n_layers=None, kv_layers=None):
+    shape = workload(name)
+    w = weights_for(name, n_layers)
+    say(f"[case] {name} layers={len(w['layers'])} T={T} steps={steps}")
+    orc = TalkerOracle(shape, w)
+    emb = prefill_embeddings(shape, T)
+    steps_emb = [step_embedding(shape, s) for s in range(steps)]
+    # one oracle pass over all rows gives the prefill's last row and every
+    # decode step (prefill == prefill + decodes is pinned on the oracle)
+    allrows = np.concatenate([emb] + [e[None] for e in steps_emb])
+    ref_logits, ref_hidden = orc.prefill(0, allrows, all_rows=True)
+    tk = _talker(shape, w)
+    lg, hd = tk.prefill(0, dev(emb), hidden=True)
+    errs = [rel_err(host(lg), ref_logits[T - 1])]
+    assert rel_err(host(hd), ref_hidden[T - 1]) <= tol
+    assert argmax_ok(host(lg), ref_logits[T - 1], tol)
+    bad_argmax = exact = 0
+    for s in range(steps):
+        lg = tk.decode(0, dev(steps_emb[s]))
+        g = host(lg)
+        errs.append(rel_err(g, ref_logits[T + s]))
+        bad_argmax += not argmax_ok(g, ref_logits[T + s], tol)
+        exact += int(np.argmax(g)) == int(np.argmax(ref_logits[T + s]))
+        if (s + 1) % 256 == 0:
+            say(f"  step {s + 1}: rel err {errs[-1]:.2e}")
+    band = sum(argmax_in_band(ref_logits[T + s], tol) for s in range(steps))
+    say(f"  logits rel err: prefill {errs[0]:.2e}, decode max {max(errs[1:] or [0]):.2e}; "
+        f"argmax equal {exact}/{steps} (oracle top-2 inside the band at {band})")
+    assert max(errs) <= tol, max(errs)
+    assert bad_argmax == 0
+    assert tk.kv_len(0) == T + steps
+    kv = _check_kv(tk, orc, shape, tol, layers=kv_layers)
+    say(f"  kv rel err max {kv:.2e}")
+    tk.close()
+    return max(errs)
+
+
+def test_tiny_f32_prefill16_decode8():
+    _prefill_decode("tiny_f32_2l", 16, 8, TOL_F32)
+
+
+def test_talker_1layer_prefill128_decode64():
+    # T = 128 runs the matrix-core prefill, the steps the matrix-vector path
+    _prefill_decode("talker_1l_t128", 128, 64, TOL_BF16)
+
+
+def test_talker_1layer_short_prefill_matrix_vector_path():
+    _prefill_decode("talker_1l_t128", 16, 4, TOL_BF16)
+
+
+def test_talker_1layer_ragged_prefill_lengths():
+    # M tails of the matrix-core tiles (not multiples of 64 or 128)
+    for T in (17, 65, 200):
+        _prefill_decode("talker_1l_t128", T, 1, TOL_BF16)
+
+
+def test_talker_28_layers_prefill128_decode1024():
+    _prefill_decode("talker_28l_t128_d1024", 128, 1024, TOL_BF16,
+                    kv_layers=[0, 13, 27])
+
+
+# -- path invariants on the GPU -----------------------------------------------
+
+
+def test_prefill_equals_prefill_then_decode_bitwise_on_matrix_vector_path(monkeypatch):
+    # per-step decode kernels: the same per-row arithmetic as a short prefill
+    monkeypatch.setenv("QTALK_FUSED_DECODE", "0")
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, 16)
+    a = _talker(shape, w)
+    la = host(a.prefill(0, dev(emb)))
+    b = _talker(shape, w)
+    b.prefill(0, dev(emb[:15]))
+    lb = host(b.decode(0, dev(emb[15])))
+    assert np.array_equal(la, lb)
+    for l in (0,):
+        for which in (0, 1):
+            assert np.array_equal(host(a.kv_read(0, l, which)),
+                                  host(b.kv_read(0, l, which)))
+
+
+def test_prefill_equals_prefill_then_decode_across_paths():
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, 101)
+    a = _talker(shape, w)
+    la = host(a.prefill(0, dev(emb)))
+    b = _talker(shape, w)
+    b.prefill(0, dev(emb[:100]))
+    lb = host(b.decode(0, dev(emb[100])))
+    assert rel_err(lb, la) <= TOL_BF16
+
+
+def test_chunked_extend_equals_one_shot():
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, 150)
+    orc = TalkerOracle(shape, w)
+    lo, _ = orc.prefill(0, emb)
+    a = _talker(shape, w)
+    la = host(a.prefill(0, dev(emb)))
+    a.prefill(0, dev(emb[:40]))
+    a.extend(0, dev(emb[40:47]))
+    lb = host(a.extend(0, dev(emb[47:])))
+    assert a.kv_len(0) == 150
+    assert rel_err(la, lo) <= TOL_BF16
+    assert rel_err(lb, lo) <= TOL_BF16
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_batched_decode_equals_serial(monkeypatch, fused):
+    # bitwise on the per-step kernels; the persistent batch-1 kernel reduces
+    # in another order, so there the serial side agrees to rounding
+    if not fused:
+        monkeypatch.setenv("QTALK_FUSED_DECODE", "0")
+    shape = workload("talker_1l_t128").with_(n_seqs=5, cap=256)
+    w = weights_for("talker_1l_t128")
+    a = _talker(shape, w)
+    b = _talker(shape, w)
+    lens = [3, 40, 17, 90, 1]
+    for s, n in enumerate(lens):
+        e = dev(prefill_embeddings(shape, n, seq=s))
+        a.prefill(s, e)
+        b.prefill(s, e)
+    order = [3, 0, 4, 1, 2]
+    for step in range(3):
+        steps = np.stack([step_embedding(shape, step, seq=s) for s in order])
+        lg, hg = a.decode_batch(order, dev(steps), hidden=True)
+        lg, hg = host(lg), host(hg)
+        for i, s in enumerate(order):
+            ls, hs = b.decode(s, dev(steps[i]), hidden=True)
+            if fused:
+                assert rel_err(lg[i], host(ls)) <= 1e-4, (step, s)
+                assert rel_err(hg[i], host(hs)) <= 1e-4, (step, s)
+            else:
+                assert np.array_equal(lg[i], host(ls)), (step, s)
+                assert np.array_equal(hg[i], host(hs)), (step, s)
+    assert [a.kv_len(s) for s in range(5)] == [n + 3 for n in lens]
+
+
+def test_stale_cache_tail_is_never_read():
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, 16)
+    poisoned = emb.copy()
+    poisoned[11:] = np.nan
+    a = _talker(shape, w)
+    a.prefill(0, dev(poisoned))      # positions 11..15 of every layer hold NaN
+    a.kv_rewind(0, 11)
+    la = host(a.decode(0, dev(emb[11])))
+    b = _talker(shape, w)
+    b.prefill(0, dev(emb[:11]))
+    lb = host(b.decode(0, dev(emb[11])))
+    assert np.isfinite(la).all()
+    assert np.array_equal(la, lb)
+
+
+def test_runs_are_deterministic():
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = dev(prefill_embeddings(shape, 130))
+    a = _talker(shape, w)
+    r1 = host(a.prefill(0, emb))
+    r2 = host(a.prefill(0, emb))
+    assert np.array_equal(r1, r2)
+
+
+def test_errors_leave_state_unchanged():
+    from qwen3_tts_talker_amd import QtalkError
+    shape = workload("tiny_f32_2l").with_(cap=20, n_seqs=2)
+    w = weights_for("tiny_f32_2l")
+    tk = _talker(shape, w)
+    emb = prefill_embeddings(shape, 19)
+    tk.prefill(0, dev(emb))
+    ref = _talker(shape, w)
+    ref.prefill(0, dev(emb))
+    st = dev(step_embedding(shape, 0))
+    with pytest.raises(QtalkError) as e:
+        tk.prefill(1, dev(prefill_embeddings(shape, 21)))
+    assert e.value.status == -2
+    with pytest.raises(QtalkError) as e:
+        tk.decode(2, st)
+    assert e.value.status == -1
+    with pytest.raises(QtalkError) as e:
+        tk.decode_batch([0, 0], dev(np.stack([step_embedding(shape, 0)] * 2)))
+    assert e.value.status == -1
+    with pytest.raises(QtalkError):
+        tk.kv_rewind(0, 20)
+    assert tk.kv_len(0) == 19 and tk.kv_len(1) == 0
+    tk.decode(0, st)                   # fills the last slot
+    with pytest.raises(QtalkError) as e:
+        tk.decode(0, st)
+    assert e.value.status == -2
+    with pytest.raises(QtalkError) as e:
+        tk.decode_batch([1, 0], dev(np.stack([step_embedding(shape, 0)] * 2)))
+    assert e.value.status == -2
+    assert tk.kv_len(0) == 20 and tk.kv_len(1) == 0
+    # the failed calls changed nothing: the same decode as the reference
+    tk.kv_rewind(0, 19)
+    assert np.array_equal(host(tk.decode(0, st)), host(ref.decode(0, st)))
+
+
+# -- ragged batched decode ------------------------------------------------------
+
+
+def test_batched_ragged_decode_16_sequences():
+    name = "talker_28l_batch16_ragged"
+    shape = workload(name)
+    w = weights_for(name)
+    lens = batch_lengths(shape)
+    say(f"[case] {name} lengths={lens.tolist()}")
+    tk = _talker(shape, w)
+    pre = []
+    for s in range(shape.n_seqs):
+        e = prefill_embeddings(shape, int(lens[s]), seq=s)
+        pre.append(e)
+        tk.prefill(s, dev(e[:shape.chunk]))
+        for c0 in range(shape.chunk, len(e), shape.chunk):
+            tk.extend(s, dev(e[c0:c0 + shape.chunk]))
+    seqs = list(range(shape.n_seqs))
+    steps = 8
+    outs = []
+    for k in range(steps):
+        em = np.stack([step_embedding(shape, k, seq=s) for s in seqs])
+        outs.append(host(tk.decode_batch(seqs, dev(em))))
+    assert [tk.kv_len(s) for s in seqs] == [int(n) + steps for n in lens]
+    # the oracle follows the shortest sequence through its prefill and steps
+    s = int(np.argmin(lens))
+    orc = TalkerOracle(shape.with_(n_seqs=1), w)
+    rows = np.concatenate([pre[s]] + [step_embedding(shape, k, seq=s)[None]
+                                      for k in range(steps)])
+    ref, _ = orc.prefill(0, rows, all_rows=True)
+    errs = [rel_err(outs[k][s], ref[len(pre[s]) + k]) for k in range(steps)]
+    say(f"  seq {s} (len {lens[s]}) decode rel err max {max(errs):.2e}")
+    assert max(errs) <= TOL_BF16
+    assert all(argmax_ok(outs[k][s], ref[len(pre[s]) + k], TOL_BF16)
+               for k in range(steps))
+
+
+# -- persistent batch-1 decode --------------------------------------------------
+
+
+def test_persistent_decode_matches_per_step_kernels(monkeypatch):
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, 128)
+    steps = [step_embedding(shape, s) for s in range(16)]
+    orc = TalkerOracle(shape, w)
+    ref, ref_h = orc.prefill(0, np.concatenate([emb] + [e[None] for e in steps]),
+                             all_rows=True)
+    fused = _talker(shape, w)
+    monkeypatch.setenv("QTALK_FUSED_DECODE", "0")
+    plain = _talker(shape, w)
+    monkeypatch.delenv("QTALK_FUSED_DECODE")
+    fused.prefill(0, dev(emb))
+    plain.prefill(0, dev(emb))
+    worst = 0.0
+    for s, e in enumerate(steps):
+        lf, hf = fused.decode(0, dev(e), hidden=True)
+        lp, hp = plain.decode(0, dev(e), hidden=True)
+        lf, lp = host(lf), host(lp)
+        worst = max(worst, rel_err(lf, lp))
+        assert rel_err(lf, ref[128 + s]) <= TOL_BF16
+        assert rel_err(host(hf), ref_h[128 + s]) <= TOL_BF16
+    fused.sync()
+    say(f"  persistent vs per-step decode rel diff {worst:.2e}")
+    assert worst <= 1e-4
+    for which in (0, 1):
+        assert rel_err(host(fused.kv_read(0, 0, which)),
+                       host(plain.kv_read(0, 0, which))) <= 1e-3
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 63, 64, 65, 100, 1000, 2046])
+def test_persistent_decode_context_lengths(T):
+    # key-chunk edges of the persistent attention: contexts shorter than the
+    # 32 chunks, exact multiples, ragged tails, and the last cache slots
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    emb = prefill_embeddings(shape, T)
+    steps = [step_embedding(shape, s) for s in range(2)]
+    orc = TalkerOracle(shape, w)
+    ref, _ = orc.prefill(0, np.concatenate([emb] + [e[None] for e in steps]),
+                         all_rows=True)
+    tk = _talker(shape, w)
+    tk.prefill(0, dev(emb))
+    for s, e in enumerate(steps):
+        g = host(tk.decode(0, dev(e)))
+        assert rel_err(g, ref[T + s]) <= TOL_BF16, (T, s)
+    tk.sync()
+    assert tk.kv_len(0) == T + 2
