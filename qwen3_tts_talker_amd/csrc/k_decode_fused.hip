@@ -555,8 +555,17 @@ size_t fused_decode_part_words(int n_layers) { return (size_t)n_layers * pd::PAR
 int fused_decode_blocks() { return pd::NB; }
 int fused_decode_threads() { return pd::NT; }
 
-hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st) {
+// Cooperative launch guarantees that all NB blocks are resident together (or
+// fails).  `cooperative == false` issues an ordinary launch of the same grid,
+// for tracing tools that cannot follow cooperative launches; residency then
+// rests on fused_decode_fits() and on this stream running nothing else at the
+// same time, which holds for the library's single in-order stream.
+hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool cooperative) {
   FusedDecodeArgs a = args;
+  if (!cooperative) {
+    hipLaunchKernelGGL(k_decode_fused, dim3(pd::NB), dim3(pd::NT), 0, st, a);
+    return hipGetLastError();
+  }
   void* params[] = {&a};
   return hipLaunchCooperativeKernel((const void*)k_decode_fused, dim3(pd::NB), dim3(pd::NT), params,
                                     0, st);

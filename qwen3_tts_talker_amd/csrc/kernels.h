@@ -117,6 +117,6 @@ bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vo
 bool fused_decode_fits();
 size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
-hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);
 
 }  // namespace qtalk

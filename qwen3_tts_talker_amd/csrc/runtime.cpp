@@ -69,6 +69,10 @@ struct qtalk_ctx {
   float* work = nullptr;
   // persistent batch-1 decode (Talker geometry only)
   bool fused = false;
+  // cooperative launch of the persistent decode; QTALK_COOPERATIVE=0 selects
+  // an ordinary launch of the same grid (for tracers that skip cooperative
+  // launches)
+  bool coop = true;
   uint64_t* ll = nullptr;
   uint64_t* fpart = nullptr;
   int* ferr = nullptr;
@@ -282,7 +286,7 @@ struct Fwd {
     a.part = c->fpart;
     a.err = c->ferr;
     a.epoch = c->epoch + 1;
-    const hipError_t e = launch_decode_fused(a, st);
+    const hipError_t e = launch_decode_fused(a, st, c->coop);
     if (e != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
     c->epoch += 1;
@@ -374,6 +378,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   c->per_layer = per_layer;
   c->norms_per_layer = norms_per_layer;
   const char* env = getenv("QTALK_FUSED_DECODE");
+  const char* env_coop = getenv("QTALK_COOPERATIVE");
+  c->coop = !(env_coop && env_coop[0] == '0');
   c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') &&
              fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
