@@ -13,7 +13,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqtalk.so")
-SOURCES = ["runtime.cpp", "k_gemv.hip", "k_attn.hip", "k_gemm.hip", "k_decode_fused.hip"]
+SOURCES = ["runtime.cpp", "k_gemv.hip", "k_attn.hip", "k_gemm.hip", "k_attn_prefill.hip",
+           "k_decode_fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -63,6 +63,22 @@ struct AttnArgs {
 void launch_attn_decode(bool kv_f16, AttnOut mode, AttnArgs a, hipStream_t st);
 void launch_attn_merge(AttnArgs a, hipStream_t st);
 
+// Causal GQA attention of T uniform rows (positions p0 .. p0+T-1 of one
+// sequence) over the f16 cache on the matrix cores; output bf16 rows.
+struct PrefillAttnArgs {
+  const float* q;  // q of row t, head h at q + t*ldq + h*head_dim (normed, roped)
+  int ldq;
+  const f16_t* kc;
+  const f16_t* vc;  // [S][n_kv][cap][hd] of this layer
+  int n_heads, n_kv_heads, head_dim, cap;
+  int seq, p0, T;
+  float qscale;  // log2(e) / sqrt(head_dim)
+  bf16_t* out;   // row t at out + t*ldo
+  int ldo;
+};
+bool attn_prefill_supported(int head_dim, int group);
+void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st);
+
 // C = A[M][K] (bf16) * B[N][K]^T (bf16) on MFMA, float32 accumulation.
 struct GemmArgs {
   const bf16_t* A;

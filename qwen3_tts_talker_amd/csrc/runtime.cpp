@@ -220,10 +220,29 @@ struct Fwd {
     launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
     qk_append(l, rows);
-    AttnArgs a = attn_args(l, rows);
-    a.keys_per_split = max_ctx(rows);
-    a.n_splits = 1;
-    launch_attn_decode(c->kv_f16, ATT_BF16, a, st);
+    if (c->kv_f16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads)) {
+      PrefillAttnArgs p{};
+      p.q = c->qkv;
+      p.ldq = c->qkv_dim;
+      p.kc = reinterpret_cast<const f16_t*>(kv_layer(c->kc, l));
+      p.vc = reinterpret_cast<const f16_t*>(kv_layer(c->vc, l));
+      p.n_heads = g.n_heads;
+      p.n_kv_heads = g.n_kv_heads;
+      p.head_dim = g.head_dim;
+      p.cap = g.max_seq_len;
+      p.seq = rows.seq0;
+      p.p0 = rows.p0;
+      p.T = T;
+      p.qscale = 1.4426950408889634f / sqrtf((float)g.head_dim);
+      p.out = att_b;
+      p.ldo = c->q_dim;
+      launch_attn_prefill(p, st);
+    } else {
+      AttnArgs a = attn_args(l, rows);
+      a.keys_per_split = max_ctx(rows);
+      a.n_splits = 1;
+      launch_attn_decode(c->kv_f16, ATT_BF16, a, st);
+    }
     gemm(att_b, c->q_dim, L.wo, T, H, c->q_dim, c->x, H, EPI_ADD);
     launch_rmsnorm_bf16(c->x, H, T, H, L.g_post, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wgu, T, 2 * I, H, act_b, I, EPI_SWIGLU);

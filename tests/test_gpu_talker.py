@@ -106,6 +106,32 @@ def test_talker_28_layers_prefill128_decode1024():
                     kv_layers=[0, 13, 27])
 
 
+def test_prefill_attention_many_tiles_ragged_extend_to_capacity():
+    # two real-shape layers: layer 1's cache depends on layer 0's attention
+    # output at every row, so comparing it checks every row of the matrix-core
+    # prefill attention; 700 and 1348 rows leave ragged 64-key tiles and
+    # 64-position blocks, the extend starts at p0 = 700 and ends at the cap
+    shape = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128", 2)
+    say("[case] 2 real-shape layers: prefill 700, extend 1348 (to cap 2048)")
+    emb = prefill_embeddings(shape, 2048)
+    orc = TalkerOracle(shape, w)
+    lo1, ho1 = orc.prefill(0, emb[:700])
+    tk = _talker(shape, w)
+    lg, hd = tk.prefill(0, dev(emb[:700]), hidden=True)
+    e1 = rel_err(host(lg), lo1)
+    assert e1 <= TOL_BF16 and rel_err(host(hd), ho1) <= TOL_BF16
+    kv1 = _check_kv(tk, orc, shape, TOL_BF16)
+    lo2, ho2 = orc.extend(0, emb[700:])
+    lg, hd = tk.extend(0, dev(emb[700:]), hidden=True)
+    e2 = rel_err(host(lg), lo2)
+    assert e2 <= TOL_BF16 and rel_err(host(hd), ho2) <= TOL_BF16
+    assert argmax_ok(host(lg), lo2, TOL_BF16)
+    kv2 = _check_kv(tk, orc, shape, TOL_BF16)
+    say(f"  logits rel err {e1:.2e} / {e2:.2e}; kv rel err {kv1:.2e} / {kv2:.2e}")
+    tk.close()
+
+
 # -- path invariants on the GPU -----------------------------------------------
 
 
