@@ -131,6 +131,146 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
   }
 }
 
+// Large-M variant: 256 x BN block tile over 8 waves (4 x 2, a 64 x BN/2 tile
+// each, 32x32x16 MFMA), so every SIMD runs two waves and the LDS reads of one
+// hide behind the MFMAs of the other.  BN = 192 gives the 6144-wide gate|up
+// projection exactly 256 tiles at M = 2048.  LDS holds two K-tile stages; global
+// loads run two K tiles ahead of the MFMAs (two register stages), one
+// barrier per K tile.
+template <int BN, int EPI, bool SPLIT>
+__global__ __launch_bounds__(512) void k_gemm_m32(GemmArgs a, int k_per_split) {
+  constexpr int BM = 256, NT = 512;
+  constexpr int BK = GB_K, LS = G_STRIDE;
+  constexpr int WTM = BM / 4, WTN = BN / 2;  // 64 x 64 per wave
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int AR = BM * BK / 8 / NT;  // 16-byte chunks per thread and K tile
+  constexpr int BR = BN * BK / 8 / NT;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LS];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int nkt = k_per_split / BK;
+  const int M = a.M, K = a.K;
+
+  // chunk i of this thread: row tid / 8 + 64 i, column chunk tid % 8 (A rows
+  // past M re-read row M - 1; their results are never stored)
+  const int lrow = tid >> 3, lchunk = (tid & 7) * 8;
+  const bf16_t* Ab0 = a.A + kbeg + lchunk;
+  const bf16_t* Bb0 = a.B + (size_t)(n0 + lrow) * K + kbeg + lchunk;
+  const size_t lda = a.lda;
+
+  // two register stages as named scalars (4 A chunks, 2 B chunks each): an
+  // array here is left in private memory by the compiler
+  static_assert(AR == 4 && (BR == 2 || BR == 3), "stage layout");
+  uint4 s0a0, s0a1, s0a2, s0a3, s0b0, s0b1, s0b2, s1a0, s1a1, s1a2, s1a3, s1b0, s1b1, s1b2;
+#define QT_LDA(I, KT) \
+  (*reinterpret_cast<const uint4*>(Ab0 + (size_t)min(m0 + lrow + 64 * (I), M - 1) * lda + (KT) * BK))
+#define QT_LDB(I, KT) ld_stream16(Bb0 + (size_t)(64 * (I)) * K + (KT) * BK)
+#define QT_GLOAD(S, KT)      \
+  do {                       \
+    const int kt_ = (KT);    \
+    S##a0 = QT_LDA(0, kt_);  \
+    S##a1 = QT_LDA(1, kt_);  \
+    S##a2 = QT_LDA(2, kt_);  \
+    S##a3 = QT_LDA(3, kt_);  \
+    S##b0 = QT_LDB(0, kt_);  \
+    S##b1 = QT_LDB(1, kt_);  \
+    if (BR == 3) S##b2 = QT_LDB(2, kt_); \
+  } while (0)
+#define QT_ST(BUFA, ROW, V) *reinterpret_cast<uint4*>(&BUFA[(lrow + (ROW)) * LS + lchunk]) = (V)
+#define QT_LSTORE(S, BUF)        \
+  do {                           \
+    QT_ST(As[BUF], 0, S##a0);    \
+    QT_ST(As[BUF], 64, S##a1);   \
+    QT_ST(As[BUF], 128, S##a2);  \
+    QT_ST(As[BUF], 192, S##a3);  \
+    QT_ST(Bs[BUF], 0, S##b0);    \
+    QT_ST(Bs[BUF], 64, S##b1);   \
+    if (BR == 3) QT_ST(Bs[BUF], 128, S##b2); \
+  } while (0)
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+#define QT_COMPUTE(BUF)                                                                     \
+  do {                                                                                      \
+    const bf16_t* Ab = As[BUF] + (wm * WTM + fr) * LS + fk;                                 \
+    const bf16_t* Bb = Bs[BUF] + (wn * WTN + fr) * LS + fk;                                 \
+    _Pragma("unroll") for (int ks = 0; ks < BK; ks += 16) {                                 \
+      bf16x8_t af[TM], bfr[TN];                                                             \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
+          af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 32 * LS + ks);                \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 32 * LS + ks);               \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
+          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                        \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);  \
+    }                                                                                       \
+  } while (0)
+
+  // tile kt sits in register stage kt & 1 and LDS buffer kt & 1.  Loads and
+  // stores run unconditionally (past the last tile they repeat it) so both
+  // register stages stay in registers.
+  QT_GLOAD(s0, 0);
+  QT_GLOAD(s1, min(1, nkt - 1));
+  QT_LSTORE(s0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    // even tile kt in LDS 0; tile kt + 1 in flight in stage 1
+    QT_GLOAD(s0, min(kt + 2, nkt - 1));
+    QT_COMPUTE(0);
+    QT_LSTORE(s1, 1);
+    __syncthreads();
+    if (kt + 1 >= nkt) break;
+    // odd tile kt + 1 in LDS 1; tile kt + 2 in flight in stage 0
+    QT_GLOAD(s1, min(kt + 3, nkt - 1));
+    QT_COMPUTE(1);
+    QT_LSTORE(s0, 0);
+    __syncthreads();
+  }
+#undef QT_LDA
+#undef QT_LDB
+#undef QT_ST
+#undef QT_GLOAD
+#undef QT_LSTORE
+#undef QT_COMPUTE
+
+  // epilogue: register r of lane l is C[row (r/4)*8 + (l/32)*4 + r%4][col l%32]
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int rbase = m0 + wm * WTM + i * 32 + (lane >> 5) * 4;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int cbase = n0 + wn * WTN + j * 32;
+      const int col = cbase + fr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + (r >> 2) * 8 + (r & 3);
+        const float v = acc[i][j][r];
+        if (EPI == EPI_SWIGLU && !SPLIT) {
+          // columns cbase..+15 are gate rows, cbase+16..+31 the matching up rows
+          const float u = __shfl_xor(v, 16);
+          if (fr < 16 && row < M)
+            reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + cbase / 2 + fr] =
+                (bf16_t)f32_to_bf16(silu_f(v) * u);
+          continue;
+        }
+        if (row >= M) continue;
+        if (SPLIT) a.work[((size_t)blockIdx.z * M + row) * a.N + col] = v;
+        else if (EPI == EPI_STORE) reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = v;
+        else reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] += v;
+      }
+    }
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a, int ks) {
   const size_t MN = (size_t)a.M * a.N;
@@ -162,6 +302,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a, int ks) {
 bool gemm_shape_ok(int M, int N, int K) {
   return M >= 1 && N % GB_N == 0 && K % GB_K == 0;
 }
+// (N % 128 == 0 also covers the 256 x 128 tiles of the large-M kernel)
 
 template <int BM, int EPI>
 static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
@@ -177,10 +318,51 @@ static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
   }
 }
 
+template <int BN, int EPI>
+static void launch_m32(GemmArgs a, int ks, hipStream_t st) {
+  const dim3 grid(a.N / BN, (a.M + 255) / 256, ks);
+  const int kps = a.K / ks;
+  if (ks == 1) {
+    hipLaunchKernelGGL((k_gemm_m32<BN, EPI, false>), grid, dim3(512), 0, st, a, kps);
+  } else {
+    hipLaunchKernelGGL((k_gemm_m32<BN, EPI, true>), grid, dim3(512), 0, st, a, kps);
+    const size_t n_out = (size_t)a.M * a.N / (EPI == EPI_SWIGLU ? 2 : 1);
+    const unsigned blocks = (unsigned)((n_out + 255) / 256 < 4096 ? (n_out + 255) / 256 : 4096);
+    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3(blocks), dim3(256), 0, st, a, ks);
+  }
+}
+
+static void launch_m32_epi(Epilogue epi, GemmArgs a, int ks, hipStream_t st) {
+  switch (epi) {
+    case EPI_STORE: launch_m32<128, EPI_STORE>(a, ks, st); break;
+    case EPI_ADD: launch_m32<128, EPI_ADD>(a, ks, st); break;
+    case EPI_SWIGLU: launch_m32<128, EPI_SWIGLU>(a, ks, st); break;
+  }
+}
+
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
+  const int nkt = a.K / GB_K;
+  if (a.M >= 512) {
+    // 256-row tiles.  The gate|up projection takes 192-column blocks when
+    // that gives the grid whole rounds of 256 CUs (6144 wide at M = 2048);
+    // otherwise 128 columns, splitting K while the doubled grid still fits
+    // one round of 256 blocks (the split-K reduce costs a full pass over C,
+    // so a full grid is never split).
+    const int mt = (a.M + 255) / 256;
+    if (epi == EPI_SWIGLU && a.N % 192 == 0 && (mt * (a.N / 192)) % 256 == 0) {
+      launch_m32<192, EPI_SWIGLU>(a, 1, st);
+      return;
+    }
+    const int tiles = mt * (a.N / 128);
+    int ks = 1;
+    while (tiles * ks * 2 <= 256 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 &&
+           (size_t)(ks * 2) * a.M * a.N <= a.work_elems)
+      ks *= 2;
+    launch_m32_epi(epi, a, ks, st);
+    return;
+  }
   const int BM = a.M > 64 ? 128 : 64;
   const int tiles = (a.N / GB_N) * ((a.M + BM - 1) / BM);
-  const int nkt = a.K / GB_K;
   int ks = 1;
   // split K while the grid is short of the 256 CUs and each split keeps >= 4
   // K tiles; ks divides the K tile count

@@ -35,7 +35,7 @@ constexpr int GEMV_ROWS = MAX_ROWS;  // rows per matrix-vector pass
 constexpr int MFMA_MIN_ROWS = 17;    // prefill rows that switch to the matrix cores
 constexpr int MAX_SPLITS = 128;      // key splits of the decode attention
 constexpr int MAX_CHUNK = 2048;      // rows per matrix-core pass
-constexpr size_t WORK_ELEMS = (size_t)4 << 20;  // split-K workspace (floats)
+constexpr size_t WORK_ELEMS = (size_t)8 << 20;  // split-K workspace (floats)
 
 struct LayerDev {
   void* wqkv;  // [q_dim + 2 kv_dim][H]: q rows, then k rows, then v rows
