@@ -12,14 +12,17 @@
 //
 // Steps per layer (math as in "qwentts.cpp src/talker-forward.h",
 // talker_layer_forward):
-//   QKV : x -> RMSNorm(g_in) -> [q|k|v] rows 16b..16b+15      -> E1
+//   QKV : x -> RMSNorm(g_in) -> [q|k|v] rows 16b..16b+15         -> E1
 //   ATT : q/k norm + NEOX RoPE, new K/V appended (f16), split-KV causal GQA
-//         over 32 key chunks per KV head; the last chunk block of a head
-//         merges the chunks (log-sum-exp)                    -> E2
+//         over 32 key chunks per KV head, one online softmax per wave  -> P
+//   MRG : chunk blocks 0 and 1 of each head merge the chunks (log-sum-exp) -> E2
 //   O   : x + o @ Wo^T, rows 4b..4b+3                         -> E3
 //   GU  : RMSNorm(g_post), 12 gate|up row pairs, silu(g)*u    -> E4
 //   D   : x + a @ Wd^T, rows 4b..4b+3                         -> E5
-// then final RMSNorm + codec_head rows 12b..12b+11 -> logits.
+// then final RMSNorm + codec_head rows 12b..12b+11 -> logits.  The RMSNorms
+// are folded into the exchange: the received vector is stored times its gain
+// while the sum of squares accumulates, and the norm scale multiplies the dot
+// products, so a norm costs no extra block barrier.
 //
 // Specialised to the Talker geometry (hidden 1024, 16/8 heads of 128,
 // intermediate 3072, vocab 3072, bf16 weights, f16 cache); other shapes use
@@ -141,6 +144,34 @@ struct Gp {
       }
     }
   }
+  // out[i] = dot(unit wave + NW*i's weights, xs segment), in every lane
+  __device__ __forceinline__ void dot_all(const float* xs, float (&out)[NU], int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + NW * i;
+      out[i] = 0.f;
+      if (u < units) {
+        const float* xb = xs + (u % S) * KSEG + lane * 8;
+        float acc = 0.f;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          float f[8];
+          unpack8_bf16(w[i][l], f);
+          const float4 a = *reinterpret_cast<const float4*>(xb + l * 512);
+          const float4 b = *reinterpret_cast<const float4*>(xb + l * 512 + 4);
+          acc = fmaf(f[0], a.x, acc);
+          acc = fmaf(f[1], a.y, acc);
+          acc = fmaf(f[2], a.z, acc);
+          acc = fmaf(f[3], a.w, acc);
+          acc = fmaf(f[4], b.x, acc);
+          acc = fmaf(f[5], b.y, acc);
+          acc = fmaf(f[6], b.z, acc);
+          acc = fmaf(f[7], b.w, acc);
+        }
+        out[i] = wave_sum(acc);
+      }
+    }
+  }
   // red[u] = dot(unit u's weights, xs segment)
   __device__ __forceinline__ void dot(const float* xs, float* red, int wave, int lane) const {
 #pragma unroll
@@ -182,16 +213,27 @@ struct Gain2 {
 };
 static_assert(H == 2 * NT, "two hidden channels per thread");
 
-// xn[k] = x[k] * rsqrt(mean(x^2) + eps) * g[k] over K = H
-__device__ __forceinline__ void rms_to(const float* x, const Gain2& g, float eps, float* xn,
-                                       float* redw) {
-  const int tid = threadIdx.x;
-  const float x0 = x[tid], x1 = x[tid + NT];
-  const float ss = block_sum<NT>(x0 * x0 + x1 * x1, redw);
-  const float inv = rsqrtf(ss / (float)H + eps);
-  xn[tid] = x0 * inv * g.g0;
-  xn[tid + NT] = x1 * inv * g.g1;
-  __syncthreads();
+// Receive an H-vector: x[k] to `x` (LDS), x[k] * g[k] to `xg` (LDS), and this
+// thread's share of sum(x^2) to *ss.  RMSNorm is then applied as one scale
+// on the dot products: W (x * rsqrt(mean(x^2) + eps) * g) = rsqrt(.) * W (x g).
+__device__ __forceinline__ bool recv_norm(LLWait<2>& w, uint32_t ep, int* err, float* x, float* xg,
+                                          const Gain2& g, float* ss) {
+  float s = 0.f;
+  const bool ok = w.finish(ep, err, [&](int i, float v) {
+    x[i] = v;
+    xg[i] = v * (i < NT ? g.g0 : g.g1);
+    s = fmaf(v, v, s);
+  });
+  *ss = s;
+  return ok;
+}
+
+// 1 / sqrt(mean(x^2) + eps) from per-wave partial sums in redw[0..NW)
+__device__ __forceinline__ float inv_rms(const float* redw, float eps) {
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += redw[i];
+  return rsqrtf(t / (float)H + eps);
 }
 
 }  // namespace pd
@@ -199,44 +241,68 @@ __device__ __forceinline__ void rms_to(const float* x, const Gain2& g, float eps
 __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   using namespace pd;
   __shared__ __attribute__((aligned(16))) float xres[H];  // residual stream
-  __shared__ __attribute__((aligned(16))) float xin[I];   // input of the current step
+  __shared__ __attribute__((aligned(16))) float xin[I];   // input of the current product
+  __shared__ float araw[QKV / NKV];                        // this head group's q0 | q1 | k | v
   __shared__ float red[32];
   __shared__ float redw[NW];
-  __shared__ float qs[G][HD];                              // roped, scaled q
-  __shared__ float knew[HD], vnew[HD];
-  __shared__ float sp[G][64];
-  __shared__ float s_m[G], s_l[G], s_alpha[G];
-  __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // slot sums; chunk o's
-  __shared__ float mlbuf[NCH][G][2];
+  __shared__ float qs[G][HD];                              // normed, roped, scaled q
+  __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
+  __shared__ float mw[NW][G], lw[NW][G];                   // per-wave softmax state
+  __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t ep = a.epoch;
   const int pos = a.pos;
   const int n_ctx = pos + 1;
   // attention role of this block: KV head g (= the XCD it runs on), key chunk
-  // c; the c == 0 block of each head also merges the head's chunks
+  // c; chunk blocks 0 and 1 of each head also merge the chunks of query heads
+  // 2g and 2g+1
   const int g = b % NKV, c = b / NKV;
   const int kpb = (n_ctx + NCH - 1) / NCH;
   const int k0 = c * kpb, k1 = min(k0 + kpb, n_ctx);
   const float scale = rsqrtf((float)HD);
   const int slot = tid >> 4, sub = tid & 15;
 
-  // Every step's weight slice is requested one step ahead of its use, right
-  // behind that step's first exchange poll, so the HBM stream of step k+1
-  // overlaps step k's exchange wait and arithmetic.
-  Gp<16, 1, H> gq;        // Wqkv rows 16b .. 16b+15; after the last layer,
-                          // codec_head rows 12b .. 12b+11
+  // QKV rows of this block: 16b .. 16b+15 of the packed [q | k | v].  (Giving
+  // head group g's rows to the 32 blocks of its own XCD measured slower: the
+  // attention step's gather then waits on producers that share its L2.)
+  const int qkv_row0 = b * 16;
+
+  // Bulk loads (weight slices, cached K/V rows, norm gains) are issued right
+  // after a step's exchange wait has succeeded, for use one step later.  The
+  // polls of a wave complete in issue order behind its outstanding loads, so a
+  // bulk load requested while a poll is still repeating would hold that poll
+  // back by a full HBM round trip; requested after the wait, it has the
+  // step's arithmetic plus the next exchange to land.
+  Gp<16, 1, H> gq;        // Wqkv rows qkv_row0 .. +15 (two per wave); after the
+                          // last layer, codec_head rows 12b .. 12b+11
   Gp<8, 2, QD / 2> go;    // Wo rows 4b .. 4b+3, two K halves
   Gp<24, 1, H> gg;        // 12 gate|up row pairs
   Gp<8, 2, I / 2> gd;     // Wd rows 4b .. 4b+3, two K halves
   auto wqkv_row = [&](int l) {
     const bf16_t* W = a.w + (size_t)l * a.layer_stride;
-    return [=](int r) { return W + (size_t)(b * 16 + r) * H; };
+    return [=](int r) { return W + (size_t)(qkv_row0 + r) * H; };
   };
+  // the first 64 keys of this block's chunk in layer l (in bounds: keys <
+  // n_ctx <= cap; the new position is replaced in the attention step)
+  f16x8_t kr[2], vr[2];
+  auto load_kv = [&](int l) {
+    const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j = k0 + p * 32 + slot;
+      kr[p] = f16x8_t{};
+      vr[p] = f16x8_t{};
+      if (j < k1) {
+        kr[p] = *reinterpret_cast<const f16x8_t*>(a.kc + hoff + (size_t)j * HD + sub * 8);
+        vr[p] = *reinterpret_cast<const f16x8_t*>(a.vc + hoff + (size_t)j * HD + sub * 8);
+      }
+    }
+  };
+  Gain2 gin;  // input-norm gain of the next layer
   gq.load(wqkv_row(0), wave, lane);
-
-  for (int k = tid; k < H; k += NT) xres[k] = a.emb[k];
-  __syncthreads();
+  load_kv(0);
+  gin.load(a.norms);
 
   for (int l = 0; l < a.n_layers; ++l) {
     const bf16_t* Wl = a.w + (size_t)l * a.layer_stride;
@@ -244,7 +310,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     const bf16_t* Wgu = Wo + (size_t)H * QD;
     const bf16_t* Wd = Wgu + (size_t)2 * I * H;
     const float* nl = a.norms + (size_t)l * a.norm_stride;
-    const float *g_in = nl, *g_post = nl + H, *g_q = nl + 2 * H, *g_k = nl + 2 * H + HD;
+    const float *g_post = nl + H, *g_q = nl + 2 * H, *g_k = nl + 2 * H + HD;
     uint64_t* E = a.ll + (size_t)l * WORDS_PER_LAYER;
     const uint64_t* Eprev = a.ll + (size_t)(l == 0 ? a.n_layers : l - 1) * WORDS_PER_LAYER;
     uint64_t* P = a.part + (size_t)l * PART_WORDS;  // this layer's chunk partials
@@ -253,243 +319,233 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     f16_t* Vp = a.vc + hoff;
 
     // ---------------- QKV ----------------
+    float gn, gnp;  // QK-norm gains of this thread's attention channel and of its RoPE partner
+    float2 cs;      // RoPE (cos, sin) of this thread's pair
     {
-      LLWait<2> w5;
-      if (l > 0) w5.issue(Eprev + OFF_E5, H);
-      Gain2 gin;
-      gin.load(g_in);
-      // the first 64 keys of this block's chunk, for the attention step (in
-      // bounds: keys < n_ctx <= cap; the new position is replaced later)
-      f16x8_t kr[2], vr[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int j = k0 + p * 32 + slot;
-        kr[p] = f16x8_t{};
-        vr[p] = f16x8_t{};
-        if (j < k1) {
-          kr[p] = *reinterpret_cast<const f16x8_t*>(Kp + (size_t)j * HD + sub * 8);
-          vr[p] = *reinterpret_cast<const f16x8_t*>(Vp + (size_t)j * HD + sub * 8);
-        }
-      }
-      __asm__ volatile("" ::: "memory");  // keep the prefetch here, ahead of the wait
+      float ss;
+      bool bail = false;
       if (l > 0) {
-        const bool bail = !w5.finish_to(ep, a.err, xres);
-        if (__syncthreads_or(bail)) return;
+        LLWait<2> w5;
+        w5.issue(Eprev + OFF_E5, H);
+        bail = !recv_norm(w5, ep, a.err, xres, xin, gin, &ss);
+      } else {
+        const float x0 = a.emb[tid], x1 = a.emb[tid + NT];
+        xres[tid] = x0;
+        xres[tid + NT] = x1;
+        xin[tid] = x0 * gin.g0;
+        xin[tid + NT] = x1 * gin.g1;
+        ss = x0 * x0 + x1 * x1;
       }
-      rms_to(xres, gin, a.eps, xin, redw);
-      gq.dot(xin, red, wave, lane);
-      __syncthreads();
-      if (tid < 16) st_ll(E + OFF_E1 + b * 16 + tid, red[tid], ep);
+      // next step's bulk loads
+      go.load([&](int r) { return Wo + (size_t)(b * 4 + r) * QD; }, wave, lane);
+      const float* gsel = tid < 256 ? g_q : g_k;
+      gn = gsel[tid & 127];
+      gnp = gsel[(tid & 127) ^ 64];
+      cs = a.rope[(size_t)pos * (HD / 2) + (tid & 63)];
+      ss = wave_sum(ss);
+      if (lane == 0) redw[wave] = ss;
+      if (__syncthreads_or(bail)) return;
+      const float inv = inv_rms(redw, a.eps);
+      float v[2];  // rows wave and wave + 8 of this block's 16
+      gq.dot_all(xin, v, wave, lane);
+      if (lane < 2) st_ll(E + OFF_E1 + qkv_row0 + wave + NW * lane, (lane ? v[1] : v[0]) * inv, ep);
+    }
 
-      // ---------------- attention ----------------
-      // this head group's q (2 heads), k, v: one word per thread
-      float* raw = xin;  // [0,256) q, [256,384) k, [384,512) v
-      float gn;          // QK-norm gain of this thread's channel
-      float2 cs;         // RoPE (cos, sin) of this thread's pair
+    // ---------------- attention ----------------
+    {
       {
+        // q0 | q1 | k | v of head group g, one word per thread
         LLWait<1> w1;
         const int src = tid < 256 ? OFF_E1 + g * 256 + tid
                                   : (tid < 384 ? OFF_E1 + QD + g * HD + (tid - 256)
                                                : OFF_E1 + QD + KVD + g * HD + (tid - 384));
         w1.issue(E + src - tid, tid + 1);  // word tid of (E + src - tid)
-        go.load([&](int r) { return Wo + (size_t)(b * 4 + r) * QD; }, wave, lane);
-        gn = tid < 256 ? g_q[tid & 127] : g_k[tid & 127];
-        if (tid < 192) cs = a.rope[(size_t)pos * (HD / 2) + (tid & 63)];
-        const bool bail = !w1.finish(ep, a.err, [&](int, float x) { raw[tid] = x; });
+        float v = 0.f;
+        const bool bail = !w1.finish(ep, a.err, [&](int, float x) { v = x; });
+        araw[tid] = v;
+        const float sq = wave_sum(v * v);  // waves 0-1 q0, 2-3 q1, 4-5 k, 6-7 v
+        if (lane == 0) redw[wave] = sq;
         if (__syncthreads_or(bail)) return;
       }
-      // per-head RMSNorm over 128 dims: waves 0-1 q head 0, 2-3 q head 1, 4-5 k
-      {
-        const float xv = raw[tid];
-        const float ss = wave_sum(tid < 384 ? xv * xv : 0.f);
-        if (lane == 0) redw[wave] = ss;
-        __syncthreads();
-        if (tid < 384) {
-          const int hh = tid >> 7;  // 0, 1: q heads; 2: k
-          const float inv = rsqrtf((redw[2 * hh] + redw[2 * hh + 1]) / (float)HD + a.eps);
-          xin[512 + tid] = xv * inv * gn;
-        }
-        __syncthreads();
-      }
-      // NEOX RoPE on (i, i + 64); k and v round through the cache type
-      if (tid < 192) {
-        const int hh = tid >> 6, i = tid & 63;
-        const float x1 = xin[512 + hh * 128 + i], x2 = xin[512 + hh * 128 + i + 64];
-        const float y1 = x1 * cs.x - x2 * cs.y, y2 = x2 * cs.x + x1 * cs.y;
-        if (hh < 2) {
-          qs[hh][i] = y1 * scale;
-          qs[hh][i + 64] = y2 * scale;
-        } else {
-          knew[i] = (float)(f16_t)y1;
-          knew[i + 64] = (float)(f16_t)y2;
-        }
-      } else if (tid >= 384) {
-        vnew[tid - 384] = (float)(f16_t)raw[tid];
-      }
-      if (tid < G) {
-        s_m[tid] = -INFINITY;
-        s_l[tid] = 0.f;
+      // next step's bulk loads (the o_proj input comes from the merge, a
+      // further exchange away)
+      gg.load([&](int r) {
+        // unit r: logical row 12b + r/2, gate (r even) or up (r odd); rows are
+        // interleaved in blocks of 16 (gate rows, up rows)
+        const int lr = b * 12 + (r >> 1);
+        return Wgu + ((size_t)(lr >> 4) * 32 + (lr & 15) + (r & 1) * 16) * H;
+      }, wave, lane);
+      // per-head RMSNorm, NEOX RoPE on (i, i + 64); k and v round through the
+      // cache type
+      if (tid < 384) {
+        const int hh = tid >> 7, j = tid & 127;
+        const float inv = rsqrtf((redw[2 * hh] + redw[2 * hh + 1]) / (float)HD + a.eps);
+        const float xj = araw[tid] * inv * gn;
+        const float xp = araw[tid ^ 64] * inv * gnp;
+        const float y = j < 64 ? xj * cs.x - xp * cs.y : xj * cs.x + xp * cs.y;
+        if (hh < 2) qs[hh][j] = y * scale;
+        else knew[j] = (float)(f16_t)y;
+      } else {
+        vnew[tid - 384] = (float)(f16_t)araw[tid];
       }
       __syncthreads();
       if (k0 <= pos && pos < k1 && tid < HD) {  // this block owns the new position
         Kp[(size_t)pos * HD + tid] = (f16_t)knew[tid];
         Vp[(size_t)pos * HD + tid] = (f16_t)vnew[tid];
       }
-      float acc[G][8];
+      // keys [k0, k1), 64 per pass: thread (slot, sub) takes keys kb + slot and
+      // kb + 32 + slot, dims sub*8 .. +8; wave w keeps an online softmax over its
+      // 8 keys of every pass (no block barrier inside the loop)
+      float qr[G][8], kn[8], vn[8];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int e = 0; e < 8; ++e) {
+        kn[e] = knew[sub * 8 + e];
+        vn[e] = vnew[sub * 8 + e];
+#pragma unroll
+        for (int h = 0; h < G; ++h) qr[h][e] = qs[h][sub * 8 + e];
+      }
+      float acc[G][8];
+      float m_run[G], l_run[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-      // q of this thread's 8 dims, both heads of the group
-      float qr[G][8];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qr[h][e] = qs[h][sub * 8 + e];
-      // one sub-chunk of 64 keys [kb, kb + 64) from registers kk / vv
-      auto sub_chunk = [&](int kb, f16x8_t (&kk)[2], f16x8_t (&vv)[2]) {
-        if (kb <= pos && pos < kb + 64) {  // the new position: take the fresh K/V
+      }
+      for (int kb = k0; kb < k1; kb += 64) {
+        if (kb != k0) {  // contexts above 32 x 64 keys
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            if (kb + p * 32 + slot == pos) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                kk[p][e] = (f16_t)knew[sub * 8 + e];
-                vv[p][e] = (f16_t)vnew[sub * 8 + e];
-              }
+            const int j = kb + p * 32 + slot;
+            kr[p] = f16x8_t{};
+            vr[p] = f16x8_t{};
+            if (j < k1) {
+              kr[p] = *reinterpret_cast<const f16x8_t*>(Kp + (size_t)j * HD + sub * 8);
+              vr[p] = *reinterpret_cast<const f16x8_t*>(Vp + (size_t)j * HD + sub * 8);
             }
           }
         }
-        // scores: 16 lanes per key, 8 dims per lane
+        float s[2][G], vf[2][8];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int jl = p * 32 + slot, j = kb + jl;
+          const int j = kb + p * 32 + slot;
+          const bool fresh = j == pos;  // the new position: take the fresh K/V
           float kf[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = (float)kk[p][e];
+          for (int e = 0; e < 8; ++e) {
+            kf[e] = fresh ? kn[e] : (float)kr[p][e];
+            vf[p][e] = fresh ? vn[e] : (float)vr[p][e];
+          }
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float d = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) d = fmaf(qr[h][e], kf[e], d);
             d = group_sum<16>(d);
-            if (sub == 0) sp[h][jl] = j < k1 ? d : -INFINITY;
+            s[p][h] = j < k1 ? d : -INFINITY;
           }
         }
-        __syncthreads();
-        if (wave < G) {  // online softmax, one wave per query head
-          const int h = wave;
-          const float s = sp[h][lane];
-          const float mold = s_m[h];
-          const float mnew = fmaxf(mold, wave_max(s));
-          const float pv = (s == -INFINITY) ? 0.f : __expf(s - mnew);
-          sp[h][lane] = pv;
-          const float ps = wave_sum(pv);
-          if (lane == 0) {
-            const float alpha = (mold == -INFINITY) ? 0.f : __expf(mold - mnew);
-            s_alpha[h] = alpha;
-            s_l[h] = s_l[h] * alpha + ps;
-            s_m[h] = mnew;
-          }
-        }
-        __syncthreads();
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float al = s_alpha[h];
+          const float mx = wave_max(fmaxf(s[0][h], s[1][h]));
+          const float m_new = fmaxf(m_run[h], mx);
+          if (m_new == -INFINITY) continue;  // no key of this wave yet (uniform)
+          const float alpha = m_run[h] == -INFINITY ? 0.f : __expf(m_run[h] - m_new);
+          const float p0 = s[0][h] == -INFINITY ? 0.f : __expf(s[0][h] - m_new);
+          const float p1 = s[1][h] == -INFINITY ? 0.f : __expf(s[1][h] - m_new);
+          l_run[h] = l_run[h] * alpha + wave_sum(sub == 0 ? p0 + p1 : 0.f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p1, vf[1][e], fmaf(p0, vf[0][e], acc[h][e] * alpha));
+          m_run[h] = m_new;
         }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int jl = p * 32 + slot;
-          float vf[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = (float)vv[p][e];
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            // keys past the chunk have probability 0; their (unloaded)
-            // registers are zeroed first so no stale value can reach acc
-            const float pv = sp[h][jl];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
-          }
-        }
-        __syncthreads();
-      };
-      if (k0 < k1) sub_chunk(k0, kr, vr);
-      for (int kb = k0 + 64; kb < k1; kb += 64) {  // contexts above 32 x 64 keys
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int j = kb + p * 32 + slot;
-          kr[p] = f16x8_t{};
-          vr[p] = f16x8_t{};
-          if (j < k1) {
-            kr[p] = *reinterpret_cast<const f16x8_t*>(Kp + (size_t)j * HD + sub * 8);
-            vr[p] = *reinterpret_cast<const f16x8_t*>(Vp + (size_t)j * HD + sub * 8);
-          }
-        }
-        sub_chunk(kb, kr, vr);
       }
-      // reduce the 32 key slots; publish this chunk's (o, m, l) as words
+      // sum the wave's 4 key groups (lanes 16 apart share the dims), then
+      // combine the 8 waves with per-wave scales
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ored[slot][h * HD + sub * 8 + e] = acc[h][e];
-      __syncthreads();
-      // partial words of (head g, query head h, chunk c) at
-      // P + ((g * G + h) * NCH + c) * (HD + 2): o[128], m, l
-      if (tid < G * HD) {
-        float o = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < 32; ++s) o += ored[s][tid];
-        st_ll(P + ((size_t)(g * G + (tid >> 7)) * NCH + c) * (HD + 2) + (tid & 127), o, ep);
-      } else if (tid < G * HD + G) {
-        const int h = tid - G * HD;
-        const bool empty = k0 >= k1;
-        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * (HD + 2);
-        st_ll(pw + HD, empty ? -INFINITY : s_m[h], ep);
-        st_ll(pw + HD + 1, empty ? 0.f : s_l[h], ep);
+        for (int e = 0; e < 8; ++e) {
+          float t = acc[h][e];
+          t += __shfl_xor(t, 16);
+          t += __shfl_xor(t, 32);
+          acc[h][e] = t;
+        }
+      if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ored[wave][h * HD + sub * 8 + e] = acc[h][e];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          mw[wave][h] = m_run[h];
+          lw[wave][h] = l_run[h];
+        }
       }
       __syncthreads();
+      // partial words of (head g, query head h, chunk c) at
+      // P + ((g * G + h) * NCH + c) * (HD + 2): o[128] (unnormalised), m, l
+      if (tid < G * HD + G) {
+        const int h = tid < G * HD ? tid >> 7 : tid - G * HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][h]);
+        float sc[NW];
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          sc[w] = mw[w][h] == -INFINITY ? 0.f : __expf(mw[w][h] - M);
+          L = fmaf(sc[w], lw[w][h], L);
+        }
+        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * (HD + 2);
+        if (tid < G * HD) {
+          const int d = tid & 127;
+          float o = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) o = fmaf(sc[w], ored[w][h * HD + d], o);
+          st_ll(pw + d, o, ep);
+        } else {
+          st_ll(pw + HD, M, ep);  // -inf and 0 for a chunk past the context
+          st_ll(pw + HD + 1, L, ep);
+        }
+      }
     }
     if (c < G) {  // chunk blocks 0 and 1 merge query heads 2g and 2g+1 (log-sum-exp)
       const int h = c;
       constexpr int NWD = NCH * (HD + 2);
+      float* pb = &ored[0][0];  // [NCH][HD + 2]
+      __syncthreads();          // every wave is done reading ored
       LLWait<(NWD + NT - 1) / NT> wp;
       wp.issue(P + (size_t)(g * G + h) * NWD, NWD);
-      const bool bail = !wp.finish(ep, a.err, [&](int i, float x) {
-        const int cc = i / (HD + 2), k = i % (HD + 2);
-        if (k < HD) ored[cc][k] = x;
-        else mlbuf[cc][0][k - HD] = x;
-      });
+      const bool bail = !wp.finish(ep, a.err, [&](int i, float x) { pb[i] = x; });
       if (__syncthreads_or(bail)) return;
       if (tid < HD) {
         float M = -INFINITY;
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) M = fmaxf(M, mlbuf[cc][0][0]);
+        for (int cc = 0; cc < NCH; ++cc) M = fmaxf(M, pb[cc * (HD + 2) + HD]);
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) {
-          const float lc = mlbuf[cc][0][1];
-          const float wgt = lc > 0.f ? __expf(mlbuf[cc][0][0] - M) : 0.f;
+          const float lc = pb[cc * (HD + 2) + HD + 1];
+          const float wgt = lc > 0.f ? __expf(pb[cc * (HD + 2) + HD] - M) : 0.f;
           L = fmaf(wgt, lc, L);
-          o = fmaf(wgt, ored[cc][tid], o);
+          o = fmaf(wgt, pb[cc * (HD + 2) + tid], o);
         }
         st_ll(E + OFF_E2 + (g * G + h) * HD + tid, o / L, ep);
       }
     }
 
     // ---------------- o_proj + residual ----------------
+    Gain2 gpost;
     {
       LLWait<4> w2;
       w2.issue(E + OFF_E2, QD);
-      // unit r of the gate|up step: logical row 12b + r/2, gate (r even) or
-      // up (r odd); rows are interleaved in blocks of 16 (gate rows, up rows)
-      gg.load([&](int r) {
-        const int lr = b * 12 + (r >> 1);
-        return Wgu + ((size_t)(lr >> 4) * 32 + (lr & 15) + (r & 1) * 16) * H;
-      }, wave, lane);
       const bool bail = !w2.finish_to(ep, a.err, xin);
+      // next step's bulk loads
+      gd.load([&](int r) { return Wd + (size_t)(b * 4 + r) * I; }, wave, lane);
+      gpost.load(g_post);
       if (__syncthreads_or(bail)) return;
       go.dot(xin, red, wave, lane);
       __syncthreads();
@@ -501,23 +557,32 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     {
       LLWait<2> w3;
       w3.issue(E + OFF_E3, H);
-      Gain2 gpost;
-      gpost.load(g_post);
-      gd.load([&](int r) { return Wd + (size_t)(b * 4 + r) * I; }, wave, lane);
-      const bool bail = !w3.finish_to(ep, a.err, xres);
+      float ss;
+      const bool bail = !recv_norm(w3, ep, a.err, xres, xin, gpost, &ss);
+      // next step's bulk loads: the next layer's QKV slice (or the head),
+      // its input-norm gain and its cached keys
+      if (l + 1 < a.n_layers) {
+        gq.load(wqkv_row(l + 1), wave, lane);
+        gin.load(a.norms + (size_t)(l + 1) * a.norm_stride);
+        load_kv(l + 1);
+      } else {
+        gq.load([&](int r) { return a.head + (size_t)(b * 12 + r) * H; }, wave, lane, 12);
+        gin.load(a.g_final);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) redw[wave] = ss;
       if (__syncthreads_or(bail)) return;
-      rms_to(xres, gpost, a.eps, xin, redw);
+      const float inv = inv_rms(redw, a.eps);
       gg.dot(xin, red, wave, lane);
       __syncthreads();
-      if (tid < 12) st_ll(E + OFF_E4 + b * 12 + tid, silu_f(red[2 * tid]) * red[2 * tid + 1], ep);
+      if (tid < 12)
+        st_ll(E + OFF_E4 + b * 12 + tid, silu_f(red[2 * tid] * inv) * (red[2 * tid + 1] * inv), ep);
     }
 
     // ---------------- down + residual ----------------
     {
       LLWait<6> w4;
       w4.issue(E + OFF_E4, I);
-      if (l + 1 < a.n_layers) gq.load(wqkv_row(l + 1), wave, lane);
-      else gq.load([&](int r) { return a.head + (size_t)(b * 12 + r) * H; }, wave, lane, 12);
       const bool bail = !w4.finish_to(ep, a.err, xin);
       if (__syncthreads_or(bail)) return;
       gd.dot(xin, red, wave, lane);
@@ -528,20 +593,21 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   }
 
   // ---------------- final norm + codec head ----------------
-  Gain2 gfin;
   {
     LLWait<2> w5;
     w5.issue(a.ll + (size_t)(a.n_layers - 1) * WORDS_PER_LAYER + OFF_E5, H);
-    gfin.load(a.g_final);
-    const bool bail = !w5.finish_to(ep, a.err, xres);
+    float ss;
+    const bool bail = !recv_norm(w5, ep, a.err, xres, xin, gin, &ss);  // gin = final gain
+    ss = wave_sum(ss);
+    if (lane == 0) redw[wave] = ss;
     if (__syncthreads_or(bail)) return;
+    const float inv = inv_rms(redw, a.eps);
+    if (b == 0 && a.hidden_out)
+      for (int k = tid; k < H; k += NT) a.hidden_out[k] = xin[k] * inv;
+    gq.dot(xin, red, wave, lane);
+    __syncthreads();
+    if (tid < 12) a.logits[b * 12 + tid] = red[tid] * inv;
   }
-  rms_to(xres, gfin, a.eps, xin, redw);
-  if (b == 0 && a.hidden_out)
-    for (int k = tid; k < H; k += NT) a.hidden_out[k] = xin[k];
-  gq.dot(xin, red, wave, lane);
-  __syncthreads();
-  if (tid < 12) a.logits[b * 12 + tid] = red[tid];
 }
 
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
