@@ -251,7 +251,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t ep = a.epoch;
+  // exchange words carry epoch (launch epoch * 64 + layer); layers of equal
+  // parity share one buffer region (see the layer loop)
+  const uint32_t ep0 = a.epoch * 64u;
   const int pos = a.pos;
   const int n_ctx = pos + 1;
   // attention role of this block: KV head g (= the XCD it runs on), key chunk
@@ -311,9 +313,15 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     const bf16_t* Wd = Wgu + (size_t)2 * I * H;
     const float* nl = a.norms + (size_t)l * a.norm_stride;
     const float *g_post = nl + H, *g_q = nl + 2 * H, *g_k = nl + 2 * H + HD;
-    uint64_t* E = a.ll + (size_t)l * WORDS_PER_LAYER;
-    const uint64_t* Eprev = a.ll + (size_t)(l == 0 ? a.n_layers : l - 1) * WORDS_PER_LAYER;
-    uint64_t* P = a.part + (size_t)l * PART_WORDS;  // this layer's chunk partials
+    // Layers l and l + 2 share the exchange and partial regions (parity
+    // double buffering keeps them cache-resident).  Reuse is safe: a block
+    // writes layer l + 2's words only after it has received layer l + 1 words
+    // from every block, and every block produced those after it finished
+    // reading layer l's words.  The epoch tells the two layers apart.
+    const uint32_t ep = ep0 + (uint32_t)l;
+    uint64_t* E = a.ll + (size_t)(l & 1) * WORDS_PER_LAYER;
+    const uint64_t* Eprev = a.ll + (size_t)((l + 1) & 1) * WORDS_PER_LAYER;
+    uint64_t* P = a.part + (size_t)(l & 1) * PART_WORDS;  // this layer's chunk partials
     const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
     f16_t* Kp = a.kc + hoff;
     f16_t* Vp = a.vc + hoff;
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       if (l > 0) {
         LLWait<2> w5;
         w5.issue(Eprev + OFF_E5, H);
-        bail = !recv_norm(w5, ep, a.err, xres, xin, gin, &ss);
+        bail = !recv_norm(w5, ep - 1, a.err, xres, xin, gin, &ss);  // layer l - 1's output
       } else {
         const float x0 = a.emb[tid], x1 = a.emb[tid + NT];
         xres[tid] = x0;
@@ -460,23 +468,11 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
           m_run[h] = m_new;
         }
       }
-      // sum the wave's 4 key groups (lanes 16 apart share the dims), then
-      // combine the 8 waves with per-wave scales
+      // combine the 32 slots (8 waves x 4 key groups) with per-wave scales
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float t = acc[h][e];
-          t += __shfl_xor(t, 16);
-          t += __shfl_xor(t, 32);
-          acc[h][e] = t;
-        }
-      if (lane < 16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ored[wave][h * HD + sub * 8 + e] = acc[h][e];
-      }
+        for (int e = 0; e < 8; ++e) ored[slot][h * HD + sub * 8 + e] = acc[h][e];
       if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -504,7 +500,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
           const int d = tid & 127;
           float o = 0.f;
 #pragma unroll
-          for (int w = 0; w < NW; ++w) o = fmaf(sc[w], ored[w][h * HD + d], o);
+          for (int sl = 0; sl < NCH; ++sl) o = fmaf(sc[sl >> 2], ored[sl][h * HD + d], o);
           st_ll(pw + d, o, ep);
         } else {
           st_ll(pw + HD, M, ep);  // -inf and 0 for a chunk past the context
@@ -595,9 +591,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   // ---------------- final norm + codec head ----------------
   {
     LLWait<2> w5;
-    w5.issue(a.ll + (size_t)(a.n_layers - 1) * WORDS_PER_LAYER + OFF_E5, H);
+    w5.issue(a.ll + (size_t)((a.n_layers - 1) & 1) * WORDS_PER_LAYER + OFF_E5, H);
     float ss;
-    const bool bail = !recv_norm(w5, ep, a.err, xres, xin, gin, &ss);  // gin = final gain
+    const bool bail = !recv_norm(w5, ep0 + (uint32_t)(a.n_layers - 1), a.err, xres, xin, gin, &ss);  // gin = final gain
     ss = wave_sum(ss);
     if (lane == 0) redw[wave] = ss;
     if (__syncthreads_or(bail)) return;
@@ -616,8 +612,8 @@ bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vo
          vocab == pd::V && n_heads == pd::NQ && n_kv_heads == pd::NKV && head_dim == pd::HD;
 }
 
-size_t fused_decode_ll_words(int n_layers) { return (size_t)(n_layers + 1) * pd::WORDS_PER_LAYER; }
-size_t fused_decode_part_words(int n_layers) { return (size_t)n_layers * pd::PART_WORDS; }
+size_t fused_decode_ll_words(int) { return (size_t)2 * pd::WORDS_PER_LAYER; }
+size_t fused_decode_part_words(int) { return (size_t)2 * pd::PART_WORDS; }
 int fused_decode_blocks() { return pd::NB; }
 int fused_decode_threads() { return pd::NT; }
 

@@ -123,10 +123,11 @@ struct FusedDecodeArgs {
   const float* emb;
   float* logits;
   float* hidden_out;
-  uint64_t* ll;    // [n_layers + 1][words per layer] exchange words
-  uint64_t* part;  // [n_layers][NKV][NCH][G][HD + 2] chunk partials, as words
+  uint64_t* ll;    // [2][words per layer] exchange words (layer parity)
+  uint64_t* part;  // [2][NKV][G][NCH][HD + 2] chunk partials, as words
   int* err;
-  uint32_t epoch;
+  uint32_t epoch;  // >= 1 and < 2^26; words carry epoch * 64 + layer
+
 };
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim);

@@ -304,6 +304,12 @@ struct Fwd {
     a.ll = c->ll;
     a.part = c->fpart;
     a.err = c->ferr;
+    if (c->epoch + 1 >= (1u << 26)) {  // epochs would wrap: clear the words and restart
+      if (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, st) != hipSuccess ||
+          hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, st) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot clear the decode exchange words");
+      c->epoch = 0;
+    }
     a.epoch = c->epoch + 1;
     const hipError_t e = launch_decode_fused(a, st, c->coop);
     if (e != hipSuccess)
@@ -400,6 +406,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   const char* env_coop = getenv("QTALK_COOPERATIVE");
   c->coop = !(env_coop && env_coop[0] == '0');
   c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') &&
+             g.n_layers <= 64 &&
              fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
              fused_decode_fits();
