@@ -261,6 +261,47 @@ class TalkerOracle:
             return logits, hidden
         return logits[0], hidden[0]
 
+    def extend_rows(self, seq: int, emb: np.ndarray, rows: Sequence[int]):
+        """Append ``T`` rows at ``cur_len`` like :meth:`extend`, but return
+        (logits, hidden) only for the listed rows (indices into ``emb``).
+
+        One-layer models only: there the cache a row writes depends on that
+        row's embedding alone (input RMSNorm, K/V projection, QK-norm, RoPE),
+        and a row's output depends on its own query and the cache up to its
+        position, so the attention of the other rows never has to be formed.
+        This lets the long-context workloads be checked on sampled rows
+        ("qwentts.cpp src/talker-forward.h", ``talker_layer_forward``: the
+        per-row attention over the cache window).
+        """
+        s = self.s
+        if self.L != 1:
+            raise ValueError("extend_rows needs a one-layer model")
+        emb = np.asarray(emb)
+        T = emb.shape[0]
+        p0 = self.cur_len[seq]
+        if p0 + T > s.cap:
+            raise OverflowError("KV capacity exceeded")
+        self._reserve(seq, p0 + T)
+        w = self.layers[0]
+        x = emb.astype(self.dtype)
+        pos = p0 + np.arange(T)
+        h = rms_norm(x, w["g_in"], s.rms_eps)
+        k = (h @ w["wk"].T).reshape(T, s.n_kv_heads, s.head_dim)
+        v = (h @ w["wv"].T).reshape(T, s.n_kv_heads, s.head_dim)
+        k = rope_neox(rms_norm(k, w["g_k"], s.rms_eps), pos[:, None], s.rope_theta)
+        self.kc[seq][0, :, p0:p0 + T, :] = round_kv(k.transpose(1, 0, 2), s.kv_dtype, self.dtype)
+        self.vc[seq][0, :, p0:p0 + T, :] = round_kv(v.transpose(1, 0, 2), s.kv_dtype, self.dtype)
+        self.cur_len[seq] = p0 + T
+        r = np.asarray(list(rows), dtype=np.int64)
+        hr = h[r]
+        q = (hr @ w["wq"].T).reshape(len(r), s.n_heads, s.head_dim)
+        q = rope_neox(rms_norm(q, w["g_q"], s.rms_eps), pos[r][:, None], s.rope_theta)
+        o = causal_gqa_attention(q, self.kc[seq][0], self.vc[seq][0], pos[r], self.scale)
+        xr = x[r] + o.reshape(len(r), s.q_dim) @ w["wo"].T
+        h2 = rms_norm(xr, w["g_post"], s.rms_eps)
+        xr = xr + swiglu(h2 @ w["wg"].T, h2 @ w["wu"].T) @ w["wd"].T
+        return self.head(xr)
+
     def prefill(self, seq: int, emb: np.ndarray, all_rows: bool = False):
         """Rewind ``seq`` to 0, then write ``T`` positions."""
         s = self.s

@@ -311,6 +311,83 @@ def test_batched_ragged_decode_16_sequences():
                for k in range(steps))
 
 
+# -- long context with outlier channels -----------------------------------------
+
+
+def test_long_context_outliers_one_layer_32k_sampled_rows():
+    # the 32k workload's embeddings (+-3e4 on four channels) through one real
+    # layer: 16 chunks of 2048 rows to 32768 positions, then decode steps;
+    # the oracle forms only the rows the GPU reports (the last row of every
+    # chunk, each decode step), which a one-layer model allows
+    name = "talker_28l_ctx32k_outlier"
+    shape = workload(name)
+    w = weights_for(name, 1)
+    say(f"[case] {name}, one layer, 16 x 2048 rows then 16 decode steps")
+    emb = prefill_embeddings(shape, shape.prefill_len)
+    assert np.abs(emb).max() > 2.9e4
+    orc = TalkerOracle(shape, w)
+    tk = _talker(shape, w)
+    errs = []
+    for ci, c0 in enumerate(range(0, shape.prefill_len, shape.chunk)):
+        chunk = emb[c0:c0 + shape.chunk]
+        lo, _ = orc.extend_rows(0, chunk, [len(chunk) - 1])
+        lg = tk.prefill(0, dev(chunk)) if ci == 0 else tk.extend(0, dev(chunk))
+        errs.append(rel_err(host(lg), lo[0]))
+        assert argmax_ok(host(lg), lo[0], TOL_BF16)
+        if ci % 4 == 3:
+            say(f"  chunk {ci}: logits rel err {errs[-1]:.2e}")
+    assert tk.kv_len(0) == shape.prefill_len
+    picks = np.array([0, 1, 2047, 2048, 16383, 30000, 32767])
+    for which in (0, 1):
+        g = host(tk.kv_read(0, 0, which))[:, picks]
+        o = orc.kv(0, 0, which)[:, picks]
+        assert rel_err(g, o) <= TOL_BF16
+    for k in range(16):
+        e = step_embedding(shape, k)
+        lo, _ = orc.decode(0, e)
+        g = host(tk.decode(0, dev(e)))
+        errs.append(rel_err(g, lo))
+        assert argmax_ok(g, lo, TOL_BF16)
+    say(f"  logits rel err max {max(errs):.2e} over 16 chunks and 16 steps")
+    assert max(errs) <= TOL_BF16
+    tk.close()
+
+
+def test_long_context_28_layers_32k_persistent_matches_per_step(monkeypatch):
+    # the full 28-layer model at 32k positions (outlier embeddings): the
+    # persistent decode, which walks 1025 keys per chunk block here, against
+    # the per-step decode kernels on the same cache contents; every logit
+    # finite (the f32 sums of squares carry the 3e4 channels)
+    name = "talker_28l_ctx32k_outlier"
+    shape = workload(name)
+    w = weights_for(name)
+    say(f"[case] {name}: 28 layers, 16 x 2048 rows then 24 decode steps, two paths")
+    emb = prefill_embeddings(shape, shape.prefill_len)
+    tks = []
+    for fused in ("1", "0"):
+        monkeypatch.setenv("QTALK_FUSED_DECODE", fused)
+        tks.append(_talker(shape, w))
+    monkeypatch.delenv("QTALK_FUSED_DECODE")
+    last = []
+    for tk in tks:
+        for ci, c0 in enumerate(range(0, shape.prefill_len, shape.chunk)):
+            chunk = dev(emb[c0:c0 + shape.chunk])
+            lg = tk.prefill(0, chunk) if ci == 0 else tk.extend(0, chunk)
+        last.append(host(lg))
+        assert tk.kv_len(0) == shape.prefill_len
+    assert np.array_equal(last[0], last[1])  # same prefill kernels on both
+    worst = 0.0
+    for k in range(24):
+        e = dev(step_embedding(shape, k))
+        a, b = host(tks[0].decode(0, e)), host(tks[1].decode(0, e))
+        worst = max(worst, rel_err(a, b))
+        assert argmax_ok(a, b, TOL_BF16)
+    say(f"  persistent vs per-step decode at 32k: rel diff max {worst:.2e}")
+    assert worst <= TOL_BF16
+    for tk in tks:
+        tk.close()
+
+
 # -- persistent batch-1 decode --------------------------------------------------
 
 

@@ -8,7 +8,7 @@ import torch
 
 import oracle.talker as ot
 from oracle import TalkerOracle
-from synth import TalkerShape, make_weights, prefill_embeddings, step_embedding
+from synth import TalkerShape, make_weights, prefill_embeddings, step_embedding, workload
 
 
 def small_shape(**kw):
@@ -339,3 +339,26 @@ def test_planted_swapped_gate_up_is_caught(monkeypatch):
     monkeypatch.setattr(ot, "swiglu", lambda g, u: ot.silu(u) * g)
     with pytest.raises(AssertionError):
         test_oracle_matches_transformers_qwen3_all_rows()
+
+
+def test_sampled_rows_equal_full_extend_on_one_layer():
+    # the sampled-row path of the long-context checks is the full extend
+    # restricted to the listed rows (same cache, same outputs)
+    shape = workload("tiny_f32_2l").with_(cap=64)
+    w = make_weights(shape, n_layers=1)
+    emb = prefill_embeddings(shape, 40)
+    full = TalkerOracle(shape, w)
+    lf, hf = full.prefill(0, emb[:25], all_rows=True)
+    lf2, hf2 = full.extend(0, emb[25:], all_rows=True)
+    samp = TalkerOracle(shape, w)
+    rows1 = [0, 7, 24]
+    ls, hs = samp.extend_rows(0, emb[:25], rows1)
+    rows2 = [0, 3, 14]
+    ls2, hs2 = samp.extend_rows(0, emb[25:], rows2)
+    np.testing.assert_allclose(ls, lf[rows1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hs2, hf2[rows2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ls2, lf2[rows2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(samp.kv(0, 0, 0), full.kv(0, 0, 0))
+    np.testing.assert_array_equal(samp.kv(0, 0, 1), full.kv(0, 0, 1))
+    with pytest.raises(ValueError):
+        TalkerOracle(shape, make_weights(shape)).extend_rows(0, emb[:4], [0])
