@@ -13,8 +13,10 @@ resident in device memory before the timed region starts.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,6 +58,37 @@ def prefill_flops(s, T: int, p0: int = 0) -> float:
     return proj + attn + 2.0 * s.vocab * s.hidden
 
 
+DECODE_SOURCES = ("qwen3_tts_talker_amd/csrc/k_decode_fused.hip",
+                  "qwen3_tts_talker_amd/csrc/kernels.h",
+                  "qwen3_tts_talker_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_fused_talker28_kv2k_pmc.md")
+
+
+def decode_source_digest() -> str:
+    """sha256 over the persistent decode kernel's sources (the counters in
+    profiles/ apply only to the kernel they were taken on)."""
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a device copy of known size),
+    or None when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    d = re.search(r"decode_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not d or d.group(1) != decode_source_digest():
+        return None
+    return float(m.group(1))
+
+
 def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
     """The oracle (float64 NumPy) on this host: a bounded sample of the same
     workload — the 1920-row prefill, then `n_steps` decode steps."""
@@ -94,6 +127,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="talker_28l_kv2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--pmc-calibration-mib", type=int, default=0,
+                    help="before the timed region, copy this many MiB device to "
+                         "device (a known-size reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -138,6 +174,14 @@ def main(argv=None):
     pre_ms = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(args.prefill_reps))
     pre_med = pre_ms[len(pre_ms) // 2]
 
+    if args.pmc_calibration_mib > 0:
+        n = args.pmc_calibration_mib << 18  # float32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # decode warmup from context T, then rewind and time K steps
     for k in range(args.warmup):
         s = lib.qtalk_decode(ctx, 0, steps[k % K].data_ptr(), logits.data_ptr(), None)
@@ -160,9 +204,11 @@ def main(argv=None):
 
     alg_bytes = sum(decode_bytes(shape, T + k + 1) for k in range(K))
     achieved = alg_bytes / (total_ms / 1e3) / 1e9
+    traffic = measured_traffic()
     roof = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None if traffic is None else int(traffic),
         "kernel": ("k_decode_fused (one persistent launch per token)"
                    if os.environ.get("QTALK_FUSED_DECODE", "1") != "0"
                    else "decode step (all launches of one token)"),
