@@ -59,7 +59,7 @@ struct KVIO<f16_t> {
 template <int HD, typename KVT>
 __global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
   constexpr int HALF = HD / 2;
-  const int t = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int t = blockIdx.x, hh = blockIdx.y + (a.skip_q ? a.n_heads : 0), lane = threadIdx.x;
   const int nq = a.n_heads, nkv = a.n_kv_heads;
   float* row = a.qkv + (size_t)t * a.ldqkv;
   const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
 }
 
 void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st) {
-  const dim3 grid(a.rows.n, a.n_heads + 2 * a.n_kv_heads);
+  const dim3 grid(a.rows.n, (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads);
   if (a.head_dim == 128) {
     if (kv_f16) hipLaunchKernelGGL((k_qk_rope_append<128, f16_t>), grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL((k_qk_rope_append<128, float>), grid, dim3(64), 0, st, a);

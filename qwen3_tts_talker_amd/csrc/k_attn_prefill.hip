@@ -1,17 +1,25 @@
 // Causal GQA prefill attention on the matrix cores, reading the f16 KV cache.
 //
 // Semantics as the per-row attention ("qwentts.cpp src/talker-forward.h",
-// talker_layer_forward: scores q.k / sqrt(head_dim) over the cache window,
-// causal mask key <= position, softmax, weighted sum of V; "transcribe.cpp
-// src/causal_lm/causal_lm.cpp", block_prefill: query head h reads KV head
-// h / (n_heads / n_kv_heads)).  The rows' own K/V were appended to the cache
-// before this kernel runs, so keys are read back in their cache precision.
+// talker_layer_forward: per-head RMSNorm of q with the shared q_norm gain,
+// NEOX RoPE at the absolute position, scores q.k / sqrt(head_dim) over the
+// cache window, causal mask key <= position, softmax, weighted sum of V;
+// "transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill: query head h
+// reads KV head h / (n_heads / n_kv_heads)).  The rows' own K/V were
+// appended to the cache before this kernel runs, so keys are read back in
+// their cache precision.  q arrives raw from the QKV projection; its QK-norm
+// and RoPE are applied here, on the fragment each lane already holds.
 //
-// Work split: a block owns one KV head g and PB consecutive positions; its 4
-// waves each own 32 positions of one query head of the group, so one staging
-// of a 64-key K/V tile in LDS serves every query head that shares it.  Per
-// wave and tile (flash-attention order, online softmax in float32):
-//   S^T[key][row] = K . Q^T   v_mfma_f32_32x32x16_f16, A = K tile rows, B = q
+// Work split (two query heads per KV head): a block owns one KV head g and
+// 32 consecutive positions; its 4 waves are (query head of the group) x (key
+// half), so one staging of a 64-key K/V tile in LDS serves both query heads,
+// and each wave runs the MFMAs of one 32-key half of every tile with its own
+// online softmax.  The two halves are merged (log-sum-exp) at the end.  Small
+// blocks (480 of them at 2048 rows) spread the causal triangle over all CUs
+// two blocks deep, longest first.
+//
+// Per wave and tile (flash-attention order, softmax state in float32):
+//   S^T[key][row] = K . Q^T   v_mfma_f32_32x32x16_f16, A = K rows, B = q
 //   P = exp2(S' - m)          S' carries 1/sqrt(hd) * log2(e) through q
 //   O^T[hd][row] += V^T . P^T v_mfma_f32_32x32x16_f16, A = V^T (LDS), B = P
 // Computing the transposed products makes the score accumulator of a lane
@@ -27,6 +35,8 @@ namespace pa {
 constexpr int NWV = 4;        // waves per block
 constexpr int NT = NWV * 64;  // threads per block
 constexpr int KT = 64;        // keys per tile
+constexpr int PB = 32;        // positions per block
+constexpr int G = 2;          // query heads per KV head
 
 // key (0..31) held by score-tile row m: m = a*8 + h*4 + b -> (a>>1)*16 + h*8 + (a&1)*4 + b
 __device__ __forceinline__ int tau(int m) {
@@ -43,19 +53,21 @@ __device__ __forceinline__ int vt_index(int d, int key) {
 
 }  // namespace pa
 
-template <int HD, int G>
+template <int HD>
 __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   using namespace pa;
-  constexpr int PB = 32 * NWV / G;  // positions per block
-  constexpr int KSTR = HD + 8;      // K row stride in LDS (halfs)
-  constexpr int NKS = HD / 16;      // k-steps of the score product
-  constexpr int NMT = HD / 32;      // hd tiles of the value product
-  constexpr int CPR = HD / 8;       // 16-byte chunks per key row
-  constexpr int NLD = KT * CPR / NT;         // K chunks per thread per tile
+  constexpr int KSTR = HD + 8;              // K row stride in LDS (halfs)
+  constexpr int NKS = HD / 16;              // k-steps of the score product
+  constexpr int NMT = HD / 32;              // hd tiles of the value product
+  constexpr int CPR = HD / 8;               // 16-byte chunks per key row
+  constexpr int NLD = KT * CPR / NT;        // K chunks per thread per tile
   constexpr int NLDV = KT / 2 * CPR / NT;   // V chunk pairs per thread per tile
   static_assert(KT * CPR % NT == 0 && KT / 2 * CPR % NT == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) f16_t Ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) f16_t Vt[HD * KT];
+  constexpr int LDS_HALFS = KT * KSTR + HD * KT;
+  __shared__ __attribute__((aligned(16))) f16_t lds[LDS_HALFS];
+  __shared__ __attribute__((aligned(16))) f16_t qlds[G * NKS * 64 * 8];  // q fragments
+  f16_t* Ks = lds;
+  f16_t* Vt = lds + KT * KSTR;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nkv = a.n_kv_heads;
@@ -67,72 +79,123 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   const int kend = P1;                      // keys [0, kend)
   const int nkt = (kend + KT - 1) / KT;
 
-  const int hq = g * G + wave % G;
-  const int Pw = P0 + (wave / G) * 32;  // wave positions [Pw, Pw + 32)
-  const bool wave_live = Pw < P1;
-  const int wave_last = min(Pw + 31, P1 - 1);
+  const int hh = wave >> 1, kh = wave & 1;  // query head of the group, key half
+  const int hq = g * G + hh;
+  const int last = P1 - 1;
   const int n = lane & 31, h = lane >> 5;
-  const int posn = Pw + n;
+  const int posn = P0 + n;
 
   const size_t head_off = (size_t)(a.seq * nkv + g) * a.cap * HD;
   const f16_t* Kg = a.kc + head_off;
   const f16_t* Vg = a.vc + head_off;
 
-  // q (B operand of the score product): row posn, hd ks*16 + h*8 .. +8
-  f16x8_t qf[NKS];
-  {
+  // q (B operand of the score product): row posn, hd ks*16 + h*8 + e.  The
+  // lane pair (n, n + 32) holds the whole head, and the RoPE partner d + 64 of
+  // hd d < 64 sits in the same lane at ks + NKS/2.  The two waves of a query
+  // head share its fragments through LDS (qlds), re-read every tile, which
+  // keeps registers free for two stages of K/V prefetch.
+  if (kh == 0) {
     const int t = min(posn - a.p0, a.T - 1);
+    const int pr = min(posn, a.p0 + a.T - 1);
     const float* qp = a.q + (size_t)t * a.ldq + (size_t)hq * HD + h * 8;
+    float qv[NKS][8];
+    float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const float4 u = *reinterpret_cast<const float4*>(qp + ks * 16);
       const float4 v = *reinterpret_cast<const float4*>(qp + ks * 16 + 4);
-      qf[ks] = f16x8_t{(f16_t)(u.x * a.qscale), (f16_t)(u.y * a.qscale), (f16_t)(u.z * a.qscale),
-                       (f16_t)(u.w * a.qscale), (f16_t)(v.x * a.qscale), (f16_t)(v.y * a.qscale),
-                       (f16_t)(v.z * a.qscale), (f16_t)(v.w * a.qscale)};
+      qv[ks][0] = u.x; qv[ks][1] = u.y; qv[ks][2] = u.z; qv[ks][3] = u.w;
+      qv[ks][4] = v.x; qv[ks][5] = v.y; qv[ks][6] = v.z; qv[ks][7] = v.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(qv[ks][e], qv[ks][e], ss);
+    }
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[ks][e] *= inv * a.g_q[ks * 16 + h * 8 + e];
+    const float2* cs = a.rope + (size_t)pr * (HD / 2) + h * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = cs[ks * 16 + e];
+        const float x1 = qv[ks][e], x2 = qv[ks + NKS / 2][e];
+        qv[ks][e] = (x1 * c.x - x2 * c.y) * a.qscale;
+        qv[ks + NKS / 2][e] = (x2 * c.x + x1 * c.y) * a.qscale;
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f16x8_t f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (f16_t)qv[ks][e];
+      *reinterpret_cast<f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]) = f;
     }
   }
 
-  // staging, per 64-key tile.  K: chunk i of this thread is key (tid + NT*i) / CPR,
-  // column chunk (tid + NT*i) % CPR (16 lanes cover one 256-byte key row).  V:
-  // the same chunk of two adjacent keys, so that the transposed store writes
-  // whole dwords (keys 2kp, 2kp+1 of one hd row).
-  uint4 rk[NLD], rv[NLDV][2];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + NT * i, key = kt * KT + idx / CPR, c = idx % CPR;
-      rk[i] = key < kend ? *reinterpret_cast<const uint4*>(Kg + (size_t)key * HD + c * 8)
-                         : make_uint4(0, 0, 0, 0);  // never-written slots read as 0
-    }
-#pragma unroll
-    for (int i = 0; i < NLDV; ++i) {
-      const int idx = tid + NT * i, key = kt * KT + 2 * (idx / CPR), c = idx % CPR;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        rv[i][u] = key + u < kend
-                       ? *reinterpret_cast<const uint4*>(Vg + (size_t)(key + u) * HD + c * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
+  // staging, per 64-key tile, in two register stages (tile kt in stage kt & 1,
+  // requested two tiles ahead of its use).  K: chunk i of this thread is key
+  // (tid + NT*i) / CPR, column chunk (tid + NT*i) % CPR (16 lanes cover one
+  // 256-byte key row).  V: the same chunk of two adjacent keys, so that the
+  // transposed store writes whole dwords (keys 2kp, 2kp+1 of one hd row).
+  // Named registers: an array here would be left in private memory.
+  static_assert(NLD == 4 || NLD == 2, "K chunks per thread");
+  static_assert(NLDV == 2 || NLDV == 1, "V pairs per thread");
+  uint4 s0k0, s0k1, s0k2, s0k3, s0v0, s0v1, s0v2, s0v3;  // stage 0
+  uint4 s1k0, s1k1, s1k2, s1k3, s1v0, s1v1, s1v2, s1v3;  // stage 1
+#define QA_LDK(I, KT)                                                                   \
+  ((KT) * KT_ + (tid + NT * (I)) / CPR < kend                                          \
+       ? *reinterpret_cast<const uint4*>(Kg + (size_t)((KT) * KT_ + (tid + NT * (I)) / CPR) * HD + \
+                                         ((tid + NT * (I)) % CPR) * 8)                  \
+       : make_uint4(0, 0, 0, 0))
+#define QA_LDV(I, U, KT)                                                                \
+  ((KT) * KT_ + 2 * ((tid + NT * (I)) / CPR) + (U) < kend                              \
+       ? *reinterpret_cast<const uint4*>(Vg + (size_t)((KT) * KT_ + 2 * ((tid + NT * (I)) / CPR) + (U)) * HD + \
+                                         ((tid + NT * (I)) % CPR) * 8)                  \
+       : make_uint4(0, 0, 0, 0))
+#define QA_GLOAD(S, KT)                                          \
+  do {                                                           \
+    const int kt_ = (KT);                                        \
+    S##k0 = QA_LDK(0, kt_);                                      \
+    S##k1 = QA_LDK(1, kt_);                                      \
+    if (NLD == 4) {                                              \
+      S##k2 = QA_LDK(2, kt_);                                    \
+      S##k3 = QA_LDK(3, kt_);                                    \
+    }                                                            \
+    S##v0 = QA_LDV(0, 0, kt_);                                   \
+    S##v1 = QA_LDV(0, 1, kt_);                                   \
+    if (NLDV == 2) {                                             \
+      S##v2 = QA_LDV(1, 0, kt_);                                 \
+      S##v3 = QA_LDV(1, 1, kt_);                                 \
+    }                                                            \
+  } while (0)
+#define QA_LSTORE(S)                                             \
+  do {                                                           \
+    store_k(0, S##k0);                                           \
+    store_k(1, S##k1);                                           \
+    if (NLD == 4) {                                              \
+      store_k(2, S##k2);                                         \
+      store_k(3, S##k3);                                         \
+    }                                                            \
+    store_v(0, S##v0, S##v1);                                    \
+    if (NLDV == 2) store_v(1, S##v2, S##v3);                     \
+  } while (0)
+  constexpr int KT_ = KT;
+  auto store_k = [&](int i, const uint4& r) {
+    const int idx = tid + NT * i, key = idx / CPR, c = idx % CPR;
+    *reinterpret_cast<uint4*>(&Ks[key * KSTR + c * 8]) = r;
   };
-  auto lstore = [&]() {
+  auto store_v = [&](int i, const uint4& r0, const uint4& r1) {
+    const int idx = tid + NT * i, key = 2 * (idx / CPR), c = idx % CPR;
+    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+    const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + NT * i, key = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<uint4*>(&Ks[key * KSTR + c * 8]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NLDV; ++i) {
-      const int idx = tid + NT * i, key = 2 * (idx / CPR), c = idx % CPR;
-      const uint32_t w0[4] = {rv[i][0].x, rv[i][0].y, rv[i][0].z, rv[i][0].w};
-      const uint32_t w1[4] = {rv[i][1].x, rv[i][1].y, rv[i][1].z, rv[i][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = c * 8 + e;
-        const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xFFFFu);
-        const uint32_t hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xFFFFu);
-        *reinterpret_cast<uint32_t*>(&Vt[vt_index(d, key)]) = lo | (hi << 16);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int d = c * 8 + e;
+      const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xFFFFu);
+      const uint32_t hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(&Vt[vt_index(d, key)]) = lo | (hi << 16);
     }
   };
 
@@ -141,119 +204,137 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // A-operand row of the score product held by this lane: key tau(n) of each 32-key half
-  const int krow = tau(n);
+  // A-operand row of the score product held by this lane: key tau(n) of this
+  // wave's 32-key half
+  const int krow = kh * 32 + tau(n);
+  const f16_t* qmine = &qlds[(hh * NKS * 64 + lane) * 8];
 
-  gload(0);
-  lstore();
+  auto compute = [&](int kt) {
+    const int kbase = kt * KT + kh * 32;  // this wave's first key
+    if (kbase > last) return;
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[krow * KSTR + ks * 16 + h * 8]);
+      const f16x8_t qf = *reinterpret_cast<const f16x8_t*>(qmine + ks * 64 * 8);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf, s, 0, 0, 0);
+    }
+    // causal mask (key <= position) where the half reaches the block's rows
+    if (kbase + 31 > P0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + (r >> 3) * 16 + h * 8 + ((r >> 2) & 1) * 4 + (r & 3);
+        if (key > posn) s[r] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new == -INFINITY) return;  // no key of this half is visible to any row yet
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    f16x8_t pf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] - m_new);  // masked: exp2(-inf) = 0
+      psum += p;
+      pf[r >> 3][r & 7] = (f16_t)p;
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
+    // O^T += V^T P^T over this half's 32 keys (2 k-steps of 16)
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(
+            &Vt[vt_index(mt * 32 + n, kh * 32 + sk * 16 + h * 8)]);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sk], o[mt], 0, 0, 0);
+      }
+  };
+
+  // loads run unconditionally (past the last tile they repeat it) so both
+  // register stages stay in registers
+  QA_GLOAD(s0, 0);
+  QA_GLOAD(s1, min(1, nkt - 1));
+  QA_LSTORE(s0);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
-    const int kbase = kt * KT;
-    if (wave_live && kbase <= wave_last) {
-      // scores of two 32-key halves
-      f32x16_t s[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const f16x8_t kf =
-              *reinterpret_cast<const f16x8_t*>(&Ks[(st * 32 + krow) * KSTR + ks * 16 + h * 8]);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[st], 0, 0, 0);
-        }
-      }
-      // causal mask (key <= position) on the tiles that reach the block's rows
-      if (kbase + KT - 1 > Pw) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + st * 32 + (r >> 3) * 16 + h * 8 + ((r >> 2) & 1) * 4 + (r & 3);
-            if (key > posn) s[st][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-      f16x8_t pf[2][2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[st][r] - m_new);  // masked: exp2(-inf) = 0
-          psum += p;
-          pf[st][r >> 3][r & 7] = (f16_t)p;
-        }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
-      // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(
-                &Vt[vt_index(mt * 32 + n, st * 32 + sk * 16 + h * 8)]);
-            o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[st][sk], o[mt], 0, 0, 0);
-          }
-    }
+  for (int kt = 0; kt < nkt; kt += 2) {
+    // tile kt in LDS, tile kt + 1 in flight in stage 1
+    QA_GLOAD(s0, min(kt + 2, nkt - 1));
+    compute(kt);
     __syncthreads();
-    if (kt + 1 < nkt) {
-      lstore();
-      __syncthreads();
-    }
+    if (kt + 1 >= nkt) break;
+    QA_LSTORE(s1);
+    __syncthreads();
+    // tile kt + 1 in LDS, tile kt + 2 in flight in stage 0
+    QA_GLOAD(s1, min(kt + 3, nkt - 1));
+    compute(kt + 1);
+    __syncthreads();
+    if (kt + 2 >= nkt) break;
+    QA_LSTORE(s0);
+    __syncthreads();
   }
+#undef QA_LDK
+#undef QA_LDV
+#undef QA_GLOAD
+#undef QA_LSTORE
 
-  if (!wave_live || posn >= P1) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
+  // merge the two key halves of each query head through LDS (the tiles are
+  // no longer needed): the key-half-1 wave hands over (m, l, O), the key-half-0
+  // wave combines and writes
+  float* xs = reinterpret_cast<float*>(lds);  // [G][64 lanes][NMT*16 + 2]
+  constexpr int XS = NMT * 16 + 2;
+  static_assert((size_t)G * 64 * XS * 4 <= sizeof(f16_t) * LDS_HALFS, "merge buffer");
+  float* mine = xs + ((size_t)hh * 64 + lane) * XS;
+  if (kh == 1) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[mt * 16 + r] = o[mt][r];
+    mine[NMT * 16] = m_run;
+    mine[NMT * 16 + 1] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1 || posn >= P1) return;
+  const float m1 = mine[NMT * 16], l1 = mine[NMT * 16 + 1];
+  const float M = fmaxf(m_run, m1);  // finite: key 0 is visible to every row
+  const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+  const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
+  const float l = l_run * a0 + l1 * a1;
+  const float inv = 1.0f / (l + __shfl_xor(l, 32));
   bf16_t* orow = a.out + (size_t)(posn - a.p0) * a.ldo + (size_t)hq * HD;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d = mt * 32 + rg * 8 + h * 4;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = (o[mt][rg * 4 + j] * a0 + mine[mt * 16 + rg * 4 + j] * a1) * inv;
       uint2 w;
-      w.x = f32_to_bf16(o[mt][rg * 4] * inv) | (f32_to_bf16(o[mt][rg * 4 + 1] * inv) << 16);
-      w.y = f32_to_bf16(o[mt][rg * 4 + 2] * inv) | (f32_to_bf16(o[mt][rg * 4 + 3] * inv) << 16);
+      w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
 }
 
 bool attn_prefill_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4);
-}
-
-template <int HD, int G>
-static void launch_hg(const PrefillAttnArgs& a, hipStream_t st) {
-  constexpr int PB = 32 * pa::NWV / G;
-  const int nqb = (a.T + PB - 1) / PB;
-  hipLaunchKernelGGL((k_attn_prefill<HD, G>), dim3(nqb * a.n_kv_heads), dim3(pa::NT), 0, st, a);
+  return (head_dim == 64 || head_dim == 128) && group == pa::G;
 }
 
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st) {
-  const int G = a.n_heads / a.n_kv_heads;
-  if (a.head_dim == 128) {
-    if (G == 1) launch_hg<128, 1>(a, st);
-    else if (G == 2) launch_hg<128, 2>(a, st);
-    else launch_hg<128, 4>(a, st);
-  } else {
-    if (G == 1) launch_hg<64, 1>(a, st);
-    else if (G == 2) launch_hg<64, 2>(a, st);
-    else launch_hg<64, 4>(a, st);
-  }
+  const int nqb = (a.T + pa::PB - 1) / pa::PB;
+  const dim3 grid(nqb * a.n_kv_heads);
+  if (a.head_dim == 128) hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(pa::NT), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(pa::NT), 0, st, a);
 }
 
 }  // namespace qtalk

@@ -39,6 +39,7 @@ struct QkArgs {
   void* kc;
   void* vc;  // cache base of this layer: [S][n_kv][cap][hd]
   int cap;
+  int skip_q;  // 1: leave q as is (the matrix-core attention norms and ropes it)
   RowMeta rows;
 };
 void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st);
@@ -66,8 +67,11 @@ void launch_attn_merge(AttnArgs a, hipStream_t st);
 // Causal GQA attention of T uniform rows (positions p0 .. p0+T-1 of one
 // sequence) over the f16 cache on the matrix cores; output bf16 rows.
 struct PrefillAttnArgs {
-  const float* q;  // q of row t, head h at q + t*ldq + h*head_dim (normed, roped)
+  const float* q;  // raw q of row t, head h at q + t*ldq + h*head_dim
   int ldq;
+  const float* g_q;     // [head_dim] QK-norm gain of q
+  float eps;
+  const float2* rope;   // [cap][head_dim/2] (cos, sin)
   const f16_t* kc;
   const f16_t* vc;  // [S][n_kv][cap][hd] of this layer
   int n_heads, n_kv_heads, head_dim, cap;

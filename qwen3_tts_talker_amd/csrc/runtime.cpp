@@ -138,7 +138,7 @@ struct Fwd {
     return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_elems * (c->kv_f16 ? 2 : 4);
   }
 
-  void qk_append(int l, const RowMeta& rows) {
+  void qk_append(int l, const RowMeta& rows, bool skip_q = false) {
     QkArgs q{};
     q.qkv = c->qkv;
     q.ldqkv = c->qkv_dim;
@@ -152,6 +152,7 @@ struct Fwd {
     q.kc = kv_layer(c->kc, l);
     q.vc = kv_layer(c->vc, l);
     q.cap = g.max_seq_len;
+    q.skip_q = skip_q ? 1 : 0;
     q.rows = rows;
     launch_qk_rope_append(c->kv_f16, q, st);
   }
@@ -219,11 +220,15 @@ struct Fwd {
     bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
     launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
-    qk_append(l, rows);
-    if (c->kv_f16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads)) {
+    const bool mfma_attn = c->kv_f16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
+    qk_append(l, rows, mfma_attn);
+    if (mfma_attn) {
       PrefillAttnArgs p{};
       p.q = c->qkv;
       p.ldq = c->qkv_dim;
+      p.g_q = L.g_q;
+      p.eps = g.rms_eps;
+      p.rope = c->rope;
       p.kc = reinterpret_cast<const f16_t*>(kv_layer(c->kc, l));
       p.vc = reinterpret_cast<const f16_t*>(kv_layer(c->vc, l));
       p.n_heads = g.n_heads;
