@@ -139,63 +139,71 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   // (tid + NT*i) / CPR, column chunk (tid + NT*i) % CPR (16 lanes cover one
   // 256-byte key row).  V: the same chunk of two adjacent keys, so that the
   // transposed store writes whole dwords (keys 2kp, 2kp+1 of one hd row).
-  // Named registers: an array here would be left in private memory.
+  // Offsets are fixed per thread; only the tile base moves.  Named registers:
+  // an array here would be left in private memory.
   static_assert(NLD == 4 || NLD == 2, "K chunks per thread");
   static_assert(NLDV == 2 || NLDV == 1, "V pairs per thread");
+  const int kkey0 = tid / CPR, kc0 = tid % CPR;  // chunk i: key kkey0 + i*(NT/CPR)
+  constexpr int KSTEP = NT / CPR;
+  const int vkey0 = 2 * (tid / CPR);             // pair i: keys vkey0 + i*2*KSTEP, +1
   uint4 s0k0, s0k1, s0k2, s0k3, s0v0, s0v1, s0v2, s0v3;  // stage 0
   uint4 s1k0, s1k1, s1k2, s1k3, s1v0, s1v1, s1v2, s1v3;  // stage 1
-#define QA_LDK(I, KT)                                                                   \
-  ((KT) * KT_ + (tid + NT * (I)) / CPR < kend                                          \
-       ? *reinterpret_cast<const uint4*>(Kg + (size_t)((KT) * KT_ + (tid + NT * (I)) / CPR) * HD + \
-                                         ((tid + NT * (I)) % CPR) * 8)                  \
-       : make_uint4(0, 0, 0, 0))
-#define QA_LDV(I, U, KT)                                                                \
-  ((KT) * KT_ + 2 * ((tid + NT * (I)) / CPR) + (U) < kend                              \
-       ? *reinterpret_cast<const uint4*>(Vg + (size_t)((KT) * KT_ + 2 * ((tid + NT * (I)) / CPR) + (U)) * HD + \
-                                         ((tid + NT * (I)) % CPR) * 8)                  \
-       : make_uint4(0, 0, 0, 0))
+  // Loads read a clamped key row (always in bounds) and run unconditionally;
+  // keys past the block's last position are zeroed when the stage is stored.
+  // (A conditional load would make the compiler drain every outstanding load
+  // at the join, the prefetch of the other stage included.)
+#define QA_LD(BASE, KEY) \
+  (*reinterpret_cast<const uint4*>((BASE) + (size_t)min((KEY), kend - 1) * HD + kc0 * 8))
 #define QA_GLOAD(S, KT)                                          \
   do {                                                           \
-    const int kt_ = (KT);                                        \
-    S##k0 = QA_LDK(0, kt_);                                      \
-    S##k1 = QA_LDK(1, kt_);                                      \
+    const int kb_ = (KT) * KT_;                                  \
+    S##k0 = QA_LD(Kg, kb_ + kkey0);                              \
+    S##k1 = QA_LD(Kg, kb_ + kkey0 + KSTEP);                      \
     if (NLD == 4) {                                              \
-      S##k2 = QA_LDK(2, kt_);                                    \
-      S##k3 = QA_LDK(3, kt_);                                    \
+      S##k2 = QA_LD(Kg, kb_ + kkey0 + 2 * KSTEP);                \
+      S##k3 = QA_LD(Kg, kb_ + kkey0 + 3 * KSTEP);                \
     }                                                            \
-    S##v0 = QA_LDV(0, 0, kt_);                                   \
-    S##v1 = QA_LDV(0, 1, kt_);                                   \
+    S##v0 = QA_LD(Vg, kb_ + vkey0);                              \
+    S##v1 = QA_LD(Vg, kb_ + vkey0 + 1);                          \
     if (NLDV == 2) {                                             \
-      S##v2 = QA_LDV(1, 0, kt_);                                 \
-      S##v3 = QA_LDV(1, 1, kt_);                                 \
+      S##v2 = QA_LD(Vg, kb_ + vkey0 + 2 * KSTEP);                \
+      S##v3 = QA_LD(Vg, kb_ + vkey0 + 2 * KSTEP + 1);            \
     }                                                            \
   } while (0)
-#define QA_LSTORE(S)                                             \
-  do {                                                           \
-    store_k(0, S##k0);                                           \
-    store_k(1, S##k1);                                           \
-    if (NLD == 4) {                                              \
-      store_k(2, S##k2);                                         \
-      store_k(3, S##k3);                                         \
-    }                                                            \
-    store_v(0, S##v0, S##v1);                                    \
-    if (NLDV == 2) store_v(1, S##v2, S##v3);                     \
+#define QA_LSTORE(S, KT)                                                   \
+  do {                                                                     \
+    const int kb_ = (KT) * KT_;                                            \
+    store_k(0, kb_, S##k0);                                                \
+    store_k(1, kb_, S##k1);                                                \
+    if (NLD == 4) {                                                        \
+      store_k(2, kb_, S##k2);                                              \
+      store_k(3, kb_, S##k3);                                              \
+    }                                                                      \
+    store_v(0, kb_, S##v0, S##v1);                                         \
+    if (NLDV == 2) store_v(1, kb_, S##v2, S##v3);                          \
   } while (0)
   constexpr int KT_ = KT;
-  auto store_k = [&](int i, const uint4& r) {
-    const int idx = tid + NT * i, key = idx / CPR, c = idx % CPR;
-    *reinterpret_cast<uint4*>(&Ks[key * KSTR + c * 8]) = r;
+  f16_t* const kst = &Ks[kkey0 * KSTR + kc0 * 8];
+  auto zero_past = [&](const uint4& r, int key) {
+    const bool ok = key < kend;
+    return make_uint4(ok ? r.x : 0u, ok ? r.y : 0u, ok ? r.z : 0u, ok ? r.w : 0u);
   };
-  auto store_v = [&](int i, const uint4& r0, const uint4& r1) {
-    const int idx = tid + NT * i, key = 2 * (idx / CPR), c = idx % CPR;
+  auto store_k = [&](int i, int kb, const uint4& r) {
+    *reinterpret_cast<uint4*>(kst + i * KSTEP * KSTR) = zero_past(r, kb + kkey0 + i * KSTEP);
+  };
+  // transposed V: hd row d = kc0*8 + e; its swizzle (((d >> 3) ^ d) & 7) is
+  // (kc0 ^ e) & 7, so the 8 row addresses of a pair differ only in e
+  auto store_v = [&](int i, int kb, const uint4& q0, const uint4& q1) {
+    const int key = vkey0 + i * 2 * KSTEP;
+    const uint4 r0 = zero_past(q0, kb + key), r1 = zero_past(q1, kb + key + 1);
     const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
     const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = c * 8 + e;
       const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xFFFFu);
       const uint32_t hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(&Vt[vt_index(d, key)]) = lo | (hi << 16);
+      const int d = kc0 * 8 + e;
+      *reinterpret_cast<uint32_t*>(&Vt[d * KT + (key ^ (((kc0 ^ e) & 7) << 3))]) = lo | (hi << 16);
     }
   };
 
@@ -227,9 +235,12 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
         if (key > posn) s[r] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    float t8[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    for (int r = 0; r < 8; ++r) t8[r] = fmaxf(s[r], s[r + 8]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t8[r] = fmaxf(t8[r], t8[r + 4]);
+    float mx = fmaxf(fmaxf(t8[0], t8[2]), fmaxf(t8[1], t8[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     if (m_new == -INFINITY) return;  // no key of this half is visible to any row yet
@@ -244,10 +255,12 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
       pf[r >> 3][r & 7] = (f16_t)p;
     }
     l_run = l_run * alpha + psum;
+    if (!__all(alpha == 1.0f)) {  // once the running max settles this is skipped
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
+    }
     // O^T += V^T P^T over this half's 32 keys (2 k-steps of 16)
 #pragma unroll
     for (int sk = 0; sk < 2; ++sk)
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   // register stages stay in registers
   QA_GLOAD(s0, 0);
   QA_GLOAD(s1, min(1, nkt - 1));
-  QA_LSTORE(s0);
+  QA_LSTORE(s0, 0);
   __syncthreads();
   for (int kt = 0; kt < nkt; kt += 2) {
     // tile kt in LDS, tile kt + 1 in flight in stage 1
@@ -271,18 +284,17 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
     compute(kt);
     __syncthreads();
     if (kt + 1 >= nkt) break;
-    QA_LSTORE(s1);
+    QA_LSTORE(s1, kt + 1);
     __syncthreads();
     // tile kt + 1 in LDS, tile kt + 2 in flight in stage 0
     QA_GLOAD(s1, min(kt + 3, nkt - 1));
     compute(kt + 1);
     __syncthreads();
     if (kt + 2 >= nkt) break;
-    QA_LSTORE(s0);
+    QA_LSTORE(s0, kt + 2);
     __syncthreads();
   }
-#undef QA_LDK
-#undef QA_LDV
+#undef QA_LD
 #undef QA_GLOAD
 #undef QA_LSTORE
 
