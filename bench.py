@@ -59,8 +59,8 @@ def prefill_flops(s, T: int, p0: int = 0) -> float:
 
 
 DECODE_SOURCES = ("qwen3_tts_talker_amd/csrc/k_decode_fused.hip",
-                  "qwen3_tts_talker_amd/csrc/kernels.h",
                   "qwen3_tts_talker_amd/csrc/common.h")
+DECODE_ARGS_HEADER = "qwen3_tts_talker_amd/csrc/kernels.h"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_fused_talker28_kv2k_pmc.md")
 
 
@@ -71,6 +71,10 @@ def decode_source_digest() -> str:
     for rel in DECODE_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, DECODE_ARGS_HEADER)) as f:
+        hdr = f.read()
+    m = re.search(r"struct FusedDecodeArgs \{.*?\};", hdr, re.S)
+    h.update((m.group(0) if m else hdr).encode())
     return h.hexdigest()
 
 
