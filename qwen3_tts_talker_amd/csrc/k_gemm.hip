@@ -48,22 +48,39 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
 #pragma unroll
   for (int i = 0; i < BR; ++i) Bg[i] = a.B + (size_t)(n0 + lrow + 32 * i) * K + kbeg + lchunk;
 
-  uint4 ra[AR], rb[BR];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < AR; ++i) ra[i] = *reinterpret_cast<const uint4*>(Ag[i] + kt * GB_K);
-#pragma unroll
-    for (int i = 0; i < BR; ++i)
-      rb[i] = ld_stream16(Bg[i] + kt * GB_K);
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < AR; ++i)
-      *reinterpret_cast<uint4*>(&As[(lrow + 32 * i) * G_STRIDE + lchunk]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BR; ++i)
-      *reinterpret_cast<uint4*>(&Bs[(lrow + 32 * i) * G_STRIDE + lchunk]) = rb[i];
-  };
+  // staging registers as named scalars (AR is 2 or 4, BR is 4): an array
+  // here is left in private memory by the compiler
+  static_assert((AR == 2 || AR == 4) && BR == 4, "staging layout");
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define QG_LDA(I, KT) (*reinterpret_cast<const uint4*>(Ag[I] + (KT) * GB_K))
+#define QG_GLOAD(KT)                                                    \
+  do {                                                                  \
+    const int kt_ = (KT);                                               \
+    ra0 = QG_LDA(0, kt_);                                               \
+    ra1 = QG_LDA(1, kt_);                                               \
+    if (AR == 4) {                                                      \
+      ra2 = QG_LDA(AR == 4 ? 2 : 0, kt_);                               \
+      ra3 = QG_LDA(AR == 4 ? 3 : 0, kt_);                               \
+    }                                                                   \
+    rb0 = ld_stream16(Bg[0] + kt_ * GB_K);                              \
+    rb1 = ld_stream16(Bg[1] + kt_ * GB_K);                              \
+    rb2 = ld_stream16(Bg[2] + kt_ * GB_K);                              \
+    rb3 = ld_stream16(Bg[3] + kt_ * GB_K);                              \
+  } while (0)
+#define QG_ST(BUF, ROW, V) *reinterpret_cast<uint4*>(&BUF[(lrow + (ROW)) * G_STRIDE + lchunk]) = (V)
+#define QG_LSTORE()                  \
+  do {                               \
+    QG_ST(As, 0, ra0);               \
+    QG_ST(As, 32, ra1);              \
+    if (AR == 4) {                   \
+      QG_ST(As, 64, ra2);            \
+      QG_ST(As, 96, ra3);            \
+    }                                \
+    QG_ST(Bs, 0, rb0);               \
+    QG_ST(Bs, 32, rb1);              \
+    QG_ST(Bs, 64, rb2);              \
+    QG_ST(Bs, 96, rb3);              \
+  } while (0)
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -72,11 +89,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  gload(0);
-  lstore();
+  QG_GLOAD(0);
+  QG_LSTORE();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
+    QG_GLOAD(min(kt + 1, nkt - 1));  // unconditional (repeats the last tile) so ra/rb stay in registers
 #pragma unroll
     for (int ks = 0; ks < GB_K; ks += 32) {
       bf16x8_t af[TM], bfr[TN];
@@ -96,10 +113,14 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
     }
     __syncthreads();
     if (kt + 1 < nkt) {
-      lstore();
+      QG_LSTORE();
       __syncthreads();
     }
   }
+#undef QG_LDA
+#undef QG_GLOAD
+#undef QG_ST
+#undef QG_LSTORE
 
   // epilogue: lane holds C[rbase + r][cbase + (lane & 15)], r = 0..3
   const int rq = (lane >> 4) * 4;
@@ -304,6 +325,43 @@ bool gemm_shape_ok(int M, int N, int K) {
 }
 // (N % 128 == 0 also covers the 256 x 128 tiles of the large-M kernel)
 
+// ---------------------------------------------------------------------------
+// Split-K reduce fused with the residual add and the next pre-norm: row t of
+// C (= the residual stream x) becomes x + sum_z work[z][t], and
+// hn[t] = bf16(RMSNorm(x[t]) * g).  One block per row, N/4 columns per pass.
+// The splits are summed in a fixed order (deterministic).
+
+__global__ __launch_bounds__(256) void k_splitk_reduce_add_norm(GemmArgs a, int ks, const float* g,
+                                                                float eps, bf16_t* hn, int ldh) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const size_t MN = (size_t)a.M * a.N;
+  float* xr = reinterpret_cast<float*>(a.C) + (size_t)t * a.ldc;
+  float ss = 0.f;
+  for (int k = tid * 4; k < a.N; k += 1024) {
+    float4 v = *reinterpret_cast<const float4*>(xr + k);
+    for (int z = 0; z < ks; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(a.work + z * MN + (size_t)t * a.N + k);
+      v.x += p.x;
+      v.y += p.y;
+      v.z += p.z;
+      v.w += p.w;
+    }
+    *reinterpret_cast<float4*>(xr + k) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum<256>(ss, red);
+  const float inv = rsqrtf(ss / (float)a.N + eps);
+  for (int k = tid * 4; k < a.N; k += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + k);
+    const float4 gg = *reinterpret_cast<const float4*>(g + k);
+    uint2 o;
+    o.x = f32_to_bf16(v.x * inv * gg.x) | (f32_to_bf16(v.y * inv * gg.y) << 16);
+    o.y = f32_to_bf16(v.z * inv * gg.z) | (f32_to_bf16(v.w * inv * gg.w) << 16);
+    *reinterpret_cast<uint2*>(hn + (size_t)t * ldh + k) = o;
+  }
+}
+
 template <int BM, int EPI>
 static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
   const dim3 grid(a.N / GB_N, (a.M + BM - 1) / BM, ks);
@@ -324,7 +382,7 @@ static void launch_m32(GemmArgs a, int ks, hipStream_t st) {
   const int kps = a.K / ks;
   if (ks == 1) {
     hipLaunchKernelGGL((k_gemm_m32<BN, EPI, false>), grid, dim3(512), 0, st, a, kps);
-  } else {
+  } else if constexpr (BN == 128) {  // the 192-wide tile is never split
     hipLaunchKernelGGL((k_gemm_m32<BN, EPI, true>), grid, dim3(512), 0, st, a, kps);
     const size_t n_out = (size_t)a.M * a.N / (EPI == EPI_SWIGLU ? 2 : 1);
     const unsigned blocks = (unsigned)((n_out + 255) / 256 < 4096 ? (n_out + 255) / 256 : 4096);
@@ -340,6 +398,32 @@ static void launch_m32_epi(Epilogue epi, GemmArgs a, int ks, hipStream_t st) {
   }
 }
 
+static int m32_splits(const GemmArgs& a) {
+  const int nkt = a.K / GB_K;
+  const int tiles = ((a.M + 255) / 256) * (a.N / 128);
+  int ks = 1;
+  while (tiles * ks * 2 <= 256 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 &&
+         (size_t)(ks * 2) * a.M * a.N <= a.work_elems)
+    ks *= 2;
+  return ks;
+}
+
+void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
+                          hipStream_t st) {
+  if (a.M >= 512 && a.N % 4 == 0) {
+    const int ks = m32_splits(a);
+    if (ks > 1) {
+      const dim3 grid(a.N / 128, (a.M + 255) / 256, ks);
+      hipLaunchKernelGGL((k_gemm_m32<128, EPI_ADD, true>), grid, dim3(512), 0, st, a, a.K / ks);
+      hipLaunchKernelGGL(k_splitk_reduce_add_norm, dim3(a.M), dim3(256), 0, st, a, ks, g, eps, hn,
+                         ldh);
+      return;
+    }
+  }
+  launch_gemm(EPI_ADD, a, st);
+  launch_rmsnorm_bf16(reinterpret_cast<const float*>(a.C), a.ldc, a.M, a.N, g, eps, hn, ldh, st);
+}
+
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
   const int nkt = a.K / GB_K;
   if (a.M >= 512) {
@@ -353,12 +437,7 @@ void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
       launch_m32<192, EPI_SWIGLU>(a, 1, st);
       return;
     }
-    const int tiles = mt * (a.N / 128);
-    int ks = 1;
-    while (tiles * ks * 2 <= 256 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 &&
-           (size_t)(ks * 2) * a.M * a.N <= a.work_elems)
-      ks *= 2;
-    launch_m32_epi(epi, a, ks, st);
+    launch_m32_epi(epi, a, m32_splits(a), st);
     return;
   }
   const int BM = a.M > 64 ? 128 : 64;

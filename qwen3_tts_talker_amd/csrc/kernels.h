@@ -95,6 +95,10 @@ struct GemmArgs {
   size_t work_elems;
 };
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
+// C += A * B^T (C = the f32 residual stream [M][N]), then hn = bf16(RMSNorm(C) * g)
+// row by row; split-K partials are reduced in the same pass as the norm.
+void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
+                          hipStream_t st);
 bool gemm_shape_ok(int M, int N, int K);
 
 // out[t][k] = bf16(RMSNorm(x[t]) * g)

@@ -212,13 +212,16 @@ struct Fwd {
     launch_gemm(epi, a, st);
   }
 
-  // matrix-core layer on rows.n <= c->tc uniform rows held in c->x
-  void layer_mfma(int l, const RowMeta& rows) {
+  // matrix-core layer on rows.n <= c->tc uniform rows held in c->x.  On entry
+  // c->hn holds RMSNorm(x) * g_in when `normed` (the previous layer's down
+  // projection produced it); on return it holds the next layer's input norm
+  // unless this is the last layer.
+  void layer_mfma(int l, const RowMeta& rows, bool normed) {
     const LayerDev& L = c->layers[l];
     const int T = rows.n, H = g.hidden, I = g.intermediate;
     bf16_t* att_b = reinterpret_cast<bf16_t*>(c->att);
     bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
-    launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
+    if (!normed) launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
     const bool mfma_attn = c->kv_f16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
     qk_append(l, rows, mfma_attn);
@@ -248,10 +251,16 @@ struct Fwd {
       a.n_splits = 1;
       launch_attn_decode(c->kv_f16, ATT_BF16, a, st);
     }
-    gemm(att_b, c->q_dim, L.wo, T, H, c->q_dim, c->x, H, EPI_ADD);
-    launch_rmsnorm_bf16(c->x, H, T, H, L.g_post, g.rms_eps, c->hn, H, st);
+    gemm_add_norm(att_b, c->q_dim, L.wo, T, H, c->q_dim, L.g_post);
     gemm(c->hn, H, L.wgu, T, 2 * I, H, act_b, I, EPI_SWIGLU);
-    gemm(act_b, I, L.wd, T, H, I, c->x, H, EPI_ADD);
+    if (l + 1 < g.n_layers) gemm_add_norm(act_b, I, L.wd, T, H, I, c->layers[l + 1].g_in);
+    else gemm(act_b, I, L.wd, T, H, I, c->x, H, EPI_ADD);
+  }
+
+  // x += A * B^T, then hn = bf16(RMSNorm(x) * gain)
+  void gemm_add_norm(const bf16_t* A, int lda, const void* B, int M, int N, int K, const float* gain) {
+    GemmArgs a{A, lda, reinterpret_cast<const bf16_t*>(B), M, N, K, c->x, N, c->work, WORK_ELEMS};
+    launch_gemm_add_norm(a, gain, g.rms_eps, c->hn, N, st);
   }
 
   void head(const float* X, int n, float* logits, float* hidden_out) {
@@ -277,7 +286,7 @@ struct Fwd {
       (void)hipMemcpyAsync(c->x, emb + (size_t)done * g.hidden, (size_t)n * g.hidden * 4,
                            hipMemcpyDeviceToDevice, st);
       for (int l = 0; l < g.n_layers; ++l) {
-        if (mfma && n >= MFMA_MIN_ROWS) layer_mfma(l, rows);
+        if (mfma && n >= MFMA_MIN_ROWS) layer_mfma(l, rows, l > 0);
         else layer_gemv(l, rows);
       }
       done += n;
