@@ -12,7 +12,7 @@
 //
 // Steps per layer (math as in "qwentts.cpp src/talker-forward.h",
 // talker_layer_forward):
-//   QKV : x -> RMSNorm(g_in) -> [q|k|v] rows 16b..16b+15         -> E1
+//   QKV : x -> RMSNorm(g_in) -> 16 rows of [q|k|v]               -> E1
 //   ATT : q/k norm + NEOX RoPE, new K/V appended (f16), split-KV causal GQA
 //         over 32 key chunks per KV head, one online softmax per wave  -> P
 //   MRG : chunk blocks 0 and 1 of each head merge the chunks (log-sum-exp) -> E2
@@ -23,6 +23,17 @@
 // are folded into the exchange: the received vector is stored times its gain
 // while the sum of squares accumulates, and the norm scale multiplies the dot
 // products, so a norm costs no extra block barrier.
+//
+// Two kinds of exchange.  Words that blocks on other XCDs read are stored and
+// polled at device scope; that traffic meets at the memory side (~0.6 us one
+// way).  Blocks are dispatched to the 8 XCDs round-robin, so block b runs on
+// XCD b % 8, the 32 blocks of KV head g = b % 8 share one L2, and the QKV ->
+// attention and attention -> merge exchanges can stay inside that L2 when
+// head group g's q/k/v rows are also produced there: plain stores (the vector
+// L1 writes through to L2) and non-temporal loads (which are not served from
+// a stale L1 line) make a hop of ~0.3 us.  Every block checks the XCD it runs
+// on and stops with an error if the placement does not hold; the
+// device-scope variant is the fallback.
 //
 // Specialised to the Talker geometry (hidden 1024, 16/8 heads of 128,
 // intermediate 3072, vocab 3072, bf16 weights, f16 cache); other shapes use
@@ -40,7 +51,10 @@ constexpr int HD = 128, NQ = 16, NKV = 8, G = 2;
 constexpr int NCH = NB / NKV;  // key chunks per KV head
 constexpr int OFF_E1 = 0, OFF_E2 = OFF_E1 + QKV, OFF_E3 = OFF_E2 + QD, OFF_E4 = OFF_E3 + H,
               OFF_E5 = OFF_E4 + I, WORDS_PER_LAYER = OFF_E5 + H;
-constexpr int PART_WORDS = NKV * NCH * G * (HD + 2);  // per layer
+// chunk partial (o[HD], m, l) padded to 144 words: each block writes whole
+// 128-byte lines, so no line holds words of two writers
+constexpr int PST = 144;
+constexpr int PART_WORDS = NKV * NCH * G * PST;  // per layer
 constexpr long SPIN_LIMIT = 1L << 21;
 
 static_assert(QKV % NB == 0 && H % NB == 0 && I % NB == 0 && V % NB == 0, "row split");
@@ -57,6 +71,31 @@ __device__ __forceinline__ uint64_t ld_ll(const uint64_t* p) {
 __device__ __forceinline__ void st_ll(uint64_t* p, float v, uint32_t ep) {
   __hip_atomic_store(p, ((uint64_t)ep << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
+}
+// XCD-local exchange words: written with plain stores into the shared L2 and
+// read with non-temporal loads, which are not served from a (possibly stale)
+// vector L1 line
+__device__ __forceinline__ uint64_t ld_loc(const uint64_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void st_loc(uint64_t* p, float v, uint32_t ep) {
+  __hip_atomic_store(p, ((uint64_t)ep << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+template <bool LOCAL>
+__device__ __forceinline__ uint64_t ld_x(const uint64_t* p) {
+  if constexpr (LOCAL) return ld_loc(p);
+  else return ld_ll(p);
+}
+template <bool LOCAL>
+__device__ __forceinline__ void st_x(uint64_t* p, float v, uint32_t ep) {
+  if constexpr (LOCAL) st_loc(p, v, ep);
+  else st_ll(p, v, ep);
+}
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
 }
 __device__ __forceinline__ float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -75,7 +114,7 @@ __device__ __forceinline__ void raise_err(int* err, int code) {
 // caller can queue the next step's weight loads behind it (loads complete in
 // issue order); finish() re-polls stale words until every epoch equals `ep`
 // and stores the values to dst (LDS).  finish() is false if the wait gave up.
-template <int MAXW>
+template <int MAXW, bool LOCAL = false>
 struct LLWait {
   uint64_t v[MAXW];
   const uint64_t* src;
@@ -86,7 +125,7 @@ struct LLWait {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < MAXW; ++k)
-      if (k * NT + tid < n) v[k] = ld_ll(src + k * NT + tid);
+      if (k * NT + tid < n) v[k] = ld_x<LOCAL>(src + k * NT + tid);
   }
   template <typename Store>
   __device__ __forceinline__ bool finish(uint32_t ep, int* err, Store store) {
@@ -105,9 +144,10 @@ struct LLWait {
         return false;
       }
       __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");  // the words change under us: reload them
 #pragma unroll
       for (int k = 0; k < MAXW; ++k)
-        if (k * NT + tid < n && (uint32_t)(v[k] >> 32) != ep) v[k] = ld_ll(src + k * NT + tid);
+        if (k * NT + tid < n && (uint32_t)(v[k] >> 32) != ep) v[k] = ld_x<LOCAL>(src + k * NT + tid);
     }
 #pragma unroll
     for (int k = 0; k < MAXW; ++k)
@@ -238,6 +278,7 @@ __device__ __forceinline__ float inv_rms(const float* redw, float eps) {
 
 }  // namespace pd
 
+template <bool LOCAL>
 __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   using namespace pd;
   __shared__ __attribute__((aligned(16))) float xres[H];  // residual stream
@@ -265,10 +306,18 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   const float scale = rsqrtf((float)HD);
   const int slot = tid >> 4, sub = tid & 15;
 
-  // QKV rows of this block: 16b .. 16b+15 of the packed [q | k | v].  (Giving
-  // head group g's rows to the 32 blocks of its own XCD measured slower: the
-  // attention step's gather then waits on producers that share its L2.)
-  const int qkv_row0 = b * 16;
+  // QKV rows of this block (16 of the packed [q | k | v]).  XCD-local: the
+  // rows of head group g (q heads 2g, 2g+1, then k and v of head g) come from
+  // the 32 blocks of XCD g, chunk c taking rows 16c .. 16c+15 of that group.
+  // Otherwise rows 16b .. 16b+15.
+  const int qkv_row0 = !LOCAL ? b * 16
+                              : (c < 16 ? g * 2 * HD + c * 16
+                                        : (c < 24 ? QD + g * HD + (c - 16) * 16
+                                                  : QD + KVD + g * HD + (c - 24) * 16));
+  if (LOCAL && xcc_id() != (uint32_t)g) {  // not where the local exchanges assume
+    if (tid == 0) raise_err(a.err, 3);
+    return;
+  }
 
   // Bulk loads (weight slices, cached K/V rows, norm gains) are issued right
   // after a step's exchange wait has succeeded, for use one step later.  The
@@ -356,14 +405,14 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       const float inv = inv_rms(redw, a.eps);
       float v[2];  // rows wave and wave + 8 of this block's 16
       gq.dot_all(xin, v, wave, lane);
-      if (lane < 2) st_ll(E + OFF_E1 + qkv_row0 + wave + NW * lane, (lane ? v[1] : v[0]) * inv, ep);
+      if (lane < 2) st_x<LOCAL>(E + OFF_E1 + qkv_row0 + wave + NW * lane, (lane ? v[1] : v[0]) * inv, ep);
     }
 
     // ---------------- attention ----------------
     {
       {
         // q0 | q1 | k | v of head group g, one word per thread
-        LLWait<1> w1;
+        LLWait<1, LOCAL> w1;
         const int src = tid < 256 ? OFF_E1 + g * 256 + tid
                                   : (tid < 384 ? OFF_E1 + QD + g * HD + (tid - 256)
                                                : OFF_E1 + QD + KVD + g * HD + (tid - 384));
@@ -482,9 +531,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       }
       __syncthreads();
       // partial words of (head g, query head h, chunk c) at
-      // P + ((g * G + h) * NCH + c) * (HD + 2): o[128] (unnormalised), m, l
-      if (tid < G * HD + G) {
-        const int h = tid < G * HD ? tid >> 7 : tid - G * HD;
+      // P + ((g * G + h) * NCH + c) * PST: o[128] (unnormalised), m, l, padding
+      if (tid < G * PST) {
+        const int h = tid / PST, i = tid - h * PST;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][h]);
@@ -495,39 +544,40 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
           sc[w] = mw[w][h] == -INFINITY ? 0.f : __expf(mw[w][h] - M);
           L = fmaf(sc[w], lw[w][h], L);
         }
-        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * (HD + 2);
-        if (tid < G * HD) {
-          const int d = tid & 127;
-          float o = 0.f;
+        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * PST;
+        float o = 0.f;
+        if (i < HD) {
 #pragma unroll
-          for (int sl = 0; sl < NCH; ++sl) o = fmaf(sc[sl >> 2], ored[sl][h * HD + d], o);
-          st_ll(pw + d, o, ep);
-        } else {
-          st_ll(pw + HD, M, ep);  // -inf and 0 for a chunk past the context
-          st_ll(pw + HD + 1, L, ep);
+          for (int sl = 0; sl < NCH; ++sl) o = fmaf(sc[sl >> 2], ored[sl][h * HD + i], o);
+        } else if (i == HD) {
+          o = M;  // -inf and 0 for a chunk past the context
+        } else if (i == HD + 1) {
+          o = L;
         }
+        st_x<LOCAL>(pw + i, o, ep);
       }
     }
     if (c < G) {  // chunk blocks 0 and 1 merge query heads 2g and 2g+1 (log-sum-exp)
       const int h = c;
-      constexpr int NWD = NCH * (HD + 2);
-      float* pb = &ored[0][0];  // [NCH][HD + 2]
+      constexpr int NWD = NCH * PST;
+      static_assert(NWD <= NCH * G * HD, "merge input fits the slot buffer");
+      float* pb = &ored[0][0];  // [NCH][PST]
       __syncthreads();          // every wave is done reading ored
-      LLWait<(NWD + NT - 1) / NT> wp;
+      LLWait<(NWD + NT - 1) / NT, LOCAL> wp;
       wp.issue(P + (size_t)(g * G + h) * NWD, NWD);
       const bool bail = !wp.finish(ep, a.err, [&](int i, float x) { pb[i] = x; });
       if (__syncthreads_or(bail)) return;
       if (tid < HD) {
         float M = -INFINITY;
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) M = fmaxf(M, pb[cc * (HD + 2) + HD]);
+        for (int cc = 0; cc < NCH; ++cc) M = fmaxf(M, pb[cc * PST + HD]);
         float L = 0.f, o = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) {
-          const float lc = pb[cc * (HD + 2) + HD + 1];
-          const float wgt = lc > 0.f ? __expf(pb[cc * (HD + 2) + HD] - M) : 0.f;
+          const float lc = pb[cc * PST + HD + 1];
+          const float wgt = lc > 0.f ? __expf(pb[cc * PST + HD] - M) : 0.f;
           L = fmaf(wgt, lc, L);
-          o = fmaf(wgt, pb[cc * (HD + 2) + tid], o);
+          o = fmaf(wgt, pb[cc * PST + tid], o);
         }
         st_ll(E + OFF_E2 + (g * G + h) * HD + tid, o / L, ep);
       }
@@ -625,19 +675,40 @@ int fused_decode_threads() { return pd::NT; }
 hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool cooperative) {
   FusedDecodeArgs a = args;
   if (!cooperative) {
-    hipLaunchKernelGGL(k_decode_fused, dim3(pd::NB), dim3(pd::NT), 0, st, a);
+    if (a.xcd_local) hipLaunchKernelGGL(k_decode_fused<true>, dim3(pd::NB), dim3(pd::NT), 0, st, a);
+    else hipLaunchKernelGGL(k_decode_fused<false>, dim3(pd::NB), dim3(pd::NT), 0, st, a);
     return hipGetLastError();
   }
+  const void* fn = a.xcd_local ? (const void*)k_decode_fused<true> : (const void*)k_decode_fused<false>;
   void* params[] = {&a};
-  return hipLaunchCooperativeKernel((const void*)k_decode_fused, dim3(pd::NB), dim3(pd::NT), params,
-                                    0, st);
+  return hipLaunchCooperativeKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
+}
+
+__global__ void k_xcc_ids(int* ids) {
+  if (threadIdx.x == 0) ids[blockIdx.x] = (int)pd::xcc_id();
+}
+
+// Whether a co-resident grid of NB blocks puts block b on XCD b % 8 (the
+// dispatcher's round-robin), which the XCD-local exchanges rely on.
+bool fused_decode_xcd_layout_ok(hipStream_t st) {
+  int* d = nullptr;
+  if (hipMalloc(&d, pd::NB * sizeof(int)) != hipSuccess) return false;
+  void* params[] = {&d};
+  int h[pd::NB];
+  bool ok = hipLaunchCooperativeKernel((const void*)k_xcc_ids, dim3(pd::NB), dim3(64), params, 0,
+                                       st) == hipSuccess &&
+            hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, st) == hipSuccess &&
+            hipStreamSynchronize(st) == hipSuccess;
+  for (int b = 0; ok && b < pd::NB; ++b) ok = h[b] == b % pd::NKV;
+  (void)hipFree(d);
+  return ok;
 }
 
 bool fused_decode_fits() {
   int dev = 0, ncu = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused, pd::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused<true>, pd::NT, 0) !=
       hipSuccess)
     return false;
   return (long)per * ncu >= pd::NB;

@@ -132,14 +132,16 @@ struct FusedDecodeArgs {
   float* logits;
   float* hidden_out;
   uint64_t* ll;    // [2][words per layer] exchange words (layer parity)
-  uint64_t* part;  // [2][NKV][G][NCH][HD + 2] chunk partials, as words
-  int* err;
+  uint64_t* part;  // [2][NKV][G][NCH][144] chunk partials (o, m, l, padding), as words
+  int* err;        // 0; 1 a wait gave up; 3 a block ran on an unexpected XCD
   uint32_t epoch;  // >= 1 and < 2^26; words carry epoch * 64 + layer
+  int xcd_local;   // QKV -> attention -> merge exchanges inside each XCD's L2
 
 };
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim);
 bool fused_decode_fits();
+bool fused_decode_xcd_layout_ok(hipStream_t st);
 size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);

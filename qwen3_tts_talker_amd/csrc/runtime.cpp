@@ -73,6 +73,10 @@ struct qtalk_ctx {
   // an ordinary launch of the same grid (for tracers that skip cooperative
   // launches)
   bool coop = true;
+  // QKV -> attention -> merge exchanges of the persistent decode inside each
+  // XCD (needs the dispatcher's block b -> XCD b % 8 placement, checked at
+  // create and by every launch); QTALK_XCD_LOCAL=0 turns it off
+  bool xcd_local = false;
   uint64_t* ll = nullptr;
   uint64_t* fpart = nullptr;
   int* ferr = nullptr;
@@ -325,6 +329,7 @@ struct Fwd {
       c->epoch = 0;
     }
     a.epoch = c->epoch + 1;
+    a.xcd_local = c->xcd_local;
     const hipError_t e = launch_decode_fused(a, st, c->coop);
     if (e != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
@@ -425,6 +430,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
              fused_decode_fits();
   if (c->fused) {
+    const char* env_loc = getenv("QTALK_XCD_LOCAL");
+    c->xcd_local = !(env_loc && env_loc[0] == '0') && fused_decode_xcd_layout_ok(c->stream);
     ok = dev_alloc((void**)&c->ll, fused_decode_ll_words(g.n_layers) * 8) &&
          dev_alloc((void**)&c->fpart, fused_decode_part_words(g.n_layers) * 8) &&
          dev_alloc((void**)&c->ferr, 4);
@@ -607,6 +614,14 @@ qtalk_status qtalk_sync(qtalk_ctx* c) {
     int code = 0;
     if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "cannot read the decode status word");
+    if (code == 3) {  // placement changed: fall back to device-scope exchanges
+      c->xcd_local = false;
+      if (hipMemset(c->ferr, 0, 4) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot clear the decode status word");
+      return fail(c, QTALK_E_DEVICE,
+                  "persistent decode: blocks did not run on the expected XCDs (step not done; "
+                  "later steps use device-scope exchanges)");
+    }
     if (code)
       return fail(c, QTALK_E_DEVICE, "persistent decode gave up waiting (code %d)", code);
   }

@@ -439,3 +439,27 @@ def test_persistent_decode_context_lengths(T):
         assert rel_err(g, ref[T + s]) <= TOL_BF16, (T, s)
     tk.sync()
     assert tk.kv_len(0) == T + 2
+
+
+def test_persistent_decode_xcd_local_exchange_equals_device_scope(monkeypatch):
+    # the XCD-local QKV -> attention -> merge exchanges move rows between
+    # blocks, not the arithmetic: logits must match the device-scope variant
+    # bit for bit (4 layers: both exchange-buffer parities are reused)
+    shape = workload("talker_28l_t128_d1024")
+    w = weights_for("talker_28l_t128_d1024", 4)
+    emb = prefill_embeddings(shape, 300)
+    steps = [step_embedding(shape, s) for s in range(24)]
+    local = _talker(shape, w)
+    monkeypatch.setenv("QTALK_XCD_LOCAL", "0")
+    device = _talker(shape, w)
+    monkeypatch.delenv("QTALK_XCD_LOCAL")
+    local.prefill(0, dev(emb))
+    device.prefill(0, dev(emb))
+    for s, e in enumerate(steps):
+        a = host(local.decode(0, dev(e)))
+        b = host(device.decode(0, dev(e)))
+        assert np.array_equal(a, b), s
+    local.sync()
+    device.sync()
+    for which in (0, 1):
+        assert np.array_equal(host(local.kv_read(0, 3, which)), host(device.kv_read(0, 3, which)))
