@@ -288,7 +288,8 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float redw[NW];
   __shared__ float qs[G][HD];                              // normed, roped, scaled q
   __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
-  __shared__ float mw[NW][G], lw[NW][G];                   // per-wave softmax state
+  __shared__ __attribute__((aligned(16))) float ms[G][NCH];  // per-slot softmax state
+  __shared__ float ls[G][NCH], scs[G][NCH], Ms[G];
   __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   const int g = b % NKV, c = b / NKV;
   const int kpb = (n_ctx + NCH - 1) / NCH;
   const int k0 = c * kpb, k1 = min(k0 + kpb, n_ctx);
-  const float scale = rsqrtf((float)HD);
+  const float scale = 1.4426950408889634f * rsqrtf((float)HD);  // log2(e) / sqrt(HD)
   const int slot = tid >> 4, sub = tid & 15;
 
   // QKV rows of this block (16 of the packed [q | k | v]).  XCD-local: the
@@ -334,21 +335,26 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     const bf16_t* W = a.w + (size_t)l * a.layer_stride;
     return [=](int r) { return W + (size_t)(qkv_row0 + r) * H; };
   };
-  // the first 64 keys of this block's chunk in layer l (in bounds: keys <
-  // n_ctx <= cap; the new position is replaced in the attention step)
+  // cached K/V rows of keys kb + slot and kb + 32 + slot, dims sub*8 .. +8.
+  // The loads are unconditional, their key clamped to the last position
+  // (n_ctx - 1 = pos < cap, always in bounds); keys at or past the chunk end
+  // are masked by selects in the attention step.  (A conditional load would
+  // make the compiler wait for every outstanding load where the branches
+  // join, including the weight slices in flight for the next step.)
   f16x8_t kr[2], vr[2];
-  auto load_kv = [&](int l) {
-    const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
+  auto load_rows = [&](const f16_t* K, const f16_t* V, int kb) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int j = k0 + p * 32 + slot;
-      kr[p] = f16x8_t{};
-      vr[p] = f16x8_t{};
-      if (j < k1) {
-        kr[p] = *reinterpret_cast<const f16x8_t*>(a.kc + hoff + (size_t)j * HD + sub * 8);
-        vr[p] = *reinterpret_cast<const f16x8_t*>(a.vc + hoff + (size_t)j * HD + sub * 8);
-      }
+      const int j = min(kb + p * 32 + slot, n_ctx - 1);
+      kr[p] = *reinterpret_cast<const f16x8_t*>(K + (size_t)j * HD + sub * 8);
+      vr[p] = *reinterpret_cast<const f16x8_t*>(V + (size_t)j * HD + sub * 8);
     }
+  };
+  // the first 64 keys of this block's chunk in layer l (the new position is
+  // replaced in the attention step)
+  auto load_kv = [&](int l) {
+    const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
+    load_rows(a.kc + hoff, a.vc + hoff, k0);
   };
   Gain2 gin;  // input-norm gain of the next layer
   gq.load(wqkv_row(0), wave, lane);
@@ -451,8 +457,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         Vp[(size_t)pos * HD + tid] = (f16_t)vnew[tid];
       }
       // keys [k0, k1), 64 per pass: thread (slot, sub) takes keys kb + slot and
-      // kb + 32 + slot, dims sub*8 .. +8; wave w keeps an online softmax over its
-      // 8 keys of every pass (no block barrier inside the loop)
+      // kb + 32 + slot, dims sub*8 .. +8.  Each slot (16 lanes) keeps its own
+      // online softmax, scores in log2 units (q carries log2(e)), so the loop
+      // needs no reduction across slots; the 32 slots are combined once after.
       float qr[G][8], kn[8], vn[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -470,89 +477,112 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
       }
-      for (int kb = k0; kb < k1; kb += 64) {
-        if (kb != k0) {  // contexts above 32 x 64 keys
+      // one pass over keys kb + slot, kb + 32 + slot held in kr, vr
+      auto pass = [&](int kb, bool first) {
+        const int j0 = kb + slot, j1 = kb + 32 + slot;
+        float kf[2][8], vf[2][8];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kf[p][e] = (float)kr[p][e];
+            vf[p][e] = (float)vr[p][e];
+          }
+        if (j1 >= pos) {  // rare: the new position (fresh K/V) or keys past the chunk
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const int j = kb + p * 32 + slot;
-            kr[p] = f16x8_t{};
-            vr[p] = f16x8_t{};
-            if (j < k1) {
-              kr[p] = *reinterpret_cast<const f16x8_t*>(Kp + (size_t)j * HD + sub * 8);
-              vr[p] = *reinterpret_cast<const f16x8_t*>(Vp + (size_t)j * HD + sub * 8);
+            const int j = p ? j1 : j0;
+            const bool fresh = j == pos, dead = j >= k1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              kf[p][e] = fresh ? kn[e] : kf[p][e];
+              vf[p][e] = dead ? 0.f : (fresh ? vn[e] : vf[p][e]);  // stale rows out
             }
           }
         }
-        float s[2][G], vf[2][8];
+        float s[2][G];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int j = kb + p * 32 + slot;
-          const bool fresh = j == pos;  // the new position: take the fresh K/V
-          float kf[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kf[e] = fresh ? kn[e] : (float)kr[p][e];
-            vf[p][e] = fresh ? vn[e] : (float)vr[p][e];
-          }
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float d = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d = fmaf(qr[h][e], kf[e], d);
-            d = group_sum<16>(d);
-            s[p][h] = j < k1 ? d : -INFINITY;
+            for (int e = 0; e < 8; ++e) d = fmaf(qr[h][e], kf[p][e], d);
+            s[p][h] = group_sum<16>(d);
+          }
+        if (j1 >= k1) {  // rare: keys past the chunk end
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            if (j0 >= k1) s[0][h] = -INFINITY;
+            s[1][h] = -INFINITY;
           }
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float mx = wave_max(fmaxf(s[0][h], s[1][h]));
-          const float m_new = fmaxf(m_run[h], mx);
-          if (m_new == -INFINITY) continue;  // no key of this wave yet (uniform)
-          const float alpha = m_run[h] == -INFINITY ? 0.f : __expf(m_run[h] - m_new);
-          const float p0 = s[0][h] == -INFINITY ? 0.f : __expf(s[0][h] - m_new);
-          const float p1 = s[1][h] == -INFINITY ? 0.f : __expf(s[1][h] - m_new);
-          l_run[h] = l_run[h] * alpha + wave_sum(sub == 0 ? p0 + p1 : 0.f);
+          const float m_new = fmaxf(m_run[h], fmaxf(s[0][h], s[1][h]));
+          const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // slot with no key yet
+          const float p0 = __builtin_amdgcn_exp2f(s[0][h] - m_ref);
+          const float p1 = __builtin_amdgcn_exp2f(s[1][h] - m_ref);
+          if (first) {
+            l_run[h] = p0 + p1;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p1, vf[1][e], fmaf(p0, vf[0][e], acc[h][e] * alpha));
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p1, vf[1][e], p0 * vf[0][e]);
+          } else {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_ref);
+            l_run[h] = fmaf(l_run[h], alpha, p0 + p1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              acc[h][e] = fmaf(p1, vf[1][e], fmaf(p0, vf[0][e], acc[h][e] * alpha));
+          }
           m_run[h] = m_new;
         }
+      };
+      if (k0 < k1) pass(k0, true);                    // rows loaded a step ahead
+      for (int kb = k0 + 64; kb < k1; kb += 64) {     // contexts above 32 x 64 keys
+        load_rows(Kp, Vp, kb);
+        pass(kb, false);
       }
-      // combine the 32 slots (8 waves x 4 key groups) with per-wave scales
+      // combine the 32 slots: per-slot scale 2^(m_slot - M)
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) ored[slot][h * HD + sub * 8 + e] = acc[h][e];
-      if (lane == 0) {
+      if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          mw[wave][h] = m_run[h];
-          lw[wave][h] = l_run[h];
+          ms[h][slot] = m_run[h];
+          ls[h][slot] = l_run[h];
         }
       }
       __syncthreads();
-      // partial words of (head g, query head h, chunk c) at
-      // P + ((g * G + h) * NCH + c) * PST: o[128] (unnormalised), m, l, padding
-      if (tid < G * PST) {
-        const int h = tid / PST, i = tid - h * PST;
+      if (wave == 0) {  // lane (h, slot): the slot's scale
+        const int h = lane >> 5, sl = lane & 31;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][h]);
-        float sc[NW];
-        float L = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          sc[w] = mw[w][h] == -INFINITY ? 0.f : __expf(mw[w][h] - M);
-          L = fmaf(sc[w], lw[w][h], L);
+        for (int k = 0; k < NCH; k += 4) {
+          const float4 m4 = *reinterpret_cast<const float4*>(&ms[h][k]);
+          M = fmaxf(M, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
         }
+        const float m = ms[h][sl];
+        scs[h][sl] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        if (sl == 0) Ms[h] = M;
+      }
+      __syncthreads();
+      // partial words of (head g, query head h, chunk c) at
+      // P + ((g * G + h) * NCH + c) * PST: o[128] (unnormalised), m (log2
+      // units), l, padding
+      if (tid < G * PST) {
+        const int h = tid / PST, i = tid - h * PST;
         uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * PST;
         float o = 0.f;
         if (i < HD) {
 #pragma unroll
-          for (int sl = 0; sl < NCH; ++sl) o = fmaf(sc[sl >> 2], ored[sl][h * HD + i], o);
+          for (int sl = 0; sl < NCH; ++sl) o = fmaf(scs[h][sl], ored[sl][h * HD + i], o);
         } else if (i == HD) {
-          o = M;  // -inf and 0 for a chunk past the context
+          o = Ms[h];  // -inf and 0 for a chunk past the context
         } else if (i == HD + 1) {
-          o = L;
+#pragma unroll
+          for (int sl = 0; sl < NCH; ++sl) o = fmaf(scs[h][sl], ls[h][sl], o);
         }
         st_x<LOCAL>(pw + i, o, ep);
       }
@@ -575,7 +605,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) {
           const float lc = pb[cc * PST + HD + 1];
-          const float wgt = lc > 0.f ? __expf(pb[cc * PST + HD] - M) : 0.f;
+          const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(pb[cc * PST + HD] - M) : 0.f;
           L = fmaf(wgt, lc, L);
           o = fmaf(wgt, pb[cc * PST + tid], o);
         }
