@@ -635,14 +635,12 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       w3.issue(E + OFF_E3, H);
       float ss;
       const bool bail = !recv_norm(w3, ep, a.err, xres, xin, gpost, &ss);
-      // next step's bulk loads: the next layer's QKV slice (or the head),
-      // its input-norm gain and its cached keys
+      // bulk loads for the next layer: its input-norm gain and cached keys
+      // (its QKV slice follows in the down step, which loads nothing else)
       if (l + 1 < a.n_layers) {
-        gq.load(wqkv_row(l + 1), wave, lane);
         gin.load(a.norms + (size_t)(l + 1) * a.norm_stride);
         load_kv(l + 1);
       } else {
-        gq.load([&](int r) { return a.head + (size_t)(b * 12 + r) * H; }, wave, lane, 12);
         gin.load(a.g_final);
       }
       ss = wave_sum(ss);
@@ -665,6 +663,15 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       __syncthreads();
       if (tid < 4)
         st_ll(E + OFF_E5 + b * 4 + tid, xres[b * 4 + tid] + red[2 * tid] + red[2 * tid + 1], ep);
+      // after the publish: the next layer's QKV slice, or after the last layer
+      // the 12 head rows (unconditional loads; units past 12 re-read row 11
+      // and are not used)
+      const bool last = l + 1 == a.n_layers;
+      const bf16_t* Wn = a.w + (size_t)(last ? l : l + 1) * a.layer_stride;
+      gq.load([&](int r) {
+        return last ? a.head + (size_t)(b * 12 + min(r, 11)) * H : Wn + (size_t)(qkv_row0 + r) * H;
+      }, wave, lane);
+      gq.units = last ? 12 : 16;
     }
   }
 
