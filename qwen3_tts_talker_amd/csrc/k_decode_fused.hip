@@ -597,19 +597,20 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       wp.issue(P + (size_t)(g * G + h) * NWD, NWD);
       const bool bail = !wp.finish(ep, a.err, [&](int i, float x) { pb[i] = x; });
       if (__syncthreads_or(bail)) return;
+      if (wave == 0) {  // lane cc < NCH: chunk cc's weight 2^(m_c - M) / L
+        const float mc = lane < NCH ? pb[lane * PST + HD] : -INFINITY;
+        const float lc = lane < NCH ? pb[lane * PST + HD + 1] : 0.f;
+        const float M = wave_max(mc);
+        const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
+        const float L = wave_sum(wgt * lc);
+        if (lane < NCH) scs[0][lane] = wgt / L;
+      }
+      __syncthreads();
       if (tid < HD) {
-        float M = -INFINITY;
+        float o = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) M = fmaxf(M, pb[cc * PST + HD]);
-        float L = 0.f, o = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-          const float lc = pb[cc * PST + HD + 1];
-          const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(pb[cc * PST + HD] - M) : 0.f;
-          L = fmaf(wgt, lc, L);
-          o = fmaf(wgt, pb[cc * PST + tid], o);
-        }
-        st_ll(E + OFF_E2 + (g * G + h) * HD + tid, o / L, ep);
+        for (int cc = 0; cc < NCH; ++cc) o = fmaf(scs[0][cc], pb[cc * PST + tid], o);
+        st_ll(E + OFF_E2 + (g * G + h) * HD + tid, o, ep);
       }
     }
 
