@@ -191,16 +191,21 @@ def main(argv=None):
         s = lib.qtalk_decode(ctx, 0, steps[k % K].data_ptr(), logits.data_ptr(), None)
         assert s == 0, qtalk.qtalk_last_error(ctx)
     torch.cuda.synchronize()
+    # the persistent decode reports a failed step (a wait that gave up, an
+    # unexpected block placement) through the library's status word
+    assert lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
     lib.qtalk_kv_rewind(ctx, 0, T)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record(st)
+    status = 0
     for k in range(K):
-        lib.qtalk_decode(ctx, 0, steps[k].data_ptr(), logits.data_ptr(), None)
+        status |= lib.qtalk_decode(ctx, 0, steps[k].data_ptr(), logits.data_ptr(), None)
         evs[k + 1].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    assert status == 0 and lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
     assert tk.kv_len(0) == T + K
     step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(K)])
     total_ms = evs[0].elapsed_time(evs[K])

@@ -26,13 +26,13 @@
 //
 // Two kinds of exchange.  Words that blocks on other XCDs read are stored and
 // polled at device scope; that traffic meets at the memory side (~0.6 us one
-// way).  Blocks are dispatched to the 8 XCDs round-robin, so block b runs on
-// XCD b % 8, the 32 blocks of KV head g = b % 8 share one L2, and the QKV ->
-// attention and attention -> merge exchanges can stay inside that L2 when
-// head group g's q/k/v rows are also produced there: plain stores (the vector
-// L1 writes through to L2) and non-temporal loads (which are not served from
-// a stale L1 line) make a hop of ~0.3 us.  Every block checks the XCD it runs
-// on and stops with an error if the placement does not hold; the
+// way).  Blocks are dealt to the 8 XCDs in turn, so block b runs on XCD
+// (b + r) % 8 for some rotation r.  KV head g is given to the 32 blocks on
+// XCD g, which share one L2, and the QKV -> attention and attention -> merge
+// exchanges stay inside that L2 when head group g's q/k/v rows are also
+// produced there: plain stores (the vector L1 writes through to L2) and
+// non-temporal loads (which are not served from a stale L1 line) make a hop
+// of ~0.3 us.  The placement is checked when the library is set up; the
 // device-scope variant is the fallback.
 //
 // Specialised to the Talker geometry (hidden 1024, 16/8 heads of 128,
@@ -298,10 +298,12 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   const uint32_t ep0 = a.epoch * 64u;
   const int pos = a.pos;
   const int n_ctx = pos + 1;
-  // attention role of this block: KV head g (= the XCD it runs on), key chunk
-  // c; chunk blocks 0 and 1 of each head also merge the chunks of query heads
-  // 2g and 2g+1
-  const int g = b % NKV, c = b / NKV;
+  // attention role of this block: KV head g, key chunk c; chunk blocks 0 and
+  // 1 of each head also merge the chunks of query heads 2g and 2g+1.  With
+  // XCD-local exchanges g is the XCD the block runs on: the dispatcher deals
+  // blocks to the 8 XCDs in turn (starting where the previous dispatch left
+  // off), so blocks 8c .. 8c+7 cover every XCD once and (g, c) is a bijection.
+  const int g = LOCAL ? (int)xcc_id() : b % NKV, c = b / NKV;
   const int kpb = (n_ctx + NCH - 1) / NCH;
   const int k0 = c * kpb, k1 = min(k0 + kpb, n_ctx);
   const float scale = 1.4426950408889634f * rsqrtf((float)HD);  // log2(e) / sqrt(HD)
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
                               : (c < 16 ? g * 2 * HD + c * 16
                                         : (c < 24 ? QD + g * HD + (c - 16) * 16
                                                   : QD + KVD + g * HD + (c - 24) * 16));
-  if (LOCAL && xcc_id() != (uint32_t)g) {  // not where the local exchanges assume
+  if (LOCAL && g >= NKV) {  // more XCDs than KV heads: not the expected device
     if (tid == 0) raise_err(a.err, 3);
     return;
   }
@@ -726,8 +728,9 @@ __global__ void k_xcc_ids(int* ids) {
   if (threadIdx.x == 0) ids[blockIdx.x] = (int)pd::xcc_id();
 }
 
-// Whether a co-resident grid of NB blocks puts block b on XCD b % 8 (the
-// dispatcher's round-robin), which the XCD-local exchanges rely on.
+// Whether a co-resident grid of NB blocks places blocks 8c .. 8c+7 on 8
+// different XCDs for every c (the dispatcher's round-robin), which the
+// XCD-local exchanges rely on.
 bool fused_decode_xcd_layout_ok(hipStream_t st) {
   int* d = nullptr;
   if (hipMalloc(&d, pd::NB * sizeof(int)) != hipSuccess) return false;
@@ -737,7 +740,14 @@ bool fused_decode_xcd_layout_ok(hipStream_t st) {
                                        st) == hipSuccess &&
             hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, st) == hipSuccess &&
             hipStreamSynchronize(st) == hipSuccess;
-  for (int b = 0; ok && b < pd::NB; ++b) ok = h[b] == b % pd::NKV;
+  for (int c = 0; ok && c < pd::NB / pd::NKV; ++c) {
+    unsigned seen = 0;
+    for (int i = 0; i < pd::NKV; ++i) {
+      const int x = h[c * pd::NKV + i];
+      ok = ok && x >= 0 && x < pd::NKV && !(seen >> x & 1u);
+      seen |= ok ? 1u << x : 0u;
+    }
+  }
   (void)hipFree(d);
   return ok;
 }

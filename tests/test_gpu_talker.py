@@ -463,3 +463,25 @@ def test_persistent_decode_xcd_local_exchange_equals_device_scope(monkeypatch):
     device.sync()
     for which in (0, 1):
         assert np.array_equal(host(local.kv_read(0, 3, which)), host(device.kv_read(0, 3, which)))
+
+
+def test_persistent_decode_ordinary_launch_matches_cooperative(monkeypatch):
+    # an ordinary launch (as under tracing tools) deals blocks to the XCDs
+    # from wherever the previous dispatch stopped; head groups follow the
+    # XCD each block runs on, so results match the cooperative launch
+    shape = workload("talker_28l_t128_d1024")
+    w = weights_for("talker_28l_t128_d1024", 2)
+    emb = prefill_embeddings(shape, 200)
+    steps = [step_embedding(shape, s) for s in range(12)]
+    coop = _talker(shape, w)
+    monkeypatch.setenv("QTALK_COOPERATIVE", "0")
+    plain = _talker(shape, w)
+    monkeypatch.delenv("QTALK_COOPERATIVE")
+    coop.prefill(0, dev(emb))
+    plain.prefill(0, dev(emb))
+    for s, e in enumerate(steps):
+        a = host(coop.decode(0, dev(e)))
+        b = host(plain.decode(0, dev(e)))
+        assert np.array_equal(a, b), s
+    coop.sync()
+    plain.sync()
