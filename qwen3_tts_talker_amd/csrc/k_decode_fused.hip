@@ -731,13 +731,19 @@ __global__ void k_xcc_ids(int* ids) {
 // Whether a co-resident grid of NB blocks places blocks 8c .. 8c+7 on 8
 // different XCDs for every c (the dispatcher's round-robin), which the
 // XCD-local exchanges rely on.
-bool fused_decode_xcd_layout_ok(hipStream_t st) {
+bool fused_decode_xcd_layout_ok(hipStream_t st, bool cooperative) {
   int* d = nullptr;
   if (hipMalloc(&d, pd::NB * sizeof(int)) != hipSuccess) return false;
   void* params[] = {&d};
   int h[pd::NB];
-  bool ok = hipLaunchCooperativeKernel((const void*)k_xcc_ids, dim3(pd::NB), dim3(64), params, 0,
-                                       st) == hipSuccess &&
+  hipError_t e;
+  if (cooperative) {
+    e = hipLaunchCooperativeKernel((const void*)k_xcc_ids, dim3(pd::NB), dim3(64), params, 0, st);
+  } else {
+    hipLaunchKernelGGL(k_xcc_ids, dim3(pd::NB), dim3(64), 0, st, d);
+    e = hipGetLastError();
+  }
+  bool ok = e == hipSuccess &&
             hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, st) == hipSuccess &&
             hipStreamSynchronize(st) == hipSuccess;
   for (int c = 0; ok && c < pd::NB / pd::NKV; ++c) {

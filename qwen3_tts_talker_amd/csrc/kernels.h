@@ -141,7 +141,7 @@ struct FusedDecodeArgs {
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim);
 bool fused_decode_fits();
-bool fused_decode_xcd_layout_ok(hipStream_t st);
+bool fused_decode_xcd_layout_ok(hipStream_t st, bool cooperative);
 size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);

@@ -431,7 +431,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
              fused_decode_fits();
   if (c->fused) {
     const char* env_loc = getenv("QTALK_XCD_LOCAL");
-    c->xcd_local = !(env_loc && env_loc[0] == '0') && fused_decode_xcd_layout_ok(c->stream);
+    c->xcd_local = !(env_loc && env_loc[0] == '0') && fused_decode_xcd_layout_ok(c->stream, c->coop);
     ok = dev_alloc((void**)&c->ll, fused_decode_ll_words(g.n_layers) * 8) &&
          dev_alloc((void**)&c->fpart, fused_decode_part_words(g.n_layers) * 8) &&
          dev_alloc((void**)&c->ferr, 4);
