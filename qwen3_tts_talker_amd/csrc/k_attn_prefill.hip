@@ -91,9 +91,9 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 
   // q (B operand of the score product): row posn, hd ks*16 + h*8 + e.  The
   // lane pair (n, n + 32) holds the whole head, and the RoPE partner d + 64 of
-  // hd d < 64 sits in the same lane at ks + NKS/2.  The two waves of a query
-  // head share its fragments through LDS (qlds), re-read every tile, which
-  // keeps registers free for two stages of K/V prefetch.
+  // hd d < 64 sits in the same lane at ks + NKS/2.  The key-half-0 wave of a
+  // query head prepares the fragments and hands them to its partner through
+  // LDS; both keep them in registers for the whole key loop.
   if (kh == 0) {
     const int t = min(posn - a.p0, a.T - 1);
     const int pr = min(posn, a.p0 + a.T - 1);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   // A-operand row of the score product held by this lane: key tau(n) of this
   // wave's 32-key half
   const int krow = kh * 32 + tau(n);
-  const f16_t* qmine = &qlds[(hh * NKS * 64 + lane) * 8];
+  f16x8_t qf[NKS];
 
   auto compute = [&](int kt) {
     const int kbase = kt * KT + kh * 32;  // this wave's first key
@@ -224,8 +224,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[krow * KSTR + ks * 16 + h * 8]);
-      const f16x8_t qf = *reinterpret_cast<const f16x8_t*>(qmine + ks * 64 * 8);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf, s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s, 0, 0, 0);
     }
     // causal mask (key <= position) where the half reaches the block's rows
     if (kbase + 31 > P0) {
@@ -278,6 +277,9 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   QA_GLOAD(s1, min(1, nkt - 1));
   QA_LSTORE(s0, 0);
   __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
   for (int kt = 0; kt < nkt; kt += 2) {
     // tile kt in LDS, tile kt + 1 in flight in stage 1
     QA_GLOAD(s0, min(kt + 2, nkt - 1));
