@@ -170,40 +170,50 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
       S##v3 = QA_LD(Vg, kb_ + vkey0 + 2 * KSTEP + 1);            \
     }                                                            \
   } while (0)
-#define QA_LSTORE(S, KT)                                                   \
+#define QA_LSTORE_M(S, KT, MASK)                                           \
   do {                                                                     \
     const int kb_ = (KT) * KT_;                                            \
-    store_k(0, kb_, S##k0);                                                \
-    store_k(1, kb_, S##k1);                                                \
+    store_k(0, kb_, S##k0, MASK);                                          \
+    store_k(1, kb_, S##k1, MASK);                                          \
     if (NLD == 4) {                                                        \
-      store_k(2, kb_, S##k2);                                              \
-      store_k(3, kb_, S##k3);                                              \
+      store_k(2, kb_, S##k2, MASK);                                        \
+      store_k(3, kb_, S##k3, MASK);                                        \
     }                                                                      \
-    store_v(0, kb_, S##v0, S##v1);                                         \
-    if (NLDV == 2) store_v(1, kb_, S##v2, S##v3);                          \
+    store_v(0, kb_, S##v0, S##v1, MASK);                                   \
+    if (NLDV == 2) store_v(1, kb_, S##v2, S##v3, MASK);                    \
+  } while (0)
+  // only the tile holding the block's last key needs its tail zeroed
+#define QA_LSTORE(S, KT)                                                   \
+  do {                                                                     \
+    if (((KT) + 1) * KT_ <= kend) QA_LSTORE_M(S, KT, false);               \
+    else QA_LSTORE_M(S, KT, true);                                         \
   } while (0)
   constexpr int KT_ = KT;
   f16_t* const kst = &Ks[kkey0 * KSTR + kc0 * 8];
-  auto zero_past = [&](const uint4& r, int key) {
+  auto zero_past = [&](const uint4& r, int key, bool mask) {
+    if (!mask) return r;
     const bool ok = key < kend;
     return make_uint4(ok ? r.x : 0u, ok ? r.y : 0u, ok ? r.z : 0u, ok ? r.w : 0u);
   };
-  auto store_k = [&](int i, int kb, const uint4& r) {
-    *reinterpret_cast<uint4*>(kst + i * KSTEP * KSTR) = zero_past(r, kb + kkey0 + i * KSTEP);
+  auto store_k = [&](int i, int kb, const uint4& r, bool mask) {
+    *reinterpret_cast<uint4*>(kst + i * KSTEP * KSTR) = zero_past(r, kb + kkey0 + i * KSTEP, mask);
   };
   // transposed V: hd row d = kc0*8 + e; its swizzle (((d >> 3) ^ d) & 7) is
   // (kc0 ^ e) & 7, so the 8 row addresses of a pair differ only in e
-  auto store_v = [&](int i, int kb, const uint4& q0, const uint4& q1) {
+  // (one byte permute per dword: halves e of key and key + 1)
+  auto store_v = [&](int i, int kb, const uint4& q0, const uint4& q1, bool mask) {
     const int key = vkey0 + i * 2 * KSTEP;
-    const uint4 r0 = zero_past(q0, kb + key), r1 = zero_past(q1, kb + key + 1);
+    const uint4 r0 = zero_past(q0, kb + key, mask), r1 = zero_past(q1, kb + key + 1, mask);
     const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
     const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xFFFFu);
-      const uint32_t hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xFFFFu);
+      // bytes 0-3 select from w0[e/2], 4-7 from w1[e/2]: low half of each for
+      // even e, high half for odd e
+      const uint32_t dw = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1],
+                                                (e & 1) ? 0x07060302u : 0x05040100u);
       const int d = kc0 * 8 + e;
-      *reinterpret_cast<uint32_t*>(&Vt[d * KT + (key ^ (((kc0 ^ e) & 7) << 3))]) = lo | (hi << 16);
+      *reinterpret_cast<uint32_t*>(&Vt[d * KT + (key ^ (((kc0 ^ e) & 7) << 3))]) = dw;
     }
   };
 
