@@ -53,6 +53,18 @@ __device__ __forceinline__ int vt_index(int d, int key) {
 
 }  // namespace pa
 
+// value of lane l ^ 32 combined with lane l's own: v_permlane32_swap exchanges
+// the upper half of one operand with the lower half of the other, so the two
+// results hold {v[l], v[l ^ 32]} in every lane
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int HD>
 __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   using namespace pa;
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) t8[r] = fmaxf(t8[r], t8[r + 4]);
     float mx = fmaxf(fmaxf(t8[0], t8[2]), fmaxf(t8[1], t8[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
     if (m_new == -INFINITY) return;  // no key of this half is visible to any row yet
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
   const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
   const float l = l_run * a0 + l1 * a1;
-  const float inv = 1.0f / (l + __shfl_xor(l, 32));
+  const float inv = 1.0f / xor32_sum(l);
   bf16_t* orow = a.out + (size_t)(posn - a.p0) * a.ldo + (size_t)hq * HD;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
