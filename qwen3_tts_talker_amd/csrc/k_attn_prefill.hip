@@ -83,9 +83,16 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nkv = a.n_kv_heads;
-  const int g = blockIdx.x % nkv;
   const int nqb = (a.T + PB - 1) / PB;
-  const int qb = nqb - 1 - (int)(blockIdx.x / nkv);  // longest blocks first
+  // work item r (0 = longest: the last 32 positions) of this block.  Blocks b
+  // and b + ncu are dispatched to the same CU when the whole grid fits two
+  // deep, so the second one takes the item complementary to the first
+  // (longest with shortest) and every CU gets about the same number of key
+  // tiles; otherwise plain longest first.
+  const int nb = nqb * nkv, b = blockIdx.x;
+  const int r = (b < a.ncu || nb > 2 * a.ncu) ? b : nb - 1 - (b - a.ncu);
+  const int g = r % nkv;
+  const int qb = nqb - 1 - r / nkv;
   const int P0 = a.p0 + qb * PB;
   const int P1 = min(P0 + PB, a.p0 + a.T);  // block positions [P0, P1)
   const int kend = P1;                      // keys [0, kend)

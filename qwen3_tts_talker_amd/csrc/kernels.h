@@ -79,6 +79,7 @@ struct PrefillAttnArgs {
   float qscale;  // log2(e) / sqrt(head_dim)
   bf16_t* out;   // row t at out + t*ldo
   int ldo;
+  int ncu;  // compute units (block placement only)
 };
 bool attn_prefill_supported(int head_dim, int group);
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st);

@@ -73,6 +73,7 @@ struct qtalk_ctx {
   // an ordinary launch of the same grid (for tracers that skip cooperative
   // launches)
   bool coop = true;
+  int ncu = 256;  // compute units of the device (placement heuristics only)
   // QKV -> attention -> merge exchanges of the persistent decode inside each
   // XCD (needs the dispatcher's block b -> XCD b % 8 placement, checked at
   // create and by every launch); QTALK_XCD_LOCAL=0 turns it off
@@ -248,6 +249,7 @@ struct Fwd {
       p.qscale = 1.4426950408889634f / sqrtf((float)g.head_dim);
       p.out = att_b;
       p.ldo = c->q_dim;
+      p.ncu = c->ncu;
       launch_attn_prefill(p, st);
     } else {
       AttnArgs a = attn_args(l, rows);
@@ -424,6 +426,12 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   const char* env = getenv("QTALK_FUSED_DECODE");
   const char* env_coop = getenv("QTALK_COOPERATIVE");
   c->coop = !(env_coop && env_coop[0] == '0');
+  {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      c->ncu = ncu;
+  }
   c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') &&
              g.n_layers <= 64 &&
              fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
