@@ -143,7 +143,8 @@ struct LLWait {
         raise_err(err, 1);
         return false;
       }
-      __builtin_amdgcn_s_sleep(1);
+      // re-poll at once: a poll round trip is the detection granularity,
+      // which measured more expensive than the poll traffic
       asm volatile("" ::: "memory");  // the words change under us: reload them
 #pragma unroll
       for (int k = 0; k < MAXW; ++k)
