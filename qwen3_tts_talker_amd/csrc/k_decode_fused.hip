@@ -11,15 +11,20 @@
 // before it waits, so the HBM stream overlaps the exchange latency.
 //
 // Steps per layer (math as in "qwentts.cpp src/talker-forward.h",
-// talker_layer_forward):
-//   QKV : x -> RMSNorm(g_in) -> 16 rows of [q|k|v]               -> E1
+// talker_layer_forward), block (g, c) = (group, chunk):
+//   QKV : x -> RMSNorm(g_in) -> 16 rows of head group g's [q|k|v]     -> E1
 //   ATT : q/k norm + NEOX RoPE, new K/V appended (f16), split-KV causal GQA
-//         over 32 key chunks per KV head, one online softmax per wave  -> P
-//   MRG : chunk blocks 0 and 1 of each head merge the chunks (log-sum-exp) -> E2
-//   O   : x + o @ Wo^T, rows 4b..4b+3                         -> E3
-//   GU  : RMSNorm(g_post), 12 gate|up row pairs, silu(g)*u    -> E4
-//   D   : x + a @ Wd^T, rows 4b..4b+3                         -> E5
-// then final RMSNorm + codec_head rows 12b..12b+11 -> logits.  The RMSNorms
+//         over 32 key chunks per KV head, one online softmax per slot   -> P
+//   MRG : chunk blocks 0 and 1 of each head merge the chunks (log-sum-exp) -> OG
+//   OP  : o_proj split by group: rows 32c..32c+31 of Wo[:, 256g..256g+255]
+//         times head group g's output                                   -> OP
+//   XM  : x + sum of the 8 groups' partials for rows 32c..32c+31        -> XM
+//   GU  : RMSNorm(g_post), gate|up pairs 384g+12c..+11, silu(g)*u       -> A
+//   DP  : down split by group: rows 32c..32c+31 of Wd[:, 384g..384g+383] -> DP
+//   XD  : x + sum of the 8 groups' down partials, rows 32c..32c+31      -> XD
+// then final RMSNorm + codec_head rows 12b..12b+11 -> logits.  Only OP and DP
+// are read across groups, 256 words per block; every other exchange stays
+// inside a group.  The RMSNorms
 // are folded into the exchange: the received vector is stored times its gain
 // while the sum of squares accumulates, and the norm scale multiplies the dot
 // products, so a norm costs no extra block barrier.
@@ -49,8 +54,17 @@ constexpr int NW = NT / 64;
 constexpr int H = 1024, QD = 2048, KVD = 1024, QKV = QD + 2 * KVD, I = 3072, V = 3072;
 constexpr int HD = 128, NQ = 16, NKV = 8, G = 2;
 constexpr int NCH = NB / NKV;  // key chunks per KV head
-constexpr int OFF_E1 = 0, OFF_E2 = OFF_E1 + QKV, OFF_E3 = OFF_E2 + QD, OFF_E4 = OFF_E3 + H,
-              OFF_E5 = OFF_E4 + I, WORDS_PER_LAYER = OFF_E5 + H;
+// exchange regions of one layer (words); "group" = the 32 blocks of one KV
+// head, which share an XCD when the exchanges are XCD-local
+constexpr int OFF_E1 = 0;                   // QKV rows [4096], by group
+constexpr int OFF_OG = OFF_E1 + QKV;        // merged attention output [16 heads][128], by group
+constexpr int OFF_OP = OFF_OG + QD;         // o_proj partials [8 groups][1024], all blocks
+constexpr int OFF_XM = OFF_OP + NKV * H;    // x after attention [8 groups][1024], one copy per group
+constexpr int OFF_A = OFF_XM + NKV * H;     // SwiGLU output [8 groups][32 blocks][16] (12 used)
+constexpr int OFF_DP = OFF_A + NKV * 512;   // down partials [8 groups][1024], all blocks
+constexpr int OFF_XD = OFF_DP + NKV * H;    // layer output [8 groups][1024], one copy per group
+constexpr int WORDS_PER_LAYER = OFF_XD + NKV * H;
+constexpr int ISEG = I / NKV, OSEG = QD / NKV;  // down / o_proj input columns per group
 // chunk partial (o[HD], m, l) padded to 144 words: each block writes whole
 // 128-byte lines, so no line holds words of two writers
 constexpr int PST = 144;
@@ -257,8 +271,9 @@ static_assert(H == 2 * NT, "two hidden channels per thread");
 // Receive an H-vector: x[k] to `x` (LDS), x[k] * g[k] to `xg` (LDS), and this
 // thread's share of sum(x^2) to *ss.  RMSNorm is then applied as one scale
 // on the dot products: W (x * rsqrt(mean(x^2) + eps) * g) = rsqrt(.) * W (x g).
-__device__ __forceinline__ bool recv_norm(LLWait<2>& w, uint32_t ep, int* err, float* x, float* xg,
-                                          const Gain2& g, float* ss) {
+template <bool LOCAL>
+__device__ __forceinline__ bool recv_norm(LLWait<2, LOCAL>& w, uint32_t ep, int* err, float* x,
+                                          float* xg, const Gain2& g, float* ss) {
   float s = 0.f;
   const bool ok = w.finish(ep, err, [&](int i, float v) {
     x[i] = v;
@@ -268,6 +283,43 @@ __device__ __forceinline__ bool recv_norm(LLWait<2>& w, uint32_t ep, int* err, f
   *ss = s;
   return ok;
 }
+
+// A block's 32 rows of a column slice of SEG bf16 weights per row: wave w
+// takes rows 4w .. 4w+3, 16 lanes per row, SEG / 128 chunks of 8 per lane.
+template <int SEG>
+struct Slab {
+  static constexpr int NC = SEG / 128;
+  static_assert(SEG % 128 == 0, "slab width");
+  uint4 w[NC];
+  // rowp(r): pointer to the first weight of the block's row r (0..31)
+  template <typename RowP>
+  __device__ __forceinline__ void load(RowP rowp, int wave, int lane) {
+    const bf16_t* p = rowp(4 * wave + (lane >> 4)) + (lane & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) w[j] = ld_stream16(p + j * 128);
+  }
+  // dot of the lane's row with xs[0 .. SEG), in all 16 lanes of the row
+  __device__ __forceinline__ float dot(const float* xs, int lane) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float f[8];
+      unpack8_bf16(w[j], f);
+      const float* xb = xs + (lane & 15) * 8 + j * 128;
+      const float4 a = *reinterpret_cast<const float4*>(xb);
+      const float4 b = *reinterpret_cast<const float4*>(xb + 4);
+      acc = fmaf(f[0], a.x, acc);
+      acc = fmaf(f[1], a.y, acc);
+      acc = fmaf(f[2], a.z, acc);
+      acc = fmaf(f[3], a.w, acc);
+      acc = fmaf(f[4], b.x, acc);
+      acc = fmaf(f[5], b.y, acc);
+      acc = fmaf(f[6], b.z, acc);
+      acc = fmaf(f[7], b.w, acc);
+    }
+    return row16_sum(acc);
+  }
+};
 
 // 1 / sqrt(mean(x^2) + eps) from per-wave partial sums in redw[0..NW)
 __device__ __forceinline__ float inv_rms(const float* redw, float eps) {
@@ -329,11 +381,12 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   // bulk load requested while a poll is still repeating would hold that poll
   // back by a full HBM round trip; requested after the wait, it has the
   // step's arithmetic plus the next exchange to land.
-  Gp<16, 1, H> gq;        // Wqkv rows qkv_row0 .. +15 (two per wave); after the
-                          // last layer, codec_head rows 12b .. 12b+11
-  Gp<8, 2, QD / 2> go;    // Wo rows 4b .. 4b+3, two K halves
-  Gp<24, 1, H> gg;        // 12 gate|up row pairs
-  Gp<8, 2, I / 2> gd;     // Wd rows 4b .. 4b+3, two K halves
+  Gp<16, 1, H> gq;   // Wqkv rows qkv_row0 .. +15 (two per wave); after the
+                     // last layer, codec_head rows 12b .. 12b+11
+  Slab<OSEG> go;     // Wo rows 32c .. +31, columns 256g .. +255
+  Gp<24, 1, H> gg;   // gate|up row pairs of SwiGLU outputs gu_row0 .. +11
+  Slab<ISEG> gd;     // Wd rows 32c .. +31, columns 384g .. +383
+  const int gu_row0 = g * ISEG + c * 12;
   auto wqkv_row = [&](int l) {
     const bf16_t* W = a.w + (size_t)l * a.layer_stride;
     return [=](int r) { return W + (size_t)(qkv_row0 + r) * H; };
@@ -359,6 +412,21 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
     load_rows(a.kc + hoff, a.vc + hoff, k0);
   };
+  // Rows 32c .. 32c+31 of x + (sum of the 8 groups' partials in PP): thread t
+  // polls partial t & 15 (duplicated for t & 15 >= 8, weighted 0) of row
+  // 32c + t / 16 (device scope); a fixed-order 16-lane sum adds them onto the
+  // residual and lane 0 of the row publishes it to this group's copy XOUT.
+  auto reduce_rows = [&](const uint64_t* PP, uint32_t epw, uint64_t* XOUT) -> bool {
+    const int jr = tid >> 4, gp = tid & 15;
+    const uint64_t* word = PP + (gp & 7) * H + 32 * c + jr;
+    LLWait<1> wr;
+    wr.issue(word - tid, NT);
+    float v = 0.f;
+    const bool ok = wr.finish(epw, a.err, [&](int, float x) { v = x; });
+    const float s = row16_sum(gp < NKV ? v : 0.f);
+    if (gp == 0) st_x<LOCAL>(XOUT + g * H + 32 * c + jr, xres[32 * c + jr] + s, epw);
+    return ok;
+  };
   Gain2 gin;  // input-norm gain of the next layer
   gq.load(wqkv_row(0), wave, lane);
   load_kv(0);
@@ -373,27 +441,29 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     const float *g_post = nl + H, *g_q = nl + 2 * H, *g_k = nl + 2 * H + HD;
     // Layers l and l + 2 share the exchange and partial regions (parity
     // double buffering keeps them cache-resident).  Reuse is safe: a block
-    // writes layer l + 2's words only after it has received layer l + 1 words
-    // from every block, and every block produced those after it finished
-    // reading layer l's words.  The epoch tells the two layers apart.
+    // writes layer l + 2's words only after it has received words of layer
+    // l + 1 that, through the chain of waits, every block produced after it
+    // finished reading layer l's words.  The epoch tells the two layers apart.
     const uint32_t ep = ep0 + (uint32_t)l;
     uint64_t* E = a.ll + (size_t)(l & 1) * WORDS_PER_LAYER;
-    const uint64_t* Eprev = a.ll + (size_t)((l + 1) & 1) * WORDS_PER_LAYER;
+    uint64_t* Eprev = a.ll + (size_t)((l + 1) & 1) * WORDS_PER_LAYER;
     uint64_t* P = a.part + (size_t)(l & 1) * PART_WORDS;  // this layer's chunk partials
     const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
     f16_t* Kp = a.kc + hoff;
     f16_t* Vp = a.vc + hoff;
 
-    // ---------------- QKV ----------------
+    // ---------------- XD (previous layer's output) + QKV ----------------
     float gn, gnp;  // QK-norm gains of this thread's attention channel and of its RoPE partner
     float2 cs;      // RoPE (cos, sin) of this thread's pair
     {
       float ss;
       bool bail = false;
       if (l > 0) {
-        LLWait<2> w5;
-        w5.issue(Eprev + OFF_E5, H);
-        bail = !recv_norm(w5, ep - 1, a.err, xres, xin, gin, &ss);  // layer l - 1's output
+        // layer l - 1's down partials -> its output rows -> this group's copy
+        bail = !reduce_rows(Eprev + OFF_DP, ep - 1, Eprev + OFF_XD);
+        LLWait<2, LOCAL> wx;
+        wx.issue(Eprev + OFF_XD + g * H, H);
+        bail = bail || !recv_norm(wx, ep - 1, a.err, xres, xin, gin, &ss);
       } else {
         const float x0 = a.emb[tid], x1 = a.emb[tid + NT];
         xres[tid] = x0;
@@ -403,7 +473,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         ss = x0 * x0 + x1 * x1;
       }
       // next step's bulk loads
-      go.load([&](int r) { return Wo + (size_t)(b * 4 + r) * QD; }, wave, lane);
+      go.load([&](int r) { return Wo + (size_t)(32 * c + r) * QD + g * OSEG; }, wave, lane);
       const float* gsel = tid < 256 ? g_q : g_k;
       gn = gsel[tid & 127];
       gnp = gsel[(tid & 127) ^ 64];
@@ -438,7 +508,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       gg.load([&](int r) {
         // unit r: logical row 12b + r/2, gate (r even) or up (r odd); rows are
         // interleaved in blocks of 16 (gate rows, up rows)
-        const int lr = b * 12 + (r >> 1);
+        const int lr = gu_row0 + (r >> 1);
         return Wgu + ((size_t)(lr >> 4) * 32 + (lr & 15) + (r & 1) * 16) * H;
       }, wave, lane);
       // per-head RMSNorm, NEOX RoPE on (i, i + 64); k and v round through the
@@ -613,32 +683,31 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         float o = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) o = fmaf(scs[0][cc], pb[cc * PST + tid], o);
-        st_ll(E + OFF_E2 + (g * G + h) * HD + tid, o, ep);
+        st_x<LOCAL>(E + OFF_OG + (g * G + h) * HD + tid, o, ep);
       }
     }
 
-    // ---------------- o_proj + residual ----------------
+    // ---------------- o_proj partial of this group ----------------
     Gain2 gpost;
     {
-      LLWait<4> w2;
-      w2.issue(E + OFF_E2, QD);
-      const bool bail = !w2.finish_to(ep, a.err, xin);
+      LLWait<1, LOCAL> wo;  // head group g's merged output, 256 words
+      wo.issue(E + OFF_OG + g * OSEG, OSEG);
+      const bool bail = !wo.finish_to(ep, a.err, xin);
       // next step's bulk loads
-      gd.load([&](int r) { return Wd + (size_t)(b * 4 + r) * I; }, wave, lane);
+      gd.load([&](int r) { return Wd + (size_t)(32 * c + r) * I + g * ISEG; }, wave, lane);
       gpost.load(g_post);
       if (__syncthreads_or(bail)) return;
-      go.dot(xin, red, wave, lane);
-      __syncthreads();
-      if (tid < 4)
-        st_ll(E + OFF_E3 + b * 4 + tid, xres[b * 4 + tid] + red[2 * tid] + red[2 * tid + 1], ep);
+      const float s = go.dot(xin, lane);
+      if ((lane & 15) == 0) st_ll(E + OFF_OP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
     }
 
-    // ---------------- gate|up + SwiGLU ----------------
+    // ---------------- XM + gate|up + SwiGLU ----------------
     {
-      LLWait<2> w3;
-      w3.issue(E + OFF_E3, H);
+      bool bail = !reduce_rows(E + OFF_OP, ep, E + OFF_XM);
+      LLWait<2, LOCAL> wx;
+      wx.issue(E + OFF_XM + g * H, H);
       float ss;
-      const bool bail = !recv_norm(w3, ep, a.err, xres, xin, gpost, &ss);
+      bail = bail || !recv_norm(wx, ep, a.err, xres, xin, gpost, &ss);
       // bulk loads for the next layer: its input-norm gain and cached keys
       // (its QKV slice follows in the down step, which loads nothing else)
       if (l + 1 < a.n_layers) {
@@ -654,19 +723,21 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       gg.dot(xin, red, wave, lane);
       __syncthreads();
       if (tid < 12)
-        st_ll(E + OFF_E4 + b * 12 + tid, silu_f(red[2 * tid] * inv) * (red[2 * tid + 1] * inv), ep);
+        st_x<LOCAL>(E + OFF_A + g * 512 + 16 * c + tid,
+                    silu_f(red[2 * tid] * inv) * (red[2 * tid + 1] * inv), ep);
     }
 
-    // ---------------- down + residual ----------------
+    // ---------------- down partial of this group ----------------
     {
-      LLWait<6> w4;
-      w4.issue(E + OFF_E4, I);
-      const bool bail = !w4.finish_to(ep, a.err, xin);
+      // SwiGLU outputs 384g .. 384g+383: thread t < 384 reads block t / 12's
+      // word t % 12
+      LLWait<1, LOCAL> wa;
+      const int ta = min(tid, ISEG - 1);
+      wa.issue(E + OFF_A + g * 512 + 16 * (ta / 12) + ta % 12 - tid, ISEG);
+      const bool bail = !wa.finish_to(ep, a.err, xin);
       if (__syncthreads_or(bail)) return;
-      gd.dot(xin, red, wave, lane);
-      __syncthreads();
-      if (tid < 4)
-        st_ll(E + OFF_E5 + b * 4 + tid, xres[b * 4 + tid] + red[2 * tid] + red[2 * tid + 1], ep);
+      const float s = gd.dot(xin, lane);
+      if ((lane & 15) == 0) st_ll(E + OFF_DP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
       // after the publish: the next layer's QKV slice, or after the last layer
       // the 12 head rows (unconditional loads; units past 12 re-read row 11
       // and are not used)
@@ -679,12 +750,15 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     }
   }
 
-  // ---------------- final norm + codec head ----------------
+  // ---------------- final output rows, norm + codec head ----------------
   {
-    LLWait<2> w5;
-    w5.issue(a.ll + (size_t)((a.n_layers - 1) & 1) * WORDS_PER_LAYER + OFF_E5, H);
+    const uint32_t epl = ep0 + (uint32_t)(a.n_layers - 1);
+    uint64_t* El = a.ll + (size_t)((a.n_layers - 1) & 1) * WORDS_PER_LAYER;
+    bool bail = !reduce_rows(El + OFF_DP, epl, El + OFF_XD);
+    LLWait<2, LOCAL> wx;
+    wx.issue(El + OFF_XD + g * H, H);
     float ss;
-    const bool bail = !recv_norm(w5, ep0 + (uint32_t)(a.n_layers - 1), a.err, xres, xin, gin, &ss);  // gin = final gain
+    bail = bail || !recv_norm(wx, epl, a.err, xres, xin, gin, &ss);  // gin = final gain
     ss = wave_sum(ss);
     if (lane == 0) redw[wave] = ss;
     if (__syncthreads_or(bail)) return;
