@@ -106,6 +106,13 @@ __device__ __forceinline__ void st_x(uint64_t* p, float v, uint32_t ep) {
   if constexpr (LOCAL) st_loc(p, v, ep);
   else st_ll(p, v, ep);
 }
+// v[l] + v[l ^ 32]: v_permlane32_swap exchanges the upper half of one operand
+// with the lower half of the other, so its two results hold both values in
+// every lane
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float qs[G][HD];                              // normed, roped, scaled q
   __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
   __shared__ __attribute__((aligned(16))) float ms[G][NCH];  // per-slot softmax state
-  __shared__ float ls[G][NCH], scs[G][NCH], Ms[G];
+  __shared__ float ls[G][NCH], scs[G][NCH], Ms[G], Ls[G];
   __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         }
       }
       __syncthreads();
-      if (wave == 0) {  // lane (h, slot): the slot's scale
+      if (wave == 0) {  // lane (h, slot): the slot's scale; the head's l
         const int h = lane >> 5, sl = lane & 31;
         float M = -INFINITY;
 #pragma unroll
@@ -637,28 +644,38 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
           M = fmaxf(M, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
         }
         const float m = ms[h][sl];
-        scs[h][sl] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        if (sl == 0) Ms[h] = M;
+        const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        scs[h][sl] = sc;
+        float lh = row16_sum(sc * ls[h][sl]);
+        lh += __shfl_xor(lh, 16);
+        if (sl == 0) {
+          Ms[h] = M;  // -inf and 0 for a chunk past the context
+          Ls[h] = lh;
+        }
       }
       __syncthreads();
       // partial words of (head g, query head h, chunk c) at
       // P + ((g * G + h) * NCH + c) * PST: o[128] (unnormalised), m (log2
-      // units), l, padding
-      if (tid < G * PST) {
-        const int h = tid / PST, i = tid - h * PST;
-        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * PST;
+      // units), l, padding.  o value (h, i) = output wave * 32 + lane % 32 is
+      // summed over slots 16 * (lane / 32) .. +15 in each half-wave and the
+      // halves added across lanes l and l ^ 32.
+      {
+        const int out = wave * 32 + (lane & 31), h = out >> 7, i = out & (HD - 1), half = lane >> 5;
         float o = 0.f;
-        if (i < HD) {
 #pragma unroll
-          for (int sl = 0; sl < NCH; ++sl) o = fmaf(scs[h][sl], ored[sl][h * HD + i], o);
-        } else if (i == HD) {
-          o = Ms[h];  // -inf and 0 for a chunk past the context
-        } else if (i == HD + 1) {
-#pragma unroll
-          for (int sl = 0; sl < NCH; ++sl) o = fmaf(scs[h][sl], ls[h][sl], o);
+        for (int k = 0; k < NCH / 2; ++k) {
+          const int sl = half * (NCH / 2) + k;
+          o = fmaf(scs[h][sl], ored[sl][h * HD + i], o);
         }
-        st_x<LOCAL>(pw + i, o, ep);
+        o = xor32_sum(o);
+        if (half == 0) st_x<LOCAL>(P + ((size_t)(g * G + h) * NCH + c) * PST + i, o, ep);
+        if (half == 1 && wave < G && (lane & 31) < PST - HD) {  // m, l, padding of head `wave`
+          const int ii = HD + (lane & 31);
+          const float v = ii == HD ? Ms[wave] : (ii == HD + 1 ? Ls[wave] : 0.f);
+          st_x<LOCAL>(P + ((size_t)(g * G + wave) * NCH + c) * PST + ii, v, ep);
+        }
       }
+      static_assert(NW * 32 == G * HD && PST - HD <= 32, "combine split");
     }
     if (c < G) {  // chunk blocks 0 and 1 merge query heads 2g and 2g+1 (log-sum-exp)
       const int h = c;
