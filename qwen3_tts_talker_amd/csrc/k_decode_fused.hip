@@ -15,7 +15,8 @@
 //   QKV : x -> RMSNorm(g_in) -> 16 rows of head group g's [q|k|v]     -> E1
 //   ATT : q/k norm + NEOX RoPE, new K/V appended (f16), split-KV causal GQA
 //         over 32 key chunks per KV head, one online softmax per slot   -> P
-//   MRG : chunk blocks 0 and 1 of each head merge the chunks (log-sum-exp) -> OG
+//   MRG : dims 8(c%16)..+7 of q head 2g+c/16 merged over the 32 chunks
+//         (log-sum-exp)                                                  -> OG
 //   OP  : o_proj split by group: rows 32c..32c+31 of Wo[:, 256g..256g+255]
 //         times head group g's output                                   -> OP
 //   XM  : x + sum of the 8 groups' partials for rows 32c..32c+31        -> XM
@@ -57,8 +58,9 @@ constexpr int NCH = NB / NKV;  // key chunks per KV head
 // exchange regions of one layer (words); "group" = the 32 blocks of one KV
 // head, which share an XCD when the exchanges are XCD-local
 constexpr int OFF_E1 = 0;                   // QKV rows [4096], by group
-constexpr int OFF_OG = OFF_E1 + QKV;        // merged attention output [16 heads][128], by group
-constexpr int OFF_OP = OFF_OG + QD;         // o_proj partials [8 groups][1024], all blocks
+constexpr int OFF_OG = OFF_E1 + QKV;        // merged attention output [8 groups][32 blocks][16]
+                                            // (8 used: dims 8(c%16).. of q head 2g + c/16), by group
+constexpr int OFF_OP = OFF_OG + NKV * 512;  // o_proj partials [8 groups][1024], all blocks
 constexpr int OFF_XM = OFF_OP + NKV * H;    // x after attention [8 groups][1024], one copy per group
 constexpr int OFF_A = OFF_XM + NKV * H;     // SwiGLU output [8 groups][32 blocks][16] (12 used)
 constexpr int OFF_DP = OFF_A + NKV * 512;   // down partials [8 groups][1024], all blocks
@@ -350,6 +352,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
   __shared__ __attribute__((aligned(16))) float ms[G][NCH];  // per-slot softmax state
   __shared__ float ls[G][NCH], scs[G][NCH], Ms[G], Ls[G];
+  __shared__ float mg[NCH * 10];  // merge input: 8 o values, m, l of each chunk
   __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -677,38 +680,41 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       }
       static_assert(NW * 32 == G * HD && PST - HD <= 32, "combine split");
     }
-    if (c < G) {  // chunk blocks 0 and 1 merge query heads 2g and 2g+1 (log-sum-exp)
-      const int h = c;
-      constexpr int NWD = NCH * PST;
-      static_assert(NWD <= NCH * G * HD, "merge input fits the slot buffer");
-      float* pb = &ored[0][0];  // [NCH][PST]
-      __syncthreads();          // every wave is done reading ored
-      LLWait<(NWD + NT - 1) / NT, LOCAL> wp;
-      wp.issue(P + (size_t)(g * G + h) * NWD, NWD);
-      const bool bail = !wp.finish(ep, a.err, [&](int i, float x) { pb[i] = x; });
+    // ---------------- merge: 8 output dims per block ----------------
+    // block (g, c) merges dims d0 .. d0+7 (d0 = 8 (c % 16)) of query head
+    // 2g + c / 16 over the group's 32 chunk partials (log-sum-exp): thread
+    // t < 320 polls chunk t / 10's word t % 10 (8 o values, then m and l)
+    {
+      const int h = c >> 4, d0 = (c & 15) * 8;
+      const uint64_t* pbase = P + (size_t)(g * G + h) * NCH * PST;
+      const int tm = min(tid, NCH * 10 - 1), cc = tm / 10, k = tm % 10;
+      LLWait<1, LOCAL> wm;
+      wm.issue(pbase + cc * PST + (k < 8 ? d0 + k : HD + k - 8) - tid, NCH * 10);
+      const bool bail = !wm.finish(ep, a.err, [&](int, float x) { mg[tm] = x; });
       if (__syncthreads_or(bail)) return;
       if (wave == 0) {  // lane cc < NCH: chunk cc's weight 2^(m_c - M) / L
-        const float mc = lane < NCH ? pb[lane * PST + HD] : -INFINITY;
-        const float lc = lane < NCH ? pb[lane * PST + HD + 1] : 0.f;
+        const float mc = lane < NCH ? mg[lane * 10 + 8] : -INFINITY;
+        const float lc = lane < NCH ? mg[lane * 10 + 9] : 0.f;
         const float M = wave_max(mc);
         const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
         const float L = wave_sum(wgt * lc);
         if (lane < NCH) scs[0][lane] = wgt / L;
-      }
-      __syncthreads();
-      if (tid < HD) {
-        float o = 0.f;
+        // one wave: its LDS writes are seen by its later reads
+        if (lane < 8) {
+          float o = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) o = fmaf(scs[0][cc], pb[cc * PST + tid], o);
-        st_x<LOCAL>(E + OFF_OG + (g * G + h) * HD + tid, o, ep);
+          for (int q = 0; q < NCH; ++q) o = fmaf(scs[0][q], mg[q * 10 + lane], o);
+          st_x<LOCAL>(E + OFF_OG + g * 512 + 16 * c + lane, o, ep);
+        }
       }
     }
 
     // ---------------- o_proj partial of this group ----------------
     Gain2 gpost;
     {
-      LLWait<1, LOCAL> wo;  // head group g's merged output, 256 words
-      wo.issue(E + OFF_OG + g * OSEG, OSEG);
+      LLWait<1, LOCAL> wo;  // head group g's merged output, 8 words from each block
+      const int to = min(tid, OSEG - 1);
+      wo.issue(E + OFF_OG + g * 512 + 16 * (to >> 3) + (to & 7) - tid, OSEG);
       const bool bail = !wo.finish_to(ep, a.err, xin);
       // next step's bulk loads
       gd.load([&](int r) { return Wd + (size_t)(32 * c + r) * I + g * ISEG; }, wave, lane);
