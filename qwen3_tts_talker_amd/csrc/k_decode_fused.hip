@@ -14,7 +14,8 @@
 // talker_layer_forward), block (g, c) = (group, chunk):
 //   QKV : x -> RMSNorm(g_in) -> 16 rows of head group g's [q|k|v]     -> E1
 //   ATT : q/k norm + NEOX RoPE, new K/V appended (f16), split-KV causal GQA
-//         over 32 key chunks per KV head, one online softmax per slot   -> P
+//         over 32 key chunks per KV head, one online softmax per slot;
+//         slots combined in-wave (permlane swaps), then across waves   -> P
 //   MRG : dims 8(c%16)..+7 of q head 2g+c/16 merged over the 32 chunks
 //         (log-sum-exp)                                                  -> OG
 //   OP  : o_proj split by group: rows 32c..32c+31 of Wo[:, 256g..256g+255]
@@ -113,6 +114,32 @@ __device__ __forceinline__ void st_x(uint64_t* p, float v, uint32_t ep) {
 // every lane
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// v[l] + v[l ^ 16], by v_permlane16_swap, which exchanges the odd rows (16
+// lanes) of one operand with the even rows of the other
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Reduce-scatter steps over the 4 rows of a wave: swap16_add(a, b) holds
+// a[l] + a[l ^ 16] in even rows and b[l] + b[l ^ 16] in odd rows;
+// swap32_add(a, b) holds a[l] + a[l ^ 32] in lanes 0-31, b[l] + b[l ^ 32] in
+// lanes 32-63.
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -350,10 +377,11 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float redw[NW];
   __shared__ float qs[G][HD];                              // normed, roped, scaled q
   __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
-  __shared__ __attribute__((aligned(16))) float ms[G][NCH];  // per-slot softmax state
-  __shared__ float ls[G][NCH], scs[G][NCH], Ms[G], Ls[G];
+  __shared__ __attribute__((aligned(16))) float ow[NW][G * HD];  // per-wave attention sums
+  __shared__ __attribute__((aligned(16))) float mws[G][NW];      // per-wave softmax max
+  __shared__ __attribute__((aligned(16))) float lws[G][NW];      // per-wave softmax sum
   __shared__ float mg[NCH * 10];  // merge input: 8 o values, m, l of each chunk
-  __shared__ __attribute__((aligned(16))) float ored[NCH][G * HD];  // per-slot sums; merge input
+  __shared__ __attribute__((aligned(16))) float cwt[NCH];  // merge weights of the chunks
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // exchange words carry epoch (launch epoch * 64 + layer); layers of equal
@@ -361,8 +389,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   const uint32_t ep0 = a.epoch * 64u;
   const int pos = a.pos;
   const int n_ctx = pos + 1;
-  // attention role of this block: KV head g, key chunk c; chunk blocks 0 and
-  // 1 of each head also merge the chunks of query heads 2g and 2g+1.  With
+  // attention role of this block: KV head g, key chunk c.  With
   // XCD-local exchanges g is the XCD the block runs on: the dispatcher deals
   // blocks to the 8 XCDs in turn (starting where the previous dispatch left
   // off), so blocks 8c .. 8c+7 cover every XCD once and (g, c) is a bijection.
@@ -625,60 +652,66 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         load_rows(Kp, Vp, kb);
         pass(kb, false);
       }
-      // combine the 32 slots: per-slot scale 2^(m_slot - M)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ored[slot][h * HD + sub * 8 + e] = acc[h][e];
-      if (sub == 0) {
+      // combine the 32 slots.  Inside a wave (its 4 rows = 4 slots): scale
+      // each slot by 2^(m_slot - m_wave) and add the rows by permlane swaps,
+      // reduce-scattered so that row r ends with head r % 2, dims sub * 8 +
+      // 4 (r / 2) .. +3.  Then across the 8 waves through LDS.
+      {
+        const int row = lane >> 4;
+        float mwv[G], scv[G], lwv[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          ms[h][slot] = m_run[h];
-          ls[h][slot] = l_run[h];
+          mwv[h] = xor32_max(xor16_max(m_run[h]));
+          scv[h] = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mwv[h]);
+          lwv[h] = xor32_sum(xor16_sum(l_run[h] * scv[h]));
         }
-      }
-      __syncthreads();
-      if (wave == 0) {  // lane (h, slot): the slot's scale; the head's l
-        const int h = lane >> 5, sl = lane & 31;
-        float M = -INFINITY;
+        float r1[8];  // rows 0, 2: head 0; rows 1, 3: head 1 (sums of row pairs)
 #pragma unroll
-        for (int k = 0; k < NCH; k += 4) {
-          const float4 m4 = *reinterpret_cast<const float4*>(&ms[h][k]);
-          M = fmaxf(M, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
-        }
-        const float m = ms[h][sl];
-        const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        scs[h][sl] = sc;
-        float lh = row16_sum(sc * ls[h][sl]);
-        lh += __shfl_xor(lh, 16);
-        if (sl == 0) {
-          Ms[h] = M;  // -inf and 0 for a chunk past the context
-          Ls[h] = lh;
+        for (int e = 0; e < 8; ++e) r1[e] = swap16_add(acc[0][e] * scv[0], acc[1][e] * scv[1]);
+        float r2[4];  // rows 0, 1: dims 0..3; rows 2, 3: dims 4..7 (sums of all rows)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r2[e] = swap32_add(r1[e], r1[e + 4]);
+        *reinterpret_cast<float4*>(&ow[wave][(row & 1) * HD + sub * 8 + (row >> 1) * 4]) =
+            make_float4(r2[0], r2[1], r2[2], r2[3]);
+        if (lane < G) {
+          mws[lane][wave] = lane ? mwv[1] : mwv[0];
+          lws[lane][wave] = lane ? lwv[1] : lwv[0];
         }
       }
       __syncthreads();
       // partial words of (head g, query head h, chunk c) at
       // P + ((g * G + h) * NCH + c) * PST: o[128] (unnormalised), m (log2
-      // units), l, padding.  o value (h, i) = output wave * 32 + lane % 32 is
-      // summed over slots 16 * (lane / 32) .. +15 in each half-wave and the
-      // halves added across lanes l and l ^ 32.
+      // units), l.  o value (h, i) = output wave * 32 + lane % 32 is summed
+      // over waves 4 (lane / 32) .. +3 in each half-wave and the halves added
+      // across lanes l and l ^ 32.
       {
         const int out = wave * 32 + (lane & 31), h = out >> 7, i = out & (HD - 1), half = lane >> 5;
-        float o = 0.f;
-#pragma unroll
-        for (int k = 0; k < NCH / 2; ++k) {
-          const int sl = half * (NCH / 2) + k;
-          o = fmaf(scs[h][sl], ored[sl][h * HD + i], o);
-        }
+        const float4 ma = *reinterpret_cast<const float4*>(&mws[h][0]);
+        const float4 mb = *reinterpret_cast<const float4*>(&mws[h][4]);
+        const float M = fmaxf(fmaxf(fmaxf(ma.x, ma.y), fmaxf(ma.z, ma.w)), fmaxf(fmaxf(mb.x, mb.y), fmaxf(mb.z, mb.w)));
+        // a wave with no key (-inf) weighs 0; so does a chunk past the context
+        auto wt = [&](float m) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); };
+        const float4 mm = half ? mb : ma;
+        const int w0 = 4 * half;
+        float o = wt(mm.x) * ow[w0][out];
+        o = fmaf(wt(mm.y), ow[w0 + 1][out], o);
+        o = fmaf(wt(mm.z), ow[w0 + 2][out], o);
+        o = fmaf(wt(mm.w), ow[w0 + 3][out], o);
         o = xor32_sum(o);
-        if (half == 0) st_x<LOCAL>(P + ((size_t)(g * G + h) * NCH + c) * PST + i, o, ep);
-        if (half == 1 && wave < G && (lane & 31) < PST - HD) {  // m, l, padding of head `wave`
-          const int ii = HD + (lane & 31);
-          const float v = ii == HD ? Ms[wave] : (ii == HD + 1 ? Ls[wave] : 0.f);
-          st_x<LOCAL>(P + ((size_t)(g * G + wave) * NCH + c) * PST + ii, v, ep);
+        uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * PST;
+        if (half == 0) st_x<LOCAL>(pw + i, o, ep);
+        if (half == 1 && i < PST - HD) {  // m, l of head h (-inf, 0 past the context), padding
+          float v = i == 0 ? M : 0.f;
+          if (i == 1) {
+            const float4 la = *reinterpret_cast<const float4*>(&lws[h][0]);
+            const float4 lb = *reinterpret_cast<const float4*>(&lws[h][4]);
+            v = wt(ma.x) * la.x + wt(ma.y) * la.y + wt(ma.z) * la.z + wt(ma.w) * la.w +
+                (wt(mb.x) * lb.x + wt(mb.y) * lb.y + wt(mb.z) * lb.z + wt(mb.w) * lb.w);
+          }
+          st_x<LOCAL>(pw + HD + i, v, ep);
         }
       }
-      static_assert(NW * 32 == G * HD && PST - HD <= 32, "combine split");
+      static_assert(NW * 32 == G * HD && NW == 8 && G == 2, "combine split");
     }
     // ---------------- merge: 8 output dims per block ----------------
     // block (g, c) merges dims d0 .. d0+7 (d0 = 8 (c % 16)) of query head
@@ -698,14 +731,19 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         const float M = wave_max(mc);
         const float wgt = lc > 0.f ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
         const float L = wave_sum(wgt * lc);
-        if (lane < NCH) scs[0][lane] = wgt / L;
-        // one wave: its LDS writes are seen by its later reads
-        if (lane < 8) {
-          float o = 0.f;
-#pragma unroll
-          for (int q = 0; q < NCH; ++q) o = fmaf(scs[0][q], mg[q * 10 + lane], o);
-          st_x<LOCAL>(E + OFF_OG + g * 512 + 16 * c + lane, o, ep);
-        }
+        if (lane < NCH) cwt[lane] = wgt / L;
+        // one wave: its LDS writes are seen by its later reads.  Lane
+        // (q, k) = (lane / 8, lane % 8) sums chunks 4q .. 4q+3 of dim k, then
+        // the 8 lanes of each dim are added (lanes k + 8q)
+        const int k = lane & 7, q = lane >> 3;
+        const float4 w4 = *reinterpret_cast<const float4*>(&cwt[4 * q]);
+        float o = w4.x * mg[(4 * q) * 10 + k];
+        o = fmaf(w4.y, mg[(4 * q + 1) * 10 + k], o);
+        o = fmaf(w4.z, mg[(4 * q + 2) * 10 + k], o);
+        o = fmaf(w4.w, mg[(4 * q + 3) * 10 + k], o);
+        o += dpp_mov<0x128>(o);  // row_ror:8 -> lane k + 8 of the row
+        o = xor32_sum(xor16_sum(o));
+        if (lane < 8) st_x<LOCAL>(E + OFF_OG + g * 512 + 16 * c + lane, o, ep);
       }
     }
 
