@@ -2,8 +2,8 @@
 //
 // Why: a decode token at the Talker's shapes is ~170 dependent steps of at
 // most a few MiB each; as separate launches every step pays launch and ramp
-// latency.  Here 256 blocks (one per CU, co-resident by cooperative launch)
-// walk the layers together.  Between steps they exchange activations as
+// latency.  Here 256 blocks (one per CU, all resident together) walk the
+// layers together.  Between steps they exchange activations as
 // 8-byte words (float value, 32-bit epoch) written with device-coherent
 // stores: a reader polls the words themselves until every epoch matches the
 // current launch, so data and synchronisation travel together and no grid
@@ -843,11 +843,13 @@ size_t fused_decode_part_words(int) { return (size_t)2 * pd::PART_WORDS; }
 int fused_decode_blocks() { return pd::NB; }
 int fused_decode_threads() { return pd::NT; }
 
-// Cooperative launch guarantees that all NB blocks are resident together (or
-// fails).  `cooperative == false` issues an ordinary launch of the same grid,
-// for tracing tools that cannot follow cooperative launches; residency then
-// rests on fused_decode_fits() and on this stream running nothing else at the
-// same time, which holds for the library's single in-order stream.
+// The NB blocks must be resident together.  An ordinary launch gets that
+// from fused_decode_fits() (one block per compute unit, NB <= compute units)
+// and from the caller running no other persistent decode on the device at
+// the same time; work that merely occupies compute units for a while only
+// delays the late blocks, and a wait that outlasts the spin limit becomes
+// error 1.  `cooperative == true` has the runtime guarantee it (or fail the
+// launch), at ~18 us more per launch.
 hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool cooperative) {
   FusedDecodeArgs a = args;
   if (!cooperative) {

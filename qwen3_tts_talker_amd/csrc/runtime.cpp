@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -69,10 +70,14 @@ struct qtalk_ctx {
   float* work = nullptr;
   // persistent batch-1 decode (Talker geometry only)
   bool fused = false;
-  // cooperative launch of the persistent decode; QTALK_COOPERATIVE=0 selects
-  // an ordinary launch of the same grid (for tracers that skip cooperative
-  // launches)
-  bool coop = true;
+  // launch of the persistent decode: an ordinary launch of the 256-block
+  // grid (one block per compute unit, checked at create; persistent decodes
+  // of all contexts in the process serialised per device, see DecodeChain),
+  // or with QTALK_COOPERATIVE=1 a cooperative launch, which the runtime
+  // guarantees co-resident but which costs ~18 us more per token
+  bool coop = false;
+  int dev = 0;
+  hipEvent_t chain_ev = nullptr;  // marks another context's stream (DecodeChain)
   int ncu = 256;  // compute units of the device (placement heuristics only)
   // QKV -> attention -> merge exchanges of the persistent decode inside each
   // XCD (needs the dispatcher's block b -> XCD b % 8 placement, checked at
@@ -87,6 +92,20 @@ struct qtalk_ctx {
 };
 
 namespace {
+
+// Persistent decodes run one at a time per device across every context of
+// the process.  Without a cooperative launch nothing stops two persistent
+// grids from sharing the compute units, and each would then wait for blocks
+// that the other one occupies (until the spin limit turns it into an error).
+// Launches on one stream are ordered by the stream; a launch on another
+// stream first waits for everything enqueued so far on the stream of the
+// previous persistent decode.
+struct DecodeChain {
+  std::mutex mu;
+  hipStream_t stream = nullptr;  // stream of the latest persistent decode on the device
+};
+constexpr int MAX_DEVICES = 64;
+DecodeChain g_chain[MAX_DEVICES];
 
 qtalk_status fail(qtalk_ctx* c, qtalk_status s, const char* fmt, ...) {
   if (c) {
@@ -332,9 +351,18 @@ struct Fwd {
     }
     a.epoch = c->epoch + 1;
     a.xcd_local = c->xcd_local;
+    DecodeChain& ch = g_chain[c->dev];
+    std::lock_guard<std::mutex> lock(ch.mu);
+    if (ch.stream && ch.stream != st) {
+      if ((!c->chain_ev && hipEventCreateWithFlags(&c->chain_ev, hipEventDisableTiming) != hipSuccess) ||
+          hipEventRecord(c->chain_ev, ch.stream) != hipSuccess ||
+          hipStreamWaitEvent(st, c->chain_ev, 0) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot order the persistent decode after another context's");
+    }
     const hipError_t e = launch_decode_fused(a, st, c->coop);
     if (e != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
+    ch.stream = st;
     c->epoch += 1;
     return QTALK_OK;
   }
@@ -425,14 +453,15 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   c->norms_per_layer = norms_per_layer;
   const char* env = getenv("QTALK_FUSED_DECODE");
   const char* env_coop = getenv("QTALK_COOPERATIVE");
-  c->coop = !(env_coop && env_coop[0] == '0');
+  c->coop = env_coop && env_coop[0] == '1';
   {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
       c->ncu = ncu;
+    c->dev = dev;
   }
-  c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') &&
+  c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') && c->dev < MAX_DEVICES &&
              g.n_layers <= 64 &&
              fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
@@ -514,6 +543,12 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
 void qtalk_destroy(qtalk_ctx* c) {
   if (!c) return;
   (void)hipStreamSynchronize(c->stream);
+  if (c->fused) {
+    DecodeChain& ch = g_chain[c->dev];
+    std::lock_guard<std::mutex> lock(ch.mu);
+    if (ch.stream == c->stream) ch.stream = nullptr;
+  }
+  if (c->chain_ev) (void)hipEventDestroy(c->chain_ev);
   free_all(c);
   delete c;
 }

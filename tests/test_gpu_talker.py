@@ -465,18 +465,51 @@ def test_persistent_decode_xcd_local_exchange_equals_device_scope(monkeypatch):
         assert np.array_equal(host(local.kv_read(0, 3, which)), host(device.kv_read(0, 3, which)))
 
 
+def test_persistent_decode_two_streams_interleaved():
+    # two contexts on two streams enqueue persistent decodes alternately with
+    # no host synchronisation between them: the library orders each launch
+    # after the other stream's latest one, so the grids never share the GPU
+    # and both produce the same logits as each other
+    import torch
+    from qwen3_tts_talker_amd import Talker
+    shape = workload("talker_28l_t128_d1024")
+    w = weights_for("talker_28l_t128_d1024", 2)
+    emb = dev(prefill_embeddings(shape, 150))
+    steps = [dev(step_embedding(shape, s)) for s in range(10)]
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    a = Talker(shape, w)
+    b = Talker(shape, w, stream=side.cuda_stream)
+    # every output tensor stays referenced until the device is synchronised:
+    # torch's allocator would hand a dropped one (allocated on the current
+    # stream) to the next allocation while the side stream still writes it
+    outs = [(a.prefill(0, emb), b.prefill(0, emb))]
+    outs += [(a.decode(0, e), b.decode(0, e)) for e in steps]
+    a.sync()
+    b.sync()
+    torch.cuda.synchronize()
+    for s, (la, lb) in enumerate(outs):
+        assert np.array_equal(host(la), host(lb)), s
+    assert a.kv_len(0) == b.kv_len(0) == 160
+    del outs
+    torch.cuda.synchronize()
+    a.close()
+    b.close()
+
+
 def test_persistent_decode_ordinary_launch_matches_cooperative(monkeypatch):
-    # an ordinary launch (as under tracing tools) deals blocks to the XCDs
-    # from wherever the previous dispatch stopped; head groups follow the
-    # XCD each block runs on, so results match the cooperative launch
+    # an ordinary launch (the default) deals blocks to the XCDs from wherever
+    # the previous dispatch stopped; head groups follow the XCD each block
+    # runs on, so results match the cooperative launch.  The two contexts'
+    # decodes interleave on two streams, which the library serialises.
     shape = workload("talker_28l_t128_d1024")
     w = weights_for("talker_28l_t128_d1024", 2)
     emb = prefill_embeddings(shape, 200)
     steps = [step_embedding(shape, s) for s in range(12)]
+    monkeypatch.setenv("QTALK_COOPERATIVE", "1")
     coop = _talker(shape, w)
-    monkeypatch.setenv("QTALK_COOPERATIVE", "0")
-    plain = _talker(shape, w)
     monkeypatch.delenv("QTALK_COOPERATIVE")
+    plain = _talker(shape, w)
     coop.prefill(0, dev(emb))
     plain.prefill(0, dev(emb))
     for s, e in enumerate(steps):
