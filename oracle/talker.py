@@ -20,6 +20,12 @@ timing), one step after another in the pages' order:
 * after the stack: final RMSNorm and the codec_head projection to codebook-0
   logits of the last row ("qwentts.cpp src/talker-forward.h",
   ``talker_forward_core``);
+* output heads: a model may stack several output projections (the code
+  predictor's per-codebook heads); ``select_head`` picks the one that forms
+  the logits of the following calls, head 0 for the code predictor's two-row
+  prefill and head j at its generation step j ("rightkit-qts 0.2.3
+  src/pipeline/tts_transformer.rs", ``forward_code_pred_prefill_cached``,
+  ``forward_code_pred_step_cached``);
 * cache bookkeeping: prefill rewinds the sequence to 0 and writes T
   positions; decode appends one position at ``cur_len`` and attends to
   ``[0, cur_len + 1)``; ``cur_len`` advances only on success
@@ -162,7 +168,9 @@ class TalkerOracle:
                        for lw in weights["layers"]]
         self.L = len(self.layers)
         self.g_final = cv(weights["g_final"])
-        self.w_head = cv(weights["w_head"])
+        heads = cv(weights["w_head"])
+        self.w_heads = heads if heads.ndim == 3 else heads[None]
+        self.w_head = self.w_heads[0]
         self.scale = 1.0 / np.sqrt(shape.head_dim)
         # per sequence: K and V [L][n_kv][alloc][hd], grown on demand
         self.kc: List[Optional[np.ndarray]] = [None] * shape.n_seqs
@@ -226,6 +234,12 @@ class TalkerOracle:
         h2 = rms_norm(x, w["g_post"], s.rms_eps)
         a = swiglu(h2 @ w["wg"].T, h2 @ w["wu"].T)
         return x + a @ w["wd"].T
+
+    def select_head(self, i: int) -> None:
+        """Form the logits of the following calls with stacked head ``i``."""
+        if not 0 <= i < self.w_heads.shape[0]:
+            raise ValueError("head index out of range")
+        self.w_head = self.w_heads[i]
 
     def head(self, x: np.ndarray):
         """Final RMSNorm and codec_head on rows ``x``: (logits, hidden)."""
@@ -324,3 +338,28 @@ class TalkerOracle:
                 raise OverflowError("KV capacity exceeded")
         outs = [self.decode(sq, embs[i]) for i, sq in enumerate(seqs)]
         return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]))
+
+
+def code_predictor_frame(orc: TalkerOracle, hidden: np.ndarray,
+                         cb0_embedding: np.ndarray,
+                         step_embeddings: np.ndarray, seq: int = 0):
+    """One frame of the code predictor on the oracle ``orc``: a two-row
+    prefill of (the Talker's last hidden state, the codebook-0 embedding)
+    read through head 0, then one decode step per further codebook, step j
+    (1-based) fed ``step_embeddings[j - 1]`` and read through head j.  Returns
+    the list of logits, one per codebook after the first
+    ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+    ``predict_remaining_codebooks_kv_with_cache``).  The step inputs are the
+    caller's: on the pages, the previous code's row of embedding table j - 1,
+    passed through ``project_input``, taken here as the identity since the
+    two hidden sizes agree.
+    """
+    out = []
+    orc.select_head(0)
+    lg, _ = orc.prefill(seq, np.stack([hidden, cb0_embedding]))
+    out.append(lg)
+    for j in range(1, len(step_embeddings) + 1):
+        orc.select_head(j)
+        lg, _ = orc.decode(seq, step_embeddings[j - 1])
+        out.append(lg)
+    return out

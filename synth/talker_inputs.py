@@ -18,7 +18,11 @@ Draw recipe (every array is independent and reproducible on its own):
   the float32 array holds exactly the bf16 numbers both sides use;
 * RMSNorm gains (input, post-attention, q, k, final) are ``1 + 0.05 * N(0, 1)``
   in float32 and are never rounded;
-* prefill and step embeddings are ``N(0, 1)`` float32;
+* prefill and step embeddings are ``N(0, 1)`` float32 (for the code
+  predictor they stand in for the Talker's last hidden state, the codebook-0
+  embedding and the per-step table rows);
+* stacked output heads (code predictor) draw head i with key
+  ``[seed, final tag, 1, i]``;
 * the long-context stress workload adds ``sign * 3.0e4`` to four fixed channels
   of every embedding row.
 
@@ -66,6 +70,7 @@ class TalkerShape:
     chunk: int = 0             # prefill chunk for extend (0: one shot)
     batch_lengths: bool = False
     outliers: bool = False
+    n_out_heads: int = 1       # stacked output projections (code predictor: 15)
 
     @property
     def q_dim(self) -> int:
@@ -124,6 +129,12 @@ WORKLOADS: Dict[str, TalkerShape] = {
     "talker_28l_kv2k": TalkerShape(
         name="talker_28l_kv2k", n_layers=28, cap=2048, n_seqs=1, seed=1003,
         emb_seed=1006, prefill_len=1920, decode_steps=128, **_TALKER),
+    # code predictor: 5 layers of the Talker's block geometry, 15 heads of
+    # 2048 codes; per frame a 2-row prefill, then 14 one-token steps
+    "code_predictor_5l": TalkerShape(
+        name="code_predictor_5l", n_layers=5, cap=16, n_seqs=1, seed=1007,
+        emb_seed=1007, prefill_len=2, decode_steps=14, n_out_heads=15,
+        **{**_TALKER, "vocab": 2048}),
 }
 
 
@@ -172,8 +183,13 @@ def make_weights(shape: TalkerShape, n_layers: Optional[int] = None) -> Dict:
                                            for l in range(L)]
     g_final = np.float32(1.0) + np.float32(0.05) * _normal(
         (shape.hidden,), shape.seed, _TAG_FINAL, 0)
-    w_head = np.float32(0.02) * _normal((shape.vocab, shape.hidden),
-                                        shape.seed, _TAG_FINAL, 1)
+    if shape.n_out_heads == 1:
+        w_head = np.float32(0.02) * _normal((shape.vocab, shape.hidden),
+                                            shape.seed, _TAG_FINAL, 1)
+    else:
+        w_head = np.float32(0.02) * np.stack([
+            _normal((shape.vocab, shape.hidden), shape.seed, _TAG_FINAL, 1, i)
+            for i in range(shape.n_out_heads)])
     if shape.weight_dtype == "bf16":
         w_head = round_to_bf16(w_head)
     return {"layers": layers, "g_final": g_final, "w_head": w_head}

@@ -362,3 +362,44 @@ def test_sampled_rows_equal_full_extend_on_one_layer():
     np.testing.assert_array_equal(samp.kv(0, 0, 1), full.kv(0, 0, 1))
     with pytest.raises(ValueError):
         TalkerOracle(shape, make_weights(shape)).extend_rows(0, emb[:4], [0])
+
+
+# -- stacked output heads and the code predictor frame ---------------------------
+
+def test_selected_head_forms_the_logits():
+    # heads i = 2^i * head 0 (exact in float32), so the logits read through
+    # head i are exactly 2^i times head 0's; a wrong index changes the factor
+    shape = small_shape(n_out_heads=4)
+    w = scaled_weights(shape)
+    w["w_head"] = np.stack([np.float32(2 ** i) * w["w_head"][0] for i in range(4)])
+    emb = prefill_embeddings(shape, 6)
+    base = None
+    for i in range(4):
+        orc = TalkerOracle(shape, w)
+        orc.select_head(i)
+        lg, hid = orc.prefill(0, emb)
+        if base is None:
+            base, hid0 = lg, hid
+        np.testing.assert_array_equal(lg, 2 ** i * base)
+        np.testing.assert_array_equal(hid, hid0)  # the hidden state does not depend on the head
+    with pytest.raises(ValueError):
+        orc.select_head(4)
+
+
+def test_code_predictor_frame_equals_prefills_through_each_head():
+    # step j of a frame (cache of j + 1 positions plus the new one, head j)
+    # gives what a fresh prefill of the same j + 2 rows gives through head j
+    shape = small_shape(n_out_heads=5, vocab=24)
+    w = scaled_weights(shape)
+    rows = prefill_embeddings(shape, 6)
+    frame = ot.code_predictor_frame(TalkerOracle(shape, w), rows[0], rows[1], rows[2:])
+    assert len(frame) == 5
+    for j in range(5):
+        orc = TalkerOracle(shape, w)
+        orc.select_head(j)
+        lg, _ = orc.prefill(0, rows[:j + 2])
+        np.testing.assert_allclose(frame[j], lg, rtol=1e-10, atol=1e-12)
+    # the heads differ, so a frame that kept head 0 would not match
+    orc = TalkerOracle(shape, w)
+    lg, _ = orc.prefill(0, rows[:4])
+    assert not np.allclose(frame[2], lg, rtol=1e-3)
