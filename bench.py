@@ -122,6 +122,64 @@ def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
     }
 
 
+def code_predictor(n_frames: int, warmup: int) -> dict:
+    """Frames of the 5-layer code predictor (15 heads of 2048 codes): per
+    frame a two-row prefill through head 0, then 14 one-token decode steps,
+    step j through head j.  Inputs are synthetic rows standing in for the
+    Talker's hidden state, the codebook-0 embedding and the per-step table
+    rows.  Events on the library's stream time the frame and its 14 steps."""
+    import torch
+    from qwen3_tts_talker_amd import Talker, qtalk
+    from synth import make_weights, prefill_embeddings, step_embedding, workload
+
+    shape = workload("code_predictor_5l")
+    tk = Talker(shape, make_weights(shape))
+    lib = qtalk.load_library()
+    ctx = tk.ctx
+    first = torch.from_numpy(prefill_embeddings(shape, 2)).cuda()
+    steps = torch.from_numpy(np.stack([step_embedding(shape, j) for j in range(14)])).cuda()
+    lg = torch.empty(15, shape.vocab, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def frame():
+        s = lib.qtalk_select_head(ctx, 0) | lib.qtalk_prefill(ctx, 0, first.data_ptr(), 2,
+                                                               lg[0].data_ptr(), None)
+        for j in range(1, 15):
+            s |= lib.qtalk_select_head(ctx, j)
+            s |= lib.qtalk_decode(ctx, 0, steps[j - 1].data_ptr(), lg[j].data_ptr(), None)
+        return s
+
+    for _ in range(warmup):
+        assert frame() == 0, qtalk.qtalk_last_error(ctx)
+    torch.cuda.synchronize()
+    assert lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_frames)]
+    status = 0
+    for f in range(n_frames):
+        ev[f][0].record(st)
+        status |= lib.qtalk_select_head(ctx, 0) | lib.qtalk_prefill(
+            ctx, 0, first.data_ptr(), 2, lg[0].data_ptr(), None)
+        ev[f][1].record(st)
+        for j in range(1, 15):
+            status |= lib.qtalk_select_head(ctx, j)
+            status |= lib.qtalk_decode(ctx, 0, steps[j - 1].data_ptr(), lg[j].data_ptr(), None)
+        ev[f][2].record(st)
+    torch.cuda.synchronize()
+    assert status == 0 and lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
+    frame_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 14
+    step_bytes = float(np.mean([decode_bytes(shape, 2 + j) for j in range(1, 15)]))
+    achieved = step_bytes / (step_ms / 1e3) / 1e9
+    tk.close()
+    return {"workload": shape.name, "layers": shape.n_layers, "vocab": shape.vocab,
+            "heads": 15, "frames": n_frames, "frame_us": round(frame_ms * 1e3, 1),
+            "frames_per_s": round(1e3 / frame_ms, 1),
+            "prefill_2rows_us": round(pre_ms * 1e3, 1), "step_us": round(step_ms * 1e3, 2),
+            "step_bytes": int(step_bytes), "step_achieved_gbs": round(achieved, 1),
+            "step_hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +189,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="talker_28l_kv2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--cp-frames", type=int, default=20,
+                    help="code predictor frames timed after the Talker (0: skip)")
     ap.add_argument("--pmc-calibration-mib", type=int, default=0,
                     help="before the timed region, copy this many MiB device to "
                          "device (a known-size reference for HBM byte counters)")
@@ -245,6 +305,8 @@ def main(argv=None):
         "roofline": roof,
     }
     tk.close()
+    if args.cp_frames > 0:
+        out["code_predictor"] = code_predictor(args.cp_frames, warmup=3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)

@@ -71,6 +71,9 @@ typedef struct {
   int32_t max_seqs;     /* number of independent sequences (KV sets)   */
   int32_t weight_dtype; /* qtalk_dtype: F32 or BF16 (projections, head) */
   int32_t kv_dtype;     /* qtalk_dtype: F32 or F16 (cache storage)      */
+  int32_t n_output_heads; /* output projections stacked in codec_head
+                             (0 or 1: one; the code predictor has 15),
+                             at most 64; see qtalk_select_head           */
 } qtalk_config;
 
 /* One layer's weights.  Projections are row-major [out][in] in weight_dtype,
@@ -94,7 +97,8 @@ typedef struct {
 typedef struct {
   const qtalk_layer_weights *layers; /* host array [n_layers]              */
   const float *final_norm;           /* [hidden] float32                    */
-  const void *codec_head;            /* [vocab][hidden] in weight_dtype     */
+  const void *codec_head;            /* [n_output_heads][vocab][hidden] in
+                                        weight_dtype                        */
 } qtalk_weights;
 
 typedef struct qtalk_ctx qtalk_ctx;
@@ -161,6 +165,17 @@ int32_t qtalk_kv_len(const qtalk_ctx *ctx, int32_t seq);
  * [n_kv_heads][cur_len][head_dim].  Errors: QTALK_E_INVAL. */
 qtalk_status qtalk_kv_read(qtalk_ctx *ctx, int32_t seq, int32_t layer,
                            int32_t kv, float *dst);
+
+/* Choose which of the n_output_heads stacked output projections produces
+ * the logits of the calls enqueued after this one (initially head 0).  The
+ * code predictor, a second decoder of the same block structure, reads step
+ * j's logits through its own head j: head 0 after its two-row prefill
+ * (the Talker's last hidden state, then the codebook-0 embedding) and head j
+ * at generation step j ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+ * forward_code_pred_prefill_cached, forward_code_pred_step_cached).  Host
+ * state only; nothing is enqueued.  Errors: QTALK_E_INVAL (head outside
+ * 0 .. n_output_heads-1); the selection is then unchanged. */
+qtalk_status qtalk_select_head(qtalk_ctx *ctx, int32_t head);
 
 /* Block until the context's stream has finished all enqueued work.
  * Errors: QTALK_E_DEVICE if a kernel failed. */

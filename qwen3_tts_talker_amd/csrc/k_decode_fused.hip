@@ -24,7 +24,8 @@
 //   GU  : RMSNorm(g_post), gate|up pairs 384g+12c..+11, silu(g)*u       -> A
 //   DP  : down split by group: rows 32c..32c+31 of Wd[:, 384g..384g+383] -> DP
 //   XD  : x + sum of the 8 groups' down partials, rows 32c..32c+31      -> XD
-// then final RMSNorm + codec_head rows 12b..12b+11 -> logits.  Only OP and DP
+// then final RMSNorm + codec_head rows hr*b..hr*b+hr-1 (hr = vocab / 256)
+// -> logits.  Only OP and DP
 // are read across groups, 256 words per block; every other exchange stays
 // inside a group.  The RMSNorms
 // are folded into the exchange: the received vector is stored times its gain
@@ -53,7 +54,7 @@ namespace pd {
 constexpr int NB = 256;
 constexpr int NT = 512;
 constexpr int NW = NT / 64;
-constexpr int H = 1024, QD = 2048, KVD = 1024, QKV = QD + 2 * KVD, I = 3072, V = 3072;
+constexpr int H = 1024, QD = 2048, KVD = 1024, QKV = QD + 2 * KVD, I = 3072;
 constexpr int HD = 128, NQ = 16, NKV = 8, G = 2;
 constexpr int NCH = NB / NKV;  // key chunks per KV head
 // exchange regions of one layer (words); "group" = the 32 blocks of one KV
@@ -74,7 +75,7 @@ constexpr int PST = 144;
 constexpr int PART_WORDS = NKV * NCH * G * PST;  // per layer
 constexpr long SPIN_LIMIT = 1L << 21;
 
-static_assert(QKV % NB == 0 && H % NB == 0 && I % NB == 0 && V % NB == 0, "row split");
+static_assert(QKV % NB == 0 && H % NB == 0 && I % NB == 0, "row split");
 
 }  // namespace pd
 
@@ -800,14 +801,15 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       const float s = gd.dot(xin, lane);
       if ((lane & 15) == 0) st_ll(E + OFF_DP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
       // after the publish: the next layer's QKV slice, or after the last layer
-      // the 12 head rows (unconditional loads; units past 12 re-read row 11
-      // and are not used)
+      // the block's head_rows head rows (unconditional loads; units past them
+      // re-read the last one and are not used)
       const bool last = l + 1 == a.n_layers;
+      const int hr = a.head_rows;
       const bf16_t* Wn = a.w + (size_t)(last ? l : l + 1) * a.layer_stride;
       gq.load([&](int r) {
-        return last ? a.head + (size_t)(b * 12 + min(r, 11)) * H : Wn + (size_t)(qkv_row0 + r) * H;
+        return last ? a.head + (size_t)(b * hr + min(r, hr - 1)) * H : Wn + (size_t)(qkv_row0 + r) * H;
       }, wave, lane);
-      gq.units = last ? 12 : 16;
+      gq.units = last ? hr : 16;
     }
   }
 
@@ -828,20 +830,20 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       for (int k = tid; k < H; k += NT) a.hidden_out[k] = xin[k] * inv;
     gq.dot(xin, red, wave, lane);
     __syncthreads();
-    if (tid < 12) a.logits[b * 12 + tid] = red[tid] * inv;
+    if (tid < a.head_rows) a.logits[b * a.head_rows + tid] = red[tid] * inv;
   }
 }
 
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim) {
   return hidden == pd::H && q_dim == pd::QD && kv_dim == pd::KVD && inter == pd::I &&
-         vocab == pd::V && n_heads == pd::NQ && n_kv_heads == pd::NKV && head_dim == pd::HD;
+         vocab % pd::NB == 0 && vocab / pd::NB >= 1 && vocab / pd::NB <= 16 && n_heads == pd::NQ &&
+         n_kv_heads == pd::NKV && head_dim == pd::HD;
 }
 
 size_t fused_decode_ll_words(int) { return (size_t)2 * pd::WORDS_PER_LAYER; }
 size_t fused_decode_part_words(int) { return (size_t)2 * pd::PART_WORDS; }
 int fused_decode_blocks() { return pd::NB; }
-int fused_decode_threads() { return pd::NT; }
 
 // The NB blocks must be resident together.  An ordinary launch gets that
 // from fused_decode_fits() (one block per compute unit, NB <= compute units)

@@ -137,12 +137,14 @@ struct FusedDecodeArgs {
   int* err;        // 0; 1 a wait gave up; 3 a block ran on an unexpected XCD
   uint32_t epoch;  // >= 1 and < 2^26; words carry epoch * 64 + layer
   int xcd_local;   // QKV -> attention -> merge exchanges inside each XCD's L2
+  int head_rows;   // vocab / 256: codec head rows per block (1..16)
 
 };
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim);
 bool fused_decode_fits();
 bool fused_decode_xcd_layout_ok(hipStream_t st, bool cooperative);
+int fused_decode_blocks();
 size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);

@@ -36,6 +36,10 @@ constexpr int GEMV_ROWS = MAX_ROWS;  // rows per matrix-vector pass
 constexpr int MFMA_MIN_ROWS = 17;    // prefill rows that switch to the matrix cores
 constexpr int MAX_SPLITS = 128;      // key splits of the decode attention
 constexpr int MAX_CHUNK = 2048;      // rows per matrix-core pass
+// prefill / extend of at most this many rows runs as consecutive persistent
+// single-row launches when the persistent decode is available (one launch
+// costs less than the matrix-vector path's per-layer launches up to here)
+constexpr int FUSED_MAX_ROWS = 2;
 constexpr size_t WORK_ELEMS = (size_t)8 << 20;  // split-K workspace (floats)
 
 struct LayerDev {
@@ -57,7 +61,9 @@ struct qtalk_ctx {
   std::vector<LayerDev> layers;
   void* wblob = nullptr;
   float* nblob = nullptr;
-  void* head = nullptr;
+  void* head = nullptr;  // [n_out_heads][vocab][hidden]
+  int n_out_heads = 1;
+  int head_sel = 0;  // head of the logits of the following calls (qtalk_select_head)
   float* g_final = nullptr;
   void *kc = nullptr, *vc = nullptr;
   size_t layer_kv_elems = 0;  // elements of one layer's cache (all sequences)
@@ -147,6 +153,7 @@ const char* check_config(const qtalk_config* g) {
   if (g->weight_dtype != QTALK_F32 && g->weight_dtype != QTALK_BF16)
     return "weight_dtype must be F32 or BF16";
   if (g->kv_dtype != QTALK_F32 && g->kv_dtype != QTALK_F16) return "kv_dtype must be F32 or F16";
+  if (g->n_output_heads < 0 || g->n_output_heads > 64) return "n_output_heads must be 0..64";
   return nullptr;
 }
 
@@ -288,8 +295,12 @@ struct Fwd {
     launch_gemm_add_norm(a, gain, g.rms_eps, c->hn, N, st);
   }
 
+  const void* head_w() const {
+    return reinterpret_cast<const char*>(c->head) + (size_t)c->head_sel * g.vocab * g.hidden * c->welem;
+  }
+
   void head(const float* X, int n, float* logits, float* hidden_out) {
-    gemv(c->head, g.vocab, g.hidden, X, g.hidden, n, c->g_final, logits, g.vocab, EPI_STORE,
+    gemv(head_w(), g.vocab, g.hidden, X, g.hidden, n, c->g_final, logits, g.vocab, EPI_STORE,
          hidden_out, g.hidden);
   }
 
@@ -319,21 +330,22 @@ struct Fwd {
     }
   }
 
-  // batch-1 decode as one persistent launch
-  qtalk_status run_fused(int seq, const float* emb, float* logits, float* hidden_out) {
+  // one row of sequence `seq` at position `pos` as one persistent launch
+  qtalk_status run_fused(int seq, int pos, const float* emb, float* logits, float* hidden_out) {
     FusedDecodeArgs a{};
     a.w = reinterpret_cast<const bf16_t*>(c->wblob);
     a.layer_stride = c->per_layer;
     a.norms = c->nblob;
     a.norm_stride = c->norms_per_layer;
-    a.head = reinterpret_cast<const bf16_t*>(c->head);
+    a.head = reinterpret_cast<const bf16_t*>(head_w());
+    a.head_rows = g.vocab / fused_decode_blocks();
     a.g_final = c->g_final;
     a.kc = reinterpret_cast<f16_t*>(c->kc);
     a.vc = reinterpret_cast<f16_t*>(c->vc);
     a.layer_kv_elems = c->layer_kv_elems;
     a.cap = g.max_seq_len;
     a.seq = seq;
-    a.pos = c->cur_len[seq];
+    a.pos = pos;
     a.n_layers = g.n_layers;
     a.eps = g.rms_eps;
     a.rope = c->rope;
@@ -422,6 +434,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   c->w_bf16 = g.weight_dtype == QTALK_BF16;
   c->kv_f16 = g.kv_dtype == QTALK_F16;
   c->welem = c->w_bf16 ? 2 : 4;
+  c->n_out_heads = std::max(1, (int)g.n_output_heads);
   c->q_dim = g.n_heads * g.head_dim;
   c->kv_dim = g.n_kv_heads * g.head_dim;
   c->qkv_dim = c->q_dim + 2 * c->kv_dim;
@@ -437,7 +450,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
 
   bool ok = dev_alloc(&c->wblob, per_layer * g.n_layers * we) &&
             dev_alloc((void**)&c->nblob, (norms_per_layer * g.n_layers + H) * 4) &&
-            dev_alloc(&c->head, (size_t)g.vocab * H * we) &&
+            dev_alloc(&c->head, (size_t)c->n_out_heads * g.vocab * H * we) &&
             dev_alloc(&c->kc, c->layer_kv_elems * g.n_layers * kvb) &&
             dev_alloc(&c->vc, c->layer_kv_elems * g.n_layers * kvb) &&
             dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
@@ -514,7 +527,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   }
   c->g_final = c->nblob + (size_t)g.n_layers * norms_per_layer;
   if (s == QTALK_OK && (copy_in(c->g_final, w->final_norm, H * 4) ||
-                        copy_in(c->head, w->codec_head, (size_t)g.vocab * H * we)))
+                        copy_in(c->head, w->codec_head, (size_t)c->n_out_heads * g.vocab * H * we)))
     s = QTALK_E_DEVICE;
   if (s == QTALK_OK) {
     const size_t kv_bytes = c->layer_kv_elems * g.n_layers * kvb;
@@ -564,8 +577,17 @@ static qtalk_status seq_call(qtalk_ctx* c, int32_t seq, const float* emb, int32_
   if ((long long)p0 + T > c->cfg.max_seq_len)
     return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + %d > %d", p0, T, c->cfg.max_seq_len);
   Fwd f(c);
-  f.run_sequence(seq, p0, emb, T, logits, hidden_out);
-  const qtalk_status s = launch_status(c);
+  qtalk_status s = QTALK_OK;
+  if (c->fused && T <= FUSED_MAX_ROWS) {
+    // a row or two (the code predictor's prefill) as consecutive persistent
+    // launches: row t attends to positions 0 .. p0 + t, as in the prefill
+    for (int t = 0; t < T && s == QTALK_OK; ++t)
+      s = f.run_fused(seq, p0 + t, emb + (size_t)t * c->cfg.hidden, logits,
+                      t + 1 == T ? hidden_out : nullptr);
+  } else {
+    f.run_sequence(seq, p0, emb, T, logits, hidden_out);
+    s = launch_status(c);
+  }
   if (s == QTALK_OK) c->cur_len[seq] = p0 + T;
   return s;
 }
@@ -590,7 +612,7 @@ qtalk_status qtalk_decode(qtalk_ctx* c, int32_t seq, const float* emb, float* lo
     return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + 1 > %d", c->cur_len[seq],
                 c->cfg.max_seq_len);
   Fwd f(c);
-  const qtalk_status s = f.run_fused(seq, emb, logits, hidden_out);
+  const qtalk_status s = f.run_fused(seq, c->cur_len[seq], emb, logits, hidden_out);
   if (s == QTALK_OK) c->cur_len[seq] += 1;
   return s;
 }
@@ -647,6 +669,15 @@ qtalk_status qtalk_kv_read(qtalk_ctx* c, int32_t seq, int32_t layer, int32_t kv,
   launch_kv_to_f32(c->kv_f16, base, g.n_kv_heads, g.max_seq_len, c->cur_len[seq], g.head_dim, dst,
                    c->stream);
   return launch_status(c);
+}
+
+qtalk_status qtalk_select_head(qtalk_ctx* c, int32_t head) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (head < 0 || head >= c->n_out_heads)
+    return fail(c, QTALK_E_INVAL, "head %d out of range 0..%d", head, c->n_out_heads - 1);
+  c->head_sel = head;
+  return QTALK_OK;
 }
 
 qtalk_status qtalk_sync(qtalk_ctx* c) {

@@ -26,7 +26,8 @@ QTALK_F32, QTALK_BF16, QTALK_F16 = 0, 1, 2
 
 EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
-           "qtalk_kv_len", "qtalk_kv_read", "qtalk_sync", "qtalk_last_error")
+           "qtalk_kv_len", "qtalk_kv_read", "qtalk_select_head", "qtalk_sync",
+           "qtalk_last_error")
 
 
 class qtalk_config(ctypes.Structure):
@@ -36,7 +37,7 @@ class qtalk_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("max_seq_len", ctypes.c_int32),
                 ("max_seqs", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("n_output_heads", ctypes.c_int32)]
 
 
 class qtalk_layer_weights(ctypes.Structure):
@@ -82,6 +83,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_kv_rewind": (st, [P, I32, I32]),
         "qtalk_kv_len": (I32, [P, I32]),
         "qtalk_kv_read": (st, [P, I32, I32, I32, P]),
+        "qtalk_select_head": (st, [P, I32]),
         "qtalk_sync": (st, [P]),
         "qtalk_last_error": (ctypes.c_char_p, [P]),
     }
@@ -166,6 +168,10 @@ def qtalk_kv_read(ctx, seq, layer, kv, dst) -> int:
                                                     _ptr(dst)))
 
 
+def qtalk_select_head(ctx, head) -> int:
+    return _check(ctx, load_library().qtalk_select_head(ctx, head))
+
+
 def qtalk_sync(ctx) -> int:
     return _check(ctx, load_library().qtalk_sync(ctx))
 
@@ -191,7 +197,9 @@ class Talker:
     """Owns one ``qtalk_ctx`` built from float32 weight arrays.
 
     ``weights`` = ``{"layers": [dict(wq, wk, wv, wo, wg, wu, wd, g_in, g_post,
-    g_q, g_k)], "g_final", "w_head"}``; projections ``[out][in]``.
+    g_q, g_k)], "g_final", "w_head"}``; projections ``[out][in]``.  ``w_head``
+    is ``[vocab][hidden]``, or ``[n][vocab][hidden]`` for n stacked output
+    heads (the code predictor), chosen with ``select_head``.
     """
 
     def __init__(self, shape, weights: Dict, stream=None):
@@ -206,7 +214,9 @@ class Talker:
             rope_theta=shape.rope_theta, max_seq_len=shape.cap,
             max_seqs=shape.n_seqs,
             weight_dtype=QTALK_BF16 if bf16 else QTALK_F32,
-            kv_dtype=QTALK_F16 if shape.kv_dtype == "f16" else QTALK_F32)
+            kv_dtype=QTALK_F16 if shape.kv_dtype == "f16" else QTALK_F32,
+            n_output_heads=(weights["w_head"].shape[0]
+                            if np.ndim(weights["w_head"]) == 3 else 1))
         keep = []
 
         def hp(a, as_weight):
@@ -283,6 +293,9 @@ class Talker:
         dst = self._out(self.shape.n_kv_heads, max(n, 1), self.shape.head_dim)
         qtalk_kv_read(self.ctx, seq, layer, which, dst)
         return dst[:, :n]
+
+    def select_head(self, head):
+        qtalk_select_head(self.ctx, head)
 
     def sync(self):
         qtalk_sync(self.ctx)

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = q.load_library()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(q.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -46,6 +46,7 @@ int main(void) {
   printf("qtalk_weights %zu\\n", sizeof(qtalk_weights));
   F(qtalk_config, rms_eps); F(qtalk_config, rope_theta);
   F(qtalk_config, max_seq_len); F(qtalk_config, kv_dtype);
+  F(qtalk_config, n_output_heads);
   F(qtalk_layer_weights, down_proj); F(qtalk_layer_weights, k_norm);
   F(qtalk_weights, final_norm); F(qtalk_weights, codec_head);
   return 0;
@@ -79,7 +80,9 @@ def _config(**kw):
                                  dict(hidden=100), dict(max_seq_len=0),
                                  dict(weight_dtype=q.QTALK_F16),
                                  dict(kv_dtype=q.QTALK_BF16),
-                                 dict(n_heads=12, n_kv_heads=4)])
+                                 dict(n_heads=12, n_kv_heads=4),
+                                 dict(n_output_heads=-1),
+                                 dict(n_output_heads=65)])
 def test_create_rejects_bad_config_before_any_device_call(bad):
     lib = q.load_library()
     w = q.qtalk_weights()
@@ -97,6 +100,7 @@ def test_null_context_calls_are_rejected():
     assert lib.qtalk_decode(None, 0, None, None, None) == q.QTALK_E_INVAL
     assert lib.qtalk_kv_rewind(None, 0, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_sync(None) == q.QTALK_E_INVAL
+    assert lib.qtalk_select_head(None, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_last_error(None) == b"null context"
     lib.qtalk_destroy(None)
     # missing weights are rejected before any allocation

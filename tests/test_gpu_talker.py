@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import TalkerOracle
+from oracle.talker import code_predictor_frame
 from synth import prefill_embeddings, step_embedding, workload, batch_lengths
 from tests.helpers import argmax_in_band, argmax_ok, dev, host, rel_err, say, weights_for
 
@@ -518,3 +519,46 @@ def test_persistent_decode_ordinary_launch_matches_cooperative(monkeypatch):
         assert np.array_equal(a, b), s
     coop.sync()
     plain.sync()
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_code_predictor_frames_match_oracle(monkeypatch, fused):
+    # two frames of the 5-layer code predictor (15 heads of 2048 codes): a
+    # two-row prefill through head 0, then 14 one-token steps, step j through
+    # head j; the second frame's prefill rewinds the cache.  fused = "1": the
+    # persistent decode (8 head rows per block); "0": the per-step kernels.
+    shape = workload("code_predictor_5l")
+    w = weights_for("code_predictor_5l")
+    monkeypatch.setenv("QTALK_FUSED_DECODE", fused)
+    tk = _talker(shape, w)
+    monkeypatch.delenv("QTALK_FUSED_DECODE")
+    orc = TalkerOracle(shape, w)
+    tol = 2e-2
+    worst, band = 0.0, 0
+    for frame in range(2):
+        first = prefill_embeddings(shape, 2, seq=frame)
+        steps = np.stack([step_embedding(shape, j, seq=frame) for j in range(14)])
+        say(f"code predictor frame {frame} fused={fused}")
+        ref = code_predictor_frame(orc, first[0], first[1], steps)
+        tk.select_head(0)
+        outs = [tk.prefill(0, dev(first))]
+        for j in range(1, 15):
+            tk.select_head(j)
+            outs.append(tk.decode(0, dev(steps[j - 1])))
+        tk.sync()
+        assert tk.kv_len(0) == 16
+        for j, (g, o) in enumerate(zip(outs, ref)):
+            g = host(g)
+            e = rel_err(g, o)
+            worst = max(worst, e)
+            assert e <= tol, (frame, j, e)
+            assert argmax_ok(g, o, tol), (frame, j)
+            assert argmax_ok(g, o, 1e-3), (frame, j)  # the measured error is far below tol
+            band += argmax_in_band(o, tol)
+    for l in (0, 4):
+        for which in (0, 1):
+            assert rel_err(host(tk.kv_read(0, l, which)), orc.kv(0, l, which)) <= tol, (l, which)
+    say(f"code predictor fused={fused}: worst rel err {worst:.2e}, argmax in band {band}")
+    with pytest.raises(Exception):
+        tk.select_head(15)
+    tk.close()
