@@ -13,4 +13,6 @@ from .talker_inputs import (  # noqa: F401
     batch_lengths,
     outlier_channels,
     round_to_bf16,
+    embedding_tables,
+    overlay_row,
 )

@@ -41,6 +41,8 @@ _TAG_PREFILL = 20_000
 _TAG_STEP = 30_000
 _TAG_OUTLIER = 40_000
 _TAG_LENGTHS = 50_000
+_TAG_TABLE = 60_000
+_TAG_OVERLAY = 70_000
 
 LAYER_TENSORS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd",
                  "g_in", "g_post", "g_q", "g_k")
@@ -226,3 +228,20 @@ def batch_lengths(shape: TalkerShape) -> np.ndarray:
     """Per-sequence prefill lengths, uniform integers in [512, 4096]."""
     return _rng(shape.emb_seed, _TAG_LENGTHS).integers(
         512, 4096, size=shape.n_seqs, endpoint=True).astype(np.int64)
+
+
+def embedding_tables(shape: TalkerShape, n_groups: int = 16,
+                     codec_rows: int = 3072, acoustic_rows: int = 2048):
+    """The frame step's tables: the codec embedding ``[codec_rows][hidden]``
+    then ``n_groups - 1`` acoustic tables ``[acoustic_rows][hidden]``, float32
+    ``0.25 * N(0, 1)`` (a 16-row sum has unit scale, like the other inputs)."""
+    out = [np.float32(0.25) * _normal((codec_rows, shape.hidden), shape.seed, _TAG_TABLE, 0)]
+    for g in range(1, n_groups):
+        out.append(np.float32(0.25) * _normal((acoustic_rows, shape.hidden),
+                                              shape.seed, _TAG_TABLE, g))
+    return out
+
+
+def overlay_row(shape: TalkerShape, frame: int) -> np.ndarray:
+    """``[hidden]`` float32 N(0, 1) trailing-text overlay of frame ``frame``."""
+    return _normal((shape.hidden,), shape.emb_seed, _TAG_OVERLAY, frame)
