@@ -122,7 +122,63 @@ def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
     }
 
 
-def code_predictor(n_frames: int, warmup: int) -> dict:
+def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
+    """Whole codec frames on the device, with no host round trip: the
+    Talker's step embedding gathered from the previous frame's 16 ids plus
+    an overlay row, one Talker decode, the suppressed codebook-0 pick, the
+    code predictor's two-row prefill (the Talker's hidden state, the codec
+    row of that id) and 14 steps, each step's input gathered from the table
+    of the previous code and each code picked on the device."""
+    import torch
+    from qwen3_tts_talker_amd import qtalk
+    from synth import embedding_tables, overlay_row
+
+    ts = talker.shape
+    V, H, EOS = ts.vocab, ts.hidden, 2150
+    tabs = [torch.from_numpy(t).cuda() for t in embedding_tables(ts)]
+    ov = torch.from_numpy(overlay_row(ts, 0)).cuda().view(1, H)
+    ids = torch.zeros((2, 16), dtype=torch.int32, device="cuda")
+    emb = torch.empty(1, H, device="cuda")
+    lg_t = torch.empty(V, device="cuda")
+    cp_in = torch.empty(2, H, device="cuda")
+    lg_c = torch.empty(15, cp.shape.vocab, device="cuda")
+    steps = torch.empty(15, 1, H, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def frame(i):
+        a, b = ids[i % 2], ids[(i + 1) % 2]
+        talker.embed_sum(tabs, a.view(16, 1), ov, out=emb)
+        qtalk.qtalk_decode(talker.ctx, 0, emb, lg_t, cp_in[0])
+        talker.argmax(lg_t, suppress_begin=V - 1024, keep_id=EOS, out=b[0:1])
+        cp.embed_sum(tabs[0:1], b[0:1].view(1, 1), out=cp_in[1:2])
+        cp.select_head(0)
+        qtalk.qtalk_prefill(cp.ctx, 0, cp_in, 2, lg_c[0])
+        cp.argmax(lg_c[0], out=b[1:2])
+        for j in range(1, 15):
+            cp.embed_sum(tabs[j:j + 1], b[j:j + 1].view(1, 1), out=steps[j])
+            cp.select_head(j)
+            qtalk.qtalk_decode(cp.ctx, 0, steps[j], lg_c[j])
+            cp.argmax(lg_c[j], out=b[j + 1:j + 2])
+
+    for i in range(warmup):
+        frame(i)
+    torch.cuda.synchronize()
+    talker.sync()
+    cp.sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(n_frames):
+        frame(warmup + i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    talker.sync()
+    cp.sync()
+    ms = e0.elapsed_time(e1) / n_frames
+    return {"frames": n_frames, "talker_ctx": [talker.kv_len(0) - n_frames + 1, talker.kv_len(0)],
+            "frame_us": round(ms * 1e3, 1), "frames_per_s": round(1e3 / ms, 1)}
+
+
+def code_predictor(n_frames: int, warmup: int, talker=None) -> dict:
     """Frames of the 5-layer code predictor (15 heads of 2048 codes): per
     frame a two-row prefill through head 0, then 14 one-token decode steps,
     step j through head j.  Inputs are synthetic rows standing in for the
@@ -166,18 +222,22 @@ def code_predictor(n_frames: int, warmup: int) -> dict:
         ev[f][2].record(st)
     torch.cuda.synchronize()
     assert status == 0 and lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
+    dev_frames = device_frames(talker, tk, n_frames, warmup) if talker is not None else None
     frame_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 14
     step_bytes = float(np.mean([decode_bytes(shape, 2 + j) for j in range(1, 15)]))
     achieved = step_bytes / (step_ms / 1e3) / 1e9
     tk.close()
-    return {"workload": shape.name, "layers": shape.n_layers, "vocab": shape.vocab,
+    res = {"workload": shape.name, "layers": shape.n_layers, "vocab": shape.vocab,
             "heads": 15, "frames": n_frames, "frame_us": round(frame_ms * 1e3, 1),
             "frames_per_s": round(1e3 / frame_ms, 1),
             "prefill_2rows_us": round(pre_ms * 1e3, 1), "step_us": round(step_ms * 1e3, 2),
             "step_bytes": int(step_bytes), "step_achieved_gbs": round(achieved, 1),
             "step_hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+    if dev_frames is not None:
+        res["device_frame"] = dev_frames
+    return res
 
 
 def main(argv=None):
@@ -304,9 +364,11 @@ def main(argv=None):
         "prefill_mfma_frac": round(pf / (pre_med / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof,
     }
-    tk.close()
     if args.cp_frames > 0:
-        out["code_predictor"] = code_predictor(args.cp_frames, warmup=3)
+        # whole frames continue the Talker from context T
+        lib.qtalk_kv_rewind(ctx, 0, T)
+        out["code_predictor"] = code_predictor(args.cp_frames, warmup=3, talker=tk)
+    tk.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)

@@ -166,6 +166,43 @@ int32_t qtalk_kv_len(const qtalk_ctx *ctx, int32_t seq);
 qtalk_status qtalk_kv_read(qtalk_ctx *ctx, int32_t seq, int32_t layer,
                            int32_t kv, float *dst);
 
+/* Step embeddings of n frame slots, on the device: for slot s,
+ *   out[s] = tables[0][ids[0*n + s]] + tables[1][ids[1*n + s]] + ...
+ *          + tables[n_groups-1][ids[(n_groups-1)*n + s]] + overlay[s]
+ * summed in float32 in that order.  With the codec embedding as table 0 and
+ * the 15 acoustic tables after it, this is the Talker's step input: the
+ * codebook-0 token's codec row, each further codebook's acoustic row and the
+ * trailing text row ("qwentts.cpp src/talker-forward.h", the batched step
+ * graph's input_embed; "rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+ * build_talker_step_embedding); with one table it is a plain row gather (the
+ * code predictor's step input).
+ *   tables     host array [n_groups] of DEVICE pointers, each a float32
+ *              [table_rows[g]][hidden] table owned by the caller
+ *   table_rows host array [n_groups]
+ *   ids        DEVICE int32 [n_groups][n], group-major
+ *   overlay    DEVICE float32 [n][hidden], or NULL for none
+ *   out        DEVICE float32 [n][hidden]
+ * Errors: QTALK_E_INVAL (n_groups outside 1..32, n < 1, a null pointer, an
+ * empty table, hidden not a multiple of 4 or above 4096).  An id outside its
+ * table cannot be seen on the host: that slot's row becomes NaN and the next
+ * qtalk_sync returns QTALK_E_DEVICE. */
+qtalk_status qtalk_embed_sum(qtalk_ctx *ctx, int32_t n_groups,
+                             const float *const *tables,
+                             const int32_t *table_rows, const int32_t *ids,
+                             int32_t n, const float *overlay, float *out);
+
+/* Greedy pick of each of n logits rows [n][vocab] (DEVICE float32) into
+ * out_ids[n] (DEVICE int32): ids from suppress_begin up are excluded except
+ * keep_id, then the maximum, the lowest id among equal maxima; NaN counts as
+ * -inf.  For codebook 0 the pages suppress [vocab - 1024, vocab) except the
+ * end-of-speech id ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+ * the suppression loop before select_token); pass suppress_begin >= vocab
+ * for none.  A row with no candidate gets -1.  Errors: QTALK_E_INVAL (null
+ * pointer, n or vocab < 1). */
+qtalk_status qtalk_argmax(qtalk_ctx *ctx, const float *logits, int32_t n,
+                          int32_t vocab, int32_t suppress_begin,
+                          int32_t keep_id, int32_t *out_ids);
+
 /* Choose which of the n_output_heads stacked output projections produces
  * the logits of the calls enqueued after this one (initially head 0).  The
  * code predictor, a second decoder of the same block structure, reads step

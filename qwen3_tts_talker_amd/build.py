@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqtalk.so")
 SOURCES = ["runtime.cpp", "k_gemv.hip", "k_attn.hip", "k_gemm.hip", "k_attn_prefill.hip",
-           "k_decode_fused.hip"]
+           "k_decode_fused.hip", "k_frame.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

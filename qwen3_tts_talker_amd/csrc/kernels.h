@@ -149,4 +149,23 @@ size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);
 
+// frame-step glue (k_frame.hip)
+constexpr int MAX_EMBED_GROUPS = 32;
+struct EmbedSumArgs {
+  const float* tables[MAX_EMBED_GROUPS];  // [rows[g]][hidden] float32 each
+  int rows[MAX_EMBED_GROUPS];
+  int n_groups, n, hidden;  // hidden % 4 == 0, hidden <= 4096
+  const int32_t* ids;       // [n_groups][n] (group-major)
+  const float* overlay;     // [n][hidden] or null
+  float* out;               // [n][hidden]
+  int* status;              // set to 5 when an id is outside its table
+};
+void launch_embed_sum(const EmbedSumArgs& a, hipStream_t st);
+struct ArgmaxArgs {
+  const float* logits;  // [n][vocab]
+  int n, vocab, suppress_begin, keep_id;
+  int32_t* out;         // [n]
+};
+void launch_argmax(const ArgmaxArgs& a, hipStream_t st);
+
 }  // namespace qtalk

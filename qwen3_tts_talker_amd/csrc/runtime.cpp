@@ -92,6 +92,7 @@ struct qtalk_ctx {
   uint64_t* ll = nullptr;
   uint64_t* fpart = nullptr;
   int* ferr = nullptr;
+  int* aux_err = nullptr;  // frame-step kernels: 5 when an id was outside its table
   uint32_t epoch = 0;
   size_t per_layer = 0, norms_per_layer = 0;
   std::string err;
@@ -134,7 +135,7 @@ bool dev_alloc(void** p, size_t bytes) {
 void free_all(qtalk_ctx* c) {
   void* ptrs[] = {c->wblob, c->nblob, c->head, c->kc,     c->vc,    c->rope,   c->x,
                   c->qkv,   c->att,   c->act,  c->hn,     c->part_o, c->part_ml, c->work,
-                  c->ll,    c->fpart, c->ferr};
+                  c->ll,    c->fpart, c->ferr, c->aux_err};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -455,6 +456,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
             dev_alloc(&c->vc, c->layer_kv_elems * g.n_layers * kvb) &&
             dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
             dev_alloc((void**)&c->x, (size_t)rows * H * 4) &&
+            dev_alloc((void**)&c->aux_err, 4) &&
             dev_alloc((void**)&c->qkv, (size_t)rows * c->qkv_dim * 4) &&
             dev_alloc((void**)&c->att, (size_t)rows * c->q_dim * 4) &&
             dev_alloc((void**)&c->act, (size_t)rows * I * 4) &&
@@ -532,7 +534,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   if (s == QTALK_OK) {
     const size_t kv_bytes = c->layer_kv_elems * g.n_layers * kvb;
     if (hipMemsetAsync(c->kc, 0, kv_bytes, c->stream) != hipSuccess ||
-        hipMemsetAsync(c->vc, 0, kv_bytes, c->stream) != hipSuccess)
+        hipMemsetAsync(c->vc, 0, kv_bytes, c->stream) != hipSuccess ||
+        hipMemsetAsync(c->aux_err, 0, 4, c->stream) != hipSuccess)
       s = QTALK_E_DEVICE;
     if (c->fused &&
         (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, c->stream) != hipSuccess ||
@@ -671,6 +674,46 @@ qtalk_status qtalk_kv_read(qtalk_ctx* c, int32_t seq, int32_t layer, int32_t kv,
   return launch_status(c);
 }
 
+qtalk_status qtalk_embed_sum(qtalk_ctx* c, int32_t n_groups, const float* const* tables,
+                             const int32_t* table_rows, const int32_t* ids, int32_t n,
+                             const float* overlay, float* out) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (n_groups < 1 || n_groups > MAX_EMBED_GROUPS)
+    return fail(c, QTALK_E_INVAL, "n_groups must be 1..%d", MAX_EMBED_GROUPS);
+  if (n < 1) return fail(c, QTALK_E_INVAL, "n must be >= 1");
+  if (!tables || !table_rows || !ids || !out)
+    return fail(c, QTALK_E_INVAL, "tables, table_rows, ids and out must not be null");
+  if (c->cfg.hidden % 4 || c->cfg.hidden > 4096)
+    return fail(c, QTALK_E_INVAL, "hidden must be a multiple of 4 and <= 4096");
+  EmbedSumArgs a{};
+  for (int g = 0; g < n_groups; ++g) {
+    if (!tables[g] || table_rows[g] < 1) return fail(c, QTALK_E_INVAL, "table %d is null or empty", g);
+    a.tables[g] = tables[g];
+    a.rows[g] = table_rows[g];
+  }
+  a.n_groups = n_groups;
+  a.n = n;
+  a.hidden = c->cfg.hidden;
+  a.ids = ids;
+  a.overlay = overlay;
+  a.out = out;
+  a.status = c->aux_err;
+  launch_embed_sum(a, c->stream);
+  return launch_status(c);
+}
+
+qtalk_status qtalk_argmax(qtalk_ctx* c, const float* logits, int32_t n, int32_t vocab,
+                          int32_t suppress_begin, int32_t keep_id, int32_t* out_ids) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (!logits || !out_ids) return fail(c, QTALK_E_INVAL, "logits and out_ids must not be null");
+  if (n < 1 || vocab < 1) return fail(c, QTALK_E_INVAL, "n and vocab must be >= 1");
+  ArgmaxArgs a{logits, n, vocab, suppress_begin, keep_id, out_ids};
+  launch_argmax(a, c->stream);
+  return launch_status(c);
+}
+
 qtalk_status qtalk_select_head(qtalk_ctx* c, int32_t head) {
   if (!c) return QTALK_E_INVAL;
   c->err.clear();
@@ -684,6 +727,17 @@ qtalk_status qtalk_sync(qtalk_ctx* c) {
   if (!c) return QTALK_E_INVAL;
   const hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return fail(c, QTALK_E_DEVICE, "stream failed: %s", hipGetErrorString(e));
+  {
+    int code = 0;
+    if (hipMemcpy(&code, c->aux_err, 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(c, QTALK_E_DEVICE, "cannot read the frame-step status word");
+    if (code) {
+      if (hipMemset(c->aux_err, 0, 4) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot clear the frame-step status word");
+      return fail(c, QTALK_E_DEVICE,
+                  "qtalk_embed_sum: an id was outside its table (those slots hold NaN)");
+    }
+  }
   if (c->fused) {
     int code = 0;
     if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)

@@ -26,8 +26,8 @@ QTALK_F32, QTALK_BF16, QTALK_F16 = 0, 1, 2
 
 EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
-           "qtalk_kv_len", "qtalk_kv_read", "qtalk_select_head", "qtalk_sync",
-           "qtalk_last_error")
+           "qtalk_kv_len", "qtalk_kv_read", "qtalk_embed_sum", "qtalk_argmax",
+           "qtalk_select_head", "qtalk_sync", "qtalk_last_error")
 
 
 class qtalk_config(ctypes.Structure):
@@ -83,6 +83,9 @@ def load_library() -> ctypes.CDLL:
         "qtalk_kv_rewind": (st, [P, I32, I32]),
         "qtalk_kv_len": (I32, [P, I32]),
         "qtalk_kv_read": (st, [P, I32, I32, I32, P]),
+        "qtalk_embed_sum": (st, [P, I32, ctypes.POINTER(P), ctypes.POINTER(I32),
+                                 P, I32, P, P]),
+        "qtalk_argmax": (st, [P, P, I32, I32, I32, I32, P]),
         "qtalk_select_head": (st, [P, I32]),
         "qtalk_sync": (st, [P]),
         "qtalk_last_error": (ctypes.c_char_p, [P]),
@@ -166,6 +169,30 @@ def qtalk_kv_len(ctx, seq) -> int:
 def qtalk_kv_read(ctx, seq, layer, kv, dst) -> int:
     return _check(ctx, load_library().qtalk_kv_read(ctx, seq, layer, kv,
                                                     _ptr(dst)))
+
+
+def _iptr(t) -> int:
+    """Device address of an int32 CUDA tensor."""
+    import torch
+    if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError("ids must be contiguous int32 device tensors")
+    return t.data_ptr()
+
+
+def qtalk_embed_sum(ctx, tables, ids, overlay, out) -> int:
+    """``tables``: list of float32 device tensors ``[rows][hidden]``;
+    ``ids``: int32 device tensor ``[n_groups][n]``."""
+    G = len(tables)
+    tp = (ctypes.c_void_p * G)(*[_ptr(t) for t in tables])
+    rows = (ctypes.c_int32 * G)(*[int(t.shape[0]) for t in tables])
+    n = int(ids.shape[1])
+    return _check(ctx, load_library().qtalk_embed_sum(
+        ctx, G, tp, rows, _iptr(ids), n, _ptr(overlay), _ptr(out)))
+
+
+def qtalk_argmax(ctx, logits, n, vocab, suppress_begin, keep_id, out_ids) -> int:
+    return _check(ctx, load_library().qtalk_argmax(
+        ctx, _ptr(logits), n, vocab, suppress_begin, keep_id, _iptr(out_ids)))
 
 
 def qtalk_select_head(ctx, head) -> int:
@@ -296,6 +323,24 @@ class Talker:
 
     def select_head(self, head):
         qtalk_select_head(self.ctx, head)
+
+    def embed_sum(self, tables, ids, overlay=None, out=None):
+        """Step embeddings ``[n][hidden]`` of the int32 ids ``[G][n]``."""
+        if out is None:
+            out = self._out(int(ids.shape[1]), self.shape.hidden)
+        qtalk_embed_sum(self.ctx, tables, ids, overlay, out)
+        return out
+
+    def argmax(self, logits, suppress_begin=None, keep_id=-1, out=None):
+        """Greedy ids (int32 device tensor ``[n]``) of logits ``[n][vocab]``."""
+        import torch
+        lg = logits if logits.dim() == 2 else logits.view(1, -1)
+        n, vocab = int(lg.shape[0]), int(lg.shape[1])
+        if out is None:
+            out = torch.empty(n, dtype=torch.int32, device="cuda")
+        qtalk_argmax(self.ctx, lg, n, vocab,
+                     vocab if suppress_begin is None else suppress_begin, keep_id, out)
+        return out
 
     def sync(self):
         qtalk_sync(self.ctx)

@@ -10,7 +10,9 @@ import pytest
 
 from oracle import TalkerOracle
 from oracle.talker import code_predictor_frame
+from oracle.frame import embed_sum, suppressed_argmax
 from synth import prefill_embeddings, step_embedding, workload, batch_lengths
+from synth import embedding_tables, overlay_row
 from tests.helpers import argmax_in_band, argmax_ok, dev, host, rel_err, say, weights_for
 
 pytestmark = pytest.mark.gpu
@@ -562,3 +564,143 @@ def test_code_predictor_frames_match_oracle(monkeypatch, fused):
     with pytest.raises(Exception):
         tk.select_head(15)
     tk.close()
+
+
+def _tables_dev(shape):
+    import torch
+    tabs = embedding_tables(shape)
+    return tabs, [torch.from_numpy(t).cuda() for t in tabs]
+
+
+def test_embed_sum_equals_oracle_bitwise():
+    import torch
+    shape = workload("talker_1l_t128")
+    tk = _talker(shape, weights_for("talker_1l_t128"))
+    tabs, tabs_d = _tables_dev(shape)
+    rng = np.random.default_rng(11)
+    n = 5
+    ids = np.stack([rng.integers(0, t.shape[0], size=n) for t in tabs]).astype(np.int32)
+    ids[:, 0] = [t.shape[0] - 1 for t in tabs]        # last rows
+    ov = np.stack([overlay_row(shape, f) for f in range(n)])
+    got = host(tk.embed_sum(tabs_d, torch.from_numpy(ids).cuda(), dev(ov)))
+    tk.sync()
+    assert np.array_equal(got, embed_sum(tabs, ids, ov).astype(np.float64))
+    # one table, no overlay: a plain gather
+    got1 = host(tk.embed_sum(tabs_d[3:4], torch.from_numpy(ids[3:4]).cuda()))
+    tk.sync()
+    assert np.array_equal(got1, tabs[3][ids[3]].astype(np.float64))
+    # an id outside its table: NaN for that slot, reported at sync, then cleared
+    bad = ids.copy()
+    bad[7, 2] = tabs[7].shape[0]
+    out = tk.embed_sum(tabs_d, torch.from_numpy(bad).cuda(), dev(ov))
+    with pytest.raises(Exception):
+        tk.sync()
+    o = host(out)
+    assert np.isnan(o[2]).all() and np.array_equal(o[[0, 1, 3, 4]], got[[0, 1, 3, 4]])
+    tk.sync()
+    tk.close()
+
+
+def test_argmax_equals_oracle():
+    import torch
+    shape = workload("talker_1l_t128")
+    tk = _talker(shape, weights_for("talker_1l_t128"))
+    rng = np.random.default_rng(12)
+    V = 3072
+    lg = rng.standard_normal((9, V)).astype(np.float32)
+    lg[0, 2500] = 40.0                  # suppressed spike
+    lg[1, 2150] = 40.0                  # the kept id
+    lg[2, [7, 900]] = 30.0              # tie: lowest index
+    lg[3, ::3] = np.nan                 # NaN never wins
+    lg[4, :] = -np.inf                  # nothing finite
+    lg[5, 2047] = 25.0                  # last unsuppressed id
+    lg[6, 3071] = 30.0                  # last id, suppressed
+    lg[7, :] = 1.0                      # all equal
+    for sb, keep in ((V - 1024, 2150), (V, -1), (0, 2150), (1, -1)):
+        got = tk.argmax(dev(lg), suppress_begin=sb, keep_id=keep).cpu().numpy()
+        want = [suppressed_argmax(r, sb, keep) for r in lg]
+        assert list(got) == want, (sb, keep)
+    got = tk.argmax(dev(lg[:1]), suppress_begin=0, keep_id=-1).cpu().numpy()
+    assert list(got) == [-1]            # no candidate at all
+    tk.sync()
+    tk.close()
+
+
+def _masked(lg, sb, keep):
+    m = np.array(lg, dtype=np.float64)
+    sup = np.arange(m.size) >= sb
+    if 0 <= keep < m.size:
+        sup[keep] = False
+    m[sup] = -np.inf
+    return m
+
+
+def test_device_frame_loop_matches_teacher_forced_oracle():
+    # Talker (2 real-shape layers) + code predictor (5 layers, 15 heads): per
+    # frame the step embedding is gathered on the device from the previous
+    # frame's 16 ids, the Talker's codebook-0 id is picked on the device with
+    # the pages' suppression, and the code predictor's 15 codes follow, each
+    # step's input gathered on the device; nothing returns to the host until
+    # the end.  The oracle then replays the frames with the GPU's ids.
+    import torch
+    from qwen3_tts_talker_amd import qtalk
+    ts = workload("talker_28l_t128_d1024")
+    tw = weights_for("talker_28l_t128_d1024", 2)
+    cs = workload("code_predictor_5l")
+    cw = weights_for("code_predictor_5l")
+    tk, cp = _talker(ts, tw), _talker(cs, cw)
+    tabs, tabs_d = _tables_dev(ts)
+    V, EOS, H = ts.vocab, 2150, ts.hidden
+    n_frames = 2
+    pre = prefill_embeddings(ts, 16)
+    tk.prefill(0, dev(pre))
+    ids = torch.zeros((n_frames + 1, 16), dtype=torch.int32, device="cuda")
+    ids[0] = torch.arange(16, dtype=torch.int32) * 37          # the prompt's last frame
+    ovs = [dev(overlay_row(ts, f)) for f in range(n_frames)]
+    keep = []
+    for f in range(n_frames):
+        emb = tk.embed_sum(tabs_d, ids[f].view(16, 1), ovs[f].view(1, H))
+        lg_t = torch.empty(V, device="cuda")
+        cp_in = torch.empty(2, H, device="cuda")
+        qtalk.qtalk_decode(tk.ctx, 0, emb, lg_t, cp_in[0])
+        tk.argmax(lg_t, suppress_begin=V - 1024, keep_id=EOS, out=ids[f + 1, 0:1])
+        cp.embed_sum(tabs_d[0:1], ids[f + 1, 0:1].view(1, 1), out=cp_in[1:2])
+        cp.select_head(0)
+        lgs = [cp.prefill(0, cp_in)]
+        cp.argmax(lgs[0], out=ids[f + 1, 1:2])
+        for j in range(1, 15):
+            e = cp.embed_sum(tabs_d[j:j + 1], ids[f + 1, j:j + 1].view(1, 1))
+            cp.select_head(j)
+            lgs.append(cp.decode(0, e))
+            cp.argmax(lgs[-1], out=ids[f + 1, j + 1:j + 2])
+        keep.append((emb, lg_t, cp_in, lgs))
+    tk.sync()
+    cp.sync()
+    ids_h = ids.cpu().numpy()
+    say("frame ids", ids_h[1:, :6].tolist())
+    to = TalkerOracle(ts, tw)
+    to.prefill(0, pre)
+    co = TalkerOracle(cs, cw)
+    tol = 2e-2
+    worst = 0.0
+    for f, (emb, lg_t, cp_in, lgs) in enumerate(keep):
+        e_ref = embed_sum(tabs, ids_h[f].reshape(16, 1), overlay_row(ts, f)[None])
+        assert np.array_equal(host(emb), e_ref.astype(np.float64)), f
+        o_lg, o_hid = to.decode(0, e_ref[0])
+        g_lg = host(lg_t)
+        worst = max(worst, rel_err(g_lg, o_lg))
+        assert rel_err(g_lg, o_lg) <= tol, f
+        assert ids_h[f + 1, 0] == suppressed_argmax(g_lg.astype(np.float32), V - 1024, EOS)
+        assert argmax_ok(_masked(g_lg, V - 1024, EOS), _masked(o_lg, V - 1024, EOS), tol)
+        assert rel_err(host(cp_in[0]), o_hid) <= tol
+        ref = code_predictor_frame(co, o_hid, tabs[0][ids_h[f + 1, 0]],
+                                   np.stack([tabs[j][ids_h[f + 1, j]] for j in range(1, 15)]))
+        for j in range(15):
+            g = host(lgs[j])
+            worst = max(worst, rel_err(g, ref[j]))
+            assert rel_err(g, ref[j]) <= tol, (f, j)
+            assert ids_h[f + 1, j + 1] == suppressed_argmax(g.astype(np.float32), cs.vocab, -1)
+            assert argmax_ok(g, ref[j], tol), (f, j)
+    say(f"device frame loop: worst rel err {worst:.2e}")
+    tk.close()
+    cp.close()
