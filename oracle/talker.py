@@ -324,6 +324,20 @@ class TalkerOracle:
         self.cur_len[seq] = 0
         return self.extend(seq, emb, all_rows=all_rows)
 
+    def prefill_batch(self, seqs: Sequence[int], embs: np.ndarray):
+        """Prefill each listed sequence from ``embs[b]`` ``[T][hidden]``: B
+        independent prefills of equal length, each into positions [0, T) of
+        its own cache ("transcribe.cpp src/causal_lm/causal_lm.cpp",
+        ``block_prefill_batched``); per-sequence (logits, hidden) stacked."""
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("duplicate sequence id")
+        embs = np.asarray(embs)
+        if embs.shape[1] > self.s.cap:
+            raise OverflowError("KV capacity exceeded")
+        outs = [self.prefill(sq, embs[i]) for i, sq in enumerate(seqs)]
+        return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]))
+
     def decode(self, seq: int, emb_row: np.ndarray):
         """One position at ``cur_len``; attends to ``[0, cur_len + 1)``."""
         return self.extend(seq, np.asarray(emb_row).reshape(1, -1))

@@ -403,3 +403,29 @@ def test_code_predictor_frame_equals_prefills_through_each_head():
     orc = TalkerOracle(shape, w)
     lg, _ = orc.prefill(0, rows[:4])
     assert not np.allclose(frame[2], lg, rtol=1e-3)
+
+
+def test_prefill_batch_is_independent_prefills():
+    # each listed sequence ends as a lone prefill leaves it; sequences not
+    # listed keep their caches; duplicates and overlong rows are rejected
+    shape = small_shape(n_seqs=4)
+    w = scaled_weights(shape)
+    embs = np.stack([prefill_embeddings(shape, 9, seq=s) for s in range(3)])
+    orc = TalkerOracle(shape, w)
+    keep_emb = prefill_embeddings(shape, 5, seq=3)
+    orc.prefill(1, keep_emb)                 # will be overwritten
+    orc.prefill(3, keep_emb)                 # not listed: untouched
+    before = orc.kv(3, 1, 0)
+    lg, hid = orc.prefill_batch([2, 0, 1], embs)
+    for b, sq in enumerate([2, 0, 1]):
+        ref = TalkerOracle(shape, w)
+        rl, rh = ref.prefill(sq, embs[b])
+        np.testing.assert_array_equal(lg[b], rl)
+        np.testing.assert_array_equal(hid[b], rh)
+        np.testing.assert_array_equal(orc.kv(sq, 1, 1), ref.kv(sq, 1, 1))
+        assert orc.kv_len(sq) == 9
+    np.testing.assert_array_equal(orc.kv(3, 1, 0), before)
+    with pytest.raises(ValueError):
+        orc.prefill_batch([0, 0], embs[:2])
+    with pytest.raises(OverflowError):
+        orc.prefill_batch([0], np.zeros((1, shape.cap + 1, shape.hidden)))
