@@ -13,6 +13,7 @@ resident in device memory before the timed region starts.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -120,6 +121,53 @@ def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
                    f"{emb.shape[0]}-row prefill; value = decode tok/s"),
         "prefill_tok_s": emb.shape[0] / (t1 - t0),
     }
+
+
+def batched_prefill(shape, weights, n: int, T: int, reps: int = 5) -> dict:
+    """Batched prefill of n utterances of T rows each (one call) against n
+    consecutive single prefills, on a context with n sequences."""
+    import torch
+    from qwen3_tts_talker_amd import Talker, qtalk
+    from synth import prefill_embeddings
+
+    s = shape.with_(n_seqs=n, cap=T)
+    tk = Talker(s, weights)
+    ctx, lib = tk.ctx, qtalk.load_library()
+    emb = torch.from_numpy(np.stack([prefill_embeddings(s, T, seq=b) for b in range(n)])).cuda()
+    lg = torch.empty(n, s.vocab, device="cuda")
+    seqs = (ctypes.c_int32 * n)(*range(n))
+    st = torch.cuda.current_stream()
+
+    def batched():
+        return lib.qtalk_prefill_batch(ctx, n, seqs, emb.data_ptr(), T, lg.data_ptr(), None)
+
+    def serial():
+        r = 0
+        for b in range(n):
+            r |= lib.qtalk_prefill(ctx, b, emb[b].data_ptr(), T, lg[b].data_ptr(), None)
+        return r
+
+    res = {}
+    for name, fn in (("batched", batched), ("serial", serial)):
+        assert fn() == 0, qtalk.qtalk_last_error(ctx)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            assert fn() == 0, qtalk.qtalk_last_error(ctx)
+            e1.record(st)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = sorted(ts)[len(ts) // 2]
+    assert lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
+    tk.close()
+    fl = n * prefill_flops(s, T)
+    return {"seqs": n, "T": T, "batched_ms": round(res["batched"], 3),
+            "tok_s": round(n * T / (res["batched"] / 1e3), 1),
+            "tflops": round(fl / (res["batched"] / 1e3) / 1e12, 2),
+            "mfma_frac": round(fl / (res["batched"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "serial_ms": round(res["serial"], 3)}
 
 
 def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
@@ -249,6 +297,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="talker_28l_kv2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--batch-prefill", type=int, default=16,
+                    help="utterances of 128 rows in the batched-prefill leg (0: skip)")
     ap.add_argument("--cp-frames", type=int, default=20,
                     help="code predictor frames timed after the Talker (0: skip)")
     ap.add_argument("--pmc-calibration-mib", type=int, default=0,
@@ -369,6 +419,8 @@ def main(argv=None):
         lib.qtalk_kv_rewind(ctx, 0, T)
         out["code_predictor"] = code_predictor(args.cp_frames, warmup=3, talker=tk)
     tk.close()
+    if args.batch_prefill > 0:
+        out["prefill_batch"] = batched_prefill(shape, weights, args.batch_prefill, 128)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)

@@ -166,6 +166,21 @@ int32_t qtalk_kv_len(const qtalk_ctx *ctx, int32_t seq);
 qtalk_status qtalk_kv_read(qtalk_ctx *ctx, int32_t seq, int32_t layer,
                            int32_t kv, float *dst);
 
+/* Batched prefill: rewind each of the n distinct sequences seqs[b] (host
+ * array) to 0 and write T positions from emb[b] (emb is [n][T][hidden]);
+ * logits [n][vocab] receive each sequence's last-row logits and hidden_out
+ * [n][hidden] (nullable) its last row after the final RMSNorm.  The pages'
+ * batched prefill: B utterances of T tokens each, every one into positions
+ * [0, T) of its own KV slab, projections over all B*T rows at once
+ * ("transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill_batched).
+ * Results equal n separate qtalk_prefill calls up to summation order.
+ * Errors: QTALK_E_INVAL (n < 1, T < 1, null pointer, a sequence id out of
+ * range or listed twice), QTALK_E_OVERFLOW (T > max_seq_len); nothing is
+ * launched and no cache length changes. */
+qtalk_status qtalk_prefill_batch(qtalk_ctx *ctx, int32_t n, const int32_t *seqs,
+                                 const float *emb, int32_t T, float *logits,
+                                 float *hidden_out);
+
 /* Step embeddings of n frame slots, on the device: for slot s,
  *   out[s] = tables[0][ids[0*n + s]] + tables[1][ids[1*n + s]] + ...
  *          + tables[n_groups-1][ids[(n_groups-1)*n + s]] + overlay[s]

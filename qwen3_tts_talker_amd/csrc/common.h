@@ -19,21 +19,24 @@ constexpr int MAX_ROWS = 64;  // rows (tokens) described by one RowMeta
 
 // Which (sequence, position) each activation row belongs to.  Prefill and
 // extend rows are uniform (one sequence, consecutive positions from p0);
+// a batched prefill stacks `per` such rows for each listed sequence;
 // batched decode rows carry one (seq, pos) each.
 struct RowMeta {
   int n;        // number of rows
-  int uniform;  // 1: row t is (seq0, p0 + t)
+  int uniform;  // 1: row t is (seq0, p0 + t); 2: (seq[t / per], p0 + t % per);
+                // 0: (seq[t], pos[t])
   int seq0;
   int p0;
+  int per;
   int seq[MAX_ROWS];
   int pos[MAX_ROWS];
 };
 
 __device__ __forceinline__ int row_seq(const RowMeta& r, int t) {
-  return r.uniform ? r.seq0 : r.seq[t];
+  return r.uniform == 1 ? r.seq0 : (r.uniform == 2 ? r.seq[t / r.per] : r.seq[t]);
 }
 __device__ __forceinline__ int row_pos(const RowMeta& r, int t) {
-  return r.uniform ? r.p0 + t : r.pos[t];
+  return r.uniform == 1 ? r.p0 + t : (r.uniform == 2 ? r.p0 + t % r.per : r.pos[t]);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {

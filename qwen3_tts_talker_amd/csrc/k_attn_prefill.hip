@@ -104,7 +104,12 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   const int n = lane & 31, h = lane >> 5;
   const int posn = P0 + n;
 
-  const size_t head_off = (size_t)(a.seq * nkv + g) * a.cap * HD;
+  // batched prefill: this block's sequence and its rows of q and out
+  const int bz = blockIdx.y;
+  const int seq = a.nbatch > 1 ? a.seqs[bz] : a.seq;
+  const float* qrows = a.q + (size_t)bz * a.T * a.ldq;
+  bf16_t* orows = a.out + (size_t)bz * a.T * a.ldo;
+  const size_t head_off = (size_t)(seq * nkv + g) * a.cap * HD;
   const f16_t* Kg = a.kc + head_off;
   const f16_t* Vg = a.vc + head_off;
 
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   if (kh == 0) {
     const int t = min(posn - a.p0, a.T - 1);
     const int pr = min(posn, a.p0 + a.T - 1);
-    const float* qp = a.q + (size_t)t * a.ldq + (size_t)hq * HD + h * 8;
+    const float* qp = qrows + (size_t)t * a.ldq + (size_t)hq * HD + h * 8;
     float qv[NKS][8];
     float ss = 0.f;
 #pragma unroll
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
   const float l = l_run * a0 + l1 * a1;
   const float inv = 1.0f / xor32_sum(l);
-  bf16_t* orow = a.out + (size_t)(posn - a.p0) * a.ldo + (size_t)hq * HD;
+  bf16_t* orow = orows + (size_t)(posn - a.p0) * a.ldo + (size_t)hq * HD;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -375,7 +380,7 @@ bool attn_prefill_supported(int head_dim, int group) {
 
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st) {
   const int nqb = (a.T + pa::PB - 1) / pa::PB;
-  const dim3 grid(nqb * a.n_kv_heads);
+  const dim3 grid(nqb * a.n_kv_heads, a.nbatch > 1 ? a.nbatch : 1);
   if (a.head_dim == 128) hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(pa::NT), 0, st, a);
   else hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(pa::NT), 0, st, a);
 }

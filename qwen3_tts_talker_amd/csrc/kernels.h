@@ -80,6 +80,10 @@ struct PrefillAttnArgs {
   bf16_t* out;   // row t at out + t*ldo
   int ldo;
   int ncu;  // compute units (block placement only)
+  // batched prefill: nbatch > 1 sequences seqs[z] of T rows each, stacked
+  // (q and out rows z*T .. z*T+T-1); nbatch <= 1: the single sequence `seq`
+  int nbatch;
+  int seqs[MAX_ROWS];
 };
 bool attn_prefill_supported(int head_dim, int group);
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st);

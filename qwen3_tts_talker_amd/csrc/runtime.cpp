@@ -209,7 +209,8 @@ struct Fwd {
   }
 
   static int max_ctx(const RowMeta& r) {
-    if (r.uniform) return r.p0 + r.n;
+    if (r.uniform == 1) return r.p0 + r.n;
+    if (r.uniform == 2) return r.p0 + r.per;
     int m = 0;
     for (int i = 0; i < r.n; ++i) m = std::max(m, r.pos[i] + 1);
     return m;
@@ -273,6 +274,12 @@ struct Fwd {
       p.seq = rows.seq0;
       p.p0 = rows.p0;
       p.T = T;
+      if (rows.uniform == 2) {  // T / per stacked sequences of per rows each
+        p.T = rows.per;
+        p.nbatch = T / rows.per;
+        for (int z = 0; z < p.nbatch; ++z) p.seqs[z] = rows.seq[z];
+        p.seq = rows.seq[0];
+      }
       p.qscale = 1.4426950408889634f / sqrtf((float)g.head_dim);
       p.out = att_b;
       p.ldo = c->q_dim;
@@ -328,6 +335,52 @@ struct Fwd {
       }
       done += n;
       if (done == T) head(c->x + (size_t)(n - 1) * g.hidden, 1, logits, hidden_out);
+    }
+  }
+
+  // batched prefill: n sequences of T rows each from position 0, stacked in
+  // groups that fit one matrix-core pass; each group's logits from its
+  // sequences' last rows
+  void run_batch_prefill(const int32_t* seqs, int n, const float* emb, int T, float* logits,
+                         float* hidden_out) {
+    const int H = g.hidden;
+    const bool mfma = c->w_bf16 && gemm_shape_ok(1, c->qkv_dim, H) && gemm_shape_ok(1, H, c->q_dim) &&
+                      gemm_shape_ok(1, 2 * g.intermediate, H) && gemm_shape_ok(1, H, g.intermediate) &&
+                      g.intermediate % 16 == 0;
+    const int cap_rows = mfma ? std::max(c->tc, GEMV_ROWS) : GEMV_ROWS;
+    if (T > cap_rows) {  // a sequence's rows exceed one pass: one prefill per sequence
+      for (int b = 0; b < n; ++b)
+        run_sequence(seqs[b], 0, emb + (size_t)b * T * H, T, logits + (size_t)b * g.vocab,
+                     hidden_out ? hidden_out + (size_t)b * H : nullptr);
+      return;
+    }
+    const int per_group = std::min(MAX_ROWS, cap_rows / T);
+    for (int b0 = 0; b0 < n; b0 += per_group) {
+      const int nb = std::min(per_group, n - b0), M = nb * T;
+      RowMeta rows{};
+      rows.n = M;
+      rows.p0 = 0;
+      if (M <= GEMV_ROWS && !(mfma && M >= MFMA_MIN_ROWS)) {
+        rows.uniform = 0;
+        for (int t = 0; t < M; ++t) {
+          rows.seq[t] = seqs[b0 + t / T];
+          rows.pos[t] = t % T;
+        }
+      } else {
+        rows.uniform = 2;
+        rows.per = T;
+        rows.seq0 = seqs[b0];
+        for (int z = 0; z < nb; ++z) rows.seq[z] = seqs[b0 + z];
+      }
+      (void)hipMemcpyAsync(c->x, emb + (size_t)b0 * T * H, (size_t)M * H * 4, hipMemcpyDeviceToDevice, st);
+      for (int l = 0; l < g.n_layers; ++l) {
+        if (mfma && M >= MFMA_MIN_ROWS) layer_mfma(l, rows, l > 0);
+        else layer_gemv(l, rows);
+      }
+      // last row of each sequence: rows T-1, 2T-1, ... (stride T rows)
+      gemv(head_w(), g.vocab, H, c->x + (size_t)(T - 1) * H, T * H, nb, c->g_final,
+           logits + (size_t)b0 * g.vocab, g.vocab, EPI_STORE,
+           hidden_out ? hidden_out + (size_t)b0 * H : nullptr, H);
     }
   }
 
@@ -444,7 +497,9 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   const size_t per_layer = n_qkv + n_o + n_gu + n_d;
   const size_t norms_per_layer = 2 * H + 2 * (size_t)g.head_dim;
   c->layer_kv_elems = (size_t)g.max_seqs * g.n_kv_heads * g.max_seq_len * g.head_dim;
-  c->tc = std::min(g.max_seq_len, MAX_CHUNK);
+  // rows per matrix-core pass: a prefill chunk of one sequence, or the
+  // stacked rows of a batched prefill over several
+  c->tc = (int)std::min<long long>((long long)g.max_seq_len * g.max_seqs, MAX_CHUNK);
   const int part_rows = GEMV_ROWS;
   const int rows = std::max(c->tc, GEMV_ROWS);
   const size_t kvb = c->kv_f16 ? 2 : 4;
@@ -603,6 +658,30 @@ qtalk_status qtalk_prefill(qtalk_ctx* c, int32_t seq, const float* emb, int32_t 
 qtalk_status qtalk_extend(qtalk_ctx* c, int32_t seq, const float* emb, int32_t T, float* logits,
                           float* hidden_out) {
   return seq_call(c, seq, emb, T, logits, hidden_out, false);
+}
+
+qtalk_status qtalk_prefill_batch(qtalk_ctx* c, int32_t n, const int32_t* seqs, const float* emb,
+                                 int32_t T, float* logits, float* hidden_out) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (n < 1 || !seqs) return fail(c, QTALK_E_INVAL, "n must be >= 1 and seqs non-null");
+  if (T < 1) return fail(c, QTALK_E_INVAL, "T must be >= 1 (got %d)", T);
+  if (!emb || !logits) return fail(c, QTALK_E_INVAL, "emb and logits must not be null");
+  std::vector<char> seen(c->cfg.max_seqs, 0);
+  for (int b = 0; b < n; ++b) {
+    if (seqs[b] < 0 || seqs[b] >= c->cfg.max_seqs)
+      return fail(c, QTALK_E_INVAL, "bad sequence id %d", seqs[b]);
+    if (seen[seqs[b]]) return fail(c, QTALK_E_INVAL, "sequence %d listed twice", seqs[b]);
+    seen[seqs[b]] = 1;
+  }
+  if (T > c->cfg.max_seq_len)
+    return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d > %d", T, c->cfg.max_seq_len);
+  Fwd f(c);
+  f.run_batch_prefill(seqs, n, emb, T, logits, hidden_out);
+  const qtalk_status s = launch_status(c);
+  if (s == QTALK_OK)
+    for (int b = 0; b < n; ++b) c->cur_len[seqs[b]] = T;
+  return s;
 }
 
 qtalk_status qtalk_decode(qtalk_ctx* c, int32_t seq, const float* emb, float* logits,

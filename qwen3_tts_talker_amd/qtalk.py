@@ -26,7 +26,8 @@ QTALK_F32, QTALK_BF16, QTALK_F16 = 0, 1, 2
 
 EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
-           "qtalk_kv_len", "qtalk_kv_read", "qtalk_embed_sum", "qtalk_argmax",
+           "qtalk_kv_len", "qtalk_kv_read", "qtalk_prefill_batch", "qtalk_embed_sum",
+           "qtalk_argmax",
            "qtalk_select_head", "qtalk_sync", "qtalk_last_error")
 
 
@@ -83,6 +84,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_kv_rewind": (st, [P, I32, I32]),
         "qtalk_kv_len": (I32, [P, I32]),
         "qtalk_kv_read": (st, [P, I32, I32, I32, P]),
+        "qtalk_prefill_batch": (st, [P, I32, ctypes.POINTER(I32), P, I32, P, P]),
         "qtalk_embed_sum": (st, [P, I32, ctypes.POINTER(P), ctypes.POINTER(I32),
                                  P, I32, P, P]),
         "qtalk_argmax": (st, [P, P, I32, I32, I32, I32, P]),
@@ -169,6 +171,13 @@ def qtalk_kv_len(ctx, seq) -> int:
 def qtalk_kv_read(ctx, seq, layer, kv, dst) -> int:
     return _check(ctx, load_library().qtalk_kv_read(ctx, seq, layer, kv,
                                                     _ptr(dst)))
+
+
+def qtalk_prefill_batch(ctx, seqs: Sequence[int], emb, T, logits,
+                        hidden_out=None) -> int:
+    arr = (ctypes.c_int32 * len(seqs))(*seqs)
+    return _check(ctx, load_library().qtalk_prefill_batch(
+        ctx, len(seqs), arr, _ptr(emb), T, _ptr(logits), _ptr(hidden_out)))
 
 
 def _iptr(t) -> int:
@@ -300,6 +309,14 @@ class Talker:
         lg = self._out(self.shape.vocab)
         hd = self._out(self.shape.hidden) if hidden else None
         qtalk_decode(self.ctx, seq, emb, lg, hd)
+        return (lg, hd) if hidden else lg
+
+    def prefill_batch(self, seqs, emb, hidden=False):
+        """``emb`` ``[n][T][hidden]``: prefill each listed sequence."""
+        n, T = len(seqs), int(emb.shape[1])
+        lg = self._out(n, self.shape.vocab)
+        hd = self._out(n, self.shape.hidden) if hidden else None
+        qtalk_prefill_batch(self.ctx, list(seqs), emb, T, lg, hd)
         return (lg, hd) if hidden else lg
 
     def decode_batch(self, seqs, emb, hidden=False):

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = q.load_library()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert sorted(q.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n

@@ -704,3 +704,38 @@ def test_device_frame_loop_matches_teacher_forced_oracle():
     say(f"device frame loop: worst rel err {worst:.2e}")
     tk.close()
     cp.close()
+
+
+@pytest.mark.parametrize("n,T", [(16, 128), (7, 100), (3, 1000), (5, 3)])
+def test_prefill_batch_matches_oracle(n, T):
+    # 16 x 128: one matrix-core pass of 2048 rows; 7 x 100: ragged tiles;
+    # 3 x 1000: two passes (2 + 1 sequences); 5 x 3: the matrix-vector path.
+    # Sequence ids are listed out of order; a decode after the batch checks
+    # that each cache is usable.
+    base = workload("talker_28l_t128_d1024")
+    shape = base.with_(n_seqs=16, cap=2048)
+    w = weights_for("talker_28l_t128_d1024", 2)
+    tk = _talker(shape, w)
+    orc = TalkerOracle(shape, w)
+    seqs = [(5 * b + 3) % 16 for b in range(n)]
+    embs = np.stack([prefill_embeddings(shape, T, seq=s) for s in seqs])
+    say(f"prefill_batch n={n} T={T}")
+    lg, hd = tk.prefill_batch(seqs, dev(embs), hidden=True)
+    ol, oh = orc.prefill_batch(seqs, embs)
+    tk.sync()
+    tol = 2e-2
+    g_lg, g_hd = host(lg), host(hd)
+    for b in range(n):
+        assert rel_err(g_lg[b], ol[b]) <= tol, b
+        assert rel_err(g_hd[b], oh[b]) <= tol, b
+        assert argmax_ok(g_lg[b], ol[b], tol), b
+        assert tk.kv_len(seqs[b]) == T
+    for b in (0, n - 1):
+        for which in (0, 1):
+            assert rel_err(host(tk.kv_read(seqs[b], 1, which)), orc.kv(seqs[b], 1, which)) <= tol
+    e = step_embedding(shape, 0, seq=seqs[-1])
+    g = host(tk.decode(seqs[-1], dev(e)))
+    o, _ = orc.decode(seqs[-1], e)
+    tk.sync()
+    assert rel_err(g, o) <= tol
+    tk.close()
