@@ -41,7 +41,13 @@ reason in the design notes of the repository):
 * attention reads the cache after the write, so K and V pass through the
   cache's storage type (float16 rounding for f16 caches) before use, in
   prefill and decode alike;
-* float16 rounding of the cache is round-to-nearest-even of the float32 value.
+* float16 rounding of the cache is round-to-nearest-even of the float32 value;
+* an 8-bit (Q8_0) cache stores blocks of 32 values along head_dim as int8
+  codes and a float16 scale, and attention reads the dequantised values for
+  every position, the current ones included (the same read-after-write
+  order as the other caches; the pages' Q8 path attends to the current
+  rows' unquantised values, which would make a prefill differ from the same
+  rows decoded one by one).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and independent library routines.
@@ -105,9 +111,41 @@ def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     return silu(gate) * up
 
 
+def q8_block_quantize(x: np.ndarray):
+    """Q8_0 quantisation of float32 values in blocks of 32 along the last axis
+    (the 8-bit KV storage, "rightkit-qts 0.2.3
+    src/pipeline/tts_transformer.rs", ``TalkerKvStorage::TurboQuantQ8_0``,
+    which stores K and V in ggml's Q8_0 type).  The pages name the type but
+    not its arithmetic; the reading is the block format as that library
+    documents it: per block, scale ``d = max|x| / 127`` (float32), codes
+    ``q = round_half_away(x * (1 / d))`` in float32 (0 when d is 0), the
+    scale stored as float16.  Returns (codes int8 [..., n/32, 32], scales
+    float16 [..., n/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.shape[-1] % 32:
+        raise ValueError("last axis must be a multiple of 32")
+    b = x.reshape(*x.shape[:-1], x.shape[-1] // 32, 32)
+    amax = np.abs(b).max(axis=-1)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d > 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
+    v = (b * inv[..., None]).astype(np.float32)
+    q = np.sign(v) * np.floor(np.abs(v) + np.float32(0.5))
+    return q.astype(np.int8), d.astype(np.float16)
+
+
+def q8_block_dequantize(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Values of Q8_0 blocks: ``code * float(scale)`` (exact in float32)."""
+    v = q.astype(np.float32) * d.astype(np.float32)[..., None]
+    return v.reshape(*v.shape[:-2], v.shape[-2] * 32)
+
+
 def round_kv(z: np.ndarray, kv_dtype: str, dtype) -> np.ndarray:
     """Value the cache holds after storing ``z``: ``float16(float32(z))`` for an
-    f16 cache, ``float32(z)`` for an f32 cache, returned in ``dtype``."""
+    f16 cache, ``float32(z)`` for an f32 cache, the Q8_0 block round trip of
+    ``float32(z)`` for a q8 cache; returned in ``dtype``."""
+    if kv_dtype == "q8":
+        return q8_block_dequantize(*q8_block_quantize(z.astype(np.float32))).astype(dtype)
     if kv_dtype == "f16":
         return z.astype(np.float32).astype(np.float16).astype(dtype)
     if kv_dtype == "f32":

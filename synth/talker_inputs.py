@@ -62,7 +62,7 @@ class TalkerShape:
     rms_eps: float
     rope_theta: float
     weight_dtype: str          # "f32" or "bf16"
-    kv_dtype: str              # "f32" or "f16"
+    kv_dtype: str              # "f32", "f16" or "q8" (Q8_0 blocks of 32)
     cap: int                   # KV capacity per sequence
     n_seqs: int                # KV sets
     seed: int                  # weight seed

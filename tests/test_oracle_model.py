@@ -138,7 +138,7 @@ def test_first_position_attention_is_v_projection():
 
 # -- path invariants -------------------------------------------------------------
 
-@pytest.mark.parametrize("kv", ["f32", "f16"])
+@pytest.mark.parametrize("kv", ["f32", "f16", "q8"])
 def test_prefill_equals_prefill_then_decode(kv):
     shape = small_shape(kv_dtype=kv)
     w = scaled_weights(shape)

@@ -225,3 +225,48 @@ def test_attention_matches_torch_sdpa_gqa():
         torch.from_numpy(kc)[None], torch.from_numpy(vc)[None],
         attn_mask=mask, enable_gqa=True)[0].numpy().transpose(1, 0, 2)
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+# -- Q8_0 KV blocks -------------------------------------------------------------
+
+def test_q8_block_closed_forms():
+    from oracle.talker import q8_block_dequantize, q8_block_quantize
+    # a block on the grid of its own scale comes back exactly
+    d = np.float32(0.5)
+    codes = np.arange(-127, 128, 8, dtype=np.int8)[:32]
+    codes = np.concatenate([codes, np.zeros(32 - codes.size, np.int8)])
+    codes[0] = 127
+    x = codes.astype(np.float32) * d
+    q, s = q8_block_quantize(x)
+    assert s[0] == np.float16(0.5)
+    np.testing.assert_array_equal(q[0], codes)
+    np.testing.assert_array_equal(q8_block_dequantize(q, s), x)
+    # zero block: zero scale and codes
+    q, s = q8_block_quantize(np.zeros(64, np.float32))
+    assert not q.any() and not s.any()
+    # sign symmetry, the largest magnitude maps to +-127
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 128)).astype(np.float32)
+    q, s = q8_block_quantize(x)
+    qn, sn = q8_block_quantize(-x)
+    np.testing.assert_array_equal(qn, -q)
+    np.testing.assert_array_equal(sn, s)
+    assert (np.abs(q).max(axis=-1) == 127).all()
+    # ties go away from zero: 0.5 and 1.5 steps of d = 127 / 127
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[2], x[3] = 127.0, 0.5, -0.5, 1.5
+    q, _ = q8_block_quantize(x)
+    assert list(q[0, :4]) == [127, 1, -1, 2]
+
+
+def test_q8_round_trip_error_bound():
+    from oracle.talker import round_kv
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((7, 128)) * rng.uniform(0.01, 10, (7, 1))).astype(np.float32)
+    y = round_kv(x, "q8", np.float64)
+    b = np.abs(x.reshape(7, 4, 32)).max(axis=-1) / 127.0     # float32 scale per block
+    err = np.abs(y - x).reshape(7, 4, 32).max(axis=-1)
+    # half a step of the float32 scale, plus the float16 rounding of the
+    # scale applied to codes up to 127
+    assert (err <= b * (0.5 + 127 * 2.0 ** -11) + 1e-12).all()
+    assert (err > 0).any()
