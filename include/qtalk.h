@@ -46,7 +46,10 @@ typedef enum {
   QTALK_E_DEVICE = -4    /* a HIP call or kernel launch failed               */
 } qtalk_status;
 
-typedef enum { QTALK_F32 = 0, QTALK_BF16 = 1, QTALK_F16 = 2 } qtalk_dtype;
+/* QTALK_Q8 (KV cache only): Q8_0 blocks of 32 values along head_dim, int8
+ * codes with one float16 scale per block ("rightkit-qts 0.2.3
+ * src/pipeline/tts_transformer.rs", TalkerKvStorage::TurboQuantQ8_0). */
+typedef enum { QTALK_F32 = 0, QTALK_BF16 = 1, QTALK_F16 = 2, QTALK_Q8 = 3 } qtalk_dtype;
 
 /* Model geometry and cache sizes.  The Talker defaults are hidden 1024,
  * 28 layers, 16 query heads, 8 KV heads, head_dim 128, intermediate 3072,
@@ -55,7 +58,7 @@ typedef enum { QTALK_F32 = 0, QTALK_BF16 = 1, QTALK_F16 = 2 } qtalk_dtype;
  * Requirements (else QTALK_E_INVAL): every size >= 1; head_dim is 64 or 128;
  * n_heads % n_kv_heads == 0; hidden, intermediate and n_heads*head_dim are
  * multiples of 64; intermediate is a multiple of 16; weight_dtype is F32 or
- * BF16; kv_dtype is F32 or F16.  q_dim = n_heads*head_dim need not equal
+ * BF16; kv_dtype is F32, F16 or Q8.  q_dim = n_heads*head_dim need not equal
  * hidden (it does not for the Talker: 2048 vs 1024). */
 typedef struct {
   int32_t n_layers;
@@ -70,7 +73,7 @@ typedef struct {
   int32_t max_seq_len;  /* KV capacity per sequence                    */
   int32_t max_seqs;     /* number of independent sequences (KV sets)   */
   int32_t weight_dtype; /* qtalk_dtype: F32 or BF16 (projections, head) */
-  int32_t kv_dtype;     /* qtalk_dtype: F32 or F16 (cache storage)      */
+  int32_t kv_dtype;     /* qtalk_dtype: F32, F16 or Q8 (cache storage)  */
   int32_t n_output_heads; /* output projections stacked in codec_head
                              (0 or 1: one; the code predictor has 15),
                              at most 64; see qtalk_select_head           */

@@ -8,16 +8,28 @@
 // "transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill (query head h
 // reads KV head h / (n_heads / n_kv_heads)).  The attention reads the cache
 // after the write, so K/V pass through the cache's storage type.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qtalk {
+
+// Cache rows: row (seq, kv head, pos) holds head_dim values.  Storage kinds:
+// float32, float16, and Q8_0 (q8_t): head_dim int8 codes followed by one
+// float16 scale per 32 codes, value = code * scale (blocks of 32 along
+// head_dim; "rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+// TalkerKvStorage::TurboQuantQ8_0).  KVIO<T>::load<N>(row, d, f) reads
+// values d .. d+N-1 (N divides 32, d a multiple of N) of one row.
+struct q8_t {};
 
 template <typename KVT>
 struct KVIO;
 template <>
 struct KVIO<float> {
+  static __host__ __device__ constexpr size_t row_bytes(int hd) { return (size_t)hd * 4; }
   template <int N>
-  static __device__ __forceinline__ void load(const float* p, float* f) {
+  static __device__ __forceinline__ void load(const char* row, int d, float* f) {
+    const float* p = reinterpret_cast<const float*>(row) + d;
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
       const float4 v = *reinterpret_cast<const float4*>(p + i);
@@ -27,12 +39,13 @@ struct KVIO<float> {
       f[i + 3] = v.w;
     }
   }
-  static __device__ __forceinline__ float cvt(float v) { return v; }
 };
 template <>
 struct KVIO<f16_t> {
+  static __host__ __device__ constexpr size_t row_bytes(int hd) { return (size_t)hd * 2; }
   template <int N>
-  static __device__ __forceinline__ void load(const f16_t* p, float* f) {
+  static __device__ __forceinline__ void load(const char* row, int d, float* f) {
+    const f16_t* p = reinterpret_cast<const f16_t*>(row) + d;
     if constexpr (N == 8) {
       const f16x8_t v = *reinterpret_cast<const f16x8_t*>(p);
 #pragma unroll
@@ -49,8 +62,44 @@ struct KVIO<f16_t> {
       }
     }
   }
-  static __device__ __forceinline__ f16_t cvt(float v) { return (f16_t)v; }
 };
+template <>
+struct KVIO<q8_t> {
+  static __host__ __device__ constexpr size_t row_bytes(int hd) { return (size_t)hd + (size_t)hd / 16; }
+  // values d .. d+N-1 of a row of hd values (the scales follow the codes)
+  template <int N>
+  static __device__ __forceinline__ void load_hd(const char* row, int hd, int d, float* f) {
+    static_assert(N == 4 || N == 8, "4 or 8 codes per load");
+    const float sc = (float)*reinterpret_cast<const f16_t*>(row + hd + (d >> 5) * 2);
+    if constexpr (N == 8) {
+      const uint2 c = *reinterpret_cast<const uint2*>(row + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = (float)(int8_t)(c.x >> (8 * i)) * sc;
+        f[i + 4] = (float)(int8_t)(c.y >> (8 * i)) * sc;
+      }
+    } else {
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(row + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = (float)(int8_t)(c >> (8 * i)) * sc;
+    }
+  }
+};
+
+// values d .. d+N-1 of cache row `row` (head_dim hd) as float
+template <typename KVT, int N>
+__device__ __forceinline__ void kv_load(const char* row, int hd, int d, float* f) {
+  if constexpr (std::is_same<KVT, q8_t>::value) KVIO<q8_t>::template load_hd<N>(row, hd, d, f);
+  else KVIO<KVT>::template load<N>(row, d, f);
+}
+
+// max over each aligned 32-lane half of the wave (DPP inside 16-lane rows,
+// then v_permlane16_swap across the row pair)
+__device__ __forceinline__ float half32_max(float v) {
+  v = row16_max(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // ---------------------------------------------------------------------------
 // QK-norm + RoPE + append.  grid (rows, n_heads + 2 n_kv), one wave per head.
@@ -83,6 +132,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
   const bool act = lane < HALF;
   float x1 = act ? x[lane] : 0.f;
   float x2 = act ? x[lane + HALF] : 0.f;
+  constexpr bool Q8 = std::is_same<KVT, q8_t>::value;
   if (kind < 2) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float inv = rsqrtf(ss / (float)HD + a.eps);
@@ -96,27 +146,50 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
       x2 = y2;
     }
   }
+  // Q8_0 blocks: dims d and d + HALF of lane d fall in blocks d / 32 and
+  // (d + HALF) / 32, each spanning one aligned 32-lane half of the wave
+  float d1 = 0.f, d2 = 0.f;
+  if constexpr (Q8) {
+    if (kind > 0) {
+      d1 = half32_max(fabsf(x1)) / 127.0f;
+      d2 = half32_max(fabsf(x2)) / 127.0f;
+    }
+  }
   if (!act) return;
   if (kind == 0) {
     x[lane] = x1;
     x[lane + HALF] = x2;
   } else {
-    KVT* c = reinterpret_cast<KVT*>(kind == 1 ? a.kc : a.vc) +
-             ((size_t)(seq * nkv + kvh) * a.cap + pos) * HD;
-    c[lane] = KVIO<KVT>::cvt(x1);
-    c[lane + HALF] = KVIO<KVT>::cvt(x2);
+    char* rowp = reinterpret_cast<char*>(kind == 1 ? a.kc : a.vc) +
+                 ((size_t)(seq * nkv + kvh) * a.cap + pos) * KVIO<KVT>::row_bytes(HD);
+    if constexpr (Q8) {
+      const float i1 = d1 > 0.f ? 1.0f / d1 : 0.f, i2 = d2 > 0.f ? 1.0f / d2 : 0.f;
+      rowp[lane] = (char)(int8_t)roundf(x1 * i1);
+      rowp[lane + HALF] = (char)(int8_t)roundf(x2 * i2);
+      f16_t* sc = reinterpret_cast<f16_t*>(rowp + HD);
+      if ((lane & 31) == 0) {
+        sc[lane >> 5] = (f16_t)d1;
+        sc[(lane + HALF) >> 5] = (f16_t)d2;
+      }
+    } else {
+      KVT* c = reinterpret_cast<KVT*>(rowp);
+      c[lane] = (KVT)x1;
+      c[lane + HALF] = (KVT)x2;
+    }
   }
 }
 
-void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st) {
+template <int HD>
+static void launch_qk_hd(KvKind kv, const QkArgs& a, const dim3& grid, hipStream_t st) {
+  if (kv == KV_F16) hipLaunchKernelGGL((k_qk_rope_append<HD, f16_t>), grid, dim3(64), 0, st, a);
+  else if (kv == KV_Q8) hipLaunchKernelGGL((k_qk_rope_append<HD, q8_t>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((k_qk_rope_append<HD, float>), grid, dim3(64), 0, st, a);
+}
+
+void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
   const dim3 grid(a.rows.n, (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads);
-  if (a.head_dim == 128) {
-    if (kv_f16) hipLaunchKernelGGL((k_qk_rope_append<128, f16_t>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((k_qk_rope_append<128, float>), grid, dim3(64), 0, st, a);
-  } else {
-    if (kv_f16) hipLaunchKernelGGL((k_qk_rope_append<64, f16_t>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((k_qk_rope_append<64, float>), grid, dim3(64), 0, st, a);
-  }
+  if (a.head_dim == 128) launch_qk_hd<128>(kv, a, grid, st);
+  else launch_qk_hd<64>(kv, a, grid, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -152,9 +225,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     return;
   }
 
-  const size_t head_off = (size_t)(seq * nkv + g) * a.cap * HD;
-  const KVT* Kp = reinterpret_cast<const KVT*>(a.kc) + head_off;
-  const KVT* Vp = reinterpret_cast<const KVT*>(a.vc) + head_off;
+  constexpr size_t RB = KVIO<KVT>::row_bytes(HD);
+  const size_t head_off = (size_t)(seq * nkv + g) * a.cap * RB;
+  const char* Kp = reinterpret_cast<const char*>(a.kc) + head_off;
+  const char* Vp = reinterpret_cast<const char*>(a.vc) + head_off;
 
   // score-phase lane roles
   const int sub = lane & 15;  // dims sub*DPL .. +DPL
@@ -187,7 +261,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       const int j = kb + jl;
       float kf[DPL];
       const bool ok = j < k_end;
-      if (ok) KVIO<KVT>::template load<DPL>(Kp + (size_t)j * HD + sub * DPL, kf);
+      if (ok) kv_load<KVT, DPL>(Kp + (size_t)j * RB, HD, sub * DPL, kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
@@ -229,7 +303,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       const int j = kb + jl;
       if (j < k_end) {
         float vf[DPL];
-        KVIO<KVT>::template load<DPL>(Vp + (size_t)j * HD + vd * DPL, vf);
+        kv_load<KVT, DPL>(Vp + (size_t)j * RB, HD, vd * DPL, vf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float pv = s_p[h][jl];
@@ -308,14 +382,16 @@ static void launch_o(AttnOut mode, const AttnArgs& a, hipStream_t st) {
   else launch_g<HD, KVT, ATT_BF16>(a, st);
 }
 
-void launch_attn_decode(bool kv_f16, AttnOut mode, AttnArgs a, hipStream_t st) {
-  if (a.head_dim == 128) {
-    if (kv_f16) launch_o<128, f16_t>(mode, a, st);
-    else launch_o<128, float>(mode, a, st);
-  } else {
-    if (kv_f16) launch_o<64, f16_t>(mode, a, st);
-    else launch_o<64, float>(mode, a, st);
-  }
+template <int HD>
+static void launch_kv(KvKind kv, AttnOut mode, const AttnArgs& a, hipStream_t st) {
+  if (kv == KV_F16) launch_o<HD, f16_t>(mode, a, st);
+  else if (kv == KV_Q8) launch_o<HD, q8_t>(mode, a, st);
+  else launch_o<HD, float>(mode, a, st);
+}
+
+void launch_attn_decode(KvKind kv, AttnOut mode, AttnArgs a, hipStream_t st) {
+  if (a.head_dim == 128) launch_kv<128>(kv, mode, a, st);
+  else launch_kv<64>(kv, mode, a, st);
 }
 
 void launch_attn_merge(AttnArgs a, hipStream_t st) {
@@ -341,23 +417,28 @@ void launch_rope_table(float2* tab, int cap, int head_dim, double theta, hipStre
                      half, head_dim, theta);
 }
 
+// grid (len, n_kv), hd / 4 threads: 4 values of one row each
 template <typename KVT>
-__global__ void k_kv_to_f32(const KVT* src, int cap, int len, int hd, float* dst) {
-  const int t = blockIdx.x, h = blockIdx.y;
-  for (int d = threadIdx.x; d < hd; d += blockDim.x)
-    dst[((size_t)h * len + t) * hd + d] = (float)src[((size_t)h * cap + t) * hd + d];
+__global__ void k_kv_to_f32(const char* src, int cap, int len, int hd, float* dst) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x * 4;
+  float f[4];
+  kv_load<KVT, 4>(src + ((size_t)h * cap + t) * KVIO<KVT>::row_bytes(hd), hd, d, f);
+  *reinterpret_cast<float4*>(dst + ((size_t)h * len + t) * hd + d) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-void launch_kv_to_f32(bool kv_f16, const void* src, int n_kv, int cap, int len, int hd, float* dst,
+void launch_kv_to_f32(KvKind kv, const void* src, int n_kv, int cap, int len, int hd, float* dst,
                       hipStream_t st) {
   if (len <= 0) return;
   const dim3 grid(len, n_kv);
-  if (kv_f16)
-    hipLaunchKernelGGL(k_kv_to_f32<f16_t>, grid, dim3(128), 0, st,
-                       reinterpret_cast<const f16_t*>(src), cap, len, hd, dst);
-  else
-    hipLaunchKernelGGL(k_kv_to_f32<float>, grid, dim3(128), 0, st,
-                       reinterpret_cast<const float*>(src), cap, len, hd, dst);
+  const char* s = reinterpret_cast<const char*>(src);
+  if (kv == KV_F16) hipLaunchKernelGGL(k_kv_to_f32<f16_t>, grid, dim3(hd / 4), 0, st, s, cap, len, hd, dst);
+  else if (kv == KV_Q8) hipLaunchKernelGGL(k_kv_to_f32<q8_t>, grid, dim3(hd / 4), 0, st, s, cap, len, hd, dst);
+  else hipLaunchKernelGGL(k_kv_to_f32<float>, grid, dim3(hd / 4), 0, st, s, cap, len, hd, dst);
+}
+
+size_t kv_row_bytes(KvKind kv, int hd) {
+  return kv == KV_F16 ? KVIO<f16_t>::row_bytes(hd)
+                      : (kv == KV_Q8 ? KVIO<q8_t>::row_bytes(hd) : KVIO<float>::row_bytes(hd));
 }
 
 }  // namespace qtalk

@@ -366,11 +366,17 @@ __device__ __forceinline__ float inv_rms(const float* redw, float eps) {
   return rsqrtf(t / (float)H + eps);
 }
 
+// max over each aligned 32-lane half of the wave
+__device__ __forceinline__ float half32_max(float v) { return xor16_max(row16_max(v)); }
+
 }  // namespace pd
 
-template <bool LOCAL>
+// LOCAL: group exchanges inside the XCD; Q8: Q8_0 cache rows (HD codes, then
+// HD / 32 float16 scales) instead of float16 rows
+template <bool LOCAL, bool Q8>
 __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   using namespace pd;
+  constexpr size_t RB = Q8 ? HD + HD / 16 : HD * 2;  // bytes per cache row
   __shared__ __attribute__((aligned(16))) float xres[H];  // residual stream
   __shared__ __attribute__((aligned(16))) float xin[I];   // input of the current product
   __shared__ float araw[QKV / NKV];                        // this head group's q0 | q1 | k | v
@@ -378,6 +384,8 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float redw[NW];
   __shared__ float qs[G][HD];                              // normed, roped, scaled q
   __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
+  __shared__ signed char kcode[HD], vcode[HD];             // Q8_0: its codes
+  __shared__ f16_t kscl[HD / 32], vscl[HD / 32];           // Q8_0: its block scales
   __shared__ __attribute__((aligned(16))) float ow[NW][G * HD];  // per-wave attention sums
   __shared__ __attribute__((aligned(16))) float mws[G][NW];      // per-wave softmax max
   __shared__ __attribute__((aligned(16))) float lws[G][NW];      // per-wave softmax sum
@@ -435,19 +443,32 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   // are masked by selects in the attention step.  (A conditional load would
   // make the compiler wait for every outstanding load where the branches
   // join, including the weight slices in flight for the next step.)
+  // f16 rows: 8 values per lane; Q8_0 rows: 8 codes and the scale of their
+  // 32-value block (codes then scales in each row)
   f16x8_t kr[2], vr[2];
-  auto load_rows = [&](const f16_t* K, const f16_t* V, int kb) {
+  uint2 kq[2], vq[2];
+  f16_t ksc[2], vsc[2];
+  auto load_rows = [&](const char* K, const char* V, int kb) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int j = min(kb + p * 32 + slot, n_ctx - 1);
-      kr[p] = *reinterpret_cast<const f16x8_t*>(K + (size_t)j * HD + sub * 8);
-      vr[p] = *reinterpret_cast<const f16x8_t*>(V + (size_t)j * HD + sub * 8);
+      const char* kp = K + (size_t)j * RB;
+      const char* vp = V + (size_t)j * RB;
+      if constexpr (Q8) {
+        kq[p] = *reinterpret_cast<const uint2*>(kp + sub * 8);
+        vq[p] = *reinterpret_cast<const uint2*>(vp + sub * 8);
+        ksc[p] = *reinterpret_cast<const f16_t*>(kp + HD + (sub >> 2) * 2);
+        vsc[p] = *reinterpret_cast<const f16_t*>(vp + HD + (sub >> 2) * 2);
+      } else {
+        kr[p] = *reinterpret_cast<const f16x8_t*>(kp + sub * 16);
+        vr[p] = *reinterpret_cast<const f16x8_t*>(vp + sub * 16);
+      }
     }
   };
   // the first 64 keys of this block's chunk in layer l (the new position is
   // replaced in the attention step)
   auto load_kv = [&](int l) {
-    const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
+    const size_t hoff = (size_t)l * a.layer_kv_bytes + ((size_t)(a.seq * NKV + g) * a.cap) * RB;
     load_rows(a.kc + hoff, a.vc + hoff, k0);
   };
   // Rows 32c .. 32c+31 of x + (sum of the 8 groups' partials in PP): thread t
@@ -486,9 +507,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     uint64_t* E = a.ll + (size_t)(l & 1) * WORDS_PER_LAYER;
     uint64_t* Eprev = a.ll + (size_t)((l + 1) & 1) * WORDS_PER_LAYER;
     uint64_t* P = a.part + (size_t)(l & 1) * PART_WORDS;  // this layer's chunk partials
-    const size_t hoff = (size_t)l * a.layer_kv_elems + ((size_t)(a.seq * NKV + g) * a.cap) * HD;
-    f16_t* Kp = a.kc + hoff;
-    f16_t* Vp = a.vc + hoff;
+    const size_t hoff = (size_t)l * a.layer_kv_bytes + ((size_t)(a.seq * NKV + g) * a.cap) * RB;
+    char* Kp = a.kc + hoff;
+    char* Vp = a.vc + hoff;
 
     // ---------------- XD (previous layer's output) + QKV ----------------
     float gn, gnp;  // QK-norm gains of this thread's attention channel and of its RoPE partner
@@ -550,22 +571,51 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         return Wgu + ((size_t)(lr >> 4) * 32 + (lr & 15) + (r & 1) * 16) * H;
       }, wave, lane);
       // per-head RMSNorm, NEOX RoPE on (i, i + 64); k and v round through the
-      // cache type
-      if (tid < 384) {
-        const int hh = tid >> 7, j = tid & 127;
-        const float inv = rsqrtf((redw[2 * hh] + redw[2 * hh + 1]) / (float)HD + a.eps);
-        const float xj = araw[tid] * inv * gn;
-        const float xp = araw[tid ^ 64] * inv * gnp;
-        const float y = j < 64 ? xj * cs.x - xp * cs.y : xj * cs.x + xp * cs.y;
-        if (hh < 2) qs[hh][j] = y * scale;
-        else knew[j] = (float)(f16_t)y;
-      } else {
-        vnew[tid - 384] = (float)(f16_t)araw[tid];
+      // cache type (Q8_0: the 32-value block of a k or v dim is one half of
+      // its wave)
+      {
+        float y;
+        if (tid < 384) {
+          const int hh = tid >> 7, j = tid & 127;
+          const float inv = rsqrtf((redw[2 * hh] + redw[2 * hh + 1]) / (float)HD + a.eps);
+          const float xj = araw[tid] * inv * gn;
+          const float xp = araw[tid ^ 64] * inv * gnp;
+          y = j < 64 ? xj * cs.x - xp * cs.y : xj * cs.x + xp * cs.y;
+          if (hh < 2) qs[hh][j] = y * scale;
+        } else {
+          y = araw[tid];
+        }
+        if (tid >= 256) {  // k (waves 4-5) or v (waves 6-7) dim tid & 127
+          const int j = tid & 127;
+          float c;
+          if constexpr (Q8) {
+            const float d = half32_max(fabsf(y)) / 127.0f;
+            const float code = roundf(y * (d > 0.f ? 1.0f / d : 0.f));
+            const f16_t d16 = (f16_t)d;
+            c = code * (float)d16;
+            (tid < 384 ? kcode : vcode)[j] = (signed char)code;
+            if ((lane & 31) == 0) (tid < 384 ? kscl : vscl)[j >> 5] = d16;
+          } else {
+            c = (float)(f16_t)y;
+          }
+          (tid < 384 ? knew : vnew)[j] = c;
+        }
       }
       __syncthreads();
       if (k0 <= pos && pos < k1 && tid < HD) {  // this block owns the new position
-        Kp[(size_t)pos * HD + tid] = (f16_t)knew[tid];
-        Vp[(size_t)pos * HD + tid] = (f16_t)vnew[tid];
+        char* kp = Kp + (size_t)pos * RB;
+        char* vp = Vp + (size_t)pos * RB;
+        if constexpr (Q8) {
+          kp[tid] = kcode[tid];
+          vp[tid] = vcode[tid];
+          if (tid < HD / 32) {
+            reinterpret_cast<f16_t*>(kp + HD)[tid] = kscl[tid];
+            reinterpret_cast<f16_t*>(vp + HD)[tid] = vscl[tid];
+          }
+        } else {
+          reinterpret_cast<f16_t*>(kp)[tid] = (f16_t)knew[tid];
+          reinterpret_cast<f16_t*>(vp)[tid] = (f16_t)vnew[tid];
+        }
       }
       // keys [k0, k1), 64 per pass: thread (slot, sub) takes keys kb + slot and
       // kb + 32 + slot, dims sub*8 .. +8.  Each slot (16 lanes) keeps its own
@@ -593,12 +643,24 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         const int j0 = kb + slot, j1 = kb + 32 + slot;
         float kf[2][8], vf[2][8];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int p = 0; p < 2; ++p) {
+          if constexpr (Q8) {
+            const float ks = (float)ksc[p], vs = (float)vsc[p];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kf[p][e] = (float)kr[p][e];
-            vf[p][e] = (float)vr[p][e];
+            for (int e = 0; e < 4; ++e) {
+              kf[p][e] = (float)(signed char)(kq[p].x >> (8 * e)) * ks;
+              kf[p][e + 4] = (float)(signed char)(kq[p].y >> (8 * e)) * ks;
+              vf[p][e] = (float)(signed char)(vq[p].x >> (8 * e)) * vs;
+              vf[p][e + 4] = (float)(signed char)(vq[p].y >> (8 * e)) * vs;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              kf[p][e] = (float)kr[p][e];
+              vf[p][e] = (float)vr[p][e];
+            }
           }
+        }
         if (j1 >= pos) {  // rare: the new position (fresh K/V) or keys past the chunk
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -854,13 +916,12 @@ int fused_decode_blocks() { return pd::NB; }
 // launch), at ~18 us more per launch.
 hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool cooperative) {
   FusedDecodeArgs a = args;
-  if (!cooperative) {
-    if (a.xcd_local) hipLaunchKernelGGL(k_decode_fused<true>, dim3(pd::NB), dim3(pd::NT), 0, st, a);
-    else hipLaunchKernelGGL(k_decode_fused<false>, dim3(pd::NB), dim3(pd::NT), 0, st, a);
-    return hipGetLastError();
-  }
-  const void* fn = a.xcd_local ? (const void*)k_decode_fused<true> : (const void*)k_decode_fused<false>;
+  const void* fn = a.kv_q8 ? (a.xcd_local ? (const void*)k_decode_fused<true, true>
+                                          : (const void*)k_decode_fused<false, true>)
+                           : (a.xcd_local ? (const void*)k_decode_fused<true, false>
+                                          : (const void*)k_decode_fused<false, false>);
   void* params[] = {&a};
+  if (!cooperative) return hipLaunchKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
   return hipLaunchCooperativeKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
 }
 
@@ -902,7 +963,7 @@ bool fused_decode_fits() {
   int dev = 0, ncu = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused<true>, pd::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused<true, false>, pd::NT, 0) !=
       hipSuccess)
     return false;
   return (long)per * ncu >= pd::NB;

@@ -42,7 +42,11 @@ struct QkArgs {
   int skip_q;  // 1: leave q as is (the matrix-core attention norms and ropes it)
   RowMeta rows;
 };
-void launch_qk_rope_append(bool kv_f16, QkArgs a, hipStream_t st);
+// KV cache storage: float32, float16, or Q8_0 rows (head_dim int8 codes then
+// head_dim / 32 float16 scales)
+enum KvKind { KV_F32 = 0, KV_F16 = 1, KV_Q8 = 2 };
+size_t kv_row_bytes(KvKind kv, int head_dim);
+void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st);
 
 // Causal GQA attention of the listed rows over the cache (split over keys).
 enum AttnOut { ATT_PARTIAL = 0, ATT_F32 = 1, ATT_BF16 = 2 };
@@ -61,7 +65,7 @@ struct AttnArgs {
   int ldo;
   RowMeta rows;
 };
-void launch_attn_decode(bool kv_f16, AttnOut mode, AttnArgs a, hipStream_t st);
+void launch_attn_decode(KvKind kv, AttnOut mode, AttnArgs a, hipStream_t st);
 void launch_attn_merge(AttnArgs a, hipStream_t st);
 
 // Causal GQA attention of T uniform rows (positions p0 .. p0+T-1 of one
@@ -115,7 +119,7 @@ void launch_rope_table(float2* tab, int cap, int head_dim, double theta,
                        hipStream_t st);
 
 // dst[h][t][d] = float(cache[h][t][d]) for t < len
-void launch_kv_to_f32(bool kv_f16, const void* src, int n_kv, int cap, int len,
+void launch_kv_to_f32(KvKind kv, const void* src, int n_kv, int cap, int len,
                       int hd, float* dst, hipStream_t st);
 
 // Batch-1 decode of the whole stack in one persistent launch (Talker
@@ -127,9 +131,10 @@ struct FusedDecodeArgs {
   size_t norm_stride;
   const bf16_t* head;
   const float* g_final;
-  f16_t* kc;
-  f16_t* vc;  // [L][S][NKV][cap][HD]
-  size_t layer_kv_elems;
+  char* kc;
+  char* vc;  // [L][S][NKV][cap] rows of HD values (f16, or Q8_0: codes then scales)
+  size_t layer_kv_bytes;
+  int kv_q8;  // 1: Q8_0 rows
   int cap, seq, pos, n_layers;
   float eps;
   const float2* rope;

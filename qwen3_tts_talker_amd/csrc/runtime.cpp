@@ -56,6 +56,8 @@ struct qtalk_ctx {
   qtalk_config cfg{};
   hipStream_t stream = nullptr;
   bool w_bf16 = true, kv_f16 = true;
+  KvKind kv = KV_F16;  // cache storage
+  size_t kv_rb = 0;    // bytes per cache row (one position of one KV head)
   size_t welem = 2;
   int q_dim = 0, kv_dim = 0, qkv_dim = 0;
   std::vector<LayerDev> layers;
@@ -66,7 +68,8 @@ struct qtalk_ctx {
   int head_sel = 0;  // head of the logits of the following calls (qtalk_select_head)
   float* g_final = nullptr;
   void *kc = nullptr, *vc = nullptr;
-  size_t layer_kv_elems = 0;  // elements of one layer's cache (all sequences)
+  size_t layer_kv_elems = 0;  // values of one layer's cache (all sequences)
+  size_t layer_kv_rows() const { return layer_kv_elems / (size_t)cfg.head_dim; }
   float2* rope = nullptr;
   std::vector<int32_t> cur_len;
   int tc = 0;  // rows per matrix-core pass
@@ -153,7 +156,8 @@ const char* check_config(const qtalk_config* g) {
   if (!(g->rms_eps >= 0.f) || !(g->rope_theta > 0.f)) return "bad rms_eps or rope_theta";
   if (g->weight_dtype != QTALK_F32 && g->weight_dtype != QTALK_BF16)
     return "weight_dtype must be F32 or BF16";
-  if (g->kv_dtype != QTALK_F32 && g->kv_dtype != QTALK_F16) return "kv_dtype must be F32 or F16";
+  if (g->kv_dtype != QTALK_F32 && g->kv_dtype != QTALK_F16 && g->kv_dtype != QTALK_Q8)
+    return "kv_dtype must be F32, F16 or Q8";
   if (g->n_output_heads < 0 || g->n_output_heads > 64) return "n_output_heads must be 0..64";
   return nullptr;
 }
@@ -167,7 +171,7 @@ struct Fwd {
   explicit Fwd(qtalk_ctx* cc) : c(cc), st(cc->stream), g(cc->cfg) {}
 
   char* kv_layer(void* base, int l) const {
-    return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_elems * (c->kv_f16 ? 2 : 4);
+    return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_rows() * c->kv_rb;
   }
 
   void qk_append(int l, const RowMeta& rows, bool skip_q = false) {
@@ -186,7 +190,7 @@ struct Fwd {
     q.cap = g.max_seq_len;
     q.skip_q = skip_q ? 1 : 0;
     q.rows = rows;
-    launch_qk_rope_append(c->kv_f16, q, st);
+    launch_qk_rope_append(c->kv, q, st);
   }
 
   AttnArgs attn_args(int l, const RowMeta& rows) const {
@@ -232,7 +236,7 @@ struct Fwd {
     const int ctx = max_ctx(rows);
     a.keys_per_split = 64 * ((ctx + 64 * MAX_SPLITS - 1) / (64 * MAX_SPLITS));
     a.n_splits = (ctx + a.keys_per_split - 1) / a.keys_per_split;
-    launch_attn_decode(c->kv_f16, ATT_PARTIAL, a, st);
+    launch_attn_decode(c->kv, ATT_PARTIAL, a, st);
     launch_attn_merge(a, st);
     gemv(L.wo, H, c->q_dim, c->att, c->q_dim, n, nullptr, c->x, H, EPI_ADD);
     gemv(L.wgu, g.intermediate, H, c->x, H, n, L.g_post, c->act, g.intermediate, EPI_SWIGLU);
@@ -256,7 +260,7 @@ struct Fwd {
     bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
     if (!normed) launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
-    const bool mfma_attn = c->kv_f16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
+    const bool mfma_attn = c->kv == KV_F16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
     qk_append(l, rows, mfma_attn);
     if (mfma_attn) {
       PrefillAttnArgs p{};
@@ -289,7 +293,7 @@ struct Fwd {
       AttnArgs a = attn_args(l, rows);
       a.keys_per_split = max_ctx(rows);
       a.n_splits = 1;
-      launch_attn_decode(c->kv_f16, ATT_BF16, a, st);
+      launch_attn_decode(c->kv, ATT_BF16, a, st);
     }
     gemm_add_norm(att_b, c->q_dim, L.wo, T, H, c->q_dim, L.g_post);
     gemm(c->hn, H, L.wgu, T, 2 * I, H, act_b, I, EPI_SWIGLU);
@@ -394,9 +398,10 @@ struct Fwd {
     a.head = reinterpret_cast<const bf16_t*>(head_w());
     a.head_rows = g.vocab / fused_decode_blocks();
     a.g_final = c->g_final;
-    a.kc = reinterpret_cast<f16_t*>(c->kc);
-    a.vc = reinterpret_cast<f16_t*>(c->vc);
-    a.layer_kv_elems = c->layer_kv_elems;
+    a.kc = reinterpret_cast<char*>(c->kc);
+    a.vc = reinterpret_cast<char*>(c->vc);
+    a.layer_kv_bytes = c->layer_kv_rows() * c->kv_rb;
+    a.kv_q8 = c->kv == KV_Q8;
     a.cap = g.max_seq_len;
     a.seq = seq;
     a.pos = pos;
@@ -487,6 +492,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   c->stream = reinterpret_cast<hipStream_t>(hip_stream);
   c->w_bf16 = g.weight_dtype == QTALK_BF16;
   c->kv_f16 = g.kv_dtype == QTALK_F16;
+  c->kv = g.kv_dtype == QTALK_F16 ? KV_F16 : (g.kv_dtype == QTALK_Q8 ? KV_Q8 : KV_F32);
+  c->kv_rb = kv_row_bytes(c->kv, g.head_dim);
   c->welem = c->w_bf16 ? 2 : 4;
   c->n_out_heads = std::max(1, (int)g.n_output_heads);
   c->q_dim = g.n_heads * g.head_dim;
@@ -502,13 +509,13 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   c->tc = (int)std::min<long long>((long long)g.max_seq_len * g.max_seqs, MAX_CHUNK);
   const int part_rows = GEMV_ROWS;
   const int rows = std::max(c->tc, GEMV_ROWS);
-  const size_t kvb = c->kv_f16 ? 2 : 4;
+
 
   bool ok = dev_alloc(&c->wblob, per_layer * g.n_layers * we) &&
             dev_alloc((void**)&c->nblob, (norms_per_layer * g.n_layers + H) * 4) &&
             dev_alloc(&c->head, (size_t)c->n_out_heads * g.vocab * H * we) &&
-            dev_alloc(&c->kc, c->layer_kv_elems * g.n_layers * kvb) &&
-            dev_alloc(&c->vc, c->layer_kv_elems * g.n_layers * kvb) &&
+            dev_alloc(&c->kc, c->layer_kv_rows() * c->kv_rb * g.n_layers) &&
+            dev_alloc(&c->vc, c->layer_kv_rows() * c->kv_rb * g.n_layers) &&
             dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
             dev_alloc((void**)&c->x, (size_t)rows * H * 4) &&
             dev_alloc((void**)&c->aux_err, 4) &&
@@ -531,7 +538,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
       c->ncu = ncu;
     c->dev = dev;
   }
-  c->fused = ok && c->w_bf16 && c->kv_f16 && !(env && env[0] == '0') && c->dev < MAX_DEVICES &&
+  c->fused = ok && c->w_bf16 && (c->kv == KV_F16 || c->kv == KV_Q8) && !(env && env[0] == '0') &&
+             c->dev < MAX_DEVICES &&
              g.n_layers <= 64 &&
              fused_decode_supported(g.hidden, c->q_dim, c->kv_dim, g.intermediate, g.vocab,
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
@@ -587,7 +595,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
                         copy_in(c->head, w->codec_head, (size_t)c->n_out_heads * g.vocab * H * we)))
     s = QTALK_E_DEVICE;
   if (s == QTALK_OK) {
-    const size_t kv_bytes = c->layer_kv_elems * g.n_layers * kvb;
+    const size_t kv_bytes = c->layer_kv_rows() * c->kv_rb * g.n_layers;
     if (hipMemsetAsync(c->kc, 0, kv_bytes, c->stream) != hipSuccess ||
         hipMemsetAsync(c->vc, 0, kv_bytes, c->stream) != hipSuccess ||
         hipMemsetAsync(c->aux_err, 0, 4, c->stream) != hipSuccess)
@@ -744,11 +752,10 @@ qtalk_status qtalk_kv_read(qtalk_ctx* c, int32_t seq, int32_t layer, int32_t kv,
       (kv != 0 && kv != 1) || !dst)
     return fail(c, QTALK_E_INVAL, "bad kv_read arguments");
   const qtalk_config& g = c->cfg;
-  const size_t eb = c->kv_f16 ? 2 : 4;
   const char* base = reinterpret_cast<const char*>(kv ? c->vc : c->kc) +
-                     ((size_t)layer * c->layer_kv_elems +
-                      (size_t)seq * g.n_kv_heads * g.max_seq_len * g.head_dim) * eb;
-  launch_kv_to_f32(c->kv_f16, base, g.n_kv_heads, g.max_seq_len, c->cur_len[seq], g.head_dim, dst,
+                     ((size_t)layer * c->layer_kv_rows() + (size_t)seq * g.n_kv_heads * g.max_seq_len) *
+                         c->kv_rb;
+  launch_kv_to_f32(c->kv, base, g.n_kv_heads, g.max_seq_len, c->cur_len[seq], g.head_dim, dst,
                    c->stream);
   return launch_status(c);
 }

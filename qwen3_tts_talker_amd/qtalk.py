@@ -22,7 +22,7 @@ QTALK_E_INVAL = -1
 QTALK_E_OVERFLOW = -2
 QTALK_E_NOMEM = -3
 QTALK_E_DEVICE = -4
-QTALK_F32, QTALK_BF16, QTALK_F16 = 0, 1, 2
+QTALK_F32, QTALK_BF16, QTALK_F16, QTALK_Q8 = 0, 1, 2, 3
 
 EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
@@ -250,7 +250,7 @@ class Talker:
             rope_theta=shape.rope_theta, max_seq_len=shape.cap,
             max_seqs=shape.n_seqs,
             weight_dtype=QTALK_BF16 if bf16 else QTALK_F32,
-            kv_dtype=QTALK_F16 if shape.kv_dtype == "f16" else QTALK_F32,
+            kv_dtype={"f16": QTALK_F16, "q8": QTALK_Q8}.get(shape.kv_dtype, QTALK_F32),
             n_output_heads=(weights["w_head"].shape[0]
                             if np.ndim(weights["w_head"]) == 3 else 1))
         keep = []

@@ -48,8 +48,10 @@ def _check_kv(tk, orc, shape, tol, seq=0, layers=None):
     return worst
 
 
-def _prefill_decode(name, T, steps, tol, n_layers=None, kv_layers=None):
+def _prefill_decode(name, T, steps, tol, n_layers=None, kv_layers=None, kv_dtype=None):
     shape = workload(name)
+    if kv_dtype is not None:
+        shape = shape.with_(kv_dtype=kv_dtype)
     w = weights_for(name, n_layers)
     say(f"[case] {name} layers={len(w['layers'])} T={T} steps={steps}")
     orc = TalkerOracle(shape, w)
@@ -739,3 +741,75 @@ def test_prefill_batch_matches_oracle(n, T):
     tk.sync()
     assert rel_err(g, o) <= tol
     tk.close()
+
+
+def _q8_structure_ok(v):
+    """Every 32-value block of a Q8_0 row is code * scale with codes in
+    [-127, 127] and the largest magnitude at 127: the block divided by its
+    own step max|v| / 127 is integral."""
+    b = np.asarray(v, dtype=np.float64).reshape(-1, 32)
+    amax = np.abs(b).max(axis=1, keepdims=True)
+    nz = amax[:, 0] > 0
+    r = b[nz] / amax[nz] * 127.0
+    return (np.abs(r - np.round(r)).max() < 1e-4 and np.abs(np.round(r)).max() <= 127
+            and (np.abs(np.round(r)).max(axis=1) == 127).all())
+
+
+def test_q8_cache_tiny_f32_prefill16_decode8():
+    # the generic kernels (f32 weights, head_dim 64): append, decode attention
+    _prefill_decode("tiny_f32_2l", 16, 8, 1e-2, kv_dtype="q8")
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
+    # real shapes, 2 layers: prefill 300 rows (matrix cores for the
+    # projections, the split-KV kernel for attention over the Q8 cache), then
+    # 40 decodes on the persistent kernel (fused = "1") or the per-step
+    # kernels; the cache holds Q8_0 blocks
+    base = workload("talker_1l_t128")
+    shape = base.with_(kv_dtype="q8")
+    w = weights_for("talker_1l_t128", 2)
+    monkeypatch.setenv("QTALK_FUSED_DECODE", fused)
+    tk = _talker(shape, w)
+    monkeypatch.delenv("QTALK_FUSED_DECODE")
+    orc = TalkerOracle(shape, w)
+    T, steps, tol = 300, 40, 2e-2
+    emb = prefill_embeddings(shape, T)
+    say(f"q8 cache fused={fused}")
+    lg = tk.prefill(0, dev(emb))
+    lo, _ = orc.prefill(0, emb)
+    errs = [rel_err(host(lg), lo)]
+    for s_ in range(steps):
+        e = step_embedding(shape, s_)
+        g = host(tk.decode(0, dev(e)))
+        o, _ = orc.decode(0, e)
+        errs.append(rel_err(g, o))
+        assert argmax_ok(g, o, tol), s_
+    tk.sync()
+    say(f"q8 fused={fused}: logits rel err max {max(errs):.2e}")
+    assert max(errs) <= tol
+    for l in (0, 1):
+        for which in (0, 1):
+            g = host(tk.kv_read(0, l, which))
+            assert rel_err(g, orc.kv(0, l, which)) <= tol, (l, which)
+            assert _q8_structure_ok(g), (l, which)
+    tk.close()
+
+
+def test_q8_cache_halves_the_cache():
+    # Q8_0 rows take head_dim + head_dim / 16 bytes against 2 * head_dim
+    import torch
+    base = workload("talker_1l_t128")
+    w = weights_for("talker_1l_t128")
+    free0 = torch.cuda.mem_get_info()[0]
+    a = _talker(base.with_(cap=32768), w)
+    free1 = torch.cuda.mem_get_info()[0]
+    b = _talker(base.with_(cap=32768, kv_dtype="q8"), w)
+    free2 = torch.cuda.mem_get_info()[0]
+    f16_bytes, q8_bytes = free0 - free1, free1 - free2
+    kv16 = 2 * 8 * 32768 * 256
+    kv8 = 2 * 8 * 32768 * 136
+    say(f"context bytes f16 {f16_bytes}, q8 {q8_bytes}")
+    assert abs((f16_bytes - q8_bytes) - (kv16 - kv8)) < 8 << 20
+    a.close()
+    b.close()
