@@ -436,6 +436,33 @@ void launch_kv_to_f32(KvKind kv, const void* src, int n_kv, int cap, int len, in
   else hipLaunchKernelGGL(k_kv_to_f32<float>, grid, dim3(hd / 4), 0, st, s, cap, len, hd, dst);
 }
 
+// grid (len, n_kv, 2), hd / 4 threads: Q8_0 rows 0 .. len-1 of one
+// sequence's K (z = 0) and V (z = 1) into float16 rows [n_kv][cap][hd], for
+// the matrix-core prefill attention
+__global__ void k_kv_q8_to_f16(const char* kq, const char* vq, int cap, int hd, f16_t* k16,
+                               f16_t* v16) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x * 4;
+  const char* src = blockIdx.z ? vq : kq;
+  f16_t* dst = blockIdx.z ? v16 : k16;
+  float f[4];
+  kv_load<q8_t, 4>(src + ((size_t)h * cap + t) * KVIO<q8_t>::row_bytes(hd), hd, d, f);
+  typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
+  h4 o;
+  o[0] = (f16_t)f[0];
+  o[1] = (f16_t)f[1];
+  o[2] = (f16_t)f[2];
+  o[3] = (f16_t)f[3];
+  *reinterpret_cast<h4*>(dst + ((size_t)h * cap + t) * hd + d) = o;
+}
+
+void launch_kv_q8_to_f16(const void* kq, const void* vq, int n_kv, int cap, int len, int hd,
+                         f16_t* k16, f16_t* v16, hipStream_t st) {
+  if (len <= 0) return;
+  hipLaunchKernelGGL(k_kv_q8_to_f16, dim3(len, n_kv, 2), dim3(hd / 4), 0, st,
+                     reinterpret_cast<const char*>(kq), reinterpret_cast<const char*>(vq), cap, hd,
+                     k16, v16);
+}
+
 size_t kv_row_bytes(KvKind kv, int hd) {
   return kv == KV_F16 ? KVIO<f16_t>::row_bytes(hd)
                       : (kv == KV_Q8 ? KVIO<q8_t>::row_bytes(hd) : KVIO<float>::row_bytes(hd));

@@ -46,6 +46,10 @@ struct QkArgs {
 // head_dim / 32 float16 scales)
 enum KvKind { KV_F32 = 0, KV_F16 = 1, KV_Q8 = 2 };
 size_t kv_row_bytes(KvKind kv, int head_dim);
+// Q8_0 rows 0 .. len-1 of one sequence (K and V, [n_kv][cap] rows each) into
+// float16 [n_kv][cap][hd] copies
+void launch_kv_q8_to_f16(const void* kq, const void* vq, int n_kv, int cap, int len, int hd,
+                         f16_t* k16, f16_t* v16, hipStream_t st);
 void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st);
 
 // Causal GQA attention of the listed rows over the cache (split over keys).

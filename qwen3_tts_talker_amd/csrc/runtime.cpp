@@ -57,6 +57,7 @@ struct qtalk_ctx {
   hipStream_t stream = nullptr;
   bool w_bf16 = true, kv_f16 = true;
   KvKind kv = KV_F16;  // cache storage
+  f16_t* kv16 = nullptr;  // Q8 cache: float16 copy of one sequence's K then V for the matrix-core prefill attention
   size_t kv_rb = 0;    // bytes per cache row (one position of one KV head)
   size_t welem = 2;
   int q_dim = 0, kv_dim = 0, qkv_dim = 0;
@@ -138,7 +139,7 @@ bool dev_alloc(void** p, size_t bytes) {
 void free_all(qtalk_ctx* c) {
   void* ptrs[] = {c->wblob, c->nblob, c->head, c->kc,     c->vc,    c->rope,   c->x,
                   c->qkv,   c->att,   c->act,  c->hn,     c->part_o, c->part_ml, c->work,
-                  c->ll,    c->fpart, c->ferr, c->aux_err};
+                  c->ll,    c->fpart, c->ferr, c->aux_err, c->kv16};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -260,7 +261,11 @@ struct Fwd {
     bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
     if (!normed) launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
-    const bool mfma_attn = c->kv == KV_F16 && attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
+    const bool sup = attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
+    // a Q8 cache reaches the matrix cores through a float16 copy of the
+    // sequence's rows 0 .. p0+T-1 (one sequence at a time)
+    const bool q8_mfma = c->kv == KV_Q8 && c->kv16 && sup && rows.uniform == 1;
+    const bool mfma_attn = (c->kv == KV_F16 && sup) || q8_mfma;
     qk_append(l, rows, mfma_attn);
     if (mfma_attn) {
       PrefillAttnArgs p{};
@@ -271,6 +276,15 @@ struct Fwd {
       p.rope = c->rope;
       p.kc = reinterpret_cast<const f16_t*>(kv_layer(c->kc, l));
       p.vc = reinterpret_cast<const f16_t*>(kv_layer(c->vc, l));
+      if (q8_mfma) {
+        const size_t seq_rows = (size_t)rows.seq0 * g.n_kv_heads * g.max_seq_len;
+        f16_t* k16 = c->kv16;
+        f16_t* v16 = c->kv16 + (size_t)g.n_kv_heads * g.max_seq_len * g.head_dim;
+        launch_kv_q8_to_f16(kv_layer(c->kc, l) + seq_rows * c->kv_rb, kv_layer(c->vc, l) + seq_rows * c->kv_rb,
+                            g.n_kv_heads, g.max_seq_len, rows.p0 + T, g.head_dim, k16, v16, st);
+        p.kc = k16;
+        p.vc = v16;
+      }
       p.n_heads = g.n_heads;
       p.n_kv_heads = g.n_kv_heads;
       p.head_dim = g.head_dim;
@@ -284,6 +298,7 @@ struct Fwd {
         for (int z = 0; z < p.nbatch; ++z) p.seqs[z] = rows.seq[z];
         p.seq = rows.seq[0];
       }
+      if (q8_mfma) p.seq = 0;  // the float16 copy holds this sequence only
       p.qscale = 1.4426950408889634f / sqrtf((float)g.head_dim);
       p.out = att_b;
       p.ldo = c->q_dim;
@@ -519,6 +534,9 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
             dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
             dev_alloc((void**)&c->x, (size_t)rows * H * 4) &&
             dev_alloc((void**)&c->aux_err, 4) &&
+            (c->kv != KV_Q8 || !c->w_bf16 ||
+             !attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads) ||
+             dev_alloc((void**)&c->kv16, (size_t)2 * g.n_kv_heads * g.max_seq_len * g.head_dim * 2)) &&
             dev_alloc((void**)&c->qkv, (size_t)rows * c->qkv_dim * 4) &&
             dev_alloc((void**)&c->att, (size_t)rows * c->q_dim * 4) &&
             dev_alloc((void**)&c->act, (size_t)rows * I * 4) &&

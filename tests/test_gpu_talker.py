@@ -762,10 +762,10 @@ def test_q8_cache_tiny_f32_prefill16_decode8():
 
 @pytest.mark.parametrize("fused", ["1", "0"])
 def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
-    # real shapes, 2 layers: prefill 300 rows (matrix cores for the
-    # projections, the split-KV kernel for attention over the Q8 cache), then
-    # 40 decodes on the persistent kernel (fused = "1") or the per-step
-    # kernels; the cache holds Q8_0 blocks
+    # real shapes, 2 layers: prefill 300 rows and extend 200 (matrix cores;
+    # the attention reads a float16 copy of the dequantised rows), then 40
+    # decodes on the persistent kernel (fused = "1") or the per-step kernels;
+    # the cache holds Q8_0 blocks
     base = workload("talker_1l_t128")
     shape = base.with_(kv_dtype="q8")
     w = weights_for("talker_1l_t128", 2)
@@ -774,11 +774,15 @@ def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
     monkeypatch.delenv("QTALK_FUSED_DECODE")
     orc = TalkerOracle(shape, w)
     T, steps, tol = 300, 40, 2e-2
-    emb = prefill_embeddings(shape, T)
+    emb = prefill_embeddings(shape, T + 200)
     say(f"q8 cache fused={fused}")
-    lg = tk.prefill(0, dev(emb))
-    lo, _ = orc.prefill(0, emb)
+    lg = tk.prefill(0, dev(emb[:T]))
+    lo, _ = orc.prefill(0, emb[:T])
     errs = [rel_err(host(lg), lo)]
+    # an extend at p0 = 300 attends to the quantised rows of both chunks
+    lg = tk.extend(0, dev(emb[T:]))
+    lo, _ = orc.extend(0, emb[T:])
+    errs.append(rel_err(host(lg), lo))
     for s_ in range(steps):
         e = step_embedding(shape, s_)
         g = host(tk.decode(0, dev(e)))
@@ -797,19 +801,23 @@ def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
 
 
 def test_q8_cache_halves_the_cache():
-    # Q8_0 rows take head_dim + head_dim / 16 bytes against 2 * head_dim
+    # Q8_0 rows take head_dim + head_dim / 16 bytes against 2 * head_dim; a
+    # Q8 context also keeps one sequence's float16 staging copy for the
+    # matrix-core prefill attention
     import torch
     base = workload("talker_1l_t128")
     w = weights_for("talker_1l_t128")
+    S, cap = 8, 8192
     free0 = torch.cuda.mem_get_info()[0]
-    a = _talker(base.with_(cap=32768), w)
+    a = _talker(base.with_(cap=cap, n_seqs=S), w)
     free1 = torch.cuda.mem_get_info()[0]
-    b = _talker(base.with_(cap=32768, kv_dtype="q8"), w)
+    b = _talker(base.with_(cap=cap, n_seqs=S, kv_dtype="q8"), w)
     free2 = torch.cuda.mem_get_info()[0]
     f16_bytes, q8_bytes = free0 - free1, free1 - free2
-    kv16 = 2 * 8 * 32768 * 256
-    kv8 = 2 * 8 * 32768 * 136
+    kv16 = 2 * S * 8 * cap * 256
+    kv8 = 2 * S * 8 * cap * 136
+    staging = 2 * 8 * cap * 256
     say(f"context bytes f16 {f16_bytes}, q8 {q8_bytes}")
-    assert abs((f16_bytes - q8_bytes) - (kv16 - kv8)) < 8 << 20
+    assert abs((f16_bytes - q8_bytes) - (kv16 - kv8 - staging)) < 8 << 20
     a.close()
     b.close()
