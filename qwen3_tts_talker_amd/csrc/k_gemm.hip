@@ -292,6 +292,66 @@ __global__ __launch_bounds__(512) void k_gemm_m32(GemmArgs a, int k_per_split) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny products, M <= 128 rows (short prefills): latency-bound, not
+// bandwidth-bound, so every wave keeps a whole chunk of 256 K values in
+// flight.  Block = one 32 x 32 output tile; its nw waves (<= 8) split K into
+// chunks of 256, wave w taking chunks w, w + nw, ...; for each it loads all
+// 16 steps of the v_mfma_f32_32x32x16_bf16 operand layout at once (16 bytes
+// of an activation row and of a weight row per lane and step, straight from
+// global memory), then runs 16 MFMAs.  The waves' tiles are added through
+// LDS in wave order (deterministic) before the epilogue: no split-K
+// workspace, no second kernel.
+constexpr int SK_KW = 256;  // K values per chunk
+
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
+  __shared__ float part[8][1024];  // per-wave tiles, [wave][lane * 16 + register]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
+  const int M = a.M;
+  const int nch = a.K / SK_KW;
+  const bf16_t* Ap = a.A + (size_t)min(m0 + (lane & 31), M - 1) * a.lda + (lane >> 5) * 8;  // rows >= M: not stored
+  const bf16_t* Bp = a.B + (size_t)(n0 + (lane & 31)) * a.K + (lane >> 5) * 8;
+  f32x16_t acc = f32x16_t{};
+  for (int ch = wave; ch < nch; ch += nw) {
+    bf16x8_t av[SK_KW / 16], bv[SK_KW / 16];
+#pragma unroll
+    for (int s = 0; s < SK_KW / 16; ++s) {
+      av[s] = *reinterpret_cast<const bf16x8_t*>(Ap + ch * SK_KW + s * 16);
+      bv[s] = *reinterpret_cast<const bf16x8_t*>(Bp + ch * SK_KW + s * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all 32 loads before the first MFMA
+#pragma unroll
+    for (int s = 0; s < SK_KW / 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s], bv[s], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; q += 4)
+    *reinterpret_cast<float4*>(&part[wave][lane * 16 + q]) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+  __syncthreads();
+  // thread t < 1024 of the tile: lane t / 16, register t % 16; register q of
+  // lane l is row (q/4)*8 + (l/32)*4 + q%4, column l%32 of the tile
+  for (int t = threadIdx.x; t < 1024; t += blockDim.x) {
+    const int l = t >> 4, q = t & 15;
+    const int row = m0 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3), col = l & 31;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += part[w][t];
+    if (EPI == EPI_SWIGLU) {
+      // columns 0..15 of the tile are gate rows, 16..31 the matching up rows:
+      // lane l + 16 holds the up value of lane l's gate value
+      if (col >= 16 || row >= M) continue;
+      float u = 0.f;
+      for (int w = 0; w < nw; ++w) u += part[w][t + 16 * 16];
+      reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + n0 / 2 + col] = (bf16_t)f32_to_bf16(silu_f(v) * u);
+      continue;
+    }
+    if (row >= M) continue;
+    float* c = reinterpret_cast<float*>(a.C) + (size_t)row * a.ldc + n0 + col;
+    if (EPI == EPI_STORE) *c = v;
+    else *c += v;
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs a, int ks) {
   const size_t MN = (size_t)a.M * a.N;
@@ -362,6 +422,19 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_add_norm(GemmArgs a, int 
   }
 }
 
+static bool skinny_ok(const GemmArgs& a) {
+  return a.M >= 1 && a.M <= 128 && a.N % 32 == 0 && a.K % SK_KW == 0;
+}
+
+// waves per block: the largest divisor of the chunk count up to 8
+template <int EPI>
+static void launch_skinny(GemmArgs a, hipStream_t st) {
+  const int nch = a.K / SK_KW;
+  int nw = 8;
+  while (nch % nw) --nw;
+  hipLaunchKernelGGL((k_gemm_skinny<EPI>), dim3(a.N / 32, (a.M + 31) / 32), dim3(64 * nw), 0, st, a);
+}
+
 template <int BM, int EPI>
 static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
   const dim3 grid(a.N / GB_N, (a.M + BM - 1) / BM, ks);
@@ -426,6 +499,14 @@ void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int
 
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
   const int nkt = a.K / GB_K;
+  if (skinny_ok(a)) {
+    switch (epi) {
+      case EPI_STORE: launch_skinny<EPI_STORE>(a, st); break;
+      case EPI_ADD: launch_skinny<EPI_ADD>(a, st); break;
+      case EPI_SWIGLU: launch_skinny<EPI_SWIGLU>(a, st); break;
+    }
+    return;
+  }
   if (a.M >= 512) {
     // 256-row tiles.  The gate|up projection takes 192-column blocks when
     // that gives the grid whole rounds of 256 CUs (6144 wide at M = 2048);
