@@ -393,6 +393,18 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float cwt[NCH];  // merge weights of the chunks
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // block-wide "some thread gave up": sticky (a block that gives up leaves
+  // the kernel), so one barrier per step suffices; a wave that reads a later
+  // step's flag early only leaves earlier, which the barrier tolerates
+  // (ended waves no longer take part in it)
+  __shared__ int s_bail;
+  if (tid == 0) s_bail = 0;
+  __syncthreads();
+  auto sync_bail = [&](bool bail) -> bool {
+    if (bail) s_bail = 1;
+    __syncthreads();
+    return s_bail != 0;
+  };
   // exchange words carry epoch (launch epoch * 64 + layer); layers of equal
   // parity share one buffer region (see the layer loop)
   const uint32_t ep0 = a.epoch * 64u;
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       cs = a.rope[(size_t)pos * (HD / 2) + (tid & 63)];
       ss = wave_sum(ss);
       if (lane == 0) redw[wave] = ss;
-      if (__syncthreads_or(bail)) return;
+      if (sync_bail(bail)) return;
       const float inv = inv_rms(redw, a.eps);
       float v[2];  // rows wave and wave + 8 of this block's 16
       gq.dot_all(xin, v, wave, lane);
@@ -560,7 +572,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         araw[tid] = v;
         const float sq = wave_sum(v * v);  // waves 0-1 q0, 2-3 q1, 4-5 k, 6-7 v
         if (lane == 0) redw[wave] = sq;
-        if (__syncthreads_or(bail)) return;
+        if (sync_bail(bail)) return;
       }
       // next step's bulk loads (the o_proj input comes from the merge, a
       // further exchange away)
@@ -787,7 +799,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       LLWait<1, LOCAL> wm;
       wm.issue(pbase + cc * PST + (k < 8 ? d0 + k : HD + k - 8) - tid, NCH * 10);
       const bool bail = !wm.finish(ep, a.err, [&](int, float x) { mg[tm] = x; });
-      if (__syncthreads_or(bail)) return;
+      if (sync_bail(bail)) return;
       if (wave == 0) {  // lane cc < NCH: chunk cc's weight 2^(m_c - M) / L
         const float mc = lane < NCH ? mg[lane * 10 + 8] : -INFINITY;
         const float lc = lane < NCH ? mg[lane * 10 + 9] : 0.f;
@@ -820,7 +832,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       // next step's bulk loads
       gd.load([&](int r) { return Wd + (size_t)(32 * c + r) * I + g * ISEG; }, wave, lane);
       gpost.load(g_post);
-      if (__syncthreads_or(bail)) return;
+      if (sync_bail(bail)) return;
       const float s = go.dot(xin, lane);
       if ((lane & 15) == 0) st_ll(E + OFF_OP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
     }
@@ -842,7 +854,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       }
       ss = wave_sum(ss);
       if (lane == 0) redw[wave] = ss;
-      if (__syncthreads_or(bail)) return;
+      if (sync_bail(bail)) return;
       const float inv = inv_rms(redw, a.eps);
       gg.dot(xin, red, wave, lane);
       __syncthreads();
@@ -859,7 +871,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       const int ta = min(tid, ISEG - 1);
       wa.issue(E + OFF_A + g * 512 + 16 * (ta / 12) + ta % 12 - tid, ISEG);
       const bool bail = !wa.finish_to(ep, a.err, xin);
-      if (__syncthreads_or(bail)) return;
+      if (sync_bail(bail)) return;
       const float s = gd.dot(xin, lane);
       if ((lane & 15) == 0) st_ll(E + OFF_DP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
       // after the publish: the next layer's QKV slice, or after the last layer
@@ -886,7 +898,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     bail = bail || !recv_norm(wx, epl, a.err, xres, xin, gin, &ss);  // gin = final gain
     ss = wave_sum(ss);
     if (lane == 0) redw[wave] = ss;
-    if (__syncthreads_or(bail)) return;
+    if (sync_bail(bail)) return;
     const float inv = inv_rms(redw, a.eps);
     if (b == 0 && a.hidden_out)
       for (int k = tid; k < H; k += NT) a.hidden_out[k] = xin[k] * inv;
