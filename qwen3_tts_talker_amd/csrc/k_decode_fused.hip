@@ -829,9 +829,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       const int to = min(tid, OSEG - 1);
       wo.issue(E + OFF_OG + g * 512 + 16 * (to >> 3) + (to & 7) - tid, OSEG);
       const bool bail = !wo.finish_to(ep, a.err, xin);
-      // next step's bulk loads
-      gd.load([&](int r) { return Wd + (size_t)(32 * c + r) * I + g * ISEG; }, wave, lane);
+      // bulk loads: the next step's gain, the next layer's cached keys
       gpost.load(g_post);
+      if (l + 1 < a.n_layers) load_kv(l + 1);
       if (sync_bail(bail)) return;
       const float s = go.dot(xin, lane);
       if ((lane & 15) == 0) st_ll(E + OFF_OP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
@@ -844,14 +844,15 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       wx.issue(E + OFF_XM + g * H, H);
       float ss;
       bail = bail || !recv_norm(wx, ep, a.err, xres, xin, gpost, &ss);
-      // bulk loads for the next layer: its input-norm gain and cached keys
-      // (its QKV slice follows in the down step, which loads nothing else)
+      // bulk loads: the next layer's input-norm gain and the down step's
+      // weight slice (the next layer's QKV slice follows after the down
+      // publish)
       if (l + 1 < a.n_layers) {
         gin.load(a.norms + (size_t)(l + 1) * a.norm_stride);
-        load_kv(l + 1);
       } else {
         gin.load(a.g_final);
       }
+      gd.load([&](int r) { return Wd + (size_t)(32 * c + r) * I + g * ISEG; }, wave, lane);
       ss = wave_sum(ss);
       if (lane == 0) redw[wave] = ss;
       if (sync_bail(bail)) return;
