@@ -544,11 +544,11 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         ss = x0 * x0 + x1 * x1;
       }
       // next step's bulk loads
-      go.load([&](int r) { return Wo + (size_t)(32 * c + r) * QD + g * OSEG; }, wave, lane);
       const float* gsel = tid < 256 ? g_q : g_k;
       gn = gsel[tid & 127];
       gnp = gsel[(tid & 127) ^ 64];
       cs = a.rope[(size_t)pos * (HD / 2) + (tid & 63)];
+      go.load([&](int r) { return Wo + (size_t)(32 * c + r) * QD + g * OSEG; }, wave, lane);
       ss = wave_sum(ss);
       if (lane == 0) redw[wave] = ss;
       if (sync_bail(bail)) return;
