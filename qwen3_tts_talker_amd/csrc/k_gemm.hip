@@ -293,41 +293,78 @@ __global__ __launch_bounds__(512) void k_gemm_m32(GemmArgs a, int k_per_split) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny products, M <= 128 rows (short prefills): latency-bound, not
-// bandwidth-bound, so every wave keeps a whole chunk of 256 K values in
-// flight.  Block = one 32 x 32 output tile; its nw waves (<= 8) split K into
-// chunks of 256, wave w taking chunks w, w + nw, ...; for each it loads all
-// 16 steps of the v_mfma_f32_32x32x16_bf16 operand layout at once (16 bytes
-// of an activation row and of a weight row per lane and step, straight from
-// global memory), then runs 16 MFMAs.  The waves' tiles are added through
-// LDS in wave order (deterministic) before the epilogue: no split-K
-// workspace, no second kernel.
-constexpr int SK_KW = 256;  // K values per chunk
+// Skinny products, M <= 128 rows (short prefills): latency-bound, so every
+// wave keeps a whole chunk in flight and the loads are coalesced.  Block =
+// one 32 x 32 output tile; its nw waves (<= 8) take the chunks of 128 K
+// values round robin.  A chunk (32 activation rows and 32 weight rows, 256
+// bytes each) is read with 16-byte loads of 16 lanes per row (8 cache lines
+// per instruction), written to the wave's own LDS region (rows padded by 16
+// bytes), then read back in the v_mfma_f32_32x32x16_bf16 operand layout for
+// 8 MFMAs while the next chunk's loads fly.  The waves' tiles are added
+// through LDS in wave order (deterministic) before the epilogue: no split-K
+// workspace, no second kernel.  (Measured slower at these sizes: splitting K
+// over more blocks with the last block of a tile adding the splits, whose
+// store / arrival / reload chain costs more than the wider grid gains; and
+// two chunks in flight per wave.)
+constexpr int SK_KC = 128;             // K values per chunk
+constexpr int SK_LD = SK_KC + 8;       // bf16 per LDS row
+constexpr int SK_WAVE = 2 * 32 * SK_LD;  // bf16 per wave region (A rows, then B rows)
 
 template <int EPI>
 __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
-  __shared__ float part[8][1024];  // per-wave tiles, [wave][lane * 16 + register]
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];  // nw * SK_WAVE; also the wave tiles at the end
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
   const int M = a.M;
-  const int nch = a.K / SK_KW;
-  const bf16_t* Ap = a.A + (size_t)min(m0 + (lane & 31), M - 1) * a.lda + (lane >> 5) * 8;  // rows >= M: not stored
-  const bf16_t* Bp = a.B + (size_t)(n0 + (lane & 31)) * a.K + (lane >> 5) * 8;
-  f32x16_t acc = f32x16_t{};
-  for (int ch = wave; ch < nch; ch += nw) {
-    bf16x8_t av[SK_KW / 16], bv[SK_KW / 16];
+  const int nch = a.K / SK_KC;
+  bf16_t* W = lds + wave * SK_WAVE;
+  // staging: instruction i covers rows 4i .. 4i+3, lane l row 4i + l/16,
+  // columns 8 (l % 16) .. +7 of the chunk
+  const int sr = lane >> 4, sc = (lane & 15) * 8;
+  const bf16_t* Bg = a.B + (size_t)(n0 + sr) * a.K + sc;
+  const size_t bstep = (size_t)4 * a.K;
+  const int arow_max = M - 1 - m0;  // last valid row of the tile (rows past it: not stored)
+  bf16x8_t ra[8], rb[8];  // vector types: the arrays stay in registers
+  int ch = wave;
+  if (ch < nch) {
 #pragma unroll
-    for (int s = 0; s < SK_KW / 16; ++s) {
-      av[s] = *reinterpret_cast<const bf16x8_t*>(Ap + ch * SK_KW + s * 16);
-      bv[s] = *reinterpret_cast<const bf16x8_t*>(Bp + ch * SK_KW + s * 16);
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(4 * i + sr, arow_max);
+      ra[i] = *reinterpret_cast<const bf16x8_t*>(a.A + (size_t)(m0 + r) * a.lda + sc + ch * SK_KC);
+      rb[i] = *reinterpret_cast<const bf16x8_t*>(Bg + i * bstep + ch * SK_KC);
     }
-    __builtin_amdgcn_sched_barrier(0);  // all 32 loads before the first MFMA
-#pragma unroll
-    for (int s = 0; s < SK_KW / 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s], bv[s], acc, 0, 0, 0);
   }
+  f32x16_t acc = f32x16_t{};
+  for (; ch < nch; ch += nw) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<bf16x8_t*>(W + (4 * i + sr) * SK_LD + sc) = ra[i];
+      *reinterpret_cast<bf16x8_t*>(W + (32 + 4 * i + sr) * SK_LD + sc) = rb[i];
+    }
+    const int nx = ch + nw;
+    if (nx < nch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = min(4 * i + sr, arow_max);
+        ra[i] = *reinterpret_cast<const bf16x8_t*>(a.A + (size_t)(m0 + r) * a.lda + sc + nx * SK_KC);
+        rb[i] = *reinterpret_cast<const bf16x8_t*>(Bg + i * bstep + nx * SK_KC);
+      }
+    }
+    // operand layout: lane l, step s: row l % 32, K 8 (l / 32) + 16 s .. +7
+    const bf16_t* ar = W + (lane & 31) * SK_LD + (lane >> 5) * 8;
+    const bf16_t* br = W + (32 + (lane & 31)) * SK_LD + (lane >> 5) * 8;
+#pragma unroll
+    for (int s2 = 0; s2 < SK_KC / 16; ++s2) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ar + s2 * 16);
+      const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(br + s2 * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with its staging region
+  float* part = reinterpret_cast<float*>(lds);  // [wave][lane * 16 + register]
 #pragma unroll
   for (int q = 0; q < 16; q += 4)
-    *reinterpret_cast<float4*>(&part[wave][lane * 16 + q]) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+    *reinterpret_cast<float4*>(&part[wave * 1024 + lane * 16 + q]) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
   __syncthreads();
   // thread t < 1024 of the tile: lane t / 16, register t % 16; register q of
   // lane l is row (q/4)*8 + (l/32)*4 + q%4, column l%32 of the tile
@@ -335,13 +372,13 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
     const int l = t >> 4, q = t & 15;
     const int row = m0 + (q >> 2) * 8 + (l >> 5) * 4 + (q & 3), col = l & 31;
     float v = 0.f;
-    for (int w = 0; w < nw; ++w) v += part[w][t];
+    for (int w = 0; w < nw; ++w) v += part[w * 1024 + t];
     if (EPI == EPI_SWIGLU) {
       // columns 0..15 of the tile are gate rows, 16..31 the matching up rows:
       // lane l + 16 holds the up value of lane l's gate value
       if (col >= 16 || row >= M) continue;
       float u = 0.f;
-      for (int w = 0; w < nw; ++w) u += part[w][t + 16 * 16];
+      for (int w = 0; w < nw; ++w) u += part[w * 1024 + t + 16 * 16];
       reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + n0 / 2 + col] = (bf16_t)f32_to_bf16(silu_f(v) * u);
       continue;
     }
@@ -423,16 +460,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_add_norm(GemmArgs a, int 
 }
 
 static bool skinny_ok(const GemmArgs& a) {
-  return a.M >= 1 && a.M <= 128 && a.N % 32 == 0 && a.K % SK_KW == 0;
+  return a.M >= 1 && a.M <= 128 && a.N % 32 == 0 && a.K % SK_KC == 0;
 }
 
-// waves per block: the largest divisor of the chunk count up to 8
+// waves per block: the largest divisor of the chunk count up to 8 (every
+// wave takes the same number of chunks)
 template <int EPI>
 static void launch_skinny(GemmArgs a, hipStream_t st) {
-  const int nch = a.K / SK_KW;
+  const int nch = a.K / SK_KC;
   int nw = 8;
   while (nch % nw) --nw;
-  hipLaunchKernelGGL((k_gemm_skinny<EPI>), dim3(a.N / 32, (a.M + 31) / 32), dim3(64 * nw), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_skinny<EPI>), dim3(a.N / 32, (a.M + 31) / 32), dim3(64 * nw),
+                     nw * SK_WAVE * sizeof(bf16_t), st, a);
 }
 
 template <int BM, int EPI>
