@@ -152,65 +152,66 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
   }
 }
 
-// Large-M variant: 256 x BN block tile over 8 waves (4 x 2, a 64 x BN/2 tile
-// each, 32x32x16 MFMA), so every SIMD runs two waves and the LDS reads of one
-// hide behind the MFMAs of the other.  BN = 192 gives the 6144-wide gate|up
-// projection exactly 256 tiles at M = 2048.  LDS holds two K-tile stages; global
-// loads run two K tiles ahead of the MFMAs (two register stages), one
-// barrier per K tile.
-template <int BN, int EPI, bool SPLIT>
-__global__ __launch_bounds__(512) void k_gemm_m32(GemmArgs a, int k_per_split) {
-  constexpr int BM = 256, NT = 512;
-  constexpr int BK = GB_K, LS = G_STRIDE;
-  constexpr int WTM = BM / 4, WTN = BN / 2;  // 64 x 64 per wave
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int AR = BM * BK / 8 / NT;  // 16-byte chunks per thread and K tile
-  constexpr int BR = BN * BK / 8 / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LS];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LS];
+// Large-M variant with direct-to-LDS loads: 256 x BN block tile over 8 waves
+// (4 x 2, a 64 x BN/2 tile each, 32x32x16 MFMA), BK 64.  Global tiles go
+// straight into LDS with global_load_lds_dwordx4 (no register staging, no
+// LDS store instructions); NS LDS stages, loads issued NS - 1 tiles ahead,
+// one barrier per K tile.  LDS rows are 128 bytes unpadded; 16-byte chunk c
+// of row r sits in slot c ^ (r & 7), which the loads produce by giving lane
+// l of an 8-row instruction row l / 8 and chunk (l % 8) ^ (l / 8), and which
+// makes the operand reads (8 consecutive rows, one chunk) conflict-free.
+// BN = 192 gives the 6144-wide gate|up projection exactly 256 tiles at
+// M = 2048 (two stages fit LDS there, three at BN = 128).
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
+// (lds uniform across the wave).  A helper function, not a lambda: a lambda
+// holding this builtin makes the host pass drop the kernel's launch stub.
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+template <int BN>
+struct DmaCfg {
+  static constexpr int NS = BN == 128 ? 3 : 2;          // LDS stages
+  static constexpr int A_LD = 4, B_LD = BN / 64;        // 1 KiB loads per wave and K tile
+  static constexpr int LPT = A_LD + B_LD;
+};
+
+template <int BN, int EPI, bool SPLIT>
+__global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
+  constexpr int BM = 256, BK = 64;
+  constexpr int NS = DmaCfg<BN>::NS, A_LD = DmaCfg<BN>::A_LD, B_LD = DmaCfg<BN>::B_LD;
+  constexpr int LPT = DmaCfg<BN>::LPT;
+  constexpr int WTM = BM / 4, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  __shared__ __attribute__((aligned(1024))) bf16_t As[NS][BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t Bs[NS][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int kbeg = blockIdx.z * k_per_split;
   const int nkt = k_per_split / BK;
   const int M = a.M, K = a.K;
 
-  // chunk i of this thread: row tid / 8 + 64 i, column chunk tid % 8 (A rows
-  // past M re-read row M - 1; their results are never stored)
-  const int lrow = tid >> 3, lchunk = (tid & 7) * 8;
-  const bf16_t* Ab0 = a.A + kbeg + lchunk;
-  const bf16_t* Bb0 = a.B + (size_t)(n0 + lrow) * K + kbeg + lchunk;
-  const size_t lda = a.lda;
+  // this lane's source rows (A rows past M re-read row M - 1; never stored)
+  const int lr = lane >> 3, lc = ((lane & 7) ^ (lane >> 3)) * 8;
+  const bf16_t* ag[A_LD];
+  const bf16_t* bg[B_LD];
+#pragma unroll
+  for (int j = 0; j < A_LD; ++j)
+    ag[j] = a.A + (size_t)min(m0 + (wave * A_LD + j) * 8 + lr, M - 1) * a.lda + kbeg + lc;
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) bg[j] = a.B + (size_t)(n0 + (wave * B_LD + j) * 8 + lr) * K + kbeg + lc;
 
-  // two register stages as named scalars (4 A chunks, 2 B chunks each): an
-  // array here is left in private memory by the compiler
-  static_assert(AR == 4 && (BR == 2 || BR == 3), "stage layout");
-  uint4 s0a0, s0a1, s0a2, s0a3, s0b0, s0b1, s0b2, s1a0, s1a1, s1a2, s1a3, s1b0, s1b1, s1b2;
-#define QT_LDA(I, KT) \
-  (*reinterpret_cast<const uint4*>(Ab0 + (size_t)min(m0 + lrow + 64 * (I), M - 1) * lda + (KT) * BK))
-#define QT_LDB(I, KT) ld_stream16(Bb0 + (size_t)(64 * (I)) * K + (KT) * BK)
-#define QT_GLOAD(S, KT)      \
-  do {                       \
-    const int kt_ = (KT);    \
-    S##a0 = QT_LDA(0, kt_);  \
-    S##a1 = QT_LDA(1, kt_);  \
-    S##a2 = QT_LDA(2, kt_);  \
-    S##a3 = QT_LDA(3, kt_);  \
-    S##b0 = QT_LDB(0, kt_);  \
-    S##b1 = QT_LDB(1, kt_);  \
-    if (BR == 3) S##b2 = QT_LDB(2, kt_); \
-  } while (0)
-#define QT_ST(BUFA, ROW, V) *reinterpret_cast<uint4*>(&BUFA[(lrow + (ROW)) * LS + lchunk]) = (V)
-#define QT_LSTORE(S, BUF)        \
-  do {                           \
-    QT_ST(As[BUF], 0, S##a0);    \
-    QT_ST(As[BUF], 64, S##a1);   \
-    QT_ST(As[BUF], 128, S##a2);  \
-    QT_ST(As[BUF], 192, S##a3);  \
-    QT_ST(Bs[BUF], 0, S##b0);    \
-    QT_ST(Bs[BUF], 64, S##b1);   \
-    if (BR == 3) QT_ST(Bs[BUF], 128, S##b2); \
+#define QD_ISSUE(KT, S)                                                                            \
+  do {                                                                                             \
+    const int kt_ = (KT), s_ = (S);                                                                \
+    _Pragma("unroll") for (int j = 0; j < A_LD; ++j)                                               \
+        lds_load16(ag[j] + kt_ * BK, &As[s_][(wave * A_LD + j) * 8 * BK]);                       \
+    _Pragma("unroll") for (int j = 0; j < B_LD; ++j)                                               \
+        lds_load16(bg[j] + kt_ * BK, &Bs[s_][(wave * B_LD + j) * 8 * BK]);                       \
   } while (0)
 
   f32x16_t acc[TM][TN];
@@ -219,49 +220,63 @@ __global__ __launch_bounds__(512) void k_gemm_m32(GemmArgs a, int k_per_split) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-#define QT_COMPUTE(BUF)                                                                     \
-  do {                                                                                      \
-    const bf16_t* Ab = As[BUF] + (wm * WTM + fr) * LS + fk;                                 \
-    const bf16_t* Bb = Bs[BUF] + (wn * WTN + fr) * LS + fk;                                 \
-    _Pragma("unroll") for (int ks = 0; ks < BK; ks += 16) {                                 \
-      bf16x8_t af[TM], bfr[TN];                                                             \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
-          af[i] = *reinterpret_cast<const bf16x8_t*>(Ab + i * 32 * LS + ks);                \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bb + j * 32 * LS + ks);               \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                        \
-          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                        \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);  \
-    }                                                                                       \
+  // operand reads: row (l % 32) of each 32-row fragment, chunk 2 s + l / 32.
+  // They are inline asm: the compiler would otherwise wait for every
+  // outstanding direct-to-LDS load (tiles in flight included) before the
+  // first read.  The statements after the wait name the fragments it guards,
+  // so no MFMA is scheduled above it.  The reads of step ks + 1 go out while
+  // the MFMAs of step ks run; a register they refill was last read by an
+  // MFMA already issued (MFMAs take their A/B operands at issue).
+  const int fr = lane & 31, fh = lane >> 5, fx = lane & 7;
+  const uint32_t a_off = (uint32_t)(uintptr_t)(As[0] + (wm * WTM + fr) * BK);
+  const uint32_t b_off = (uint32_t)(uintptr_t)(Bs[0] + (wn * WTN + fr) * BK);
+  constexpr int NF = TM + TN;  // fragments per K step: A 0..TM-1, then B
+#define QD_READ(X, KS)                                                                        \
+  do {                                                                                        \
+    const uint32_t slot_ = (((2 * (KS) + fh) ^ fx) * 16);                                     \
+    _Pragma("unroll") for (int q = 0; q < NF; ++q) {                                          \
+      const uint32_t addr_ = (q < TM ? ab + q * 32 * BK * 2 : bb + (q - TM) * 32 * BK * 2) + slot_; \
+      asm volatile("ds_read_b128 %0, %1" : "=v"(X[q]) : "v"(addr_));                         \
+    }                                                                                         \
+  } while (0)
+#define QD_COMPUTE(S)                                                                         \
+  do {                                                                                        \
+    const uint32_t ab = a_off + (S) * (BM * BK * 2), bb = b_off + (S) * (BN * BK * 2);        \
+    bf16x8_t f0[NF], f1[NF];                                                                  \
+    QD_READ(f0, 0);                                                                           \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                  \
+      bf16x8_t* x = (ks & 1) ? f1 : f0;                                                       \
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                      \
+      _Pragma("unroll") for (int q = 0; q < NF; ++q) asm volatile("" : "+v"(x[q]));           \
+      if (ks + 1 < BK / 16) {                                                                 \
+        if (ks & 1) QD_READ(f0, ks + 1);                                                      \
+        else QD_READ(f1, ks + 1);                                                             \
+      }                                                                                       \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                          \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], x[TM + j], acc[i][j], 0, 0, 0);   \
+    }                                                                                         \
   } while (0)
 
-  // tile kt sits in register stage kt & 1 and LDS buffer kt & 1.  Loads and
-  // stores run unconditionally (past the last tile they repeat it) so both
-  // register stages stay in registers.
-  QT_GLOAD(s0, 0);
-  QT_GLOAD(s1, min(1, nkt - 1));
-  QT_LSTORE(s0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    // even tile kt in LDS 0; tile kt + 1 in flight in stage 1
-    QT_GLOAD(s0, min(kt + 2, nkt - 1));
-    QT_COMPUTE(0);
-    QT_LSTORE(s1, 1);
-    __syncthreads();
-    if (kt + 1 >= nkt) break;
-    // odd tile kt + 1 in LDS 1; tile kt + 2 in flight in stage 0
-    QT_GLOAD(s1, min(kt + 3, nkt - 1));
-    QT_COMPUTE(1);
-    QT_LSTORE(s0, 0);
-    __syncthreads();
+  // The barrier is the raw instruction: __syncthreads() would also wait for
+  // every outstanding direct-to-LDS load (the tiles in flight).  Each wave
+  // first waits for its own loads of the tile about to be read; the asm
+  // statements keep the compiler from moving memory accesses across.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nkt) QD_ISSUE(s, s);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (NS == 3 && kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NS - 1 < nkt) QD_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);
+    QD_COMPUTE(kt % NS);
   }
-#undef QT_LDA
-#undef QT_LDB
-#undef QT_ST
-#undef QT_GLOAD
-#undef QT_LSTORE
-#undef QT_COMPUTE
+
+#undef QD_ISSUE
+#undef QD_READ
+#undef QD_COMPUTE
 
   // epilogue: register r of lane l is C[row (r/4)*8 + (l/32)*4 + r%4][col l%32]
 #pragma unroll
@@ -493,9 +508,9 @@ static void launch_m32(GemmArgs a, int ks, hipStream_t st) {
   const dim3 grid(a.N / BN, (a.M + 255) / 256, ks);
   const int kps = a.K / ks;
   if (ks == 1) {
-    hipLaunchKernelGGL((k_gemm_m32<BN, EPI, false>), grid, dim3(512), 0, st, a, kps);
+    hipLaunchKernelGGL((k_gemm_dma<BN, EPI, false>), grid, dim3(512), 0, st, a, kps);
   } else if constexpr (BN == 128) {  // the 192-wide tile is never split
-    hipLaunchKernelGGL((k_gemm_m32<BN, EPI, true>), grid, dim3(512), 0, st, a, kps);
+    hipLaunchKernelGGL((k_gemm_dma<BN, EPI, true>), grid, dim3(512), 0, st, a, kps);
     const size_t n_out = (size_t)a.M * a.N / (EPI == EPI_SWIGLU ? 2 : 1);
     const unsigned blocks = (unsigned)((n_out + 255) / 256 < 4096 ? (n_out + 255) / 256 : 4096);
     hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3(blocks), dim3(256), 0, st, a, ks);
@@ -526,7 +541,7 @@ void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int
     const int ks = m32_splits(a);
     if (ks > 1) {
       const dim3 grid(a.N / 128, (a.M + 255) / 256, ks);
-      hipLaunchKernelGGL((k_gemm_m32<128, EPI_ADD, true>), grid, dim3(512), 0, st, a, a.K / ks);
+      hipLaunchKernelGGL((k_gemm_dma<128, EPI_ADD, true>), grid, dim3(512), 0, st, a, a.K / ks);
       hipLaunchKernelGGL(k_splitk_reduce_add_norm, dim3(a.M), dim3(256), 0, st, a, ks, g, eps, hn,
                          ldh);
       return;
