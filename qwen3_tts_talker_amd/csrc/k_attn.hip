@@ -106,9 +106,14 @@ __device__ __forceinline__ float half32_max(float v) {
 // Lane i < hd/2 holds the NEOX pair (x_i, x_{i+hd/2}).
 
 template <int HD, typename KVT>
-__global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
+__global__ __launch_bounds__(256) void k_qk_rope_append(QkArgs a) {
   constexpr int HALF = HD / 2;
-  const int t = blockIdx.x, hh = blockIdx.y + (a.skip_q ? a.n_heads : 0), lane = threadIdx.x;
+  // one wave per (row, head) unit, four units per block (a one-wave block per
+  // unit left the dispatcher, not memory, setting the pace)
+  const int nh = (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (unit >= a.rows.n * nh) return;  // whole waves: only wave-level reductions below
+  const int t = unit / nh, hh = unit % nh + (a.skip_q ? a.n_heads : 0);
   const int nq = a.n_heads, nkv = a.n_kv_heads;
   float* row = a.qkv + (size_t)t * a.ldqkv;
   const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
@@ -181,13 +186,14 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(QkArgs a) {
 
 template <int HD>
 static void launch_qk_hd(KvKind kv, const QkArgs& a, const dim3& grid, hipStream_t st) {
-  if (kv == KV_F16) hipLaunchKernelGGL((k_qk_rope_append<HD, f16_t>), grid, dim3(64), 0, st, a);
-  else if (kv == KV_Q8) hipLaunchKernelGGL((k_qk_rope_append<HD, q8_t>), grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((k_qk_rope_append<HD, float>), grid, dim3(64), 0, st, a);
+  if (kv == KV_F16) hipLaunchKernelGGL((k_qk_rope_append<HD, f16_t>), grid, dim3(256), 0, st, a);
+  else if (kv == KV_Q8) hipLaunchKernelGGL((k_qk_rope_append<HD, q8_t>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_qk_rope_append<HD, float>), grid, dim3(256), 0, st, a);
 }
 
 void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
-  const dim3 grid(a.rows.n, (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads);
+  const int nh = (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads;
+  const dim3 grid((a.rows.n * nh + 3) / 4);
   if (a.head_dim == 128) launch_qk_hd<128>(kv, a, grid, st);
   else launch_qk_hd<64>(kv, a, grid, st);
 }
