@@ -504,7 +504,7 @@ static void launch_bm(GemmArgs a, int ks, hipStream_t st) {
 }
 
 template <int BN, int EPI>
-static void launch_m32(GemmArgs a, int ks, hipStream_t st) {
+static void launch_dma(GemmArgs a, int ks, hipStream_t st) {
   const dim3 grid(a.N / BN, (a.M + 255) / 256, ks);
   const int kps = a.K / ks;
   if (ks == 1) {
@@ -517,15 +517,15 @@ static void launch_m32(GemmArgs a, int ks, hipStream_t st) {
   }
 }
 
-static void launch_m32_epi(Epilogue epi, GemmArgs a, int ks, hipStream_t st) {
+static void launch_dma_epi(Epilogue epi, GemmArgs a, int ks, hipStream_t st) {
   switch (epi) {
-    case EPI_STORE: launch_m32<128, EPI_STORE>(a, ks, st); break;
-    case EPI_ADD: launch_m32<128, EPI_ADD>(a, ks, st); break;
-    case EPI_SWIGLU: launch_m32<128, EPI_SWIGLU>(a, ks, st); break;
+    case EPI_STORE: launch_dma<128, EPI_STORE>(a, ks, st); break;
+    case EPI_ADD: launch_dma<128, EPI_ADD>(a, ks, st); break;
+    case EPI_SWIGLU: launch_dma<128, EPI_SWIGLU>(a, ks, st); break;
   }
 }
 
-static int m32_splits(const GemmArgs& a) {
+static int dma_splits(const GemmArgs& a) {
   const int nkt = a.K / GB_K;
   const int tiles = ((a.M + 255) / 256) * (a.N / 128);
   int ks = 1;
@@ -538,7 +538,7 @@ static int m32_splits(const GemmArgs& a) {
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
                           hipStream_t st) {
   if (a.M >= 512 && a.N % 4 == 0) {
-    const int ks = m32_splits(a);
+    const int ks = dma_splits(a);
     if (ks > 1) {
       const dim3 grid(a.N / 128, (a.M + 255) / 256, ks);
       hipLaunchKernelGGL((k_gemm_dma<128, EPI_ADD, true>), grid, dim3(512), 0, st, a, a.K / ks);
@@ -569,10 +569,10 @@ void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
     // so a full grid is never split).
     const int mt = (a.M + 255) / 256;
     if (epi == EPI_SWIGLU && a.N % 192 == 0 && (mt * (a.N / 192)) % 256 == 0) {
-      launch_m32<192, EPI_SWIGLU>(a, 1, st);
+      launch_dma<192, EPI_SWIGLU>(a, 1, st);
       return;
     }
-    launch_m32_epi(epi, a, m32_splits(a), st);
+    launch_dma_epi(epi, a, dma_splits(a), st);
     return;
   }
   const int BM = a.M > 64 ? 128 : 64;
