@@ -440,36 +440,52 @@ bool gemm_shape_ok(int M, int N, int K) {
 // ---------------------------------------------------------------------------
 // Split-K reduce fused with the residual add and the next pre-norm: row t of
 // C (= the residual stream x) becomes x + sum_z work[z][t], and
-// hn[t] = bf16(RMSNorm(x[t]) * g).  One block per row, N/4 columns per pass.
-// The splits are summed in a fixed order (deterministic).
+// hn[t] = bf16(RMSNorm(x[t]) * g).  One block per row (N <= 1024).
+
+constexpr int SPLITK_MAX = 8;  // splits the fused reduce takes
 
 __global__ __launch_bounds__(256) void k_splitk_reduce_add_norm(GemmArgs a, int ks, const float* g,
                                                                 float eps, bf16_t* hn, int ldh) {
+  // N <= 1024: one float4 of the row per thread.  Every load (x, the splits,
+  // the gains) is issued before the first store, and the sums stay in
+  // registers for the norm pass: a load issued after a store waits for it
+  // (loads and stores retire through one in-order counter).  The splits are
+  // added in split order (deterministic).
   __shared__ float red[4];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, k = tid * 4;
   const size_t MN = (size_t)a.M * a.N;
   float* xr = reinterpret_cast<float*>(a.C) + (size_t)t * a.ldc;
-  float ss = 0.f;
-  for (int k = tid * 4; k < a.N; k += 1024) {
-    float4 v = *reinterpret_cast<const float4*>(xr + k);
-    for (int z = 0; z < ks; ++z) {
+  const bool act = k < a.N;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f), gg = x;
+  float q[SPLITK_MAX][4];
+  if (act) {
+    x = *reinterpret_cast<const float4*>(xr + k);
+    gg = *reinterpret_cast<const float4*>(g + k);
+#pragma unroll
+    for (int z = 0; z < SPLITK_MAX; ++z) {
+      if (z >= ks) break;
       const float4 p = *reinterpret_cast<const float4*>(a.work + z * MN + (size_t)t * a.N + k);
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
+      q[z][0] = p.x;
+      q[z][1] = p.y;
+      q[z][2] = p.z;
+      q[z][3] = p.w;
     }
-    *reinterpret_cast<float4*>(xr + k) = v;
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+    for (int z = 0; z < SPLITK_MAX; ++z) {
+      if (z >= ks) break;
+      x.x += q[z][0];
+      x.y += q[z][1];
+      x.z += q[z][2];
+      x.w += q[z][3];
+    }
+    *reinterpret_cast<float4*>(xr + k) = x;
   }
-  ss = block_sum<256>(ss, red);
+  const float ss = block_sum<256>(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w, red);
   const float inv = rsqrtf(ss / (float)a.N + eps);
-  for (int k = tid * 4; k < a.N; k += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + k);
-    const float4 gg = *reinterpret_cast<const float4*>(g + k);
+  if (act) {
     uint2 o;
-    o.x = f32_to_bf16(v.x * inv * gg.x) | (f32_to_bf16(v.y * inv * gg.y) << 16);
-    o.y = f32_to_bf16(v.z * inv * gg.z) | (f32_to_bf16(v.w * inv * gg.w) << 16);
+    o.x = f32_to_bf16(x.x * inv * gg.x) | (f32_to_bf16(x.y * inv * gg.y) << 16);
+    o.y = f32_to_bf16(x.z * inv * gg.z) | (f32_to_bf16(x.w * inv * gg.w) << 16);
     *reinterpret_cast<uint2*>(hn + (size_t)t * ldh + k) = o;
   }
 }
@@ -537,9 +553,9 @@ static int dma_splits(const GemmArgs& a) {
 
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
                           hipStream_t st) {
-  if (a.M >= 512 && a.N % 4 == 0) {
+  if (a.M >= 512 && a.N % 4 == 0 && a.N <= 1024) {
     const int ks = dma_splits(a);
-    if (ks > 1) {
+    if (ks > 1 && ks <= SPLITK_MAX) {
       const dim3 grid(a.N / 128, (a.M + 255) / 256, ks);
       hipLaunchKernelGGL((k_gemm_dma<128, EPI_ADD, true>), grid, dim3(512), 0, st, a, a.K / ks);
       hipLaunchKernelGGL(k_splitk_reduce_add_norm, dim3(a.M), dim3(256), 0, st, a, ks, g, eps, hn,
