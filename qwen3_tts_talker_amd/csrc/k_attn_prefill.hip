@@ -26,7 +26,8 @@
 // hold one query row, which is exactly the lane role of the B operand of the
 // value product, so P never leaves registers.  The key order inside a
 // 32-key score tile is permuted (tau below) so that each lane's 8 value
-// slots are 8 consecutive keys: one 16-byte LDS read of the transposed V.
+// slots are 8 consecutive keys, which two transposing LDS reads
+// (ds_read_b64_tr_b16) fetch from the key-major V tile.
 #include "kernels.h"
 
 namespace qtalk {
@@ -41,14 +42,6 @@ constexpr int G = 2;          // query heads per KV head
 // key (0..31) held by score-tile row m: m = a*8 + h*4 + b -> (a>>1)*16 + h*8 + (a&1)*4 + b
 __device__ __forceinline__ int tau(int m) {
   return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
-// Transposed V tile in LDS: hd row d holds the tile's 64 keys; the 8-key
-// groups of a row are XOR-swizzled so that both the transposing dword stores
-// (16 rows at once) and the 16-byte operand reads (32 rows at once) spread
-// over the banks.
-__device__ __forceinline__ int vt_index(int d, int key) {
-  return d * KT + (key ^ ((((d >> 3) ^ d) & 7) << 3));
 }
 
 }  // namespace pa
@@ -68,18 +61,20 @@ __device__ __forceinline__ float xor32_sum(float v) {
 template <int HD>
 __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   using namespace pa;
-  constexpr int KSTR = HD + 8;              // K row stride in LDS (halfs)
   constexpr int NKS = HD / 16;              // k-steps of the score product
   constexpr int NMT = HD / 32;              // hd tiles of the value product
   constexpr int CPR = HD / 8;               // 16-byte chunks per key row
-  constexpr int NLD = KT * CPR / NT;        // K chunks per thread per tile
-  constexpr int NLDV = KT / 2 * CPR / NT;   // V chunk pairs per thread per tile
-  static_assert(KT * CPR % NT == 0 && KT / 2 * CPR % NT == 0, "staging split");
-  constexpr int LDS_HALFS = KT * KSTR + HD * KT;
-  __shared__ __attribute__((aligned(16))) f16_t lds[LDS_HALFS];
-  __shared__ __attribute__((aligned(16))) f16_t qlds[G * NKS * 64 * 8];  // q fragments
-  f16_t* Ks = lds;
-  f16_t* Vt = lds + KT * KSTR;
+  constexpr int RPI = 64 / CPR;             // key rows per 1 KiB load instruction
+  constexpr int NLI = KT / RPI / NWV;       // load instructions per wave, tile and operand
+  static_assert((HD == 128 || HD == 64) && KT % (RPI * NWV) == 0, "staging split");
+  // two tile buffers (tile kt in buffer kt & 1), each K rows then V rows,
+  // key-major, 16-byte chunk c of key row k stored in slot c ^ (k % CPR); the
+  // q fragments pass through buffer 1 before the key loop
+  constexpr int TILE = 2 * KT * HD;  // halfs per buffer
+  constexpr int LDS_HALFS = 2 * TILE;
+  static_assert(G * NKS * 64 * 8 <= TILE, "q fragments fit one buffer");
+  __shared__ __attribute__((aligned(1024))) f16_t lds[LDS_HALFS];
+  f16_t* const qlds = lds + TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nkv = a.n_kv_heads;
@@ -158,88 +153,23 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
     }
   }
 
-  // staging, per 64-key tile, in two register stages (tile kt in stage kt & 1,
-  // requested two tiles ahead of its use).  K: chunk i of this thread is key
-  // (tid + NT*i) / CPR, column chunk (tid + NT*i) % CPR (16 lanes cover one
-  // 256-byte key row).  V: the same chunk of two adjacent keys, so that the
-  // transposed store writes whole dwords (keys 2kp, 2kp+1 of one hd row).
-  // Offsets are fixed per thread; only the tile base moves.  Named registers:
-  // an array here would be left in private memory.
-  static_assert(NLD == 4 || NLD == 2, "K chunks per thread");
-  static_assert(NLDV == 2 || NLDV == 1, "V pairs per thread");
-  const int kkey0 = tid / CPR, kc0 = tid % CPR;  // chunk i: key kkey0 + i*(NT/CPR)
-  constexpr int KSTEP = NT / CPR;
-  const int vkey0 = 2 * (tid / CPR);             // pair i: keys vkey0 + i*2*KSTEP, +1
-  uint4 s0k0, s0k1, s0k2, s0k3, s0v0, s0v1, s0v2, s0v3;  // stage 0
-  uint4 s1k0, s1k1, s1k2, s1k3, s1v0, s1v1, s1v2, s1v3;  // stage 1
-  // Loads read a clamped key row (always in bounds) and run unconditionally;
-  // keys past the block's last position are zeroed when the stage is stored.
-  // (A conditional load would make the compiler drain every outstanding load
-  // at the join, the prefetch of the other stage included.)
-#define QA_LD(BASE, KEY) \
-  (*reinterpret_cast<const uint4*>((BASE) + (size_t)min((KEY), kend - 1) * HD + kc0 * 8))
-#define QA_GLOAD(S, KT)                                          \
-  do {                                                           \
-    const int kb_ = (KT) * KT_;                                  \
-    S##k0 = QA_LD(Kg, kb_ + kkey0);                              \
-    S##k1 = QA_LD(Kg, kb_ + kkey0 + KSTEP);                      \
-    if (NLD == 4) {                                              \
-      S##k2 = QA_LD(Kg, kb_ + kkey0 + 2 * KSTEP);                \
-      S##k3 = QA_LD(Kg, kb_ + kkey0 + 3 * KSTEP);                \
-    }                                                            \
-    S##v0 = QA_LD(Vg, kb_ + vkey0);                              \
-    S##v1 = QA_LD(Vg, kb_ + vkey0 + 1);                          \
-    if (NLDV == 2) {                                             \
-      S##v2 = QA_LD(Vg, kb_ + vkey0 + 2 * KSTEP);                \
-      S##v3 = QA_LD(Vg, kb_ + vkey0 + 2 * KSTEP + 1);            \
-    }                                                            \
+  // staging: tiles go from the cache straight into LDS (global_load_lds_dwordx4,
+  // no registers, no LDS store instructions).  Load instruction i of wave w
+  // covers key rows RPI (w * NLI + i) .. +RPI-1 of the tile; lane l takes row
+  // l / CPR and global chunk (l % CPR) ^ (row % CPR), so the rows land
+  // swizzled.  Rows are clamped to the block's last key (always in bounds;
+  // keys past it are masked in the scores, and their P is 0 against finite V).
+  const int srow = lane / CPR, sslot = lane % CPR;
+#define QA_ISSUE(KT_, BUF)                                                                \
+  do {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                     \
+      const int r0_ = RPI * (wave * NLI + i), key_ = r0_ + srow;                          \
+      const size_t g_ = (size_t)min((KT_) * KT + key_, kend - 1) * HD + (sslot ^ (key_ & (CPR - 1))) * 8; \
+      f16_t* const l_ = lds + (BUF) * TILE + r0_ * HD;                                    \
+      lds_load16(Kg + g_, l_);                                                            \
+      lds_load16(Vg + g_, l_ + KT * HD);                                                  \
+    }                                                                                     \
   } while (0)
-#define QA_LSTORE_M(S, KT, MASK)                                           \
-  do {                                                                     \
-    const int kb_ = (KT) * KT_;                                            \
-    store_k(0, kb_, S##k0, MASK);                                          \
-    store_k(1, kb_, S##k1, MASK);                                          \
-    if (NLD == 4) {                                                        \
-      store_k(2, kb_, S##k2, MASK);                                        \
-      store_k(3, kb_, S##k3, MASK);                                        \
-    }                                                                      \
-    store_v(0, kb_, S##v0, S##v1, MASK);                                   \
-    if (NLDV == 2) store_v(1, kb_, S##v2, S##v3, MASK);                    \
-  } while (0)
-  // only the tile holding the block's last key needs its tail zeroed
-#define QA_LSTORE(S, KT)                                                   \
-  do {                                                                     \
-    if (((KT) + 1) * KT_ <= kend) QA_LSTORE_M(S, KT, false);               \
-    else QA_LSTORE_M(S, KT, true);                                         \
-  } while (0)
-  constexpr int KT_ = KT;
-  f16_t* const kst = &Ks[kkey0 * KSTR + kc0 * 8];
-  auto zero_past = [&](const uint4& r, int key, bool mask) {
-    if (!mask) return r;
-    const bool ok = key < kend;
-    return make_uint4(ok ? r.x : 0u, ok ? r.y : 0u, ok ? r.z : 0u, ok ? r.w : 0u);
-  };
-  auto store_k = [&](int i, int kb, const uint4& r, bool mask) {
-    *reinterpret_cast<uint4*>(kst + i * KSTEP * KSTR) = zero_past(r, kb + kkey0 + i * KSTEP, mask);
-  };
-  // transposed V: hd row d = kc0*8 + e; its swizzle (((d >> 3) ^ d) & 7) is
-  // (kc0 ^ e) & 7, so the 8 row addresses of a pair differ only in e
-  // (one byte permute per dword: halves e of key and key + 1)
-  auto store_v = [&](int i, int kb, const uint4& q0, const uint4& q1, bool mask) {
-    const int key = vkey0 + i * 2 * KSTEP;
-    const uint4 r0 = zero_past(q0, kb + key, mask), r1 = zero_past(q1, kb + key + 1, mask);
-    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-    const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // bytes 0-3 select from w0[e/2], 4-7 from w1[e/2]: low half of each for
-      // even e, high half for odd e
-      const uint32_t dw = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1],
-                                                (e & 1) ? 0x07060302u : 0x05040100u);
-      const int d = kc0 * 8 + e;
-      *reinterpret_cast<uint32_t*>(&Vt[d * KT + (key ^ (((kc0 ^ e) & 7) << 3))]) = dw;
-    }
-  };
 
   f32x16_t o[NMT];
 #pragma unroll
@@ -250,16 +180,35 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   // wave's 32-key half
   const int krow = kh * 32 + tau(n);
   f16x8_t qf[NKS];
+  // operand reads are inline asm with explicit waits: the compiler would wait
+  // for every outstanding direct-to-LDS load (the next tile's) before a read.
+  // K fragment of step ks: row krow, chunk 2 ks + h (swizzled).  V^T fragment
+  // (hd rows mt*32 + n, keys kk .. kk+7, kk = kh*32 + sk*16 + h*8) from the
+  // key-major V rows by two ds_read_b64_tr_b16: in each 16-lane group lane
+  // 4e + q of the group supplies 4 consecutive dims (4q ..) of key e, and lane
+  // j receives dim j of keys 0..3 (then 4..7 from the second read).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int gq = lane >> 4, rq = lane & 15;
+  // this lane's V source: key (gq >> 1) * 8 + (rq >> 2) of the 16-key step,
+  // dims (gq & 1) * 16 + (rq & 3) * 4 of the 32-dim tile
+  const int vkey = (gq >> 1) * 8 + (rq >> 2), vdim = (gq & 1) * 16 + (rq & 3) * 4;
 
   auto compute = [&](int kt) {
     const int kbase = kt * KT + kh * 32;  // this wave's first key
     if (kbase > last) return;
-    f32x16_t s = f32x16_t{};
+    const uint32_t kb = lds_base + (uint32_t)((kt & 1) * TILE) * 2;
+    f16x8_t kf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[krow * KSTR + ks * 16 + h * 8]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s, 0, 0, 0);
+      const uint32_t a_ = kb + (uint32_t)(krow * HD + (((2 * ks + h) ^ (krow & (CPR - 1))) * 8)) * 2;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(kf[ks]) : "v"(a_));
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kf[ks]));
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s, 0, 0, 0);
     // causal mask (key <= position) where the half reaches the block's rows
     if (kbase + 31 > P0) {
 #pragma unroll
@@ -277,6 +226,20 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
     mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
     if (m_new == -INFINITY) return;  // no key of this half is visible to any row yet
+    // V^T fragments of both 16-key steps, all 4 hd tiles
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    s16x4_t vr[2][NMT][2];
+    const uint32_t vb = kb + (uint32_t)(KT * HD) * 2;
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int key = kh * 32 + sk * 16 + vkey + hf * 4, dim = mt * 32 + vdim;
+          const uint32_t a_ = vb + (uint32_t)(key * HD + (((dim >> 3) ^ (key & (CPR - 1))) << 3) + (dim & 7)) * 2;
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[sk][mt][hf]) : "v"(a_));
+        }
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
@@ -294,45 +257,48 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) asm volatile("" : "+v"(vr[sk][mt][hf]));
     // O^T += V^T P^T over this half's 32 keys (2 k-steps of 16)
 #pragma unroll
     for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(
-            &Vt[vt_index(mt * 32 + n, kh * 32 + sk * 16 + h * 8)]);
+        const s16x4_t lo = vr[sk][mt][0], hi = vr[sk][mt][1];
+        const s16x4_t v8a = lo, v8b = hi;
+        f16x8_t vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[e] = __builtin_bit_cast(f16_t, (short)v8a[e]);
+          vf[e + 4] = __builtin_bit_cast(f16_t, (short)v8b[e]);
+        }
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sk], o[mt], 0, 0, 0);
       }
   };
 
-  // loads run unconditionally (past the last tile they repeat it) so both
-  // register stages stay in registers
-  QA_GLOAD(s0, 0);
-  QA_GLOAD(s1, min(1, nkt - 1));
-  QA_LSTORE(s0, 0);
-  __syncthreads();
+  // key loop: one tile in flight.  Each iteration waits for its own loads of
+  // tile kt, then the raw barrier (not __syncthreads, which would also wait
+  // for loads just issued) makes every wave's part of tile kt visible and
+  // frees the other buffer, whose next tile is requested before the products.
+  QA_ISSUE(0, 0);
+  __syncthreads();  // q fragments (buffer 1) written
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
-  for (int kt = 0; kt < nkt; kt += 2) {
-    // tile kt in LDS, tile kt + 1 in flight in stage 1
-    QA_GLOAD(s0, min(kt + 2, nkt - 1));
+  for (int kt = 0; kt < nkt; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nkt) QA_ISSUE(kt + 1, (kt + 1) & 1);
     compute(kt);
-    __syncthreads();
-    if (kt + 1 >= nkt) break;
-    QA_LSTORE(s1, kt + 1);
-    __syncthreads();
-    // tile kt + 1 in LDS, tile kt + 2 in flight in stage 0
-    QA_GLOAD(s1, min(kt + 3, nkt - 1));
-    compute(kt + 1);
-    __syncthreads();
-    if (kt + 2 >= nkt) break;
-    QA_LSTORE(s0, kt + 2);
-    __syncthreads();
   }
-#undef QA_LD
-#undef QA_GLOAD
-#undef QA_LSTORE
+#undef QA_ISSUE
+  __syncthreads();
 
   // merge the two key halves of each query head through LDS (the tiles are
   // no longer needed): the key-half-1 wave hands over (m, l, O), the key-half-0

@@ -163,13 +163,6 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
 // BN = 192 gives the 6144-wide gate|up projection exactly 256 tiles at
 // M = 2048 (two stages fit LDS there, three at BN = 128).
 
-// one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
-// (lds uniform across the wave).  A helper function, not a lambda: a lambda
-// holding this builtin makes the host pass drop the kernel's launch stub.
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
 template <int BN>
 struct DmaCfg {
   static constexpr int NS = BN == 128 ? 3 : 2;          // LDS stages
