@@ -11,7 +11,7 @@ import pytest
 from oracle import TalkerOracle
 from oracle.talker import code_predictor_frame
 from oracle.frame import embed_sum, suppressed_argmax
-from synth import prefill_embeddings, step_embedding, workload, batch_lengths
+from synth import prefill_embeddings, step_embedding, workload, batch_lengths, make_weights
 from synth import embedding_tables, overlay_row
 from tests.helpers import argmax_in_band, argmax_ok, dev, host, rel_err, say, weights_for
 
@@ -138,6 +138,25 @@ def test_prefill_attention_many_tiles_ragged_extend_to_capacity():
 
 
 # -- path invariants on the GPU -----------------------------------------------
+
+
+def test_prefill_attention_head_dim_64():
+    # the matrix-core prefill attention at head_dim 64 (two query heads per KV
+    # head): the tiny geometry with bf16 weights and a float16 cache; 200 rows
+    # (7 position blocks, a ragged tail, 4 key tiles), extended by 50
+    shape = workload("tiny_f32_2l").with_(weight_dtype="bf16", kv_dtype="f16", cap=256)
+    w = make_weights(shape)
+    say("[case] tiny geometry, head_dim 64, f16 cache, prefill 200 + extend 50")
+    orc = TalkerOracle(shape, w)
+    emb = prefill_embeddings(shape, 250)
+    ref, _ = orc.prefill(0, emb, all_rows=True)
+    tk = _talker(shape, w)
+    la = host(tk.prefill(0, dev(emb[:200])))
+    assert rel_err(la, ref[199]) <= TOL_BF16
+    lb = host(tk.extend(0, dev(emb[200:])))
+    assert rel_err(lb, ref[249]) <= TOL_BF16
+    assert tk.kv_len(0) == 250
+    _check_kv(tk, orc, shape, TOL_BF16)
 
 
 def test_prefill_equals_prefill_then_decode_bitwise_on_matrix_vector_path(monkeypatch):
