@@ -109,14 +109,6 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// one 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l's
-// bytes land at lds + 16 l (lds uniform across the wave).  A helper function,
-// not a lambda: a lambda holding this builtin makes the host pass drop the
-// kernel's launch stub.
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16 bytes of weights -> floats

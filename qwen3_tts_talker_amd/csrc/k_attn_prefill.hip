@@ -29,6 +29,7 @@
 // slots are 8 consecutive keys, which two transposing LDS reads
 // (ds_read_b64_tr_b16) fetch from the key-major V tile.
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace qtalk {
 namespace pa {

@@ -11,6 +11,7 @@
 // K over blockIdx.z into a float32 workspace that a second kernel sums in a
 // fixed order (deterministic), applying the epilogue there.
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace qtalk {
 
