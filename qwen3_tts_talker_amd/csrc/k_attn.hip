@@ -191,7 +191,56 @@ static void launch_qk_hd(KvKind kv, const QkArgs& a, const dim3& grid, hipStream
   else hipLaunchKernelGGL((k_qk_rope_append<HD, float>), grid, dim3(256), 0, st, a);
 }
 
+// K/V append only (q left to the matrix-core attention), float16 cache,
+// head_dim 128: 16 lanes per (row, head) unit, lane i holding dims 4i..4i+3
+// and their NEOX partners 64+4i..; all loads of a lane (x, gains, rotations)
+// go out before its two 8-byte stores.  Units: row t, head hh < n_kv (K,
+// RMSNorm + RoPE) or the V head hh - n_kv (as is).
+__global__ __launch_bounds__(256) void k_kv_append_f16_128(QkArgs a) {
+  const int nkv = a.n_kv_heads, nh = 2 * nkv;
+  const int unit = blockIdx.x * 16 + (threadIdx.x >> 4), i = threadIdx.x & 15;
+  if (unit >= a.rows.n * nh) return;  // whole 16-lane groups: only row16 reductions below
+  const int t = unit / nh, hh = unit % nh;
+  const bool is_k = hh < nkv;
+  const int kvh = is_k ? hh : hh - nkv;
+  const float* x = a.qkv + (size_t)t * a.ldqkv + (size_t)(a.n_heads + hh) * 128;
+  const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
+  float4 x1 = *reinterpret_cast<const float4*>(x + 4 * i);
+  float4 x2 = *reinterpret_cast<const float4*>(x + 64 + 4 * i);
+  if (is_k) {
+    const float4 g1 = *reinterpret_cast<const float4*>(a.g_k + 4 * i);
+    const float4 g2 = *reinterpret_cast<const float4*>(a.g_k + 64 + 4 * i);
+    const float4 c01 = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + 4 * i);
+    const float4 c23 = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + 4 * i + 2);
+    float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
+    ss += x2.x * x2.x + x2.y * x2.y + x2.z * x2.z + x2.w * x2.w;
+    ss = row16_sum(ss);
+    const float inv = rsqrtf(ss / 128.0f + a.eps);
+    const float a1[4] = {x1.x * inv * g1.x, x1.y * inv * g1.y, x1.z * inv * g1.z, x1.w * inv * g1.w};
+    const float a2[4] = {x2.x * inv * g2.x, x2.y * inv * g2.y, x2.z * inv * g2.z, x2.w * inv * g2.w};
+    const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+    float y1[4], y2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y1[e] = a1[e] * c[e] - a2[e] * sn[e];
+      y2[e] = a2[e] * c[e] + a1[e] * sn[e];
+    }
+    x1 = make_float4(y1[0], y1[1], y1[2], y1[3]);
+    x2 = make_float4(y2[0], y2[1], y2[2], y2[3]);
+  }
+  f16_t* row = reinterpret_cast<f16_t*>(is_k ? a.kc : a.vc) + ((size_t)(seq * nkv + kvh) * a.cap + pos) * 128;
+  typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
+  const f16x4_t o1 = {(f16_t)x1.x, (f16_t)x1.y, (f16_t)x1.z, (f16_t)x1.w};
+  const f16x4_t o2 = {(f16_t)x2.x, (f16_t)x2.y, (f16_t)x2.z, (f16_t)x2.w};
+  *reinterpret_cast<f16x4_t*>(row + 4 * i) = o1;
+  *reinterpret_cast<f16x4_t*>(row + 64 + 4 * i) = o2;
+}
+
 void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
+  if (kv == KV_F16 && a.skip_q && a.head_dim == 128) {
+    hipLaunchKernelGGL(k_kv_append_f16_128, dim3((a.rows.n * 2 * a.n_kv_heads + 15) / 16), dim3(256), 0, st, a);
+    return;
+  }
   const int nh = (a.skip_q ? 0 : a.n_heads) + 2 * a.n_kv_heads;
   const dim3 grid((a.rows.n * nh + 3) / 4);
   if (a.head_dim == 128) launch_qk_hd<128>(kv, a, grid, st);
