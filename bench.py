@@ -194,19 +194,23 @@ def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
     st = torch.cuda.current_stream()
 
     def frame(i):
+        # each pick also fetches the table row the next call feeds on
+        # (qtalk_argmax_embed), so no separate lookup kernel runs
         a, b = ids[i % 2], ids[(i + 1) % 2]
         talker.embed_sum(tabs, a.view(16, 1), ov, out=emb)
         qtalk.qtalk_decode(talker.ctx, 0, emb, lg_t, cp_in[0])
-        talker.argmax(lg_t, suppress_begin=V - 1024, keep_id=EOS, out=b[0:1])
-        cp.embed_sum(tabs[0:1], b[0:1].view(1, 1), out=cp_in[1:2])
+        talker.argmax_embed(lg_t, tabs[0], suppress_begin=V - 1024, keep_id=EOS, out=b[0:1],
+                            out_rows=cp_in[1:2])
         cp.select_head(0)
         qtalk.qtalk_prefill(cp.ctx, 0, cp_in, 2, lg_c[0])
-        cp.argmax(lg_c[0], out=b[1:2])
+        cp.argmax_embed(lg_c[0], tabs[1], out=b[1:2], out_rows=steps[1])
         for j in range(1, 15):
-            cp.embed_sum(tabs[j:j + 1], b[j:j + 1].view(1, 1), out=steps[j])
             cp.select_head(j)
             qtalk.qtalk_decode(cp.ctx, 0, steps[j], lg_c[j])
-            cp.argmax(lg_c[j], out=b[j + 1:j + 2])
+            if j < 14:
+                cp.argmax_embed(lg_c[j], tabs[j + 1], out=b[j + 1:j + 2], out_rows=steps[j + 1])
+            else:
+                cp.argmax(lg_c[j], out=b[j + 1:j + 2])
 
     for i in range(warmup):
         frame(i)

@@ -221,6 +221,21 @@ qtalk_status qtalk_argmax(qtalk_ctx *ctx, const float *logits, int32_t n,
                           int32_t vocab, int32_t suppress_begin,
                           int32_t keep_id, int32_t *out_ids);
 
+/* qtalk_argmax and the row lookup that feeds the next code predictor step,
+ * in one kernel: for each of the n logits rows, the pick (same suppression,
+ * tie and NaN rules as qtalk_argmax) goes to out_ids[i], and row out_ids[i]
+ * of table ([table_rows][hidden] DEVICE float32, hidden of the context) to
+ * out_rows[i] ([n][hidden] DEVICE float32): step j's input is the embedding
+ * of code j - 1 ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+ * forward_code_pred_step_cached).  A row whose pick is -1 or not below
+ * table_rows gets a NaN row, and the next qtalk_sync returns QTALK_E_DEVICE.
+ * Errors: QTALK_E_INVAL (null pointer; n, vocab or table_rows < 1). */
+qtalk_status qtalk_argmax_embed(qtalk_ctx *ctx, const float *logits,
+                                int32_t n, int32_t vocab,
+                                int32_t suppress_begin, int32_t keep_id,
+                                const float *table, int32_t table_rows,
+                                int32_t *out_ids, float *out_rows);
+
 /* Choose which of the n_output_heads stacked output projections produces
  * the logits of the calls enqueued after this one (initially head 0).  The
  * code predictor, a second decoder of the same block structure, reads step

@@ -7,7 +7,10 @@
 //    src/pipeline/tts_transformer.rs", build_talker_step_embedding);
 //  * k_argmax: the greedy pick of each logits row with ids from
 //    suppress_begin up excluded except keep_id (the codebook-0 suppression
-//    before select_token in the same file), lowest index among equal maxima.
+//    before select_token in the same file), lowest index among equal maxima;
+//    optionally also the table row of the pick, the code predictor's next
+//    input (forward_code_pred_step_cached in the same file embeds the
+//    previous code).
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -103,7 +106,22 @@ __global__ __launch_bounds__(256) void k_argmax(ArgmaxArgs a) {
         bi = si[w];
       }
     // no candidate at all (suppress_begin <= 0 and keep_id outside the row)
-    a.out[row] = bi == INT_MAX ? -1 : bi;
+    bi = bi == INT_MAX ? -1 : bi;
+    a.out[row] = bi;
+    si[0] = bi;
+  }
+  if (!a.table) return;
+  // the next step's input: row `pick` of the table (NaN and status 5 when
+  // there is none)
+  __syncthreads();
+  const int pick = si[0];
+  const bool bad = pick < 0 || pick >= a.table_rows;
+  if (bad && tid == 0) *a.status = 5;
+  const float nan = __int_as_float(0x7fc00000);
+  for (int c = tid * 4; c < a.hidden; c += 1024) {
+    const float4 r = bad ? make_float4(nan, nan, nan, nan)
+                         : *reinterpret_cast<const float4*>(a.table + (size_t)pick * a.hidden + c);
+    *reinterpret_cast<float4*>(a.rows_out + (size_t)row * a.hidden + c) = r;
   }
 }
 

@@ -178,6 +178,11 @@ struct ArgmaxArgs {
   const float* logits;  // [n][vocab]
   int n, vocab, suppress_begin, keep_id;
   int32_t* out;         // [n]
+  // optional, the pick's row lookup: rows_out[i] = table[out[i]]
+  const float* table;   // [table_rows][hidden] or null
+  int table_rows, hidden;  // hidden % 4 == 0
+  float* rows_out;      // [n][hidden]
+  int* status;          // set to 5 when a pick has no table row
 };
 void launch_argmax(const ArgmaxArgs& a, hipStream_t st);
 

@@ -813,7 +813,21 @@ qtalk_status qtalk_argmax(qtalk_ctx* c, const float* logits, int32_t n, int32_t 
   c->err.clear();
   if (!logits || !out_ids) return fail(c, QTALK_E_INVAL, "logits and out_ids must not be null");
   if (n < 1 || vocab < 1) return fail(c, QTALK_E_INVAL, "n and vocab must be >= 1");
-  ArgmaxArgs a{logits, n, vocab, suppress_begin, keep_id, out_ids};
+  ArgmaxArgs a{logits, n, vocab, suppress_begin, keep_id, out_ids, nullptr, 0, 0, nullptr, nullptr};
+  launch_argmax(a, c->stream);
+  return launch_status(c);
+}
+
+qtalk_status qtalk_argmax_embed(qtalk_ctx* c, const float* logits, int32_t n, int32_t vocab,
+                                int32_t suppress_begin, int32_t keep_id, const float* table,
+                                int32_t table_rows, int32_t* out_ids, float* out_rows) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (!logits || !out_ids || !table || !out_rows)
+    return fail(c, QTALK_E_INVAL, "logits, table, out_ids and out_rows must not be null");
+  if (n < 1 || vocab < 1 || table_rows < 1) return fail(c, QTALK_E_INVAL, "n, vocab and table_rows must be >= 1");
+  ArgmaxArgs a{logits, n, vocab, suppress_begin, keep_id, out_ids,
+               table, table_rows, c->cfg.hidden, out_rows, c->aux_err};
   launch_argmax(a, c->stream);
   return launch_status(c);
 }

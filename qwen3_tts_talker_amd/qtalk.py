@@ -27,7 +27,7 @@ QTALK_F32, QTALK_BF16, QTALK_F16, QTALK_Q8 = 0, 1, 2, 3
 EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
            "qtalk_kv_len", "qtalk_kv_read", "qtalk_prefill_batch", "qtalk_embed_sum",
-           "qtalk_argmax",
+           "qtalk_argmax", "qtalk_argmax_embed",
            "qtalk_select_head", "qtalk_sync", "qtalk_last_error")
 
 
@@ -88,6 +88,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_embed_sum": (st, [P, I32, ctypes.POINTER(P), ctypes.POINTER(I32),
                                  P, I32, P, P]),
         "qtalk_argmax": (st, [P, P, I32, I32, I32, I32, P]),
+        "qtalk_argmax_embed": (st, [P, P, I32, I32, I32, I32, P, I32, P, P]),
         "qtalk_select_head": (st, [P, I32]),
         "qtalk_sync": (st, [P]),
         "qtalk_last_error": (ctypes.c_char_p, [P]),
@@ -202,6 +203,13 @@ def qtalk_embed_sum(ctx, tables, ids, overlay, out) -> int:
 def qtalk_argmax(ctx, logits, n, vocab, suppress_begin, keep_id, out_ids) -> int:
     return _check(ctx, load_library().qtalk_argmax(
         ctx, _ptr(logits), n, vocab, suppress_begin, keep_id, _iptr(out_ids)))
+
+
+def qtalk_argmax_embed(ctx, logits, n, vocab, suppress_begin, keep_id, table, table_rows,
+                       out_ids, out_rows) -> int:
+    return _check(ctx, load_library().qtalk_argmax_embed(
+        ctx, _ptr(logits), n, vocab, suppress_begin, keep_id, _ptr(table), table_rows,
+        _iptr(out_ids), _ptr(out_rows)))
 
 
 def qtalk_select_head(ctx, head) -> int:
@@ -358,6 +366,22 @@ class Talker:
         qtalk_argmax(self.ctx, lg, n, vocab,
                      vocab if suppress_begin is None else suppress_begin, keep_id, out)
         return out
+
+    def argmax_embed(self, logits, table, suppress_begin=None, keep_id=-1, out=None,
+                     out_rows=None):
+        """Greedy ids of logits ``[n][vocab]`` (as ``argmax``) and the
+        ``table`` rows of those ids; returns ``(ids [n] int32, rows [n][hidden])``."""
+        import torch
+        lg = logits if logits.dim() == 2 else logits.view(1, -1)
+        n, vocab = int(lg.shape[0]), int(lg.shape[1])
+        if out is None:
+            out = torch.empty(n, dtype=torch.int32, device="cuda")
+        if out_rows is None:
+            out_rows = torch.empty(n, self.shape.hidden, device="cuda")
+        qtalk_argmax_embed(self.ctx, lg, n, vocab,
+                           vocab if suppress_begin is None else suppress_begin, keep_id,
+                           table, int(table.shape[0]), out, out_rows)
+        return out, out_rows
 
     def sync(self):
         qtalk_sync(self.ctx)

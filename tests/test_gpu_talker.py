@@ -647,6 +647,35 @@ def test_argmax_equals_oracle():
     tk.close()
 
 
+def test_argmax_embed_equals_argmax_then_table_row():
+    # the fused pick + row lookup against the oracle's pick and a plain row
+    # read (bitwise); a pick past the table's rows gives a NaN row and an error
+    import torch
+    shape = workload("talker_1l_t128")
+    tk = _talker(shape, weights_for("talker_1l_t128"))
+    rng = np.random.default_rng(13)
+    V, H = 3072, shape.hidden
+    lg = rng.standard_normal((6, V)).astype(np.float32)
+    lg[0, 2500] = 40.0                  # suppressed spike
+    lg[1, 2150] = 40.0                  # the kept id
+    lg[2, [7, 900]] = 30.0              # tie: lowest index
+    lg[3, ::3] = np.nan                 # NaN never wins
+    table = rng.standard_normal((V, H)).astype(np.float32)
+    for sb, keep in ((V - 1024, 2150), (V, -1)):
+        ids, rows = tk.argmax_embed(dev(lg), dev(table), suppress_begin=sb, keep_id=keep)
+        want = [suppressed_argmax(r, sb, keep) for r in lg]
+        assert list(ids.cpu().numpy()) == want, (sb, keep)
+        assert np.array_equal(rows.cpu().numpy(), table[want]), (sb, keep)
+    tk.sync()
+    # codes 0..99 only: the pick 2150 of row 1 has no row
+    ids, rows = tk.argmax_embed(dev(lg[1:2]), dev(table[:100]), suppress_begin=V - 1024, keep_id=2150)
+    with pytest.raises(RuntimeError):
+        tk.sync()
+    assert int(ids.cpu().numpy()[0]) == 2150
+    assert np.isnan(rows.cpu().numpy()).all()
+    tk.close()
+
+
 def _masked(lg, sb, keep):
     m = np.array(lg, dtype=np.float64)
     sup = np.arange(m.size) >= sb
