@@ -123,6 +123,48 @@ def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
     }
 
 
+def batched_decode(n_steps: int, warmup: int = 4) -> dict:
+    """Batched decode of 16 independent utterances on the 28-layer Talker
+    (its own seeded weights): KV lengths drawn uniformly from 512..4096, each
+    sequence filled by a prefill and 2048-row extends, then one token per
+    sequence and step (qtalk_decode_batch).  Algorithmic bytes per step:
+    every weight once plus K and V of every attended position."""
+    import torch
+    from qwen3_tts_talker_amd import Talker
+    from synth import batch_lengths, make_weights, prefill_embeddings, step_embedding, workload
+    shape = workload("talker_28l_batch16_ragged")
+    tk = Talker(shape, make_weights(shape))
+    lens = [int(x) for x in batch_lengths(shape)]
+    for s, L in enumerate(lens):
+        e = torch.from_numpy(prefill_embeddings(shape, L, seq=s)).cuda()
+        tk.prefill(s, e[:shape.chunk])
+        for c0 in range(shape.chunk, L, shape.chunk):
+            tk.extend(s, e[c0:c0 + shape.chunk])
+    seqs = list(range(shape.n_seqs))
+    embs = [torch.from_numpy(np.stack([step_embedding(shape, k, seq=s) for s in seqs])).cuda()
+            for k in range(warmup + n_steps)]
+    for k in range(warmup):
+        tk.decode_batch(seqs, embs[k])
+    tk.sync()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for k in range(n_steps):
+        tk.decode_batch(seqs, embs[warmup + k])
+    e1.record(st)
+    torch.cuda.synchronize()
+    tk.sync()
+    us = e0.elapsed_time(e1) * 1e3 / n_steps
+    ctx = [L + warmup for L in lens]  # context of the first timed step
+    kv_pos = sum(c + 1 for c in ctx) + len(seqs) * (n_steps - 1) / 2
+    nbytes = 887_095_296 + 114_688 * kv_pos
+    tk.close()
+    return {"workload": "talker_28l_batch16_ragged", "seqs": len(seqs), "kv_len_range": [min(lens), max(lens)],
+            "steps": n_steps, "step_us": round(us, 1), "tok_s": round(len(seqs) * 1e6 / us, 1),
+            "bytes_per_step": int(nbytes), "achieved_gbs": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / 8000.0, 4)}
+
+
 def batched_prefill(shape, weights, n: int, T: int, reps: int = 5) -> dict:
     """Batched prefill of n utterances of T rows each (one call) against n
     consecutive single prefills, on a context with n sequences."""
@@ -303,6 +345,8 @@ def main(argv=None):
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--batch-prefill", type=int, default=16,
                     help="utterances of 128 rows in the batched-prefill leg (0: skip)")
+    ap.add_argument("--batch-decode", type=int, default=32,
+                    help="timed steps of the 16-utterance batched decode leg (0: skip)")
     ap.add_argument("--cp-frames", type=int, default=20,
                     help="code predictor frames timed after the Talker (0: skip)")
     ap.add_argument("--pmc-calibration-mib", type=int, default=0,
@@ -425,6 +469,8 @@ def main(argv=None):
     tk.close()
     if args.batch_prefill > 0:
         out["prefill_batch"] = batched_prefill(shape, weights, args.batch_prefill, 128)
+    if args.batch_decode > 0:
+        out["decode_batch"] = batched_decode(args.batch_decode)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)

@@ -154,18 +154,23 @@ static void launch_nr(Epilogue epi, const GemvArgs& a, hipStream_t st) {
   }
 }
 
+// Each pass streams the whole weight matrix once for up to 8 rows (4 when
+// 8 rows of x would not fit 64 KiB of LDS), so a batch of n rows reads the
+// weights ceil(n / rows per pass) times.
 template <typename WT>
 static void launch_t(Epilogue epi, GemvArgs a, hipStream_t st) {
   const int n = a.nrows;
-  for (int r0 = 0; r0 < n; r0 += 4) {
+  const int per = (size_t)8 * a.K * sizeof(float) <= 65536 ? 8 : 4;
+  for (int r0 = 0; r0 < n; r0 += per) {
     GemvArgs g = a;
     g.X = a.X + (size_t)r0 * a.ldx;
     g.Y = a.Y + (size_t)r0 * a.ldy;
     g.norm_out = a.norm_out ? a.norm_out + (size_t)r0 * a.ld_norm : nullptr;
-    g.nrows = n - r0 < 4 ? n - r0 : 4;
+    g.nrows = n - r0 < per ? n - r0 : per;
     if (g.nrows == 1) launch_nr<WT, 1>(epi, g, st);
     else if (g.nrows == 2) launch_nr<WT, 2>(epi, g, st);
-    else launch_nr<WT, 4>(epi, g, st);
+    else if (g.nrows <= 4) launch_nr<WT, 4>(epi, g, st);
+    else launch_nr<WT, 8>(epi, g, st);
   }
 }
 
