@@ -38,16 +38,18 @@ reason in the design notes of the repository):
 * RMSNorm is ``x / sqrt(mean(x^2) + eps) * g`` (gain applied as is);
 * NEOX RoPE rotates the pairs ``(x_i, x_{i + hd/2})`` by ``pos * theta^(-2i/hd)``;
 * the query head ``h`` reads KV head ``h // (n_heads / n_kv_heads)``;
-* attention reads the cache after the write, so K and V pass through the
-  cache's storage type (float16 rounding for f16 caches) before use, in
-  prefill and decode alike;
+* attention reads an f32 or f16 cache after the write, so K and V pass
+  through the cache's storage type (float16 rounding for f16 caches) before
+  use, in prefill and decode alike;
 * float16 rounding of the cache is round-to-nearest-even of the float32 value;
 * an 8-bit (Q8_0) cache stores blocks of 32 values along head_dim as int8
-  codes and a float16 scale, and attention reads the dequantised values for
-  every position, the current ones included (the same read-after-write
-  order as the other caches; the pages' Q8 path attends to the current
-  rows' unquantised values, which would make a prefill differ from the same
-  rows decoded one by one).
+  codes and a float16 scale; attention reads the positions written by
+  earlier calls dequantised from the cache and the call's own rows
+  unquantised ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+  ``forward_step_cached``: the cached prefix cast back to F32 and joined
+  with the current k/v; ``forward_prefill_cached``: attention on the fresh
+  k/v).  A q8 prefill therefore differs from the same rows decoded one by
+  one, through the quantisation of the rows the decode reads back.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force and independent library routines.
@@ -266,12 +268,39 @@ class TalkerOracle:
             k.transpose(1, 0, 2), s.kv_dtype, self.dtype)
         self.vc[seq][l, :, p0:p0 + T, :] = round_kv(
             v.transpose(1, 0, 2), s.kv_dtype, self.dtype)
-        o = causal_gqa_attention(q, self.kc[seq][l], self.vc[seq][l], pos,
-                                 self.scale)
+        ka, va = self.attended_kv(l, seq, p0, k, v)
+        o = causal_gqa_attention(q, ka, va, pos, self.scale)
         x = x + o.reshape(T, s.q_dim) @ w["wo"].T
         h2 = rms_norm(x, w["g_post"], s.rms_eps)
         a = swiglu(h2 @ w["wg"].T, h2 @ w["wu"].T)
         return x + a @ w["wd"].T
+
+    def attended_kv(self, l: int, seq: int, p0: int, k: np.ndarray,
+                    v: np.ndarray):
+        """Keys and values ``[n_kv][p0 + T][hd]`` that the attention of the
+        rows at ``p0 .. p0+T-1`` reads, once their ``k``/``v`` (``[T][n_kv][hd]``)
+        are in the cache.
+
+        f32 and f16 caches: the cache itself (read after write).  q8 cache:
+        positions ``< p0`` dequantised from the cache and the call's own rows
+        as computed, unquantised ("rightkit-qts 0.2.3
+        src/pipeline/tts_transformer.rs", ``forward_step_cached``,
+        ``TalkerKvStorage::TurboQuantQ8_0`` arm: the prefix view of the
+        cache cast to F32, concatenated with ``k_cur``/``v_cur``;
+        ``forward_prefill_cached`` attends to ``k_cur``/``v_cur``).  The
+        pages give no chunked q8 extend; it is read the same way (prefix
+        from the cache, the chunk's rows fresh), which holds decode at
+        ``T = 1`` and prefill at ``p0 = 0``.
+        """
+        T = k.shape[0]
+        kc, vc = self.kc[seq][l], self.vc[seq][l]
+        if self.s.kv_dtype != "q8":
+            return kc[:, :p0 + T], vc[:, :p0 + T]
+        ka = kc[:, :p0 + T].copy()
+        va = vc[:, :p0 + T].copy()
+        ka[:, p0:] = k.transpose(1, 0, 2)
+        va[:, p0:] = v.transpose(1, 0, 2)
+        return ka, va
 
     def select_head(self, i: int) -> None:
         """Form the logits of the following calls with stacked head ``i``."""
@@ -344,11 +373,12 @@ class TalkerOracle:
         self.kc[seq][0, :, p0:p0 + T, :] = round_kv(k.transpose(1, 0, 2), s.kv_dtype, self.dtype)
         self.vc[seq][0, :, p0:p0 + T, :] = round_kv(v.transpose(1, 0, 2), s.kv_dtype, self.dtype)
         self.cur_len[seq] = p0 + T
+        ka, va = self.attended_kv(0, seq, p0, k, v)
         r = np.asarray(list(rows), dtype=np.int64)
         hr = h[r]
         q = (hr @ w["wq"].T).reshape(len(r), s.n_heads, s.head_dim)
         q = rope_neox(rms_norm(q, w["g_q"], s.rms_eps), pos[r][:, None], s.rope_theta)
-        o = causal_gqa_attention(q, self.kc[seq][0], self.vc[seq][0], pos[r], self.scale)
+        o = causal_gqa_attention(q, ka, va, pos[r], self.scale)
         xr = x[r] + o.reshape(len(r), s.q_dim) @ w["wo"].T
         h2 = rms_norm(xr, w["g_post"], s.rms_eps)
         xr = xr + swiglu(h2 @ w["wg"].T, h2 @ w["wu"].T) @ w["wd"].T

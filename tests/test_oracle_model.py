@@ -34,7 +34,7 @@ def scaled_weights(shape, wscale=0.15):
 
 # -- independent library model ---------------------------------------------------
 
-def _transformers_logits(shape, w, emb):
+def _transformers_model(shape, w):
     from transformers import Qwen3Config
     from transformers.models.qwen3.modeling_qwen3 import Qwen3Model
     cfg = Qwen3Config(
@@ -61,6 +61,11 @@ def _transformers_logits(shape, w, emb):
     sd["norm.weight"] = torch.from_numpy(w["g_final"].astype(np.float64))
     missing, unexpected = m.load_state_dict(sd, strict=False)
     assert set(missing) == {"embed_tokens.weight"} and not unexpected
+    return m
+
+
+def _transformers_logits(shape, w, emb):
+    m = _transformers_model(shape, w)
     with torch.no_grad():
         hs = m(inputs_embeds=torch.from_numpy(emb.astype(np.float64))[None],
                use_cache=False).last_hidden_state[0].numpy()
@@ -138,7 +143,7 @@ def test_first_position_attention_is_v_projection():
 
 # -- path invariants -------------------------------------------------------------
 
-@pytest.mark.parametrize("kv", ["f32", "f16", "q8"])
+@pytest.mark.parametrize("kv", ["f32", "f16"])
 def test_prefill_equals_prefill_then_decode(kv):
     shape = small_shape(kv_dtype=kv)
     w = scaled_weights(shape)
@@ -153,6 +158,80 @@ def test_prefill_equals_prefill_then_decode(kv):
         for which in (0, 1):
             np.testing.assert_allclose(b.kv(0, l, which), a.kv(0, l, which),
                                        rtol=1e-11, atol=1e-12)
+
+
+# -- the q8 cache: earlier positions quantised, the call's own rows fresh -------
+
+def _q8_round_trip(t):
+    """A cached K or V tensor [..., hd] replaced by its Q8_0 block round trip
+    (the cache content the next call reads)."""
+    a = t.numpy()
+    return torch.from_numpy(ot.q8_block_dequantize(
+        *ot.q8_block_quantize(a.astype(np.float32))).astype(np.float64).reshape(a.shape))
+
+
+def test_q8_prefill_matches_transformers_unquantised():
+    # a q8 prefill attends to its own rows unquantised, so every row equals
+    # the library model, which never rounds K or V (the quantisation error
+    # of Q8_0 is ~1/254 of a block's range, far above this tolerance)
+    shape = small_shape(kv_dtype="q8")
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 20)
+    ref = _transformers_logits(shape, w, emb)
+    logits, _ = TalkerOracle(shape, w).prefill(0, emb, all_rows=True)
+    err = np.abs(logits - ref).max() / np.abs(ref).max()
+    assert err < 2e-5, err
+
+
+def test_q8_decode_and_extend_match_transformers_over_a_quantised_prefix():
+    # transformers' own KV cache after a prefill of 12 rows, each layer's K
+    # and V replaced by their Q8_0 round trip, then (a) one decode row and
+    # (b) a 5-row extend through that cache: the library model joins the
+    # quantised prefix with the fresh rows of the call, as the q8 oracle does
+    from transformers import DynamicCache
+    shape = small_shape(kv_dtype="q8")
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 18)
+    m = _transformers_model(shape, w)
+    head = w["w_head"].astype(np.float64)
+    for rows in (emb[12:13], emb[12:17]):
+        cache = DynamicCache()
+        with torch.no_grad():
+            m(inputs_embeds=torch.from_numpy(emb[:12].astype(np.float64))[None],
+              past_key_values=cache, use_cache=True)
+            for lay in cache.layers:
+                lay.keys = _q8_round_trip(lay.keys)
+                lay.values = _q8_round_trip(lay.values)
+            hs = m(inputs_embeds=torch.from_numpy(rows.astype(np.float64))[None],
+                   past_key_values=cache, use_cache=True).last_hidden_state[0].numpy()
+        ref = hs @ head.T
+        orc = TalkerOracle(shape, w)
+        orc.prefill(0, emb[:12])
+        got, _ = orc.extend(0, rows, all_rows=True)
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        assert err < 2e-5, (len(rows), err)
+
+
+def test_q8_prefill_and_prefill_plus_decode_differ_only_through_the_prefix():
+    # prefill(T) attends to fresh rows; prefill(T-1) + decode reads rows
+    # 0..T-2 back quantised.  Rows 0..T-2 of every layer's cache, and row
+    # T-1 of layer 0 (a function of its own embedding only), are the same
+    # either way; the logits differ, by about the quantisation error.
+    shape = small_shape(kv_dtype="q8")
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 17)
+    a = TalkerOracle(shape, w)
+    la, _ = a.prefill(0, emb)
+    b = TalkerOracle(shape, w)
+    b.prefill(0, emb[:16])
+    lb, _ = b.decode(0, emb[16])
+    for l in range(shape.n_layers):
+        for which in (0, 1):
+            np.testing.assert_array_equal(a.kv(0, l, which)[:, :16], b.kv(0, l, which)[:, :16])
+    for which in (0, 1):
+        np.testing.assert_array_equal(a.kv(0, 0, which), b.kv(0, 0, which))
+    d = np.abs(la - lb).max() / np.abs(la).max()
+    assert 1e-5 < d < 5e-2, d
 
 
 def test_chunked_extend_equals_one_shot_and_batched_equals_serial():
@@ -320,6 +399,17 @@ def test_planted_fresh_kv_reading_is_caught(monkeypatch):
     monkeypatch.setattr(TalkerOracle, "layer", _fresh_kv_in_prefill)
     with pytest.raises(AssertionError):
         test_prefill_equals_prefill_then_decode("f16")
+
+
+def test_planted_quantised_current_rows_are_caught(monkeypatch):
+    # attending to the quantised current rows (the cache itself) instead of
+    # the fresh ones must fail both q8 pins against the library model
+    monkeypatch.setattr(TalkerOracle, "attended_kv",
+                        lambda self, l, seq, p0, k, v: (self.kc[seq][l], self.vc[seq][l]))
+    with pytest.raises(AssertionError):
+        test_q8_prefill_matches_transformers_unquantised()
+    with pytest.raises(AssertionError):
+        test_q8_decode_and_extend_match_transformers_over_a_quantised_prefix()
 
 
 def test_planted_missing_eps_and_gain_are_caught(monkeypatch):
