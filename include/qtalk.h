@@ -57,8 +57,8 @@ typedef enum { QTALK_F32 = 0, QTALK_BF16 = 1, QTALK_F16 = 2, QTALK_Q8 = 3 } qtal
  * src/pipeline/tts_transformer.rs", TtsTransformerConfig::default).
  * Requirements (else QTALK_E_INVAL): every size >= 1; head_dim is 64 or 128;
  * n_heads % n_kv_heads == 0; hidden, intermediate and n_heads*head_dim are
- * multiples of 64; intermediate is a multiple of 16; weight_dtype is F32 or
- * BF16; kv_dtype is F32, F16 or Q8.  q_dim = n_heads*head_dim need not equal
+ * multiples of 64 and at most 8192; intermediate is a multiple of 16;
+ * weight_dtype is F32 or BF16; kv_dtype is F32, F16 or Q8.  q_dim = n_heads*head_dim need not equal
  * hidden (it does not for the Talker: 2048 vs 1024). */
 typedef struct {
   int32_t n_layers;
@@ -248,8 +248,26 @@ qtalk_status qtalk_argmax_embed(qtalk_ctx *ctx, const float *logits,
 qtalk_status qtalk_select_head(qtalk_ctx *ctx, int32_t head);
 
 /* Block until the context's stream has finished all enqueued work.
- * Errors: QTALK_E_DEVICE if a kernel failed. */
+ * Errors: QTALK_E_DEVICE if a kernel failed, or if a kernel reported a
+ * failure of its own since the previous qtalk_sync:
+ *  - a batch-1 decode (qtalk_decode, or a one- or two-row prefill/extend,
+ *    which run on the same persistent kernel) gave up waiting for its other
+ *    blocks, or its blocks were placed differently than set-up found (then
+ *    later decodes use the slower placement-independent exchange).  Its
+ *    outputs, and those of every later call, are not valid: each sequence
+ *    such a decode wrote since the previous qtalk_sync is rolled back to
+ *    the first position it wrote there (qtalk_kv_len shows the result, the
+ *    message lists the sequences), and later calls work normally;
+ *  - an id given to qtalk_embed_sum or picked by qtalk_argmax_embed was
+ *    outside its table (those output rows hold NaN).
+ * The status words are cleared either way. */
 qtalk_status qtalk_sync(qtalk_ctx *ctx);
+
+/* Test hook for the failure path above: a batch-1 decode enqueued after this
+ * call gives up a wait after `polls` re-polls (0 restores the default, about
+ * 1-2 s of polling).  Every block of a launch that gives up leaves the
+ * kernel; nothing waits without bound.  Errors: QTALK_E_INVAL (polls < 0). */
+qtalk_status qtalk_set_wait_limit(qtalk_ctx *ctx, int64_t polls);
 
 /* Message of the last error on this context ("" if none).  The string lives
  * until the next call on the context. */

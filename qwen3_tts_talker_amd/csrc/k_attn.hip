@@ -6,8 +6,12 @@
 // absolute position, set_rows of K/V into the cache, then attention over the
 // cache window with scale 1/sqrt(head_dim) and the causal mask key <= pos);
 // "transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill (query head h
-// reads KV head h / (n_heads / n_kv_heads)).  The attention reads the cache
-// after the write, so K/V pass through the cache's storage type.
+// reads KV head h / (n_heads / n_kv_heads)).  An f32 or f16 cache is read
+// after the write, so K/V pass through its storage type.  A Q8_0 cache gives
+// the positions of earlier calls dequantised and the call's own rows as
+// computed, unquantised ("rightkit-qts 0.2.3 src/pipeline/tts_transformer.rs",
+// forward_step_cached: the cached prefix cast to F32 joined with the current
+// k/v; forward_prefill_cached: attention on the fresh k/v).
 #include <type_traits>
 
 #include "kernels.h"
@@ -161,10 +165,13 @@ __global__ __launch_bounds__(256) void k_qk_rope_append(QkArgs a) {
     }
   }
   if (!act) return;
-  if (kind == 0) {
+  // q back in place; with a Q8_0 cache k too, since the attention of this
+  // call reads its own rows unquantised from here (v is read as projected)
+  if (kind == 0 || (Q8 && kind == 1)) {
     x[lane] = x1;
     x[lane + HALF] = x2;
-  } else {
+  }
+  if (kind > 0) {
     char* rowp = reinterpret_cast<char*>(kind == 1 ? a.kc : a.vc) +
                  ((size_t)(seq * nkv + kvh) * a.cap + pos) * KVIO<KVT>::row_bytes(HD);
     if constexpr (Q8) {
@@ -285,6 +292,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   const char* Kp = reinterpret_cast<const char*>(a.kc) + head_off;
   const char* Vp = reinterpret_cast<const char*>(a.vc) + head_off;
 
+  // Q8_0 cache: keys from `fresh` on are rows of this call, read unquantised
+  // from the projection buffer (key j is row t - (pos - j): the call's rows of
+  // one sequence are consecutive rows at consecutive positions)
+  constexpr bool Q8 = std::is_same<KVT, q8_t>::value;
+  const int fresh = a.rows.uniform == 0 ? pos : a.rows.p0;
+  const float* Kf = a.q + (size_t)(nq + g) * HD;
+  const float* Vf = a.q + (size_t)(nq + nkv + g) * HD;
+
   // score-phase lane roles
   const int sub = lane & 15;  // dims sub*DPL .. +DPL
   const int kq = lane >> 4;   // key within the wave's group of 4
@@ -316,7 +331,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       const int j = kb + jl;
       float kf[DPL];
       const bool ok = j < k_end;
-      if (ok) kv_load<KVT, DPL>(Kp + (size_t)j * RB, HD, sub * DPL, kf);
+      if (ok) {
+        if (Q8 && j >= fresh) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) kf[e] = Kf[(size_t)(t - pos + j) * a.ldq + sub * DPL + e];
+        } else {
+          kv_load<KVT, DPL>(Kp + (size_t)j * RB, HD, sub * DPL, kf);
+        }
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
@@ -358,7 +380,12 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       const int j = kb + jl;
       if (j < k_end) {
         float vf[DPL];
-        kv_load<KVT, DPL>(Vp + (size_t)j * RB, HD, vd * DPL, vf);
+        if (Q8 && j >= fresh) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) vf[e] = Vf[(size_t)(t - pos + j) * a.ldq + vd * DPL + e];
+        } else {
+          kv_load<KVT, DPL>(Vp + (size_t)j * RB, HD, vd * DPL, vf);
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float pv = s_p[h][jl];
@@ -491,16 +518,28 @@ void launch_kv_to_f32(KvKind kv, const void* src, int n_kv, int cap, int len, in
   else hipLaunchKernelGGL(k_kv_to_f32<float>, grid, dim3(hd / 4), 0, st, s, cap, len, hd, dst);
 }
 
-// grid (len, n_kv, 2), hd / 4 threads: Q8_0 rows 0 .. len-1 of one
-// sequence's K (z = 0) and V (z = 1) into float16 rows [n_kv][cap][hd], for
-// the matrix-core prefill attention
+// grid (len, n_kv, 2), hd / 4 threads: positions 0 .. len-1 of one
+// sequence's K (z = 0) and V (z = 1) as float16 rows [n_kv][cap][hd], for the
+// matrix-core prefill attention: positions below `fresh` dequantised from the
+// Q8_0 cache, the call's own rows (position fresh + r is row r) from the
+// projection buffer, K after its norm and RoPE
 __global__ void k_kv_q8_to_f16(const char* kq, const char* vq, int cap, int hd, f16_t* k16,
-                               f16_t* v16) {
+                               f16_t* v16, int fresh, const float* qkv, int ldqkv, int nq,
+                               int nkv) {
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x * 4;
   const char* src = blockIdx.z ? vq : kq;
   f16_t* dst = blockIdx.z ? v16 : k16;
   float f[4];
-  kv_load<q8_t, 4>(src + ((size_t)h * cap + t) * KVIO<q8_t>::row_bytes(hd), hd, d, f);
+  if (t >= fresh) {
+    const float4 v = *reinterpret_cast<const float4*>(
+        qkv + (size_t)(t - fresh) * ldqkv + (size_t)(nq + blockIdx.z * nkv + h) * hd + d);
+    f[0] = v.x;
+    f[1] = v.y;
+    f[2] = v.z;
+    f[3] = v.w;
+  } else {
+    kv_load<q8_t, 4>(src + ((size_t)h * cap + t) * KVIO<q8_t>::row_bytes(hd), hd, d, f);
+  }
   typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 h4;
   h4 o;
   o[0] = (f16_t)f[0];
@@ -511,11 +550,12 @@ __global__ void k_kv_q8_to_f16(const char* kq, const char* vq, int cap, int hd, 
 }
 
 void launch_kv_q8_to_f16(const void* kq, const void* vq, int n_kv, int cap, int len, int hd,
-                         f16_t* k16, f16_t* v16, hipStream_t st) {
+                         f16_t* k16, f16_t* v16, int fresh, const float* qkv, int ldqkv, int nq,
+                         hipStream_t st) {
   if (len <= 0) return;
   hipLaunchKernelGGL(k_kv_q8_to_f16, dim3(len, n_kv, 2), dim3(hd / 4), 0, st,
                      reinterpret_cast<const char*>(kq), reinterpret_cast<const char*>(vq), cap, hd,
-                     k16, v16);
+                     k16, v16, fresh, qkv, ldqkv, nq, n_kv);
 }
 
 size_t kv_row_bytes(KvKind kv, int hd) {

@@ -73,7 +73,6 @@ constexpr int ISEG = I / NKV, OSEG = QD / NKV;  // down / o_proj input columns p
 // 128-byte lines, so no line holds words of two writers
 constexpr int PST = 144;
 constexpr int PART_WORDS = NKV * NCH * G * PST;  // per layer
-constexpr long SPIN_LIMIT = 1L << 21;
 
 static_assert(QKV % NB == 0 && H % NB == 0 && I % NB == 0, "row split");
 
@@ -160,6 +159,11 @@ __device__ __forceinline__ bool err_set(const int* err) {
 __device__ __forceinline__ void raise_err(int* err, int code) {
   __hip_atomic_store(err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// where a wait reports that it gave up, and after how many re-polls
+struct Bail {
+  int* err;
+  long limit;
+};
 
 // Exchange-word wait split in two: issue() sends the first poll, so the
 // caller can queue the next step's weight loads behind it (loads complete in
@@ -179,7 +183,7 @@ struct LLWait {
       if (k * NT + tid < n) v[k] = ld_x<LOCAL>(src + k * NT + tid);
   }
   template <typename Store>
-  __device__ __forceinline__ bool finish(uint32_t ep, int* err, Store store) {
+  __device__ __forceinline__ bool finish(uint32_t ep, const Bail& bl, Store store) {
     const int tid = threadIdx.x;
     long spins = 0;
     while (true) {
@@ -189,9 +193,9 @@ struct LLWait {
         if (k * NT + tid < n && (uint32_t)(v[k] >> 32) != ep) ok = false;
       if (ok) break;
       ++spins;
-      if ((spins & 255) == 0 && err_set(err)) return false;
-      if (spins > SPIN_LIMIT) {
-        raise_err(err, 1);
+      if ((spins & 255) == 0 && err_set(bl.err)) return false;
+      if (spins > bl.limit) {
+        raise_err(bl.err, 1);
         return false;
       }
       // re-poll at once: a poll round trip is the detection granularity,
@@ -206,8 +210,8 @@ struct LLWait {
       if (k * NT + tid < n) store(k * NT + tid, __uint_as_float((uint32_t)v[k]));
     return true;
   }
-  __device__ __forceinline__ bool finish_to(uint32_t ep, int* err, float* dst) {
-    return finish(ep, err, [&](int i, float x) { dst[i] = x; });
+  __device__ __forceinline__ bool finish_to(uint32_t ep, const Bail& bl, float* dst) {
+    return finish(ep, bl, [&](int i, float x) { dst[i] = x; });
   }
 };
 
@@ -309,10 +313,10 @@ static_assert(H == 2 * NT, "two hidden channels per thread");
 // thread's share of sum(x^2) to *ss.  RMSNorm is then applied as one scale
 // on the dot products: W (x * rsqrt(mean(x^2) + eps) * g) = rsqrt(.) * W (x g).
 template <bool LOCAL>
-__device__ __forceinline__ bool recv_norm(LLWait<2, LOCAL>& w, uint32_t ep, int* err, float* x,
+__device__ __forceinline__ bool recv_norm(LLWait<2, LOCAL>& w, uint32_t ep, const Bail& bl, float* x,
                                           float* xg, const Gain2& g, float* ss) {
   float s = 0.f;
-  const bool ok = w.finish(ep, err, [&](int i, float v) {
+  const bool ok = w.finish(ep, bl, [&](int i, float v) {
     x[i] = v;
     xg[i] = v * (i < NT ? g.g0 : g.g1);
     s = fmaf(v, v, s);
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ float red[32];
   __shared__ float redw[NW];
   __shared__ float qs[G][HD];                              // normed, roped, scaled q
-  __shared__ float knew[HD], vnew[HD];                     // the new position's K, V (cache precision)
+  __shared__ float knew[HD], vnew[HD];                     // the new position's K, V as attended
   __shared__ signed char kcode[HD], vcode[HD];             // Q8_0: its codes
   __shared__ f16_t kscl[HD / 32], vscl[HD / 32];           // Q8_0: its block scales
   __shared__ __attribute__((aligned(16))) float ow[NW][G * HD];  // per-wave attention sums
@@ -393,6 +397,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float cwt[NCH];  // merge weights of the chunks
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Bail bl{a.err, a.spin_limit};
   // block-wide "some thread gave up": sticky (a block that gives up leaves
   // the kernel), so one barrier per step suffices; a wave that reads a later
   // step's flag early only leaves earlier, which the barrier tolerates
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     LLWait<1> wr;
     wr.issue(word - tid, NT);
     float v = 0.f;
-    const bool ok = wr.finish(epw, a.err, [&](int, float x) { v = x; });
+    const bool ok = wr.finish(epw, bl, [&](int, float x) { v = x; });
     const float s = row16_sum(gp < NKV ? v : 0.f);
     if (gp == 0) st_x<LOCAL>(XOUT + g * H + 32 * c + jr, xres[32 * c + jr] + s, epw);
     return ok;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         bail = !reduce_rows(Eprev + OFF_DP, ep - 1, Eprev + OFF_XD);
         LLWait<2, LOCAL> wx;
         wx.issue(Eprev + OFF_XD + g * H, H);
-        bail = bail || !recv_norm(wx, ep - 1, a.err, xres, xin, gin, &ss);
+        bail = bail || !recv_norm(wx, ep - 1, bl, xres, xin, gin, &ss);
       } else {
         const float x0 = a.emb[tid], x1 = a.emb[tid + NT];
         xres[tid] = x0;
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
                                                : OFF_E1 + QD + KVD + g * HD + (tid - 384));
         w1.issue(E + src - tid, tid + 1);  // word tid of (E + src - tid)
         float v = 0.f;
-        const bool bail = !w1.finish(ep, a.err, [&](int, float x) { v = x; });
+        const bool bail = !w1.finish(ep, bl, [&](int, float x) { v = x; });
         araw[tid] = v;
         const float sq = wave_sum(v * v);  // waves 0-1 q0, 2-3 q1, 4-5 k, 6-7 v
         if (lane == 0) redw[wave] = sq;
@@ -582,9 +587,11 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         const int lr = gu_row0 + (r >> 1);
         return Wgu + ((size_t)(lr >> 4) * 32 + (lr & 15) + (r & 1) * 16) * H;
       }, wave, lane);
-      // per-head RMSNorm, NEOX RoPE on (i, i + 64); k and v round through the
-      // cache type (Q8_0: the 32-value block of a k or v dim is one half of
-      // its wave)
+      // per-head RMSNorm, NEOX RoPE on (i, i + 64).  f16 cache: the new k and
+      // v are attended as the cache stores them (read after write).  Q8_0
+      // cache: they are attended unquantised, as computed, while the codes
+      // and scales go to the cache (the 32-value block of a k or v dim is one
+      // half of its wave)
       {
         float y;
         if (tid < 384) {
@@ -603,10 +610,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
           if constexpr (Q8) {
             const float d = half32_max(fabsf(y)) / 127.0f;
             const float code = roundf(y * (d > 0.f ? 1.0f / d : 0.f));
-            const f16_t d16 = (f16_t)d;
-            c = code * (float)d16;
             (tid < 384 ? kcode : vcode)[j] = (signed char)code;
-            if ((lane & 31) == 0) (tid < 384 ? kscl : vscl)[j >> 5] = d16;
+            if ((lane & 31) == 0) (tid < 384 ? kscl : vscl)[j >> 5] = (f16_t)d;
+            c = y;
           } else {
             c = (float)(f16_t)y;
           }
@@ -798,7 +804,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       const int tm = min(tid, NCH * 10 - 1), cc = tm / 10, k = tm % 10;
       LLWait<1, LOCAL> wm;
       wm.issue(pbase + cc * PST + (k < 8 ? d0 + k : HD + k - 8) - tid, NCH * 10);
-      const bool bail = !wm.finish(ep, a.err, [&](int, float x) { mg[tm] = x; });
+      const bool bail = !wm.finish(ep, bl, [&](int, float x) { mg[tm] = x; });
       if (sync_bail(bail)) return;
       if (wave == 0) {  // lane cc < NCH: chunk cc's weight 2^(m_c - M) / L
         const float mc = lane < NCH ? mg[lane * 10 + 8] : -INFINITY;
@@ -828,7 +834,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       LLWait<1, LOCAL> wo;  // head group g's merged output, 8 words from each block
       const int to = min(tid, OSEG - 1);
       wo.issue(E + OFF_OG + g * 512 + 16 * (to >> 3) + (to & 7) - tid, OSEG);
-      const bool bail = !wo.finish_to(ep, a.err, xin);
+      const bool bail = !wo.finish_to(ep, bl, xin);
       // bulk loads: the next step's gain, the next layer's cached keys
       gpost.load(g_post);
       if (l + 1 < a.n_layers) load_kv(l + 1);
@@ -843,7 +849,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       LLWait<2, LOCAL> wx;
       wx.issue(E + OFF_XM + g * H, H);
       float ss;
-      bail = bail || !recv_norm(wx, ep, a.err, xres, xin, gpost, &ss);
+      bail = bail || !recv_norm(wx, ep, bl, xres, xin, gpost, &ss);
       // bulk loads: the next layer's input-norm gain and the down step's
       // weight slice (the next layer's QKV slice follows after the down
       // publish)
@@ -871,7 +877,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
       LLWait<1, LOCAL> wa;
       const int ta = min(tid, ISEG - 1);
       wa.issue(E + OFF_A + g * 512 + 16 * (ta / 12) + ta % 12 - tid, ISEG);
-      const bool bail = !wa.finish_to(ep, a.err, xin);
+      const bool bail = !wa.finish_to(ep, bl, xin);
       if (sync_bail(bail)) return;
       const float s = gd.dot(xin, lane);
       if ((lane & 15) == 0) st_ll(E + OFF_DP + g * H + 32 * c + 4 * wave + (lane >> 4), s, ep);
@@ -896,7 +902,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     LLWait<2, LOCAL> wx;
     wx.issue(El + OFF_XD + g * H, H);
     float ss;
-    bail = bail || !recv_norm(wx, epl, a.err, xres, xin, gin, &ss);  // gin = final gain
+    bail = bail || !recv_norm(wx, epl, bl, xres, xin, gin, &ss);  // gin = final gain
     ss = wave_sum(ss);
     if (lane == 0) redw[wave] = ss;
     if (sync_bail(bail)) return;

@@ -6,8 +6,8 @@
 // accumulate in float32 ("transcribe.cpp src/causal_lm/causal_lm.cpp",
 // mul_mat_f32acc).  Each wave streams whole weight rows with 16-byte loads
 // (1 KiB per wave per step, fully coalesced); activations sit in LDS, already
-// RMS-normalised when the call fuses the pre-norm.  Up to 4 activation rows
-// share every weight load.
+// RMS-normalised when the call fuses the pre-norm.  Up to 8 activation rows
+// share every weight load (4 where 8 rows of float32 would pass 64 KiB of LDS).
 #include "kernels.h"
 
 namespace qtalk {

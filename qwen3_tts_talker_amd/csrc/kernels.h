@@ -7,6 +7,9 @@ namespace qtalk {
 
 enum Epilogue { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
 
+// largest K of the matrix-vector kernel: 4 rows of float32 activations in LDS
+constexpr int MAX_GEMV_K = 8192;
+
 // y[n][o] (=|+=) sum_k W[o][k] * xn[n][k], xn = RMSNorm(x[n]) * gain when
 // `gain` is set (else xn = x).  EPI_SWIGLU reads W as gate|up rows
 // interleaved in blocks of 16 (see pack order in the runtime) and writes
@@ -27,7 +30,8 @@ struct GemvArgs {
 };
 void launch_gemv(bool w_bf16, Epilogue epi, GemvArgs a, hipStream_t st);
 
-// QK RMSNorm + NEOX RoPE on q (in place) and k, then K/V append into the cache.
+// QK RMSNorm + NEOX RoPE on q (in place) and k, then K/V append into the
+// cache; with a Q8_0 cache the normed and roped k also goes back in place.
 struct QkArgs {
   float* qkv;
   int ldqkv;
@@ -46,10 +50,13 @@ struct QkArgs {
 // head_dim / 32 float16 scales)
 enum KvKind { KV_F32 = 0, KV_F16 = 1, KV_Q8 = 2 };
 size_t kv_row_bytes(KvKind kv, int head_dim);
-// Q8_0 rows 0 .. len-1 of one sequence (K and V, [n_kv][cap] rows each) into
-// float16 [n_kv][cap][hd] copies
+// positions 0 .. len-1 of one sequence (K and V, [n_kv][cap] rows each) as
+// float16 [n_kv][cap][hd] copies: below `fresh` dequantised from the Q8_0
+// cache, from `fresh` on the call's own rows (row r = position fresh + r) of
+// the projection buffer qkv [rows][ldqkv] (K normed and roped in place)
 void launch_kv_q8_to_f16(const void* kq, const void* vq, int n_kv, int cap, int len, int hd,
-                         f16_t* k16, f16_t* v16, hipStream_t st);
+                         f16_t* k16, f16_t* v16, int fresh, const float* qkv, int ldqkv, int nq,
+                         hipStream_t st);
 void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st);
 
 // Causal GQA attention of the listed rows over the cache (split over keys).
@@ -148,11 +155,14 @@ struct FusedDecodeArgs {
   uint64_t* ll;    // [2][words per layer] exchange words (layer parity)
   uint64_t* part;  // [2][NKV][G][NCH][144] chunk partials (o, m, l, padding), as words
   int* err;        // 0; 1 a wait gave up; 3 a block ran on an unexpected XCD
+  long spin_limit; // re-polls after which a wait gives up (error 1)
   uint32_t epoch;  // >= 1 and < 2^26; words carry epoch * 64 + layer
   int xcd_local;   // QKV -> attention -> merge exchanges inside each XCD's L2
   int head_rows;   // vocab / 256: codec head rows per block (1..16)
 
 };
+// default bounded-wait limit of the persistent decode (~1-2 s of polling)
+constexpr long FUSED_SPIN_LIMIT = 1L << 21;
 bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vocab, int n_heads,
                             int n_kv_heads, int head_dim);
 bool fused_decode_fits();

@@ -96,6 +96,10 @@ struct qtalk_ctx {
   uint64_t* ll = nullptr;
   uint64_t* fpart = nullptr;
   int* ferr = nullptr;
+  long spin_limit = FUSED_SPIN_LIMIT;  // persistent decode: re-polls before a wait gives up
+  // per sequence, the first position written by a persistent launch since
+  // the last qtalk_sync (-1: none); a launch that gave up rolls it back
+  std::vector<int32_t> fused_first;
   int* aux_err = nullptr;  // frame-step kernels: 5 when an id was outside its table
   uint32_t epoch = 0;
   size_t per_layer = 0, norms_per_layer = 0;
@@ -160,6 +164,9 @@ const char* check_config(const qtalk_config* g) {
   if (g->kv_dtype != QTALK_F32 && g->kv_dtype != QTALK_F16 && g->kv_dtype != QTALK_Q8)
     return "kv_dtype must be F32, F16 or Q8";
   if (g->n_output_heads < 0 || g->n_output_heads > 64) return "n_output_heads must be 0..64";
+  // the matrix-vector kernel keeps up to 4 activation rows of float32 in LDS
+  if (g->hidden > MAX_GEMV_K || g->intermediate > MAX_GEMV_K || g->n_heads * g->head_dim > MAX_GEMV_K)
+    return "hidden, intermediate and n_heads*head_dim must be <= 8192";
   return nullptr;
 }
 
@@ -263,7 +270,8 @@ struct Fwd {
     gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
     const bool sup = attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
     // a Q8 cache reaches the matrix cores through a float16 copy of the
-    // sequence's rows 0 .. p0+T-1 (one sequence at a time)
+    // sequence's positions 0 .. p0+T-1 (one sequence at a time): earlier
+    // positions dequantised, this chunk's rows as computed
     const bool q8_mfma = c->kv == KV_Q8 && c->kv16 && sup && rows.uniform == 1;
     const bool mfma_attn = (c->kv == KV_F16 && sup) || q8_mfma;
     qk_append(l, rows, mfma_attn);
@@ -281,7 +289,8 @@ struct Fwd {
         f16_t* k16 = c->kv16;
         f16_t* v16 = c->kv16 + (size_t)g.n_kv_heads * g.max_seq_len * g.head_dim;
         launch_kv_q8_to_f16(kv_layer(c->kc, l) + seq_rows * c->kv_rb, kv_layer(c->vc, l) + seq_rows * c->kv_rb,
-                            g.n_kv_heads, g.max_seq_len, rows.p0 + T, g.head_dim, k16, v16, st);
+                            g.n_kv_heads, g.max_seq_len, rows.p0 + T, g.head_dim, k16, v16, rows.p0,
+                            c->qkv, c->qkv_dim, g.n_heads, st);
         p.kc = k16;
         p.vc = v16;
       }
@@ -332,7 +341,7 @@ struct Fwd {
   }
 
   // rows of one sequence at positions p0 .. p0+T-1 (prefill / extend)
-  void run_sequence(int seq, int p0, const float* emb, int T, float* logits, float* hidden_out) {
+  qtalk_status run_sequence(int seq, int p0, const float* emb, int T, float* logits, float* hidden_out) {
     const bool mfma = c->w_bf16 && T >= MFMA_MIN_ROWS &&
                       gemm_shape_ok(1, c->qkv_dim, g.hidden) && gemm_shape_ok(1, g.hidden, c->q_dim) &&
                       gemm_shape_ok(1, 2 * g.intermediate, g.hidden) &&
@@ -346,8 +355,9 @@ struct Fwd {
       rows.uniform = 1;
       rows.seq0 = seq;
       rows.p0 = p0 + done;
-      (void)hipMemcpyAsync(c->x, emb + (size_t)done * g.hidden, (size_t)n * g.hidden * 4,
-                           hipMemcpyDeviceToDevice, st);
+      if (hipMemcpyAsync(c->x, emb + (size_t)done * g.hidden, (size_t)n * g.hidden * 4,
+                         hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot copy the input rows");
       for (int l = 0; l < g.n_layers; ++l) {
         if (mfma && n >= MFMA_MIN_ROWS) layer_mfma(l, rows, l > 0);
         else layer_gemv(l, rows);
@@ -355,23 +365,27 @@ struct Fwd {
       done += n;
       if (done == T) head(c->x + (size_t)(n - 1) * g.hidden, 1, logits, hidden_out);
     }
+    return QTALK_OK;
   }
 
   // batched prefill: n sequences of T rows each from position 0, stacked in
   // groups that fit one matrix-core pass; each group's logits from its
   // sequences' last rows
-  void run_batch_prefill(const int32_t* seqs, int n, const float* emb, int T, float* logits,
-                         float* hidden_out) {
+  qtalk_status run_batch_prefill(const int32_t* seqs, int n, const float* emb, int T, float* logits,
+                                 float* hidden_out) {
     const int H = g.hidden;
     const bool mfma = c->w_bf16 && gemm_shape_ok(1, c->qkv_dim, H) && gemm_shape_ok(1, H, c->q_dim) &&
                       gemm_shape_ok(1, 2 * g.intermediate, H) && gemm_shape_ok(1, H, g.intermediate) &&
                       g.intermediate % 16 == 0;
     const int cap_rows = mfma ? std::max(c->tc, GEMV_ROWS) : GEMV_ROWS;
     if (T > cap_rows) {  // a sequence's rows exceed one pass: one prefill per sequence
-      for (int b = 0; b < n; ++b)
-        run_sequence(seqs[b], 0, emb + (size_t)b * T * H, T, logits + (size_t)b * g.vocab,
-                     hidden_out ? hidden_out + (size_t)b * H : nullptr);
-      return;
+      for (int b = 0; b < n; ++b) {
+        const qtalk_status s = run_sequence(seqs[b], 0, emb + (size_t)b * T * H, T,
+                                            logits + (size_t)b * g.vocab,
+                                            hidden_out ? hidden_out + (size_t)b * H : nullptr);
+        if (s != QTALK_OK) return s;
+      }
+      return QTALK_OK;
     }
     const int per_group = std::min(MAX_ROWS, cap_rows / T);
     for (int b0 = 0; b0 < n; b0 += per_group) {
@@ -391,7 +405,9 @@ struct Fwd {
         rows.seq0 = seqs[b0];
         for (int z = 0; z < nb; ++z) rows.seq[z] = seqs[b0 + z];
       }
-      (void)hipMemcpyAsync(c->x, emb + (size_t)b0 * T * H, (size_t)M * H * 4, hipMemcpyDeviceToDevice, st);
+      if (hipMemcpyAsync(c->x, emb + (size_t)b0 * T * H, (size_t)M * H * 4, hipMemcpyDeviceToDevice, st) !=
+          hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot copy the input rows");
       for (int l = 0; l < g.n_layers; ++l) {
         if (mfma && M >= MFMA_MIN_ROWS) layer_mfma(l, rows, l > 0);
         else layer_gemv(l, rows);
@@ -401,6 +417,7 @@ struct Fwd {
            logits + (size_t)b0 * g.vocab, g.vocab, EPI_STORE,
            hidden_out ? hidden_out + (size_t)b0 * H : nullptr, H);
     }
+    return QTALK_OK;
   }
 
   // one row of sequence `seq` at position `pos` as one persistent launch
@@ -429,6 +446,7 @@ struct Fwd {
     a.ll = c->ll;
     a.part = c->fpart;
     a.err = c->ferr;
+    a.spin_limit = c->spin_limit;
     if (c->epoch + 1 >= (1u << 26)) {  // epochs would wrap: clear the words and restart
       if (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, st) != hipSuccess ||
           hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, st) != hipSuccess)
@@ -450,11 +468,13 @@ struct Fwd {
       return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
     ch.stream = st;
     c->epoch += 1;
+    int32_t& first = c->fused_first[seq];
+    first = first < 0 ? pos : std::min(first, pos);
     return QTALK_OK;
   }
 
   // one row per listed sequence (batched decode)
-  void run_batch(const int32_t* seqs, int n, const float* emb, float* logits, float* hidden_out) {
+  qtalk_status run_batch(const int32_t* seqs, int n, const float* emb, float* logits, float* hidden_out) {
     for (int b0 = 0; b0 < n; b0 += GEMV_ROWS) {
       const int nb = std::min(GEMV_ROWS, n - b0);
       RowMeta rows{};
@@ -464,12 +484,14 @@ struct Fwd {
         rows.seq[i] = seqs[b0 + i];
         rows.pos[i] = c->cur_len[seqs[b0 + i]];
       }
-      (void)hipMemcpyAsync(c->x, emb + (size_t)b0 * g.hidden, (size_t)nb * g.hidden * 4,
-                           hipMemcpyDeviceToDevice, st);
+      if (hipMemcpyAsync(c->x, emb + (size_t)b0 * g.hidden, (size_t)nb * g.hidden * 4,
+                         hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot copy the input rows");
       for (int l = 0; l < g.n_layers; ++l) layer_gemv(l, rows);
       head(c->x, nb, logits + (size_t)b0 * g.vocab,
            hidden_out ? hidden_out + (size_t)b0 * g.hidden : nullptr);
     }
+    return QTALK_OK;
   }
 };
 
@@ -633,6 +655,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
     return s;
   }
   c->cur_len.assign(g.max_seqs, 0);
+  c->fused_first.assign(g.max_seqs, -1);
   *out = c;
   return QTALK_OK;
 }
@@ -662,15 +685,17 @@ static qtalk_status seq_call(qtalk_ctx* c, int32_t seq, const float* emb, int32_
     return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + %d > %d", p0, T, c->cfg.max_seq_len);
   Fwd f(c);
   qtalk_status s = QTALK_OK;
-  if (c->fused && T <= FUSED_MAX_ROWS) {
+  if (c->fused && (T == 1 || (T <= FUSED_MAX_ROWS && c->kv != KV_Q8))) {
     // a row or two (the code predictor's prefill) as consecutive persistent
-    // launches: row t attends to positions 0 .. p0 + t, as in the prefill
+    // launches: row t attends to positions 0 .. p0 + t, as in the prefill.
+    // Not for two rows over a Q8 cache: there the second row attends to the
+    // first unquantised, and a launch per row would read it back quantised.
     for (int t = 0; t < T && s == QTALK_OK; ++t)
       s = f.run_fused(seq, p0 + t, emb + (size_t)t * c->cfg.hidden, logits,
                       t + 1 == T ? hidden_out : nullptr);
   } else {
-    f.run_sequence(seq, p0, emb, T, logits, hidden_out);
-    s = launch_status(c);
+    s = f.run_sequence(seq, p0, emb, T, logits, hidden_out);
+    if (s == QTALK_OK) s = launch_status(c);
   }
   if (s == QTALK_OK) c->cur_len[seq] = p0 + T;
   return s;
@@ -703,8 +728,8 @@ qtalk_status qtalk_prefill_batch(qtalk_ctx* c, int32_t n, const int32_t* seqs, c
   if (T > c->cfg.max_seq_len)
     return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d > %d", T, c->cfg.max_seq_len);
   Fwd f(c);
-  f.run_batch_prefill(seqs, n, emb, T, logits, hidden_out);
-  const qtalk_status s = launch_status(c);
+  qtalk_status s = f.run_batch_prefill(seqs, n, emb, T, logits, hidden_out);
+  if (s == QTALK_OK) s = launch_status(c);
   if (s == QTALK_OK)
     for (int b = 0; b < n; ++b) c->cur_len[seqs[b]] = T;
   return s;
@@ -741,8 +766,8 @@ qtalk_status qtalk_decode_batch(qtalk_ctx* c, int32_t n, const int32_t* seqs, co
       return fail(c, QTALK_E_OVERFLOW, "cache overflow on sequence %d", s);
   }
   Fwd f(c);
-  f.run_batch(seqs, n, emb, logits, hidden_out);
-  const qtalk_status st = launch_status(c);
+  qtalk_status st = f.run_batch(seqs, n, emb, logits, hidden_out);
+  if (st == QTALK_OK) st = launch_status(c);
   if (st == QTALK_OK)
     for (int i = 0; i < n; ++i) c->cur_len[seqs[i]] += 1;
   return st;
@@ -845,6 +870,33 @@ qtalk_status qtalk_sync(qtalk_ctx* c) {
   if (!c) return QTALK_E_INVAL;
   const hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return fail(c, QTALK_E_DEVICE, "stream failed: %s", hipGetErrorString(e));
+  std::string msg;
+  if (c->fused) {
+    int code = 0;
+    if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(c, QTALK_E_DEVICE, "cannot read the decode status word");
+    if (code) {
+      // a persistent launch gave up (1) or ran on unexpected XCDs (3): the
+      // positions written by persistent launches since the last sync, and
+      // everything after them, are dropped; later launches start clean
+      if (hipMemset(c->ferr, 0, 4) != hipSuccess)
+        return fail(c, QTALK_E_DEVICE, "cannot clear the decode status word");
+      if (code == 3) c->xcd_local = false;  // later steps use device-scope exchanges
+      char buf[160];
+      snprintf(buf, sizeof buf, "persistent decode %s (code %d); rolled back:",
+               code == 3 ? "blocks did not run on the expected XCDs" : "gave up waiting", code);
+      msg = buf;
+      for (int s = 0; s < c->cfg.max_seqs; ++s) {
+        const int32_t f = c->fused_first[s];
+        if (f >= 0 && f < c->cur_len[s]) {
+          snprintf(buf, sizeof buf, " seq %d to %d;", s, f);
+          msg += buf;
+          c->cur_len[s] = f;
+        }
+      }
+    }
+    std::fill(c->fused_first.begin(), c->fused_first.end(), -1);
+  }
   {
     int code = 0;
     if (hipMemcpy(&code, c->aux_err, 4, hipMemcpyDeviceToHost) != hipSuccess)
@@ -852,25 +904,19 @@ qtalk_status qtalk_sync(qtalk_ctx* c) {
     if (code) {
       if (hipMemset(c->aux_err, 0, 4) != hipSuccess)
         return fail(c, QTALK_E_DEVICE, "cannot clear the frame-step status word");
-      return fail(c, QTALK_E_DEVICE,
-                  "qtalk_embed_sum: an id was outside its table (those slots hold NaN)");
+      msg += msg.empty() ? "" : " ";
+      msg += "frame step: an id was outside its table (those rows hold NaN)";
     }
   }
-  if (c->fused) {
-    int code = 0;
-    if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)
-      return fail(c, QTALK_E_DEVICE, "cannot read the decode status word");
-    if (code == 3) {  // placement changed: fall back to device-scope exchanges
-      c->xcd_local = false;
-      if (hipMemset(c->ferr, 0, 4) != hipSuccess)
-        return fail(c, QTALK_E_DEVICE, "cannot clear the decode status word");
-      return fail(c, QTALK_E_DEVICE,
-                  "persistent decode: blocks did not run on the expected XCDs (step not done; "
-                  "later steps use device-scope exchanges)");
-    }
-    if (code)
-      return fail(c, QTALK_E_DEVICE, "persistent decode gave up waiting (code %d)", code);
-  }
+  if (!msg.empty()) return fail(c, QTALK_E_DEVICE, "%s", msg.c_str());
+  return QTALK_OK;
+}
+
+qtalk_status qtalk_set_wait_limit(qtalk_ctx* c, int64_t polls) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (polls < 0) return fail(c, QTALK_E_INVAL, "polls must be >= 0");
+  c->spin_limit = polls ? (long)polls : FUSED_SPIN_LIMIT;
   return QTALK_OK;
 }
 

@@ -28,7 +28,8 @@ EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_decode", "qtalk_decode_batch", "qtalk_kv_rewind",
            "qtalk_kv_len", "qtalk_kv_read", "qtalk_prefill_batch", "qtalk_embed_sum",
            "qtalk_argmax", "qtalk_argmax_embed",
-           "qtalk_select_head", "qtalk_sync", "qtalk_last_error")
+           "qtalk_select_head", "qtalk_sync", "qtalk_last_error",
+           "qtalk_set_wait_limit")
 
 
 class qtalk_config(ctypes.Structure):
@@ -92,6 +93,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_select_head": (st, [P, I32]),
         "qtalk_sync": (st, [P]),
         "qtalk_last_error": (ctypes.c_char_p, [P]),
+        "qtalk_set_wait_limit": (st, [P, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -222,6 +224,10 @@ def qtalk_sync(ctx) -> int:
 
 def qtalk_last_error(ctx) -> str:
     return (load_library().qtalk_last_error(ctx) or b"").decode()
+
+
+def qtalk_set_wait_limit(ctx, polls) -> int:
+    return _check(ctx, load_library().qtalk_set_wait_limit(ctx, polls))
 
 
 # -- convenience wrapper --------------------------------------------------------
@@ -385,3 +391,6 @@ class Talker:
 
     def sync(self):
         qtalk_sync(self.ctx)
+
+    def set_wait_limit(self, polls):
+        qtalk_set_wait_limit(self.ctx, polls)

@@ -24,7 +24,11 @@ Draw recipe (every array is independent and reproducible on its own):
 * stacked output heads (code predictor) draw head i with key
   ``[seed, final tag, 1, i]``;
 * the long-context stress workload adds ``sign * 3.0e4`` to four fixed channels
-  of every embedding row.
+  of every embedding row;
+* a workload may scale the q and k norm gains by a constant (``qk_gain``):
+  the query-key scores then spread ``qk_gain^2`` times wider, so the softmax
+  picks out a few keys even at 32k positions instead of averaging thousands
+  (used where a check has to see the attention at long context).
 
 Weight layout is row-major ``[out][in]`` as in the pages' ``mul_mat(W, x)``.
 """
@@ -73,6 +77,7 @@ class TalkerShape:
     batch_lengths: bool = False
     outliers: bool = False
     n_out_heads: int = 1       # stacked output projections (code predictor: 15)
+    qk_gain: float = 1.0       # factor on the q and k norm gains
 
     @property
     def q_dim(self) -> int:
@@ -127,6 +132,12 @@ WORKLOADS: Dict[str, TalkerShape] = {
         name="talker_28l_ctx32k_outlier", n_layers=28, cap=33024, n_seqs=1,
         seed=1005, emb_seed=1005, prefill_len=32768, decode_steps=256,
         chunk=2048, outliers=True, **_TALKER),
+    # one layer of the 32k workload's weights with q/k norm gains x4 and
+    # N(0, 1) rows (no outlier channels): sharp attention at 32k positions
+    "talker_1l_ctx32k_sharp": TalkerShape(
+        name="talker_1l_ctx32k_sharp", n_layers=1, cap=33024, n_seqs=1,
+        seed=1005, emb_seed=1005, prefill_len=32768, decode_steps=256,
+        chunk=2048, qk_gain=4.0, **_TALKER),
     # bs1 decode at context 1921..2048 on the 28-layer weights of seed 1003
     "talker_28l_kv2k": TalkerShape(
         name="talker_28l_kv2k", n_layers=28, cap=2048, n_seqs=1, seed=1003,
@@ -174,7 +185,10 @@ def make_layer_weights(shape: TalkerShape, layer: int) -> Dict[str, np.ndarray]:
                 w = round_to_bf16(w)
             out[name] = w
         else:
-            out[name] = np.float32(1.0) + np.float32(0.05) * z
+            g = np.float32(1.0) + np.float32(0.05) * z
+            if name in ("g_q", "g_k") and shape.qk_gain != 1.0:
+                g = np.float32(shape.qk_gain) * g
+            out[name] = g
     return out
 
 

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = q.load_library()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert sorted(q.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -82,7 +82,9 @@ def _config(**kw):
                                  dict(kv_dtype=q.QTALK_BF16),
                                  dict(n_heads=12, n_kv_heads=4),
                                  dict(n_output_heads=-1),
-                                 dict(n_output_heads=65)])
+                                 dict(n_output_heads=65),
+                                 dict(hidden=8256), dict(intermediate=8256),
+                                 dict(n_heads=130, n_kv_heads=2)])
 def test_create_rejects_bad_config_before_any_device_call(bad):
     lib = q.load_library()
     w = q.qtalk_weights()
@@ -101,6 +103,7 @@ def test_null_context_calls_are_rejected():
     assert lib.qtalk_kv_rewind(None, 0, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_sync(None) == q.QTALK_E_INVAL
     assert lib.qtalk_select_head(None, 0) == q.QTALK_E_INVAL
+    assert lib.qtalk_set_wait_limit(None, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_embed_sum(None, 1, None, None, None, 1, None, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax(None, None, 1, 8, 8, -1, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax_embed(None, None, 1, 8, 8, -1, None, 4, None, None) == q.QTALK_E_INVAL

@@ -13,7 +13,7 @@ from oracle.talker import code_predictor_frame
 from oracle.frame import embed_sum, suppressed_argmax
 from synth import prefill_embeddings, step_embedding, workload, batch_lengths, make_weights
 from synth import embedding_tables, overlay_row
-from tests.helpers import argmax_in_band, argmax_ok, dev, host, rel_err, say, weights_for
+from tests.helpers import argmax_banded, argmax_ok, dev, host, rel_err, say, weights_for
 
 pytestmark = pytest.mark.gpu
 
@@ -65,19 +65,19 @@ def _prefill_decode(name, T, steps, tol, n_layers=None, kv_layers=None, kv_dtype
     lg, hd = tk.prefill(0, dev(emb), hidden=True)
     errs = [rel_err(host(lg), ref_logits[T - 1])]
     assert rel_err(host(hd), ref_hidden[T - 1]) <= tol
-    assert argmax_ok(host(lg), ref_logits[T - 1], tol)
-    bad_argmax = exact = 0
+    assert argmax_ok(host(lg), ref_logits[T - 1])
+    bad_argmax = exact = band = 0
     for s in range(steps):
         lg = tk.decode(0, dev(steps_emb[s]))
         g = host(lg)
         errs.append(rel_err(g, ref_logits[T + s]))
-        bad_argmax += not argmax_ok(g, ref_logits[T + s], tol)
+        bad_argmax += not argmax_ok(g, ref_logits[T + s])
+        band += argmax_banded(g, ref_logits[T + s])
         exact += int(np.argmax(g)) == int(np.argmax(ref_logits[T + s]))
         if (s + 1) % 256 == 0:
             say(f"  step {s + 1}: rel err {errs[-1]:.2e}")
-    band = sum(argmax_in_band(ref_logits[T + s], tol) for s in range(steps))
     say(f"  logits rel err: prefill {errs[0]:.2e}, decode max {max(errs[1:] or [0]):.2e}; "
-        f"argmax equal {exact}/{steps} (oracle top-2 inside the band at {band})")
+        f"argmax equal {exact}/{steps}, other pick inside 2x the measured error at {band}")
     assert max(errs) <= tol, max(errs)
     assert bad_argmax == 0
     assert tk.kv_len(0) == T + steps
@@ -131,7 +131,7 @@ def test_prefill_attention_many_tiles_ragged_extend_to_capacity():
     lg, hd = tk.extend(0, dev(emb[700:]), hidden=True)
     e2 = rel_err(host(lg), lo2)
     assert e2 <= TOL_BF16 and rel_err(host(hd), ho2) <= TOL_BF16
-    assert argmax_ok(host(lg), lo2, TOL_BF16)
+    assert argmax_ok(host(lg), lo2)
     kv2 = _check_kv(tk, orc, shape, TOL_BF16)
     say(f"  logits rel err {e1:.2e} / {e2:.2e}; kv rel err {kv1:.2e} / {kv2:.2e}")
     tk.close()
@@ -208,19 +208,26 @@ def test_chunked_extend_equals_one_shot():
 @pytest.mark.parametrize("fused", [False, True])
 def test_batched_decode_equals_serial(monkeypatch, fused):
     # bitwise on the per-step kernels; the persistent batch-1 kernel reduces
-    # in another order, so there the serial side agrees to rounding
+    # in another order, so there the serial side agrees to rounding.  Five
+    # sequences, then eleven (rows 8..10 in a second matrix-vector pass).
     if not fused:
         monkeypatch.setenv("QTALK_FUSED_DECODE", "0")
-    shape = workload("talker_1l_t128").with_(n_seqs=5, cap=256)
+    for lens in ([3, 40, 17, 90, 1], [3, 40, 17, 90, 1, 64, 33, 2, 120, 7, 55]):
+        _batched_equals_serial(lens, fused)
+
+
+def _batched_equals_serial(lens, fused):
+    n = len(lens)
+    shape = workload("talker_1l_t128").with_(n_seqs=n, cap=256)
     w = weights_for("talker_1l_t128")
     a = _talker(shape, w)
     b = _talker(shape, w)
-    lens = [3, 40, 17, 90, 1]
-    for s, n in enumerate(lens):
-        e = dev(prefill_embeddings(shape, n, seq=s))
+    say(f"[case] batched vs serial decode, {n} sequences, fused={fused}")
+    for s, m in enumerate(lens):
+        e = dev(prefill_embeddings(shape, m, seq=s))
         a.prefill(s, e)
         b.prefill(s, e)
-    order = [3, 0, 4, 1, 2]
+    order = [(3 * i + 2) % n for i in range(n)]
     for step in range(3):
         steps = np.stack([step_embedding(shape, step, seq=s) for s in order])
         lg, hg = a.decode_batch(order, dev(steps), hidden=True)
@@ -233,7 +240,9 @@ def test_batched_decode_equals_serial(monkeypatch, fused):
             else:
                 assert np.array_equal(lg[i], host(ls)), (step, s)
                 assert np.array_equal(hg[i], host(hs)), (step, s)
-    assert [a.kv_len(s) for s in range(5)] == [n + 3 for n in lens]
+    assert [a.kv_len(s) for s in range(n)] == [m + 3 for m in lens]
+    a.close()
+    b.close()
 
 
 def test_stale_cache_tail_is_never_read():
@@ -331,11 +340,58 @@ def test_batched_ragged_decode_16_sequences():
     errs = [rel_err(outs[k][s], ref[len(pre[s]) + k]) for k in range(steps)]
     say(f"  seq {s} (len {lens[s]}) decode rel err max {max(errs):.2e}")
     assert max(errs) <= TOL_BF16
-    assert all(argmax_ok(outs[k][s], ref[len(pre[s]) + k], TOL_BF16)
+    assert all(argmax_ok(outs[k][s], ref[len(pre[s]) + k])
                for k in range(steps))
 
 
-# -- long context with outlier channels -----------------------------------------
+def test_batched_ragged_decode_16_sequences_every_row():
+    # the 16-utterance workload's lengths (U{512..4096}, seed 1004) on two
+    # layers of its weights: every sequence prefilled in chunks of 2048, then
+    # 64 batched steps; all 16 rows of every step, each sequence's prefill
+    # logits and every sequence's caches compared with the oracle
+    name = "talker_28l_batch16_ragged"
+    shape = workload(name)
+    w = weights_for(name, 2)
+    lens = batch_lengths(shape)
+    say(f"[case] {name}, 2 layers, lengths={lens.tolist()}, {shape.decode_steps} steps")
+    tk = _talker(shape, w)
+    orc = TalkerOracle(shape, w)
+    seqs = list(range(shape.n_seqs))
+    worst_pre = 0.0
+    for s in seqs:
+        e = prefill_embeddings(shape, int(lens[s]), seq=s)
+        lg = tk.prefill(s, dev(e[:shape.chunk]))
+        for c0 in range(shape.chunk, len(e), shape.chunk):
+            lg = tk.extend(s, dev(e[c0:c0 + shape.chunk]))
+        lo, _ = orc.prefill(s, e)
+        worst_pre = max(worst_pre, rel_err(host(lg), lo))
+        assert argmax_ok(host(lg), lo), s
+    say(f"  prefills done, logits rel err max {worst_pre:.2e}")
+    assert worst_pre <= TOL_BF16
+    worst, band, exact = 0.0, 0, 0
+    for k in range(shape.decode_steps):
+        em = np.stack([step_embedding(shape, k, seq=s) for s in seqs])
+        g = host(tk.decode_batch(seqs, dev(em)))
+        o, _ = orc.decode_batch(seqs, em)
+        for s in seqs:
+            e = rel_err(g[s], o[s])
+            worst = max(worst, e)
+            assert e <= TOL_BF16, (k, s, e)
+            assert argmax_ok(g[s], o[s]), (k, s)
+            band += argmax_banded(g[s], o[s])
+            exact += int(np.argmax(g[s])) == int(np.argmax(o[s]))
+        if (k + 1) % 16 == 0:
+            say(f"  step {k + 1}: rel err max so far {worst:.2e}")
+    n_rows = shape.decode_steps * len(seqs)
+    say(f"  decode rel err max {worst:.2e}; argmax equal {exact}/{n_rows}, "
+        f"other pick inside 2x the measured error at {band}")
+    assert [tk.kv_len(s) for s in seqs] == [int(n) + shape.decode_steps for n in lens]
+    kv = max(_check_kv(tk, orc, shape, TOL_BF16, seq=s) for s in seqs)
+    say(f"  kv rel err max {kv:.2e} (16 sequences, 2 layers, K and V)")
+    tk.close()
+
+
+# -- long context -------------------------------------------------------------
 
 
 def test_long_context_outliers_one_layer_32k_sampled_rows():
@@ -357,7 +413,7 @@ def test_long_context_outliers_one_layer_32k_sampled_rows():
         lo, _ = orc.extend_rows(0, chunk, [len(chunk) - 1])
         lg = tk.prefill(0, dev(chunk)) if ci == 0 else tk.extend(0, dev(chunk))
         errs.append(rel_err(host(lg), lo[0]))
-        assert argmax_ok(host(lg), lo[0], TOL_BF16)
+        assert argmax_ok(host(lg), lo[0])
         if ci % 4 == 3:
             say(f"  chunk {ci}: logits rel err {errs[-1]:.2e}")
     assert tk.kv_len(0) == shape.prefill_len
@@ -371,9 +427,77 @@ def test_long_context_outliers_one_layer_32k_sampled_rows():
         lo, _ = orc.decode(0, e)
         g = host(tk.decode(0, dev(e)))
         errs.append(rel_err(g, lo))
-        assert argmax_ok(g, lo, TOL_BF16)
+        assert argmax_ok(g, lo)
     say(f"  logits rel err max {max(errs):.2e} over 16 chunks and 16 steps")
     assert max(errs) <= TOL_BF16
+    tk.close()
+
+
+def _no_attention(w):
+    """The same weights with o_proj zeroed: a one-layer model whose output
+    carries no attention term (the residual and the MLP only)."""
+    import copy
+    w0 = copy.deepcopy(w)
+    for lw in w0["layers"]:
+        lw["wo"] = np.zeros_like(lw["wo"])
+    return w0
+
+
+def test_long_context_one_layer_32k_sharp_attention_sampled_rows():
+    # N(0, 1) rows through one layer whose q/k norm gains are x4, so each
+    # query's softmax picks out a few of up to 33k keys and the attention
+    # carries about half of the logits' scale at any context (with the plain
+    # gains it averages thousands of keys and its share falls below the
+    # tolerance at 32k).  16 chunks of 2048 rows (the last row of each is
+    # reported), then 256 decode steps; beside the usual bar, the error is
+    # measured against the attention's own contribution (oracle minus the
+    # same oracle with o_proj = 0)
+    name = "talker_1l_ctx32k_sharp"
+    shape = workload(name)
+    w = weights_for(name)
+    say(f"[case] {name}: 16 x 2048 rows then {shape.decode_steps} decode steps")
+    emb = prefill_embeddings(shape, shape.prefill_len)
+    orc = TalkerOracle(shape, w)
+    orc0 = TalkerOracle(shape, _no_attention(w))
+    tk = _talker(shape, w)
+    errs, ratios, shares, band = [], [], [], 0
+
+    def check(g, lo, l0, what):
+        nonlocal band
+        e = rel_err(g, lo)
+        att = float(np.abs(lo - l0).max())
+        r = float(np.abs(g - lo).max()) / att
+        errs.append(e)
+        ratios.append(r)
+        shares.append(att / float(np.abs(lo).max()))
+        assert e <= TOL_BF16, (what, e)
+        assert r <= 0.1, (what, r)
+        assert argmax_ok(g, lo), what
+        band += argmax_banded(g, lo)
+
+    for ci, c0 in enumerate(range(0, shape.prefill_len, shape.chunk)):
+        chunk = emb[c0:c0 + shape.chunk]
+        lo, _ = orc.extend_rows(0, chunk, [len(chunk) - 1])
+        l0, _ = orc0.extend_rows(0, chunk, [len(chunk) - 1])
+        lg = tk.prefill(0, dev(chunk)) if ci == 0 else tk.extend(0, dev(chunk))
+        check(host(lg), lo[0], l0[0], ("chunk", ci))
+        if ci % 4 == 3:
+            say(f"  chunk {ci}: rel err {errs[-1]:.2e}, err / attention term {ratios[-1]:.2e}")
+    assert tk.kv_len(0) == shape.prefill_len
+    for k in range(shape.decode_steps):
+        e = step_embedding(shape, k)
+        lo, _ = orc.decode(0, e)
+        l0, _ = orc0.decode(0, e)
+        check(host(tk.decode(0, dev(e))), lo, l0, ("step", k))
+        if (k + 1) % 64 == 0:
+            say(f"  step {k + 1}: rel err {errs[-1]:.2e}, err / attention term {ratios[-1]:.2e}")
+    say(f"  logits rel err max {max(errs):.2e}; err / attention term max {max(ratios):.2e}; "
+        f"attention term / logit scale min {min(shares):.2f}; other pick accepted {band}")
+    picks = np.array([0, 1, 2047, 2048, 16383, 30000, 32767, 33023])
+    for which in (0, 1):
+        g = host(tk.kv_read(0, 0, which))[:, picks]
+        o = orc.kv(0, 0, which)[:, picks]
+        assert rel_err(g, o) <= TOL_BF16
     tk.close()
 
 
@@ -405,7 +529,7 @@ def test_long_context_28_layers_32k_persistent_matches_per_step(monkeypatch):
         e = dev(step_embedding(shape, k))
         a, b = host(tks[0].decode(0, e)), host(tks[1].decode(0, e))
         worst = max(worst, rel_err(a, b))
-        assert argmax_ok(a, b, TOL_BF16)
+        assert argmax_ok(a, b)
     say(f"  persistent vs per-step decode at 32k: rel diff max {worst:.2e}")
     assert worst <= TOL_BF16
     for tk in tks:
@@ -487,6 +611,42 @@ def test_persistent_decode_xcd_local_exchange_equals_device_scope(monkeypatch):
     device.sync()
     for which in (0, 1):
         assert np.array_equal(host(local.kv_read(0, 3, which)), host(device.kv_read(0, 3, which)))
+
+
+def test_persistent_decode_give_up_rolls_back_and_recovers():
+    # a wait limit of one re-poll makes the persistent decode give up (every
+    # block leaves the kernel); qtalk_sync reports it, clears the status and
+    # rolls the sequence back to the first position written since the last
+    # sync; with the default limit the next decodes match the oracle
+    from qwen3_tts_talker_amd import QtalkError
+    shape = workload("talker_28l_t128_d1024")
+    w = weights_for("talker_28l_t128_d1024", 4)
+    emb = prefill_embeddings(shape, 100)
+    steps = [step_embedding(shape, s) for s in range(3)]
+    say("[case] persistent decode gives up (wait limit 1), then recovers")
+    orc = TalkerOracle(shape, w)
+    orc.prefill(0, emb)
+    tk = _talker(shape, w)
+    tk.prefill(0, dev(emb))
+    tk.sync()
+    tk.set_wait_limit(1)
+    outs = [tk.decode(0, dev(e)) for e in steps[:2]]
+    assert tk.kv_len(0) == 102
+    with pytest.raises(QtalkError) as err:
+        tk.sync()
+    say(f"  sync: {err.value}")
+    assert "rolled back: seq 0 to 100" in str(err.value)
+    assert tk.kv_len(0) == 100
+    tk.set_wait_limit(0)
+    tk.sync()                          # the status word was cleared
+    for e in steps:
+        lo, _ = orc.decode(0, e)
+        g = host(tk.decode(0, dev(e)))
+        assert rel_err(g, lo) <= TOL_BF16 and argmax_ok(g, lo)
+    tk.sync()
+    assert tk.kv_len(0) == 103
+    del outs
+    tk.close()
 
 
 def test_persistent_decode_two_streams_interleaved():
@@ -575,13 +735,12 @@ def test_code_predictor_frames_match_oracle(monkeypatch, fused):
             e = rel_err(g, o)
             worst = max(worst, e)
             assert e <= tol, (frame, j, e)
-            assert argmax_ok(g, o, tol), (frame, j)
-            assert argmax_ok(g, o, 1e-3), (frame, j)  # the measured error is far below tol
-            band += argmax_in_band(o, tol)
+            assert argmax_ok(g, o), (frame, j)
+            band += argmax_banded(g, o)
     for l in (0, 4):
         for which in (0, 1):
             assert rel_err(host(tk.kv_read(0, l, which)), orc.kv(0, l, which)) <= tol, (l, which)
-    say(f"code predictor fused={fused}: worst rel err {worst:.2e}, argmax in band {band}")
+    say(f"code predictor fused={fused}: worst rel err {worst:.2e}, other pick accepted {band}")
     with pytest.raises(Exception):
         tk.select_head(15)
     tk.close()
@@ -741,7 +900,7 @@ def test_device_frame_loop_matches_teacher_forced_oracle():
         worst = max(worst, rel_err(g_lg, o_lg))
         assert rel_err(g_lg, o_lg) <= tol, f
         assert ids_h[f + 1, 0] == suppressed_argmax(g_lg.astype(np.float32), V - 1024, EOS)
-        assert argmax_ok(_masked(g_lg, V - 1024, EOS), _masked(o_lg, V - 1024, EOS), tol)
+        assert argmax_ok(_masked(g_lg, V - 1024, EOS), _masked(o_lg, V - 1024, EOS))
         assert rel_err(host(cp_in[0]), o_hid) <= tol
         ref = code_predictor_frame(co, o_hid, tabs[0][ids_h[f + 1, 0]],
                                    np.stack([tabs[j][ids_h[f + 1, j]] for j in range(1, 15)]))
@@ -750,7 +909,7 @@ def test_device_frame_loop_matches_teacher_forced_oracle():
             worst = max(worst, rel_err(g, ref[j]))
             assert rel_err(g, ref[j]) <= tol, (f, j)
             assert ids_h[f + 1, j + 1] == suppressed_argmax(g.astype(np.float32), cs.vocab, -1)
-            assert argmax_ok(g, ref[j], tol), (f, j)
+            assert argmax_ok(g, ref[j]), (f, j)
     say(f"device frame loop: worst rel err {worst:.2e}")
     tk.close()
     cp.close()
@@ -778,7 +937,7 @@ def test_prefill_batch_matches_oracle(n, T):
     for b in range(n):
         assert rel_err(g_lg[b], ol[b]) <= tol, b
         assert rel_err(g_hd[b], oh[b]) <= tol, b
-        assert argmax_ok(g_lg[b], ol[b], tol), b
+        assert argmax_ok(g_lg[b], ol[b]), b
         assert tk.kv_len(seqs[b]) == T
     for b in (0, n - 1):
         for which in (0, 1):
@@ -803,9 +962,51 @@ def _q8_structure_ok(v):
             and (np.abs(np.round(r)).max(axis=1) == 127).all())
 
 
+def _q8_codes(v):
+    """Codes and float32 scales of a read-back Q8_0 cache [..., hd]: each
+    32-value block's step is its max|v| / 127."""
+    b = np.asarray(v, dtype=np.float64).reshape(-1, 32)
+    d = np.abs(b).max(axis=1, keepdims=True) / 127.0
+    return np.round(np.divide(b, d, out=np.zeros_like(b), where=d > 0)), d
+
+
 def test_q8_cache_tiny_f32_prefill16_decode8():
-    # the generic kernels (f32 weights, head_dim 64): append, decode attention
-    _prefill_decode("tiny_f32_2l", 16, 8, 1e-2, kv_dtype="q8")
+    # the generic kernels (f32 weights, head_dim 64): append, split-KV decode
+    # attention over the quantised prefix plus the call's own rows
+    # unquantised.  Logits within the f32 bar; the cache's block scales
+    # equal to the oracle's bit for bit and its codes too, except a few that
+    # sit on a rounding boundary (one step apart)
+    shape = workload("tiny_f32_2l").with_(kv_dtype="q8")
+    w = weights_for("tiny_f32_2l")
+    say("[case] tiny_f32_2l, q8 cache: prefill 16, 8 decodes")
+    orc = TalkerOracle(shape, w)
+    tk = _talker(shape, w)
+    emb = prefill_embeddings(shape, 16)
+    lo, _ = orc.prefill(0, emb)
+    errs = [rel_err(host(tk.prefill(0, dev(emb))), lo)]
+    for s_ in range(8):
+        e = step_embedding(shape, s_)
+        lo, _ = orc.decode(0, e)
+        g = host(tk.decode(0, dev(e)))
+        errs.append(rel_err(g, lo))
+        assert argmax_ok(g, lo), s_
+    say(f"  logits rel err max {max(errs):.2e}")
+    assert max(errs) <= TOL_F32
+    ties = total = 0
+    for l in range(shape.n_layers):
+        for which in (0, 1):
+            g = host(tk.kv_read(0, l, which))
+            o = orc.kv(0, l, which)
+            (cg, dg), (co, do) = _q8_codes(g), _q8_codes(o)
+            total += cg.size
+            assert np.array_equal(dg, do), (l, which)          # every block scale
+            assert (np.abs(cg - co) <= 1).all(), (l, which)     # codes: one step at most
+            ties += int((cg != co).sum())
+    # a code can differ only where the float32 value sits on a rounding
+    # boundary, which the two sides' last-bit differences may cross
+    assert ties <= total // 200, (ties, total)
+    say(f"  q8 cache: scales bit-exact, codes equal except {ties} of {total} (one step each)")
+    tk.close()
 
 
 @pytest.mark.parametrize("fused", ["1", "0"])
@@ -827,7 +1028,8 @@ def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
     lg = tk.prefill(0, dev(emb[:T]))
     lo, _ = orc.prefill(0, emb[:T])
     errs = [rel_err(host(lg), lo)]
-    # an extend at p0 = 300 attends to the quantised rows of both chunks
+    # an extend at p0 = 300 attends to the first chunk quantised and to its
+    # own 200 rows unquantised
     lg = tk.extend(0, dev(emb[T:]))
     lo, _ = orc.extend(0, emb[T:])
     errs.append(rel_err(host(lg), lo))
@@ -836,7 +1038,7 @@ def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
         g = host(tk.decode(0, dev(e)))
         o, _ = orc.decode(0, e)
         errs.append(rel_err(g, o))
-        assert argmax_ok(g, o, tol), s_
+        assert argmax_ok(g, o), s_
     tk.sync()
     say(f"q8 fused={fused}: logits rel err max {max(errs):.2e}")
     assert max(errs) <= tol
@@ -845,6 +1047,16 @@ def test_q8_cache_talker_prefill_decode(monkeypatch, fused):
             g = host(tk.kv_read(0, l, which))
             assert rel_err(g, orc.kv(0, l, which)) <= tol, (l, which)
             assert _q8_structure_ok(g), (l, which)
+    # a two-row prefill (the code predictor's shape): the second row attends
+    # to the first unquantised
+    two = prefill_embeddings(shape, 2, seq=5)
+    lo, _ = orc.prefill(0, two)
+    g = host(tk.prefill(0, dev(two)))
+    assert rel_err(g, lo) <= tol and argmax_ok(g, lo)
+    e = step_embedding(shape, 99)
+    lo, _ = orc.decode(0, e)
+    g = host(tk.decode(0, dev(e)))
+    assert rel_err(g, lo) <= tol and argmax_ok(g, lo)
     tk.close()
 
 

@@ -341,11 +341,14 @@ def _sign_flipped_rope(x, pos, theta):
     return ot.rope_neox(x, -np.asarray(pos), theta)
 
 
+_plain_attention = ot.causal_gqa_attention
+
+
 def _modulo_gqa(q, kc, vc, positions, scale):
     # wrong group map: h % n_kv instead of h // G
     nkv = kc.shape[0]
     perm = [h % nkv for h in range(q.shape[1])]
-    return ot.causal_gqa_attention(q, kc[perm], vc[perm], positions, scale)
+    return _plain_attention(q, kc[perm], vc[perm], positions, scale)
 
 
 def _fresh_kv_in_prefill(self, l, x, seq, p0):
@@ -519,3 +522,57 @@ def test_prefill_batch_is_independent_prefills():
         orc.prefill_batch([0, 0], embs[:2])
     with pytest.raises(OverflowError):
         orc.prefill_batch([0], np.zeros((1, shape.cap + 1, shape.hidden)))
+
+
+# -- power of the long-context attention check -----------------------------------
+
+def _window_attention(q, kc, vc, positions, scale):
+    # planted: keys older than 2048 positions dropped
+    out = np.empty_like(q)
+    for t in range(q.shape[0]):
+        lo = max(0, int(positions[t]) - 2047)
+        out[t:t + 1] = _plain_attention(q[t:t + 1], kc[:, lo:], vc[:, lo:],
+                                        positions[t:t + 1] - lo, scale)
+    return out
+
+
+def _long_context_rows(shape, w, n_ctx, steps):
+    """Logits of the rows the long-context GPU check reads: the last row of
+    each 2048-row chunk, then ``steps`` decode steps."""
+    from synth import step_embedding as se
+    orc = TalkerOracle(shape, w)
+    emb = prefill_embeddings(shape, n_ctx)
+    out = []
+    for c0 in range(0, n_ctx, 2048):
+        ch = emb[c0:c0 + 2048]
+        out.append(orc.extend_rows(0, ch, [len(ch) - 1])[0][0])
+    for k in range(steps):
+        out.append(orc.decode(0, se(shape, k))[0])
+    return np.stack(out)
+
+
+def test_long_context_check_sees_the_attention(monkeypatch):
+    # the sharp-attention workload (q/k norm gains x4) at 4096 positions: the
+    # GPU check's statistics (logit error over the checked rows; error over
+    # the attention term) must reject an attention that is zeroed, that drops
+    # keys older than 2048 positions, or that maps query heads to the wrong
+    # KV head.  With the plain gains the attention term at long context is
+    # about the size of the tolerance, which is why the check uses this one.
+    shape = workload("talker_1l_ctx32k_sharp").with_(cap=4200)
+    w = make_weights(shape)
+    ref = _long_context_rows(shape, w, 4096, 4)
+    import copy
+    w0 = copy.deepcopy(w)
+    w0["layers"][0]["wo"][:] = 0
+    noatt = _long_context_rows(shape, w0, 4096, 4)
+    att = np.abs(ref - noatt).max(axis=1)
+    assert (att / np.abs(ref).max(axis=1) > 0.2).all()
+    bad = {"zeroed": noatt}
+    monkeypatch.setattr(ot, "causal_gqa_attention", _window_attention)
+    bad["window"] = _long_context_rows(shape, w, 4096, 4)
+    monkeypatch.setattr(ot, "causal_gqa_attention", _modulo_gqa)
+    bad["gqa map"] = _long_context_rows(shape, w, 4096, 4)
+    for name, got in bad.items():
+        err = (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max()
+        ratio = (np.abs(got - ref).max(axis=1) / att).max()
+        assert err > 2e-2 and ratio > 0.1, (name, err, ratio)
