@@ -97,6 +97,25 @@ __device__ __forceinline__ void kv_load(const char* row, int hd, int d, float* f
   else KVIO<KVT>::template load<N>(row, d, f);
 }
 
+// v[l ^ 16] and v[l ^ 32] combined with v[l] by v_permlane16_swap (odd
+// 16-lane rows of one operand with the even rows of the other) and
+// v_permlane32_swap (upper half with lower half)
+__device__ __forceinline__ float half_xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of each 16-lane row)
+__device__ __forceinline__ float xor_sum4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // max over each aligned 32-lane half of the wave (DPP inside 16-lane rows,
 // then v_permlane16_swap across the row pair)
 __device__ __forceinline__ float half32_max(float v) {
@@ -255,28 +274,78 @@ void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV attention.  grid (n_splits, n_kv, rows), 256 threads.  A block owns
-// keys [c*kps, min((c+1)*kps, pos+1)) of KV head g for row t and serves all G
-// query heads of that group from one read of K and V (the group shares the KV
-// head).  Keys are walked in chunks of 64 with an online softmax.
-//   score phase: 16 lanes per key (hd/16 dims each), 16 keys per block pass
-//   value phase: 16 lanes per key row, 16 key slots, per-thread accumulators
+// Split-KV attention.  grid (n_splits, n_kv, rows), 256 threads (4 waves).
+// Block (c, g, t) owns keys [c*kps, min((c+1)*kps, pos+1)) of KV head g for
+// row t and serves all G query heads of the group from one read of K and V.
+// Lane roles: a slot is one 16-lane row of a wave (16 slots per block), lane
+// sub of a slot holds dims sub*DPL .. +DPL.  Slot s of wave w takes keys
+// kb + 16u + 4w + s (u < U) of each 16U-key tile, so one wave instruction
+// loads 4 consecutive key rows.  Every slot keeps its own online softmax (log2
+// units: q carries scale * log2(e)), so the key loop has no cross-slot
+// reduction and no barrier; the next tile's rows are loaded (clamped to the
+// last key, always a written row) before the current tile's arithmetic.  The
+// slots are combined once at the end: within a wave by lane swaps, across the
+// 4 waves through LDS.  Partials (o unnormalised, m in log2 units, l) go to
+// part_o / part_ml for k_attn_merge, or with one split straight to out.
+
+template <typename KVT, int N>
+struct KvRaw;
+template <int N>
+struct KvRaw<f16_t, N> {
+  typedef _Float16 vec __attribute__((ext_vector_type(N)));
+  vec v;
+  __device__ __forceinline__ void load(const char* row, int, int d) {
+    v = *reinterpret_cast<const vec*>(reinterpret_cast<const f16_t*>(row) + d);
+  }
+  __device__ __forceinline__ void get(float* f) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = (float)v[i];
+  }
+};
+template <int N>
+struct KvRaw<float, N> {
+  typedef float vec __attribute__((ext_vector_type(N)));
+  vec v;
+  __device__ __forceinline__ void load(const char* row, int, int d) {
+    v = *reinterpret_cast<const vec*>(reinterpret_cast<const float*>(row) + d);
+  }
+  __device__ __forceinline__ void get(float* f) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = v[i];
+  }
+};
+template <int N>
+struct KvRaw<q8_t, N> {  // N codes of one 32-value block and its scale
+  typedef signed char vec __attribute__((ext_vector_type(N)));
+  vec c;
+  f16_t sc;
+  __device__ __forceinline__ void load(const char* row, int hd, int d) {
+    c = *reinterpret_cast<const vec*>(row + d);
+    sc = *reinterpret_cast<const f16_t*>(row + hd + (d >> 5) * 2);
+  }
+  __device__ __forceinline__ void get(float* f) const {
+    const float s = (float)sc;
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = (float)c[i] * s;
+  }
+};
 
 template <int HD, int G, typename KVT, int OUT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   constexpr int DPL = HD / 16;
-  constexpr int KC = 64;
-  __shared__ float s_p[G][KC];
-  __shared__ float s_m[G], s_l[G], s_alpha[G];
-  __shared__ float s_red[16][HD];
+  constexpr int U = 4;          // keys per slot and tile
+  constexpr int TILE = 16 * U;  // keys per tile
+  constexpr bool Q8 = std::is_same<KVT, q8_t>::value;
+  __shared__ __attribute__((aligned(16))) float s_acc[4][G][HD];
+  __shared__ float s_m[4][G], s_l[4][G];
 
   const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane >> 4, sub = lane & 15;
   const int nq = a.n_heads, nkv = a.n_kv_heads;
   const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
-  const int n_ctx = pos + 1;
   const int k_begin = c * a.keys_per_split;
-  const int k_end = min(n_ctx, k_begin + a.keys_per_split);
+  const int k_end = min(pos + 1, k_begin + a.keys_per_split);
 
   if (k_begin >= k_end) {  // this split lies past the row's context
     if (OUT == ATT_PARTIAL && tid < G) {
@@ -291,159 +360,193 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   const size_t head_off = (size_t)(seq * nkv + g) * a.cap * RB;
   const char* Kp = reinterpret_cast<const char*>(a.kc) + head_off;
   const char* Vp = reinterpret_cast<const char*>(a.vc) + head_off;
-
   // Q8_0 cache: keys from `fresh` on are rows of this call, read unquantised
-  // from the projection buffer (key j is row t - (pos - j): the call's rows of
-  // one sequence are consecutive rows at consecutive positions)
-  constexpr bool Q8 = std::is_same<KVT, q8_t>::value;
+  // from the projection buffer (key j is row t - (pos - j): the call's rows
+  // of one sequence are consecutive rows at consecutive positions)
   const int fresh = a.rows.uniform == 0 ? pos : a.rows.p0;
-  const float* Kf = a.q + (size_t)(nq + g) * HD;
-  const float* Vf = a.q + (size_t)(nq + nkv + g) * HD;
+  const float* Kf = a.q + (size_t)(nq + g) * HD + sub * DPL;
+  const float* Vf = a.q + (size_t)(nq + nkv + g) * HD + sub * DPL;
 
-  // score-phase lane roles
-  const int sub = lane & 15;  // dims sub*DPL .. +DPL
-  const int kq = lane >> 4;   // key within the wave's group of 4
   float qr[G][DPL];
+  const float qscale = a.scale * 1.4426950408889634f;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float* qp = a.q + (size_t)t * a.ldq + (size_t)(g * G + h) * HD + sub * DPL;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qr[h][e] = qp[e] * a.scale;
+    for (int e = 0; e < DPL; ++e) qr[h][e] = qp[e] * qscale;
   }
-  // value-phase roles
-  const int vs = tid >> 4;  // key slot 0..15
-  const int vd = tid & 15;  // dims vd*DPL .. +DPL
-  float acc[G][DPL];
+  // running maxima start at a finite floor far below any score, so no step
+  // has to single out a slot, wave or split without keys: their weight
+  // 2^(floor - max) is 0, and among themselves 2^0 = 1 times l = 0 and o = 0
+  constexpr float FLOOR = -1e30f;
+  float m[G], l[G], acc[G][DPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    m[h] = FLOOR;
+    l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-  if (tid < G) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.f;
   }
 
-  for (int kb = k_begin; kb < k_end; kb += KC) {
-    // scores
+  const int kofs = 4 * wave + slot;
+  KvRaw<KVT, DPL> kr[U], vr[U];
+  auto load_tile = [&](int kb) {
 #pragma unroll
-    for (int p = 0; p < KC / 16; ++p) {
-      const int jl = p * 16 + wave * 4 + kq;
-      const int j = kb + jl;
-      float kf[DPL];
-      const bool ok = j < k_end;
-      if (ok) {
-        if (Q8 && j >= fresh) {
+    for (int u = 0; u < U; ++u) {
+      const int j = min(kb + 16 * u + kofs, k_end - 1);
+      kr[u].load(Kp + (size_t)j * RB, HD, sub * DPL);
+      vr[u].load(Vp + (size_t)j * RB, HD, sub * DPL);
+    }
+  };
+  load_tile(k_begin);
+  for (int kb = k_begin; kb < k_end; kb += TILE) {
+    float kf[U][DPL], vf[U][DPL];
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) kf[e] = Kf[(size_t)(t - pos + j) * a.ldq + sub * DPL + e];
-        } else {
-          kv_load<KVT, DPL>(Kp + (size_t)j * RB, HD, sub * DPL, kf);
+    for (int u = 0; u < U; ++u) {
+      kr[u].get(kf[u]);
+      vr[u].get(vf[u]);
+    }
+    load_tile(kb + TILE < k_end ? kb + TILE : kb);  // next tile (the last one reloads itself)
+    if (Q8 && kb + TILE > fresh) {  // rows of this call: as computed
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = min(kb + 16 * u + kofs, k_end - 1);
+        if (j >= fresh) {
+          const size_t r = (size_t)(t - pos + j) * a.ldq;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) {
+            kf[u][e] = Kf[r + e];
+            vf[u][e] = Vf[r + e];
+          }
         }
       }
+    }
+    float sc[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = kb + 16 * u + kofs < k_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
-        if (ok) {
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) d = fmaf(qr[h][e], kf[e], d);
-        }
-        d = group_sum<16>(d);
-        if (sub == 0) s_p[h][jl] = ok ? d : -INFINITY;
+        for (int e = 0; e < DPL; ++e) d = fmaf(qr[h][e], kf[u][e], d);
+        d = row16_sum(d);
+        sc[u][h] = ok ? d : -INFINITY;
       }
     }
-    __syncthreads();
-    // softmax bookkeeping, one wave per head
-    for (int h = wave; h < G; h += 4) {
-      const float s = s_p[h][lane];
-      const float mold = s_m[h];
-      const float mnew = fmaxf(mold, wave_max(s));
-      const float pv = (s == -INFINITY) ? 0.f : __expf(s - mnew);
-      s_p[h][lane] = pv;
-      const float ps = wave_sum(pv);
-      if (lane == 0) {
-        const float alpha = (mold == -INFINITY) ? 0.f : __expf(mold - mnew);
-        s_alpha[h] = alpha;
-        s_l[h] = s_l[h] * alpha + ps;
-        s_m[h] = mnew;
-      }
-    }
-    __syncthreads();
-    // values
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float al = s_alpha[h];
+      float mx = m[h];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] *= al;
-    }
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+      float p[U], ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < KC / 16; ++r) {
-      const int jl = r * 16 + vs;
-      const int j = kb + jl;
-      if (j < k_end) {
-        float vf[DPL];
-        if (Q8 && j >= fresh) {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) vf[e] = Vf[(size_t)(t - pos + j) * a.ldq + vd * DPL + e];
-        } else {
-          kv_load<KVT, DPL>(Vp + (size_t)j * RB, HD, vd * DPL, vf);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pv = s_p[h][jl];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
-        }
+      for (int u = 0; u < U; ++u) {
+        p[u] = __builtin_amdgcn_exp2f(sc[u][h] - mx);  // 0 for a masked key (-inf)
+        ps += p[u];
       }
+      l[h] = fmaf(l[h], alpha, ps);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        float v = acc[h][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v = fmaf(p[u], vf[u][e], v);
+        acc[h][e] = v;
+      }
+      m[h] = mx;
     }
-    __syncthreads();
   }
 
-  // reduce the 16 key slots and write
+  // the 4 slots of a wave: scale each by 2^(m_slot - m_wave) and add them
+  // (slots are the wave's 16-lane rows: swaps across 16 and 32 lanes)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    const float mw4 = half_xor16_max(half_xor32_max(m[h]));
+    const float scl = __builtin_amdgcn_exp2f(m[h] - mw4);
+    const float lw = xor_sum4(l[h] * scl);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) s_red[vs][vd * DPL + e] = acc[h][e];
-    __syncthreads();
-    if (tid < HD) {
-      float o = 0.f;
+    for (int e = 0; e < DPL; ++e) acc[h][e] = xor_sum4(acc[h][e] * scl);
+    if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o += s_red[i][tid];
-      const int qh = g * G + h;
-      if (OUT == ATT_PARTIAL) {
-        const size_t base = (size_t)(t * nq + qh) * a.n_splits + c;
-        a.part_o[base * HD + tid] = o;
-        if (tid == 0) {
-          a.part_ml[base * 2] = s_m[h];
-          a.part_ml[base * 2 + 1] = s_l[h];
-        }
-      } else {
-        const float v = o / s_l[h];
-        const size_t oi = (size_t)t * a.ldo + (size_t)qh * HD + tid;
-        if (OUT == ATT_F32) reinterpret_cast<float*>(a.out)[oi] = v;
-        else reinterpret_cast<bf16_t*>(a.out)[oi] = (bf16_t)f32_to_bf16(v);
-      }
+      for (int e = 0; e < DPL; ++e) s_acc[wave][h][sub * DPL + e] = acc[h][e];
     }
-    __syncthreads();
+    if (lane == 0) {
+      s_m[wave][h] = mw4;
+      s_l[wave][h] = lw;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += 256) {
+    const int h = idx / HD, d = idx % HD;
+    float M = FLOOR;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(s_m[w][h] - M);
+      o = fmaf(wt, s_acc[w][h][d], o);
+      L = fmaf(wt, s_l[w][h], L);
+    }
+    const int qh = g * G + h;
+    if (OUT == ATT_PARTIAL) {
+      const size_t base = (size_t)(t * nq + qh) * a.n_splits + c;
+      a.part_o[base * HD + d] = o;
+      if (d == 0) {
+        a.part_ml[base * 2] = M;
+        a.part_ml[base * 2 + 1] = L;
+      }
+    } else {
+      const float v = o / L;
+      const size_t oi = (size_t)t * a.ldo + (size_t)qh * HD + d;
+      if (OUT == ATT_F32) reinterpret_cast<float*>(a.out)[oi] = v;
+      else reinterpret_cast<bf16_t*>(a.out)[oi] = (bf16_t)f32_to_bf16(v);
+    }
   }
 }
 
-// grid (n_heads, rows), hd threads: combine the splits' (m, l, o)
+// grid (n_heads, rows), head_dim threads: combine the splits' (o, m, l) of
+// one (row, query head).  The splits' weights 2^(m_c - M) / L are formed
+// once in LDS; each thread then sums its dim over the splits with the loads
+// of 8 splits in flight.  Output float32, or bf16 (the A operand of the
+// matrix-core o_proj).
+template <bool BF16>
 __global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
+  __shared__ float s_w[MAX_SPLITS];
   const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
   const int ns = a.n_splits, HD = a.head_dim;
   const size_t base = (size_t)(t * a.n_heads + h) * ns;
   const float* ml = a.part_ml + base * 2;
-  float M = -INFINITY;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, ml[2 * c]);
-  float L = 0.f, o = 0.f;
-  for (int c = 0; c < ns; ++c) {
-    const float l = ml[2 * c + 1];
-    if (l > 0.f) {
-      const float w = __expf(ml[2 * c] - M);
-      L = fmaf(w, l, L);
-      o = fmaf(w, a.part_o[(base + c) * HD + d], o);
+  if (d < 64) {  // one wave forms the weights
+    float M = -INFINITY;
+    for (int c = d; c < ns; c += 64) M = fmaxf(M, ml[2 * c]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int c = d; c < ns; c += 64) {
+      const float lc = ml[2 * c + 1];
+      const float w = lc > 0.f ? __builtin_amdgcn_exp2f(ml[2 * c] - M) : 0.f;
+      s_w[c] = w;
+      L = fmaf(w, lc, L);
     }
+    L = wave_sum(L);
+    for (int c = d; c < ns; c += 64) s_w[c] /= L;
   }
-  reinterpret_cast<float*>(a.out)[(size_t)t * a.ldo + (size_t)h * HD + d] = o / L;
+  __syncthreads();
+  const float* po = a.part_o + base * HD + d;
+  float o = 0.f;
+  int c = 0;
+  for (; c + 8 <= ns; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = po[(size_t)(c + i) * HD];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o = fmaf(s_w[c + i], v[i], o);
+  }
+  for (; c < ns; ++c) o = fmaf(s_w[c], po[(size_t)c * HD], o);
+  const size_t oi = (size_t)t * a.ldo + (size_t)h * HD + d;
+  if (BF16) reinterpret_cast<bf16_t*>(a.out)[oi] = (bf16_t)f32_to_bf16(o);
+  else reinterpret_cast<float*>(a.out)[oi] = o;
 }
 
 template <int HD, typename KVT, int OUT>
@@ -476,8 +579,9 @@ void launch_attn_decode(KvKind kv, AttnOut mode, AttnArgs a, hipStream_t st) {
   else launch_kv<64>(kv, mode, a, st);
 }
 
-void launch_attn_merge(AttnArgs a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.n_heads, a.rows.n), dim3(a.head_dim), 0, st, a);
+void launch_attn_merge(AttnArgs a, bool bf16_out, hipStream_t st) {
+  if (bf16_out) hipLaunchKernelGGL(k_attn_merge<true>, dim3(a.n_heads, a.rows.n), dim3(a.head_dim), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_merge<false>, dim3(a.n_heads, a.rows.n), dim3(a.head_dim), 0, st, a);
 }
 
 // ---------------------------------------------------------------------------

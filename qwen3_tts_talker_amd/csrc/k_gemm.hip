@@ -484,8 +484,10 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_add_norm(GemmArgs a, int 
   }
 }
 
+bool skinny_shape_ok(int N, int K) { return N % 32 == 0 && K % SK_KC == 0; }
+
 static bool skinny_ok(const GemmArgs& a) {
-  return a.M >= 1 && a.M <= 128 && a.N % 32 == 0 && a.K % SK_KC == 0;
+  return a.M >= 1 && a.M <= 128 && skinny_shape_ok(a.N, a.K);
 }
 
 // waves per block: the largest divisor of the chunk count up to 8 (every

@@ -71,13 +71,15 @@ struct AttnArgs {
   int keys_per_split;
   int n_splits;
   float* part_o;   // [rows][n_heads][n_splits][hd]
-  float* part_ml;  // [rows][n_heads][n_splits][2]
+  float* part_ml;  // [rows][n_heads][n_splits][2]: m (log2 units), l
   void* out;       // final output row t at out + t*ldo (f32 or bf16)
   int ldo;
   RowMeta rows;
 };
+constexpr int MAX_SPLITS = 128;  // key splits per row of the split-KV attention
 void launch_attn_decode(KvKind kv, AttnOut mode, AttnArgs a, hipStream_t st);
-void launch_attn_merge(AttnArgs a, hipStream_t st);
+// combine the ATT_PARTIAL splits into out (float32, or bf16 with bf16_out)
+void launch_attn_merge(AttnArgs a, bool bf16_out, hipStream_t st);
 
 // Causal GQA attention of T uniform rows (positions p0 .. p0+T-1 of one
 // sequence) over the f16 cache on the matrix cores; output bf16 rows.
@@ -120,6 +122,8 @@ void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
                           hipStream_t st);
 bool gemm_shape_ok(int M, int N, int K);
+// shapes the skinny (<= 128-row) product takes: N % 32 == 0, K % 128 == 0
+bool skinny_shape_ok(int N, int K);
 
 // out[t][k] = bf16(RMSNorm(x[t]) * g)
 void launch_rmsnorm_bf16(const float* x, int ldx, int T, int K, const float* g,

@@ -34,7 +34,7 @@ namespace {
 
 constexpr int GEMV_ROWS = MAX_ROWS;  // rows per matrix-vector pass
 constexpr int MFMA_MIN_ROWS = 17;    // prefill rows that switch to the matrix cores
-constexpr int MAX_SPLITS = 128;      // key splits of the decode attention
+constexpr int BATCH_MFMA_MIN = 8;    // batched-decode rows that switch to the matrix cores
 constexpr int MAX_CHUNK = 2048;      // rows per matrix-core pass
 // prefill / extend of at most this many rows runs as consecutive persistent
 // single-row launches when the persistent decode is available (one launch
@@ -228,6 +228,20 @@ struct Fwd {
     return m;
   }
 
+  // Key splits of the split-KV attention: about 1024 blocks over all rows
+  // and KV heads (multiples of 64 keys), at most MAX_SPLITS per row.
+  void set_splits(AttnArgs& a, const RowMeta& r) const {
+    long total = 0;
+    for (int t = 0; t < r.n; ++t)
+      total += 1 + (r.uniform == 1 ? r.p0 + t : (r.uniform == 2 ? r.p0 + t % r.per : r.pos[t]));
+    total *= g.n_kv_heads;
+    const int mx = max_ctx(r);
+    int kps = 64 * (int)((total + 1024L * 64 - 1) / (1024L * 64));
+    kps = std::max(kps, 64 * ((mx + 64 * MAX_SPLITS - 1) / (64 * MAX_SPLITS)));
+    a.keys_per_split = kps;
+    a.n_splits = (mx + kps - 1) / kps;
+  }
+
   void gemv(const void* W, int O, int K, const float* X, int ldx, int n, const float* gain,
             float* Y, int ldy, Epilogue epi, float* norm_out = nullptr, int ld_norm = 0) {
     GemvArgs a{W, O, K, X, ldx, n, gain, g.rms_eps, Y, ldy, norm_out, ld_norm};
@@ -241,11 +255,9 @@ struct Fwd {
     gemv(L.wqkv, c->qkv_dim, H, c->x, H, n, L.g_in, c->qkv, c->qkv_dim, EPI_STORE);
     qk_append(l, rows);
     AttnArgs a = attn_args(l, rows);
-    const int ctx = max_ctx(rows);
-    a.keys_per_split = 64 * ((ctx + 64 * MAX_SPLITS - 1) / (64 * MAX_SPLITS));
-    a.n_splits = (ctx + a.keys_per_split - 1) / a.keys_per_split;
+    set_splits(a, rows);
     launch_attn_decode(c->kv, ATT_PARTIAL, a, st);
-    launch_attn_merge(a, st);
+    launch_attn_merge(a, false, st);
     gemv(L.wo, H, c->q_dim, c->att, c->q_dim, n, nullptr, c->x, H, EPI_ADD);
     gemv(L.wgu, g.intermediate, H, c->x, H, n, L.g_post, c->act, g.intermediate, EPI_SWIGLU);
     gemv(L.wd, H, g.intermediate, c->act, g.intermediate, n, nullptr, c->x, H, EPI_ADD);
@@ -323,6 +335,34 @@ struct Fwd {
     gemm(c->hn, H, L.wgu, T, 2 * I, H, act_b, I, EPI_SWIGLU);
     if (l + 1 < g.n_layers) gemm_add_norm(act_b, I, L.wd, T, H, I, c->layers[l + 1].g_in);
     else gemm(act_b, I, L.wd, T, H, I, c->x, H, EPI_ADD);
+  }
+
+  // Matrix-core layer for decode rows held in c->x (one row per sequence,
+  // any positions: the batched decode).  The projections read bf16
+  // activations, as in the matrix-core prefill; the attention is the split-KV
+  // kernel, merged straight into bf16 for o_proj.  `normed` as in layer_mfma.
+  void layer_rows_mfma(int l, const RowMeta& rows, bool normed) {
+    const LayerDev& L = c->layers[l];
+    const int n = rows.n, H = g.hidden, I = g.intermediate;
+    bf16_t* att_b = reinterpret_cast<bf16_t*>(c->att);
+    bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
+    if (!normed) launch_rmsnorm_bf16(c->x, H, n, H, L.g_in, g.rms_eps, c->hn, H, st);
+    gemm(c->hn, H, L.wqkv, n, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
+    qk_append(l, rows);
+    AttnArgs a = attn_args(l, rows);
+    set_splits(a, rows);
+    launch_attn_decode(c->kv, ATT_PARTIAL, a, st);
+    launch_attn_merge(a, true, st);
+    gemm_add_norm(att_b, c->q_dim, L.wo, n, H, c->q_dim, L.g_post);
+    gemm(c->hn, H, L.wgu, n, 2 * I, H, act_b, I, EPI_SWIGLU);
+    if (l + 1 < g.n_layers) gemm_add_norm(act_b, I, L.wd, n, H, I, c->layers[l + 1].g_in);
+    else gemm(act_b, I, L.wd, n, H, I, c->x, H, EPI_ADD);
+  }
+
+  bool rows_mfma_ok() const {
+    return c->w_bf16 && skinny_shape_ok(c->qkv_dim, g.hidden) && skinny_shape_ok(g.hidden, c->q_dim) &&
+           skinny_shape_ok(2 * g.intermediate, g.hidden) && skinny_shape_ok(g.hidden, g.intermediate) &&
+           g.intermediate % 16 == 0;
   }
 
   // x += A * B^T, then hn = bf16(RMSNorm(x) * gain)
@@ -474,7 +514,11 @@ struct Fwd {
   }
 
   // one row per listed sequence (batched decode)
+  // one row per listed sequence (batched decode): 8 or more rows on the
+  // matrix cores (each weight matrix read once per pass), fewer on the
+  // matrix-vector kernel
   qtalk_status run_batch(const int32_t* seqs, int n, const float* emb, float* logits, float* hidden_out) {
+    const bool mfma = rows_mfma_ok();
     for (int b0 = 0; b0 < n; b0 += GEMV_ROWS) {
       const int nb = std::min(GEMV_ROWS, n - b0);
       RowMeta rows{};
@@ -487,7 +531,10 @@ struct Fwd {
       if (hipMemcpyAsync(c->x, emb + (size_t)b0 * g.hidden, (size_t)nb * g.hidden * 4,
                          hipMemcpyDeviceToDevice, st) != hipSuccess)
         return fail(c, QTALK_E_DEVICE, "cannot copy the input rows");
-      for (int l = 0; l < g.n_layers; ++l) layer_gemv(l, rows);
+      for (int l = 0; l < g.n_layers; ++l) {
+        if (mfma && nb >= BATCH_MFMA_MIN) layer_rows_mfma(l, rows, l > 0);
+        else layer_gemv(l, rows);
+      }
       head(c->x, nb, logits + (size_t)b0 * g.vocab,
            hidden_out ? hidden_out + (size_t)b0 * g.hidden : nullptr);
     }
