@@ -143,6 +143,22 @@ qtalk_status qtalk_extend(qtalk_ctx *ctx, int32_t seq, const float *emb,
 qtalk_status qtalk_decode(qtalk_ctx *ctx, int32_t seq, const float *emb,
                           float *logits, float *hidden_out);
 
+/* qtalk_decode without the context's exchange buffers, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same persistent kernel and
+ * arithmetic as qtalk_decode (same results bit for bit), whose blocks pass
+ * their words and attention partials through one static device array per GPU
+ * (2 MiB, held until the process ends) instead of buffers of the context.
+ * It allocates and frees nothing and enqueues no memset.  Calls on one GPU
+ * share that array: they are ordered per device like every batch-1 decode,
+ * and calls from several host threads on one GPU at once race.  Same
+ * arguments, outputs and errors as qtalk_decode, plus QTALK_E_INVAL when the
+ * context has no persistent decode (it needs the Talker geometry and bf16
+ * weights) or would need more than the array holds, and QTALK_E_DEVICE when
+ * the array has no address on this device. */
+qtalk_status qtalk_decode_noalloc(qtalk_ctx *ctx, int32_t seq, const float *emb,
+                                  float *logits, float *hidden_out);
+
 /* Batched decode: one position for each of n distinct sequences seqs[0..n)
  * (a HOST array), emb [n][hidden], logits [n][vocab], hidden_out [n][hidden]
  * (nullable).  Row i is exactly the single-sequence decode of seqs[i]; the

@@ -14,6 +14,7 @@ from .qtalk import (  # noqa: F401
     qtalk_create,
     qtalk_decode,
     qtalk_decode_batch,
+    qtalk_decode_noalloc,
     qtalk_destroy,
     qtalk_embed_sum,
     qtalk_extend,

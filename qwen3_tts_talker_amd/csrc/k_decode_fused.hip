@@ -944,6 +944,15 @@ hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool
   return hipLaunchCooperativeKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
 }
 
+__global__ void k_fill_zero(uint64_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+void launch_fill_zero(uint64_t* p, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(256), 0, st, p, n);
+}
+
 __global__ void k_xcc_ids(int* ids) {
   if (threadIdx.x == 0) ids[blockIdx.x] = (int)pd::xcc_id();
 }

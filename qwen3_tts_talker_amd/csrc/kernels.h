@@ -175,6 +175,8 @@ int fused_decode_blocks();
 size_t fused_decode_ll_words(int n_layers);
 size_t fused_decode_part_words(int n_layers);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st, bool cooperative);
+// zero n 8-byte words (a kernel, not a memset node)
+void launch_fill_zero(uint64_t* p, size_t n, hipStream_t st);
 
 // frame-step glue (k_frame.hip)
 constexpr int MAX_EMBED_GROUPS = 32;

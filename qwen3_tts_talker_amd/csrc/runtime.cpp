@@ -122,6 +122,42 @@ struct DecodeChain {
 constexpr int MAX_DEVICES = 64;
 DecodeChain g_chain[MAX_DEVICES];
 
+// Exchange words and chunk partials of the persistent decode for
+// qtalk_decode_noalloc, in a static device array instead of the context's
+// buffers: each device holds its own copy until the process ends.  Host code
+// uses only the address resolved per device at qtalk_create (the array's name
+// in host code is a stand-in, not a device address).  Every persistent launch
+// through it takes a fresh epoch from the device's counter, so words left by
+// an earlier launch (of any context) never match; the launches are
+// serialised per device (DecodeChain), whose mutex guards these entries.
+constexpr size_t SCRATCH_BYTES = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+struct StaticScratch {
+  void* ptr = nullptr;  // this device's copy of `scratch`
+  bool resolved = false;
+  uint32_t epoch = 0;   // last epoch used in it
+};
+StaticScratch g_scratch[MAX_DEVICES];
+
+// resolve `scratch` on the current device (once per device)
+void resolve_scratch(int dev) {
+  std::lock_guard<std::mutex> lock(g_chain[dev].mu);
+  StaticScratch& z = g_scratch[dev];
+  if (z.resolved) return;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) z.ptr = p;
+  else (void)hipGetLastError();
+  z.resolved = true;
+}
+
+// where a persistent launch exchanges its words: the context's buffers or
+// the device's static array, each with its own epoch counter
+struct Exchange {
+  uint64_t* ll;
+  uint64_t* part;
+  uint32_t* epoch;
+};
+
 qtalk_status fail(qtalk_ctx* c, qtalk_status s, const char* fmt, ...) {
   if (c) {
     char buf[512];
@@ -460,8 +496,11 @@ struct Fwd {
     return QTALK_OK;
   }
 
-  // one row of sequence `seq` at position `pos` as one persistent launch
-  qtalk_status run_fused(int seq, int pos, const float* emb, float* logits, float* hidden_out) {
+  // one row of sequence `seq` at position `pos` as one persistent launch,
+  // exchanging through the context's buffers or (static_words) the device's
+  // static array
+  qtalk_status run_fused(int seq, int pos, const float* emb, float* logits, float* hidden_out,
+                         bool static_words = false) {
     FusedDecodeArgs a{};
     a.w = reinterpret_cast<const bf16_t*>(c->wblob);
     a.layer_stride = c->per_layer;
@@ -483,23 +522,28 @@ struct Fwd {
     a.emb = emb;
     a.logits = logits;
     a.hidden_out = hidden_out;
-    a.ll = c->ll;
-    a.part = c->fpart;
     a.err = c->ferr;
     a.spin_limit = c->spin_limit;
-    if (c->epoch + 1 >= (1u << 26)) {  // epochs would wrap: clear the words and restart
-      if (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, st) != hipSuccess ||
-          hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, st) != hipSuccess)
-        return fail(c, QTALK_E_DEVICE, "cannot clear the decode exchange words");
-      c->epoch = 0;
-    }
-    a.epoch = c->epoch + 1;
     a.xcd_local = c->xcd_local;
     DecodeChain& ch = g_chain[c->dev];
     std::lock_guard<std::mutex> lock(ch.mu);
+    Exchange x{c->ll, c->fpart, &c->epoch};
+    if (static_words) {
+      char* base = reinterpret_cast<char*>(g_scratch[c->dev].ptr);
+      x = Exchange{reinterpret_cast<uint64_t*>(base),
+                   reinterpret_cast<uint64_t*>(base + fused_decode_ll_words(g.n_layers) * 8),
+                   &g_scratch[c->dev].epoch};
+    }
+    a.ll = x.ll;
+    a.part = x.part;
+    if (*x.epoch + 1 >= (1u << 26)) {  // epochs would wrap: clear the words and restart
+      launch_fill_zero(x.ll, fused_decode_ll_words(g.n_layers), st);
+      launch_fill_zero(x.part, fused_decode_part_words(g.n_layers), st);
+      *x.epoch = 0;
+    }
+    a.epoch = *x.epoch + 1;
     if (ch.stream && ch.stream != st) {
-      if ((!c->chain_ev && hipEventCreateWithFlags(&c->chain_ev, hipEventDisableTiming) != hipSuccess) ||
-          hipEventRecord(c->chain_ev, ch.stream) != hipSuccess ||
+      if (hipEventRecord(c->chain_ev, ch.stream) != hipSuccess ||
           hipStreamWaitEvent(st, c->chain_ev, 0) != hipSuccess)
         return fail(c, QTALK_E_DEVICE, "cannot order the persistent decode after another context's");
     }
@@ -507,13 +551,12 @@ struct Fwd {
     if (e != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "persistent decode launch failed: %s", hipGetErrorString(e));
     ch.stream = st;
-    c->epoch += 1;
+    *x.epoch += 1;
     int32_t& first = c->fused_first[seq];
     first = first < 0 ? pos : std::min(first, pos);
     return QTALK_OK;
   }
 
-  // one row per listed sequence (batched decode)
   // one row per listed sequence (batched decode): 8 or more rows on the
   // matrix cores (each weight matrix read once per pass), fewer on the
   // matrix-vector kernel
@@ -632,6 +675,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
                                     g.n_heads, g.n_kv_heads, g.head_dim) &&
              fused_decode_fits();
   if (c->fused) {
+    resolve_scratch(c->dev);
+    if (hipEventCreateWithFlags(&c->chain_ev, hipEventDisableTiming) != hipSuccess) ok = false;
     const char* env_loc = getenv("QTALK_XCD_LOCAL");
     c->xcd_local = !(env_loc && env_loc[0] == '0') && fused_decode_xcd_layout_ok(c->stream, c->coop);
     ok = dev_alloc((void**)&c->ll, fused_decode_ll_words(g.n_layers) * 8) &&
@@ -793,6 +838,28 @@ qtalk_status qtalk_decode(qtalk_ctx* c, int32_t seq, const float* emb, float* lo
                 c->cfg.max_seq_len);
   Fwd f(c);
   const qtalk_status s = f.run_fused(seq, c->cur_len[seq], emb, logits, hidden_out);
+  if (s == QTALK_OK) c->cur_len[seq] += 1;
+  return s;
+}
+
+qtalk_status qtalk_decode_noalloc(qtalk_ctx* c, int32_t seq, const float* emb, float* logits,
+                                  float* hidden_out) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (!c->fused)
+    return fail(c, QTALK_E_INVAL, "qtalk_decode_noalloc needs the persistent decode (Talker geometry, bf16 weights)");
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", seq);
+  if (!emb || !logits) return fail(c, QTALK_E_INVAL, "emb and logits must not be null");
+  const size_t need = (fused_decode_ll_words(c->cfg.n_layers) + fused_decode_part_words(c->cfg.n_layers)) * 8;
+  if (need > SCRATCH_BYTES)
+    return fail(c, QTALK_E_INVAL, "qtalk_decode_noalloc needs %zu bytes of static scratch, it holds %zu", need,
+                SCRATCH_BYTES);
+  if (!g_scratch[c->dev].ptr)
+    return fail(c, QTALK_E_DEVICE, "the static scratch array has no address on device %d", c->dev);
+  if (c->cur_len[seq] + 1 > c->cfg.max_seq_len)
+    return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + 1 > %d", c->cur_len[seq], c->cfg.max_seq_len);
+  Fwd f(c);
+  const qtalk_status s = f.run_fused(seq, c->cur_len[seq], emb, logits, hidden_out, true);
   if (s == QTALK_OK) c->cur_len[seq] += 1;
   return s;
 }

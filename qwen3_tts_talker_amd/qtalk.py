@@ -29,7 +29,7 @@ EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_kv_len", "qtalk_kv_read", "qtalk_prefill_batch", "qtalk_embed_sum",
            "qtalk_argmax", "qtalk_argmax_embed",
            "qtalk_select_head", "qtalk_sync", "qtalk_last_error",
-           "qtalk_set_wait_limit")
+           "qtalk_set_wait_limit", "qtalk_decode_noalloc")
 
 
 class qtalk_config(ctypes.Structure):
@@ -94,6 +94,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_sync": (st, [P]),
         "qtalk_last_error": (ctypes.c_char_p, [P]),
         "qtalk_set_wait_limit": (st, [P, ctypes.c_int64]),
+        "qtalk_decode_noalloc": (st, [P, I32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -153,6 +154,11 @@ def qtalk_extend(ctx, seq, emb, T, logits, hidden_out=None) -> int:
 
 def qtalk_decode(ctx, seq, emb, logits, hidden_out=None) -> int:
     return _check(ctx, load_library().qtalk_decode(
+        ctx, seq, _ptr(emb), _ptr(logits), _ptr(hidden_out)))
+
+
+def qtalk_decode_noalloc(ctx, seq, emb, logits, hidden_out=None) -> int:
+    return _check(ctx, load_library().qtalk_decode_noalloc(
         ctx, seq, _ptr(emb), _ptr(logits), _ptr(hidden_out)))
 
 

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = q.load_library()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert sorted(q.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +104,7 @@ def test_null_context_calls_are_rejected():
     assert lib.qtalk_sync(None) == q.QTALK_E_INVAL
     assert lib.qtalk_select_head(None, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_set_wait_limit(None, 0) == q.QTALK_E_INVAL
+    assert lib.qtalk_decode_noalloc(None, 0, None, None, None) == q.QTALK_E_INVAL
     assert lib.qtalk_embed_sum(None, 1, None, None, None, 1, None, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax(None, None, 1, 8, 8, -1, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax_embed(None, None, 1, 8, 8, -1, None, 4, None, None) == q.QTALK_E_INVAL
