@@ -165,6 +165,67 @@ def batched_decode(n_steps: int, warmup: int = 4) -> dict:
             "hbm_frac": round(nbytes / us / 1e3 / 8000.0, 4)}
 
 
+def long_context(n_steps: int, warmup: int = 4) -> dict:
+    """The long-context workload: the 28-layer Talker (its own seeded
+    weights), rows carrying +-3e4 on four fixed channels, prefilled in 16
+    chunks of 2048 rows (one qtalk_prefill, then qtalk_extend) to 32,768
+    positions, then batch-1 decode steps at context 32,769 onwards.  Events
+    on the library's stream time every chunk and every step.  Matrix flops
+    per chunk: projections on every row, causal attention over each row's
+    context, the head on the last row; bytes per step as the headline's."""
+    import torch
+    from qwen3_tts_talker_amd import Talker
+    from synth import make_weights, prefill_embeddings, step_embedding, workload
+    shape = workload("talker_28l_ctx32k_outlier")
+    tk = Talker(shape, make_weights(shape))
+    n, ch = shape.prefill_len, shape.chunk
+    emb = torch.from_numpy(prefill_embeddings(shape, n)).cuda()
+    n_steps = min(n_steps, shape.cap - n)
+    steps = torch.from_numpy(np.stack([step_embedding(shape, k) for k in range(max(n_steps, warmup))])).cuda()
+    st = torch.cuda.current_stream()
+    tk.prefill(0, emb[:ch])  # warm-up of the prefill kernels
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n // ch + 1)]
+    ev[0].record(st)
+    for ci, c0 in enumerate(range(0, n, ch)):
+        (tk.prefill if ci == 0 else tk.extend)(0, emb[c0:c0 + ch])
+        ev[ci + 1].record(st)
+    torch.cuda.synchronize()
+    tk.sync()
+    chunk_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n // ch)]
+    flops = [prefill_flops(shape, ch, c0) for c0 in range(0, n, ch)]
+    for k in range(warmup):
+        tk.decode(0, steps[k])
+    torch.cuda.synchronize()
+    tk.sync()
+    tk.kv_rewind(0, n)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    dev_ev[0].record(st)
+    for k in range(n_steps):
+        tk.decode(0, steps[k])
+        dev_ev[k + 1].record(st)
+    torch.cuda.synchronize()
+    tk.sync()
+    step_ms = np.array([dev_ev[k].elapsed_time(dev_ev[k + 1]) for k in range(n_steps)])
+    dec_ms = dev_ev[0].elapsed_time(dev_ev[n_steps])
+    nbytes = sum(decode_bytes(shape, n + k + 1) for k in range(n_steps))
+    tk.close()
+    tot = sum(chunk_ms)
+    return {"workload": shape.name, "chunks": n // ch, "chunk_rows": ch,
+            "prefill_ms": round(tot, 3), "prefill_tok_s": round(n / (tot / 1e3), 1),
+            "prefill_tflops": round(sum(flops) / (tot / 1e3) / 1e12, 2),
+            "prefill_mfma_frac": round(sum(flops) / (tot / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "last_chunk": {"p0": n - ch, "ms": round(chunk_ms[-1], 3),
+                           "tflops": round(flops[-1] / (chunk_ms[-1] / 1e3) / 1e12, 2),
+                           "mfma_frac": round(flops[-1] / (chunk_ms[-1] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "decode_steps": n_steps, "decode_ctx": [n + 1, n + n_steps],
+            "decode_us": round(dec_ms * 1e3 / n_steps, 1),
+            "decode_p99_us": round(float(np.percentile(step_ms, 99)) * 1e3, 1),
+            "decode_tok_s": round(n_steps / (dec_ms / 1e3), 1),
+            "decode_achieved_gbs": round(nbytes / (dec_ms / 1e3) / 1e9, 1),
+            "decode_hbm_frac": round(nbytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def batched_prefill(shape, weights, n: int, T: int, reps: int = 5) -> dict:
     """Batched prefill of n utterances of T rows each (one call) against n
     consecutive single prefills, on a context with n sequences."""
@@ -347,6 +408,9 @@ def main(argv=None):
                     help="utterances of 128 rows in the batched-prefill leg (0: skip)")
     ap.add_argument("--batch-decode", type=int, default=32,
                     help="timed steps of the 16-utterance batched decode leg (0: skip)")
+    ap.add_argument("--long-context", type=int, default=256,
+                    help="decode steps of the 32k long-context leg after its 16 x 2048-row "
+                         "prefill (0: skip the leg)")
     ap.add_argument("--cp-frames", type=int, default=20,
                     help="code predictor frames timed after the Talker (0: skip)")
     ap.add_argument("--pmc-calibration-mib", type=int, default=0,
@@ -471,6 +535,8 @@ def main(argv=None):
         out["prefill_batch"] = batched_prefill(shape, weights, args.batch_prefill, 128)
     if args.batch_decode > 0:
         out["decode_batch"] = batched_decode(args.batch_decode)
+    if args.long_context > 0:
+        out["long_context"] = long_context(args.long_context)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)
