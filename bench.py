@@ -273,13 +273,15 @@ def batched_prefill(shape, weights, n: int, T: int, reps: int = 5) -> dict:
             "serial_ms": round(res["serial"], 3)}
 
 
-def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
+def device_frames(talker, cp, n_frames: int, warmup: int, fused: bool = False) -> dict:
     """Whole codec frames on the device, with no host round trip: the
     Talker's step embedding gathered from the previous frame's 16 ids plus
     an overlay row, one Talker decode, the suppressed codebook-0 pick, the
     code predictor's two-row prefill (the Talker's hidden state, the codec
     row of that id) and 14 steps, each step's input gathered from the table
-    of the previous code and each code picked on the device."""
+    of the previous code and each code picked on the device.  fused: every
+    step is one qtalk_decode_step (gather and pick inside the persistent
+    decode, no other kernel); else separate gather / pick kernels."""
     import torch
     from qwen3_tts_talker_amd import qtalk
     from synth import embedding_tables, overlay_row
@@ -296,7 +298,27 @@ def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
     steps = torch.empty(15, 1, H, device="cuda")
     st = torch.cuda.current_stream()
 
+    gathers = []  # per parity: the Talker's 16-table gather, then each code predictor step's
+    for i in range(2):
+        a, b = ids[i % 2], ids[(i + 1) % 2]
+        gathers.append([qtalk.make_gather(tabs, a, ov.view(-1)), qtalk.make_gather(tabs[0:1], b[0:1])] +
+                       [qtalk.make_gather(tabs[j:j + 1], b[j:j + 1]) for j in range(1, 15)])
+
+    def frame_fused(i):
+        a, b = ids[i % 2], ids[(i + 1) % 2]
+        g = gathers[i % 2]
+        qtalk.qtalk_decode_step(talker.ctx, 0, None, g[0], lg_t, cp_in[0], V - 1024, EOS, b[0:1])
+        cp.kv_rewind(0, 0)
+        cp.select_head(0)
+        qtalk.qtalk_decode_step(cp.ctx, 0, cp_in[0], None, lg_c[0])
+        qtalk.qtalk_decode_step(cp.ctx, 0, None, g[1], lg_c[0], None, out_id=b[1:2])
+        for j in range(1, 15):
+            cp.select_head(j)
+            qtalk.qtalk_decode_step(cp.ctx, 0, None, g[j + 1], lg_c[j], None, out_id=b[j + 1:j + 2])
+
     def frame(i):
+        if fused:
+            return frame_fused(i)
         # each pick also fetches the table row the next call feeds on
         # (qtalk_argmax_embed), so no separate lookup kernel runs
         a, b = ids[i % 2], ids[(i + 1) % 2]
@@ -330,7 +352,8 @@ def device_frames(talker, cp, n_frames: int, warmup: int) -> dict:
     cp.sync()
     ms = e0.elapsed_time(e1) / n_frames
     return {"frames": n_frames, "talker_ctx": [talker.kv_len(0) - n_frames + 1, talker.kv_len(0)],
-            "frame_us": round(ms * 1e3, 1), "frames_per_s": round(1e3 / ms, 1)}
+            "frame_us": round(ms * 1e3, 1), "frames_per_s": round(1e3 / ms, 1),
+            "glue_launches": 0 if fused else 18}
 
 
 def code_predictor(n_frames: int, warmup: int, talker=None) -> dict:
@@ -378,6 +401,7 @@ def code_predictor(n_frames: int, warmup: int, talker=None) -> dict:
     torch.cuda.synchronize()
     assert status == 0 and lib.qtalk_sync(ctx) == 0, qtalk.qtalk_last_error(ctx)
     dev_frames = device_frames(talker, tk, n_frames, warmup) if talker is not None else None
+    dev_fused = device_frames(talker, tk, n_frames, warmup, fused=True) if talker is not None else None
     frame_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     step_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 14
@@ -392,6 +416,7 @@ def code_predictor(n_frames: int, warmup: int, talker=None) -> dict:
             "step_hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
     if dev_frames is not None:
         res["device_frame"] = dev_frames
+        res["device_frame_fused"] = dev_fused
     return res
 
 

@@ -143,6 +143,40 @@ qtalk_status qtalk_extend(qtalk_ctx *ctx, int32_t seq, const float *emb,
 qtalk_status qtalk_decode(qtalk_ctx *ctx, int32_t seq, const float *emb,
                           float *logits, float *hidden_out);
 
+/* The step input gathered on the device (see qtalk_embed_sum): row
+ * ids[g] of each tables[g], summed in float32 in table order, plus the
+ * overlay row. */
+#define QTALK_MAX_GATHER 16
+typedef struct {
+  int32_t n_tables;                       /* 1 .. QTALK_MAX_GATHER           */
+  const float *tables[QTALK_MAX_GATHER];  /* DEVICE float32 [table_rows[g]][hidden] */
+  int32_t table_rows[QTALK_MAX_GATHER];
+  const int32_t *ids;                     /* DEVICE int32 [n_tables]          */
+  const float *overlay;                   /* DEVICE float32 [hidden], or NULL */
+} qtalk_gather;
+
+/* One step of a codec frame: qtalk_decode of one position of
+ * `seq` whose input row is either emb [hidden] or the gather above (the
+ * Talker's 16-table step embedding plus the text overlay, or the code
+ * predictor's previous code looked up in its table), and, when out_id is
+ * set, the suppressed greedy pick of its logits written to *out_id (device
+ * int32; same rule as qtalk_argmax).  ("qwentts.cpp src/talker-forward.h",
+ * the batched step graph's input_embed; "rightkit-qts 0.2.3
+ * src/pipeline/tts_transformer.rs", build_talker_step_embedding and the
+ * suppression loop before select_token.)  The results equal
+ * qtalk_embed_sum + qtalk_decode + qtalk_argmax bit for bit.  Where the
+ * persistent decode runs, a one-table lookup and the pick happen inside its
+ * launch, and a sum of several tables is one gather kernel before it;
+ * elsewhere it runs as those three calls.  An id outside its table cannot
+ * be seen on the host: the step then computes on a NaN row, and the next
+ * qtalk_sync reports it and rolls the sequence back to before that step.
+ * Errors: QTALK_E_INVAL (bad seq, null logits, both or neither of emb and
+ * gather, a bad gather), QTALK_E_OVERFLOW as qtalk_decode. */
+qtalk_status qtalk_decode_step(qtalk_ctx *ctx, int32_t seq, const float *emb,
+                               const qtalk_gather *gather, float *logits,
+                               float *hidden_out, int32_t suppress_begin,
+                               int32_t keep_id, int32_t *out_id);
+
 /* qtalk_decode without the context's exchange buffers, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): the same persistent kernel and
@@ -266,10 +300,12 @@ qtalk_status qtalk_select_head(qtalk_ctx *ctx, int32_t head);
 /* Block until the context's stream has finished all enqueued work.
  * Errors: QTALK_E_DEVICE if a kernel failed, or if a kernel reported a
  * failure of its own since the previous qtalk_sync:
- *  - a batch-1 decode (qtalk_decode, or a one- or two-row prefill/extend,
- *    which run on the same persistent kernel) gave up waiting for its other
- *    blocks, or its blocks were placed differently than set-up found (then
- *    later decodes use the slower placement-independent exchange).  Its
+ *  - a batch-1 decode (qtalk_decode, qtalk_decode_step, or a one- or
+ *    two-row prefill/extend, which run on the same persistent kernel) gave
+ *    up waiting for its other blocks, or its blocks were placed differently
+ *    than set-up found (then later decodes use the slower
+ *    placement-independent exchange), or a qtalk_decode_step's gathered
+ *    input had an id outside its table.  Its
  *    outputs, and those of every later call, are not valid: each sequence
  *    such a decode wrote since the previous qtalk_sync is rolled back to
  *    the first position it wrote there (qtalk_kv_len shows the result, the

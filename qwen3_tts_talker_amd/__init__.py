@@ -15,6 +15,8 @@ from .qtalk import (  # noqa: F401
     qtalk_decode,
     qtalk_decode_batch,
     qtalk_decode_noalloc,
+    qtalk_decode_step,
+    make_gather,
     qtalk_destroy,
     qtalk_embed_sum,
     qtalk_extend,

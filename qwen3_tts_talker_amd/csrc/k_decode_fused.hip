@@ -46,6 +46,8 @@
 // Specialised to the Talker geometry (hidden 1024, 16/8 heads of 128,
 // intermediate 3072, vocab 3072, bf16 weights, f16 cache); other shapes use
 // the per-step kernels.
+#include <climits>
+
 #include "kernels.h"
 
 namespace qtalk {
@@ -68,6 +70,9 @@ constexpr int OFF_A = OFF_XM + NKV * H;     // SwiGLU output [8 groups][32 block
 constexpr int OFF_DP = OFF_A + NKV * 512;   // down partials [8 groups][1024], all blocks
 constexpr int OFF_XD = OFF_DP + NKV * H;    // layer output [8 groups][1024], one copy per group
 constexpr int WORDS_PER_LAYER = OFF_XD + NKV * H;
+// after the two layer regions: each block's candidate of the greedy pick
+// (value word, index word)
+constexpr int PICK_WORDS = 2 * NB;
 constexpr int ISEG = I / NKV, OSEG = QD / NKV;  // down / o_proj input columns per group
 // chunk partial (o[HD], m, l) padded to 144 words: each block writes whole
 // 128-byte lines, so no line holds words of two writers
@@ -373,11 +378,22 @@ __device__ __forceinline__ float inv_rms(const float* redw, float eps) {
 // max over each aligned 32-lane half of the wave
 __device__ __forceinline__ float half32_max(float v) { return xor16_max(row16_max(v)); }
 
+// greedy-pick candidate order: the larger value, then the lower index; an
+// empty candidate (index INT_MAX) loses to any other.  Candidates hold
+// distinct indices, so the order is total and any reduction tree gives the
+// same pick.
+__device__ __forceinline__ bool pick_better(float v, int i, float bv, int bi) {
+  if (bi == INT_MAX) return i != INT_MAX;
+  if (i == INT_MAX) return false;
+  return v > bv || (v == bv && i < bi);
+}
+
 }  // namespace pd
 
 // LOCAL: group exchanges inside the XCD; Q8: Q8_0 cache rows (HD codes, then
-// HD / 32 float16 scales) instead of float16 rows
-template <bool LOCAL, bool Q8>
+// HD / 32 float16 scales) instead of float16 rows; PICK: the greedy pick of
+// the logits after the head step
+template <bool LOCAL, bool Q8, bool PICK, bool SINGLE>
 __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   using namespace pd;
   constexpr size_t RB = Q8 ? HD + HD / 16 : HD * 2;  // bytes per cache row
@@ -420,7 +436,11 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
   // blocks to the 8 XCDs in turn (starting where the previous dispatch left
   // off), so blocks 8c .. 8c+7 cover every XCD once and (g, c) is a bijection.
   const int g = LOCAL ? (int)xcc_id() : b % NKV, c = b / NKV;
-  const int kpb = (n_ctx + NCH - 1) / NCH;
+  // SINGLE (up to 64 keys: the code predictor's contexts, a Talker's first
+  // steps): chunk 0 of each KV head takes them all and publishes the
+  // normalised output itself, so the merge step and its exchange drop out
+  constexpr bool single = SINGLE;
+  const int kpb = single ? 64 : (n_ctx + NCH - 1) / NCH;
   const int k0 = c * kpb, k1 = min(k0 + kpb, n_ctx);
   const float scale = 1.4426950408889634f * rsqrtf((float)HD);  // log2(e) / sqrt(HD)
   const int slot = tid >> 4, sub = tid & 15;
@@ -504,9 +524,35 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     return ok;
   };
   Gain2 gin;  // input-norm gain of the next layer
+  // layer-0 input: emb, or one table row looked up here (the code
+  // predictor's previous code; a sum of several tables is formed by a gather
+  // kernel before the launch).  Its loads go out first, the bulk loads
+  // behind them, and the values reach LDS once they have landed.
+  float e0, e1;
+  bool e_bad = false;
+  if (a.n_gather) {
+    const int id = a.gids[0];
+    e_bad = id < 0 || id >= a.grows[0];
+    const float* row = a.gtab[0] + (size_t)min(max(id, 0), a.grows[0] - 1) * H;
+    e0 = row[tid];
+    e1 = row[tid + NT];
+    if (a.goverlay) {
+      e0 += a.goverlay[tid];
+      e1 += a.goverlay[tid + NT];
+    }
+  } else {
+    e0 = a.emb[tid];
+    e1 = a.emb[tid + NT];
+  }
   gq.load(wqkv_row(0), wave, lane);
   load_kv(0);
   gin.load(a.norms);
+  if (e_bad) {  // an id outside the table: a NaN row, reported at sync
+    e0 = e1 = __int_as_float(0x7fc00000);
+    if (b == 0 && tid == 0) *a.gstatus = 5;
+  }
+  xres[tid] = e0;
+  xres[tid + NT] = e1;
 
   for (int l = 0; l < a.n_layers; ++l) {
     const bf16_t* Wl = a.w + (size_t)l * a.layer_stride;
@@ -541,9 +587,9 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         wx.issue(Eprev + OFF_XD + g * H, H);
         bail = bail || !recv_norm(wx, ep - 1, bl, xres, xin, gin, &ss);
       } else {
-        const float x0 = a.emb[tid], x1 = a.emb[tid + NT];
-        xres[tid] = x0;
-        xres[tid + NT] = x1;
+        // the layer-0 input row, loaded before the loop into xres (this
+        // thread's own two elements: no barrier)
+        const float x0 = xres[tid], x1 = xres[tid + NT];
         xin[tid] = x0 * gin.g0;
         xin[tid + NT] = x1 * gin.g1;
         ss = x0 * x0 + x1 * x1;
@@ -780,8 +826,18 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
         o = fmaf(wt(mm.w), ow[w0 + 3][out], o);
         o = xor32_sum(o);
         uint64_t* pw = P + ((size_t)(g * G + h) * NCH + c) * PST;
-        if (half == 0) st_x<LOCAL>(pw + i, o, ep);
-        if (half == 1 && i < PST - HD) {  // m, l of head h (-inf, 0 past the context), padding
+        if (single) {  // chunk 0 holds every key: o / l into the merged-output words
+          if (c == 0 && half == 0) {
+            const float4 la = *reinterpret_cast<const float4*>(&lws[h][0]);
+            const float4 lb = *reinterpret_cast<const float4*>(&lws[h][4]);
+            const float L = wt(ma.x) * la.x + wt(ma.y) * la.y + wt(ma.z) * la.z + wt(ma.w) * la.w +
+                            (wt(mb.x) * lb.x + wt(mb.y) * lb.y + wt(mb.z) * lb.z + wt(mb.w) * lb.w);
+            st_x<LOCAL>(E + OFF_OG + g * 512 + 16 * (h * 16 + (i >> 3)) + (i & 7), o / L, ep);
+          }
+        } else if (half == 0) {
+          st_x<LOCAL>(pw + i, o, ep);
+        }
+        if (!single && half == 1 && i < PST - HD) {  // m, l of head h (-inf, 0 past the context), padding
           float v = i == 0 ? M : 0.f;
           if (i == 1) {
             const float4 la = *reinterpret_cast<const float4*>(&lws[h][0]);
@@ -798,7 +854,7 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     // block (g, c) merges dims d0 .. d0+7 (d0 = 8 (c % 16)) of query head
     // 2g + c / 16 over the group's 32 chunk partials (log-sum-exp): thread
     // t < 320 polls chunk t / 10's word t % 10 (8 o values, then m and l)
-    {
+    if (!single) {
       const int h = c >> 4, d0 = (c & 15) * 8;
       const uint64_t* pbase = P + (size_t)(g * G + h) * NCH * PST;
       const int tm = min(tid, NCH * 10 - 1), cc = tm / 10, k = tm % 10;
@@ -912,6 +968,67 @@ __global__ __launch_bounds__(pd::NT, 1) void k_decode_fused(FusedDecodeArgs a) {
     gq.dot(xin, red, wave, lane);
     __syncthreads();
     if (tid < a.head_rows) a.logits[b * a.head_rows + tid] = red[tid] * inv;
+    if (!PICK) return;
+    // greedy pick: wave 0 forms the block's candidate over its head rows and
+    // publishes (value, index); block 0 polls the 256 candidates and keeps,
+    // in block order, the larger value (the lower index among equals)
+    uint64_t* PK = a.ll + (size_t)2 * WORDS_PER_LAYER;
+    if (wave == 0) {
+      float v = -INFINITY;
+      int i = INT_MAX;
+      const int id = b * a.head_rows + lane;
+      if (lane < a.head_rows && !(id >= a.pick_suppress && id != a.pick_keep)) {
+        v = red[lane] * inv;
+        v = v != v ? -INFINITY : v;
+        i = id;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off);
+        const int oi = __shfl_xor(i, off);
+        if (pick_better(ov, oi, v, i)) {
+          v = ov;
+          i = oi;
+        }
+      }
+      if (lane == 0) {
+        st_ll(PK + 2 * b, v, ep0);
+        st_ll(PK + 2 * b + 1, __int_as_float(i), ep0);
+      }
+    }
+    if (b != 0) return;
+    // the candidates land in the attention step's per-wave sums (free now)
+    float* cv = &ow[0][0];
+    int* ci = reinterpret_cast<int*>(&ow[1][0]);
+    static_assert(G * HD >= NB, "candidate arrays");
+    {
+      LLWait<1> wp;
+      wp.issue(PK, PICK_WORDS);
+      const bool bail = !wp.finish(ep0, bl, [&](int k, float x) {
+        if (k & 1) ci[k >> 1] = __float_as_int(x);
+        else cv[k >> 1] = x;
+      });
+      if (sync_bail(bail)) return;
+    }
+    if (wave == 0) {  // lane l takes blocks l, l + 64, ...: block order kept by the tie rule
+      float v = cv[lane];
+      int i = ci[lane];
+      for (int k = lane + 64; k < NB; k += 64)
+        if (pick_better(cv[k], ci[k], v, i)) {
+          v = cv[k];
+          i = ci[k];
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off);
+        const int oi = __shfl_xor(i, off);
+        if (pick_better(ov, oi, v, i)) {
+          v = ov;
+          i = oi;
+        }
+      }
+      if (lane == 0) *a.pick_out = i == INT_MAX ? -1 : i;
+    }
   }
 }
 
@@ -922,7 +1039,7 @@ bool fused_decode_supported(int hidden, int q_dim, int kv_dim, int inter, int vo
          n_kv_heads == pd::NKV && head_dim == pd::HD;
 }
 
-size_t fused_decode_ll_words(int) { return (size_t)2 * pd::WORDS_PER_LAYER; }
+size_t fused_decode_ll_words(int) { return (size_t)2 * pd::WORDS_PER_LAYER + pd::PICK_WORDS; }
 size_t fused_decode_part_words(int) { return (size_t)2 * pd::PART_WORDS; }
 int fused_decode_blocks() { return pd::NB; }
 
@@ -935,10 +1052,19 @@ int fused_decode_blocks() { return pd::NB; }
 // launch), at ~18 us more per launch.
 hipError_t launch_decode_fused(const FusedDecodeArgs& args, hipStream_t st, bool cooperative) {
   FusedDecodeArgs a = args;
-  const void* fn = a.kv_q8 ? (a.xcd_local ? (const void*)k_decode_fused<true, true>
-                                          : (const void*)k_decode_fused<false, true>)
-                           : (a.xcd_local ? (const void*)k_decode_fused<true, false>
-                                          : (const void*)k_decode_fused<false, false>);
+  // the greedy pick and the short-context attention are separate
+  // instantiations: their code in the common kernel measured 2-3% slower per
+  // token even where not taken
+  const void* fns[2][2][2][2] = {
+      {{{(const void*)k_decode_fused<false, false, false, false>, (const void*)k_decode_fused<false, false, false, true>},
+        {(const void*)k_decode_fused<false, false, true, false>, (const void*)k_decode_fused<false, false, true, true>}},
+       {{(const void*)k_decode_fused<false, true, false, false>, (const void*)k_decode_fused<false, true, false, true>},
+        {(const void*)k_decode_fused<false, true, true, false>, (const void*)k_decode_fused<false, true, true, true>}}},
+      {{{(const void*)k_decode_fused<true, false, false, false>, (const void*)k_decode_fused<true, false, false, true>},
+        {(const void*)k_decode_fused<true, false, true, false>, (const void*)k_decode_fused<true, false, true, true>}},
+       {{(const void*)k_decode_fused<true, true, false, false>, (const void*)k_decode_fused<true, true, false, true>},
+        {(const void*)k_decode_fused<true, true, true, false>, (const void*)k_decode_fused<true, true, true, true>}}}};
+  const void* fn = fns[a.xcd_local ? 1 : 0][a.kv_q8 ? 1 : 0][a.pick_out ? 1 : 0][a.pos + 1 <= 64 ? 1 : 0];
   void* params[] = {&a};
   if (!cooperative) return hipLaunchKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
   return hipLaunchCooperativeKernel(fn, dim3(pd::NB), dim3(pd::NT), params, 0, st);
@@ -991,7 +1117,7 @@ bool fused_decode_fits() {
   int dev = 0, ncu = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused<true, false>, pd::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_decode_fused<true, false, true, false>, pd::NT, 0) !=
       hipSuccess)
     return false;
   return (long)per * ncu >= pd::NB;

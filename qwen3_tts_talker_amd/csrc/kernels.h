@@ -163,7 +163,20 @@ struct FusedDecodeArgs {
   uint32_t epoch;  // >= 1 and < 2^26; words carry epoch * 64 + layer
   int xcd_local;   // QKV -> attention -> merge exchanges inside each XCD's L2
   int head_rows;   // vocab / 256: codec head rows per block (1..16)
-
+  // layer-0 input looked up on the device when n_gather == 1 (emb unused):
+  // x = gtab[0][gids[0]] (+ goverlay); an id outside the table gives a NaN
+  // row and *gstatus = 5 (the decode status word: rolled back at sync)
+  int n_gather;
+  const float* gtab[1];
+  int grows[1];
+  const int32_t* gids;
+  const float* goverlay;
+  int* gstatus;
+  // when set: the greedy pick of the logits (ids >= pick_suppress excluded
+  // except pick_keep; NaN as -inf; the lowest id among equal maxima; -1 if
+  // nothing is left) written to *pick_out
+  int32_t* pick_out;
+  int pick_suppress, pick_keep;
 };
 // default bounded-wait limit of the persistent decode (~1-2 s of polling)
 constexpr long FUSED_SPIN_LIMIT = 1L << 21;

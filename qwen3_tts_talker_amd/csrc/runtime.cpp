@@ -101,6 +101,7 @@ struct qtalk_ctx {
   // the last qtalk_sync (-1: none); a launch that gave up rolls it back
   std::vector<int32_t> fused_first;
   int* aux_err = nullptr;  // frame-step kernels: 5 when an id was outside its table
+  float* step_in = nullptr;  // [hidden]: a gathered step input (qtalk_decode_step without the persistent decode)
   uint32_t epoch = 0;
   size_t per_layer = 0, norms_per_layer = 0;
   std::string err;
@@ -179,7 +180,7 @@ bool dev_alloc(void** p, size_t bytes) {
 void free_all(qtalk_ctx* c) {
   void* ptrs[] = {c->wblob, c->nblob, c->head, c->kc,     c->vc,    c->rope,   c->x,
                   c->qkv,   c->att,   c->act,  c->hn,     c->part_o, c->part_ml, c->work,
-                  c->ll,    c->fpart, c->ferr, c->aux_err, c->kv16};
+                  c->ll,    c->fpart, c->ferr, c->aux_err, c->kv16, c->step_in};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -498,10 +499,29 @@ struct Fwd {
 
   // one row of sequence `seq` at position `pos` as one persistent launch,
   // exchanging through the context's buffers or (static_words) the device's
-  // static array
+  // static array; the input row is emb, or gathered on the device (gather);
+  // with pick set, the greedy pick of the logits goes to pick->out
+  struct Pick {
+    int32_t* out;
+    int suppress, keep;
+  };
   qtalk_status run_fused(int seq, int pos, const float* emb, float* logits, float* hidden_out,
-                         bool static_words = false) {
+                         bool static_words = false, const qtalk_gather* gather = nullptr,
+                         const Pick* pick = nullptr) {
     FusedDecodeArgs a{};
+    if (gather) {  // one table (several are summed by a gather kernel first)
+      a.n_gather = 1;
+      a.gtab[0] = gather->tables[0];
+      a.grows[0] = gather->table_rows[0];
+      a.gids = gather->ids;
+      a.goverlay = gather->overlay;
+      a.gstatus = c->ferr;
+    }
+    if (pick) {
+      a.pick_out = pick->out;
+      a.pick_suppress = pick->suppress;
+      a.pick_keep = pick->keep;
+    }
     a.w = reinterpret_cast<const bf16_t*>(c->wblob);
     a.layer_stride = c->per_layer;
     a.norms = c->nblob;
@@ -646,6 +666,8 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
             dev_alloc((void**)&c->rope, (size_t)g.max_seq_len * (g.head_dim / 2) * sizeof(float2)) &&
             dev_alloc((void**)&c->x, (size_t)rows * H * 4) &&
             dev_alloc((void**)&c->aux_err, 4) &&
+            dev_alloc((void**)&c->step_in, H * 4) &&
+            dev_alloc((void**)&c->ferr, 4) &&
             (c->kv != KV_Q8 || !c->w_bf16 ||
              !attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads) ||
              dev_alloc((void**)&c->kv16, (size_t)2 * g.n_kv_heads * g.max_seq_len * g.head_dim * 2)) &&
@@ -680,8 +702,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
     const char* env_loc = getenv("QTALK_XCD_LOCAL");
     c->xcd_local = !(env_loc && env_loc[0] == '0') && fused_decode_xcd_layout_ok(c->stream, c->coop);
     ok = dev_alloc((void**)&c->ll, fused_decode_ll_words(g.n_layers) * 8) &&
-         dev_alloc((void**)&c->fpart, fused_decode_part_words(g.n_layers) * 8) &&
-         dev_alloc((void**)&c->ferr, 4);
+         dev_alloc((void**)&c->fpart, fused_decode_part_words(g.n_layers) * 8);
   }
   if (!ok) {
     (void)hipGetLastError();
@@ -732,10 +753,10 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
         hipMemsetAsync(c->vc, 0, kv_bytes, c->stream) != hipSuccess ||
         hipMemsetAsync(c->aux_err, 0, 4, c->stream) != hipSuccess)
       s = QTALK_E_DEVICE;
-    if (c->fused &&
-        (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, c->stream) != hipSuccess ||
-         hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, c->stream) != hipSuccess ||
-         hipMemsetAsync(c->ferr, 0, 4, c->stream) != hipSuccess))
+    if (hipMemsetAsync(c->ferr, 0, 4, c->stream) != hipSuccess ||
+        (c->fused &&
+         (hipMemsetAsync(c->ll, 0, fused_decode_ll_words(g.n_layers) * 8, c->stream) != hipSuccess ||
+          hipMemsetAsync(c->fpart, 0, fused_decode_part_words(g.n_layers) * 8, c->stream) != hipSuccess)))
       s = QTALK_E_DEVICE;
     launch_rope_table(c->rope, g.max_seq_len, g.head_dim, (double)g.rope_theta, c->stream);
     if (hipGetLastError() != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess)
@@ -838,6 +859,80 @@ qtalk_status qtalk_decode(qtalk_ctx* c, int32_t seq, const float* emb, float* lo
                 c->cfg.max_seq_len);
   Fwd f(c);
   const qtalk_status s = f.run_fused(seq, c->cur_len[seq], emb, logits, hidden_out);
+  if (s == QTALK_OK) c->cur_len[seq] += 1;
+  return s;
+}
+
+qtalk_status qtalk_decode_step(qtalk_ctx* c, int32_t seq, const float* emb, const qtalk_gather* gather,
+                              float* logits, float* hidden_out, int32_t suppress_begin, int32_t keep_id,
+                              int32_t* out_id) {
+  if (!c) return QTALK_E_INVAL;
+  c->err.clear();
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(c, QTALK_E_INVAL, "bad sequence id %d", seq);
+  if (!logits) return fail(c, QTALK_E_INVAL, "logits must not be null");
+  if (!emb == !gather) return fail(c, QTALK_E_INVAL, "give exactly one of emb and gather");
+  if (gather) {
+    if (gather->n_tables < 1 || gather->n_tables > QTALK_MAX_GATHER || !gather->ids)
+      return fail(c, QTALK_E_INVAL, "gather: n_tables must be 1..%d and ids non-null", QTALK_MAX_GATHER);
+    for (int q = 0; q < gather->n_tables; ++q)
+      if (!gather->tables[q] || gather->table_rows[q] < 1)
+        return fail(c, QTALK_E_INVAL, "gather: table %d is null or empty", q);
+    if (c->cfg.hidden % 4 || c->cfg.hidden > 4096)
+      return fail(c, QTALK_E_INVAL, "gather: hidden must be a multiple of 4 and <= 4096");
+  }
+  if (c->cur_len[seq] + 1 > c->cfg.max_seq_len)
+    return fail(c, QTALK_E_OVERFLOW, "cache overflow: %d + 1 > %d", c->cur_len[seq], c->cfg.max_seq_len);
+  Fwd f(c);
+  qtalk_status s = QTALK_OK;
+  if (c->fused && (!gather || gather->n_tables == 1)) {
+    // one launch: a one-table lookup and the pick inside the persistent decode
+    const Fwd::Pick pk{out_id, suppress_begin, keep_id};
+    s = f.run_fused(seq, c->cur_len[seq], emb, logits, hidden_out, false, gather, out_id ? &pk : nullptr);
+  } else if (c->fused) {
+    // a sum of several tables: the gather kernel, then one launch with the pick
+    EmbedSumArgs e{};
+    for (int q = 0; q < gather->n_tables; ++q) {
+      e.tables[q] = gather->tables[q];
+      e.rows[q] = gather->table_rows[q];
+    }
+    e.n_groups = gather->n_tables;
+    e.n = 1;
+    e.hidden = c->cfg.hidden;
+    e.ids = gather->ids;
+    e.overlay = gather->overlay;
+    e.out = c->step_in;
+    e.status = c->ferr;  // the decode status word: the position is rolled back at sync
+    launch_embed_sum(e, c->stream);
+    const Fwd::Pick pk{out_id, suppress_begin, keep_id};
+    s = f.run_fused(seq, c->cur_len[seq], c->step_in, logits, hidden_out, false, nullptr,
+                    out_id ? &pk : nullptr);
+  } else {
+    // the same steps as separate launches: gather, decode, pick
+    if (gather) {
+      EmbedSumArgs e{};
+      for (int q = 0; q < gather->n_tables; ++q) {
+        e.tables[q] = gather->tables[q];
+        e.rows[q] = gather->table_rows[q];
+      }
+      e.n_groups = gather->n_tables;
+      e.n = 1;
+      e.hidden = c->cfg.hidden;
+      e.ids = gather->ids;
+      e.overlay = gather->overlay;
+      e.out = c->step_in;
+      e.status = c->ferr;  // like the persistent decode's: the position is rolled back at sync
+      launch_embed_sum(e, c->stream);
+      emb = c->step_in;
+      int32_t& first = c->fused_first[seq];
+      first = first < 0 ? c->cur_len[seq] : std::min(first, c->cur_len[seq]);
+    }
+    s = f.run_sequence(seq, c->cur_len[seq], emb, 1, logits, hidden_out);
+    if (s == QTALK_OK && out_id) {
+      ArgmaxArgs am{logits, 1, c->cfg.vocab, suppress_begin, keep_id, out_id, nullptr, 0, 0, nullptr, nullptr};
+      launch_argmax(am, c->stream);
+    }
+    if (s == QTALK_OK) s = launch_status(c);
+  }
   if (s == QTALK_OK) c->cur_len[seq] += 1;
   return s;
 }
@@ -985,20 +1080,24 @@ qtalk_status qtalk_sync(qtalk_ctx* c) {
   const hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return fail(c, QTALK_E_DEVICE, "stream failed: %s", hipGetErrorString(e));
   std::string msg;
-  if (c->fused) {
+  {
     int code = 0;
     if (hipMemcpy(&code, c->ferr, 4, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(c, QTALK_E_DEVICE, "cannot read the decode status word");
     if (code) {
-      // a persistent launch gave up (1) or ran on unexpected XCDs (3): the
-      // positions written by persistent launches since the last sync, and
-      // everything after them, are dropped; later launches start clean
+      // a persistent launch gave up (1) or ran on unexpected XCDs (3), or a
+      // step input's id was outside its table (5): the positions written by
+      // such launches since the last sync, and everything after them, are
+      // dropped; later launches start clean
       if (hipMemset(c->ferr, 0, 4) != hipSuccess)
         return fail(c, QTALK_E_DEVICE, "cannot clear the decode status word");
       if (code == 3) c->xcd_local = false;  // later steps use device-scope exchanges
       char buf[160];
-      snprintf(buf, sizeof buf, "persistent decode %s (code %d); rolled back:",
-               code == 3 ? "blocks did not run on the expected XCDs" : "gave up waiting", code);
+      snprintf(buf, sizeof buf, "%s (code %d); rolled back:",
+               code == 3   ? "persistent decode: blocks did not run on the expected XCDs"
+               : code == 5 ? "decode step: an id of the gathered input was outside its table"
+                           : "persistent decode gave up waiting",
+               code);
       msg = buf;
       for (int s = 0; s < c->cfg.max_seqs; ++s) {
         const int32_t f = c->fused_first[s];

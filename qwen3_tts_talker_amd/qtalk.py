@@ -29,7 +29,7 @@ EXPORTS = ("qtalk_create", "qtalk_destroy", "qtalk_prefill", "qtalk_extend",
            "qtalk_kv_len", "qtalk_kv_read", "qtalk_prefill_batch", "qtalk_embed_sum",
            "qtalk_argmax", "qtalk_argmax_embed",
            "qtalk_select_head", "qtalk_sync", "qtalk_last_error",
-           "qtalk_set_wait_limit", "qtalk_decode_noalloc")
+           "qtalk_set_wait_limit", "qtalk_decode_noalloc", "qtalk_decode_step")
 
 
 class qtalk_config(ctypes.Structure):
@@ -51,6 +51,16 @@ class qtalk_layer_weights(ctypes.Structure):
 class qtalk_weights(ctypes.Structure):
     _fields_ = [("layers", ctypes.POINTER(qtalk_layer_weights)),
                 ("final_norm", ctypes.c_void_p), ("codec_head", ctypes.c_void_p)]
+
+
+QTALK_MAX_GATHER = 16
+
+
+class qtalk_gather(ctypes.Structure):
+    _fields_ = [("n_tables", ctypes.c_int32),
+                ("tables", ctypes.c_void_p * QTALK_MAX_GATHER),
+                ("table_rows", ctypes.c_int32 * QTALK_MAX_GATHER),
+                ("ids", ctypes.c_void_p), ("overlay", ctypes.c_void_p)]
 
 
 class QtalkError(RuntimeError):
@@ -95,6 +105,7 @@ def load_library() -> ctypes.CDLL:
         "qtalk_last_error": (ctypes.c_char_p, [P]),
         "qtalk_set_wait_limit": (st, [P, ctypes.c_int64]),
         "qtalk_decode_noalloc": (st, [P, I32, P, P, P]),
+        "qtalk_decode_step": (st, [P, I32, P, ctypes.POINTER(qtalk_gather), P, P, I32, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -160,6 +171,29 @@ def qtalk_decode(ctx, seq, emb, logits, hidden_out=None) -> int:
 def qtalk_decode_noalloc(ctx, seq, emb, logits, hidden_out=None) -> int:
     return _check(ctx, load_library().qtalk_decode_noalloc(
         ctx, seq, _ptr(emb), _ptr(logits), _ptr(hidden_out)))
+
+
+def make_gather(tables, ids, overlay=None) -> qtalk_gather:
+    """``tables``: float32 device tensors ``[rows][hidden]``; ``ids``: int32
+    device tensor of ``len(tables)`` ids; ``overlay``: ``[hidden]`` or None."""
+    g = qtalk_gather()
+    g.n_tables = len(tables)
+    for i, t in enumerate(tables):
+        g.tables[i] = _ptr(t)
+        g.table_rows[i] = int(t.shape[0])
+    g.ids = _iptr(ids)
+    g.overlay = _ptr(overlay)
+    return g
+
+
+def qtalk_decode_step(ctx, seq, emb, gather, logits, hidden_out=None,
+                      suppress_begin=None, keep_id=-1, out_id=None) -> int:
+    """``gather``: a ``qtalk_gather`` (see ``make_gather``) or None."""
+    sb = suppress_begin if suppress_begin is not None else 1 << 30
+    return _check(ctx, load_library().qtalk_decode_step(
+        ctx, seq, _ptr(emb), ctypes.byref(gather) if gather is not None else None,
+        _ptr(logits), _ptr(hidden_out), sb, keep_id,
+        _iptr(out_id) if out_id is not None else None))
 
 
 def qtalk_decode_batch(ctx, n, seqs: Sequence[int], emb, logits,

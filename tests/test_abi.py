@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = q.load_library()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert sorted(q.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -49,6 +49,9 @@ int main(void) {
   F(qtalk_config, n_output_heads);
   F(qtalk_layer_weights, down_proj); F(qtalk_layer_weights, k_norm);
   F(qtalk_weights, final_norm); F(qtalk_weights, codec_head);
+  printf("qtalk_gather %zu\\n", sizeof(qtalk_gather));
+  F(qtalk_gather, tables); F(qtalk_gather, table_rows); F(qtalk_gather, ids);
+  F(qtalk_gather, overlay);
   return 0;
 }
 """)
@@ -61,6 +64,7 @@ int main(void) {
     assert int(got["qtalk_config"]) == ctypes.sizeof(q.qtalk_config)
     assert int(got["qtalk_layer_weights"]) == ctypes.sizeof(q.qtalk_layer_weights)
     assert int(got["qtalk_weights"]) == ctypes.sizeof(q.qtalk_weights)
+    assert int(got["qtalk_gather"]) == ctypes.sizeof(q.qtalk_gather)
     for key, val in got.items():
         if "." in key:
             st, f = key.split(".")
@@ -105,6 +109,7 @@ def test_null_context_calls_are_rejected():
     assert lib.qtalk_select_head(None, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_set_wait_limit(None, 0) == q.QTALK_E_INVAL
     assert lib.qtalk_decode_noalloc(None, 0, None, None, None) == q.QTALK_E_INVAL
+    assert lib.qtalk_decode_step(None, 0, None, None, None, None, 0, -1, None) == q.QTALK_E_INVAL
     assert lib.qtalk_embed_sum(None, 1, None, None, None, 1, None, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax(None, None, 1, 8, 8, -1, None) == q.QTALK_E_INVAL
     assert lib.qtalk_argmax_embed(None, None, 1, 8, 8, -1, None, 4, None, None) == q.QTALK_E_INVAL

@@ -932,6 +932,111 @@ def test_device_frame_loop_matches_teacher_forced_oracle():
     cp.close()
 
 
+def _frame_loop(tk, cp, tabs_d, ovs, ids, n_frames, fused):
+    """Codec frames on the device: the Talker step (input gathered from the
+    previous frame's 16 ids and the overlay row, codebook-0 pick with the
+    suppression) and the code predictor's 15 codes (two-row start, then 14
+    steps whose inputs are the previous code's table row).  fused: each
+    step is one qtalk_decode_step (gather and pick inside the persistent
+    decode); else separate gather, decode and pick kernels."""
+    import torch
+    from qwen3_tts_talker_amd import qtalk
+    from qwen3_tts_talker_amd.qtalk import make_gather
+    V, H, EOS, CV = tk.shape.vocab, tk.shape.hidden, 2150, cp.shape.vocab
+    outs = []
+    for f in range(n_frames):
+        lg_t = torch.empty(V, device="cuda")
+        cp_in = torch.empty(2, H, device="cuda")
+        lgs = torch.empty(15, CV, device="cuda")
+        if fused:
+            qtalk.qtalk_decode_step(tk.ctx, 0, None, make_gather(tabs_d, ids[f], ovs[f].view(-1)),
+                                    lg_t, cp_in[0], V - 1024, EOS, ids[f + 1, 0:1])
+            cp.kv_rewind(0, 0)
+            cp.select_head(0)
+            qtalk.qtalk_decode_step(cp.ctx, 0, cp_in[0], None, lgs[0])
+            qtalk.qtalk_decode_step(cp.ctx, 0, None, make_gather(tabs_d[0:1], ids[f + 1, 0:1]),
+                                    lgs[0], None, out_id=ids[f + 1, 1:2])
+            for j in range(1, 15):
+                cp.select_head(j)
+                qtalk.qtalk_decode_step(cp.ctx, 0, None, make_gather(tabs_d[j:j + 1], ids[f + 1, j:j + 1]),
+                                        lgs[j], None, out_id=ids[f + 1, j + 1:j + 2])
+        else:
+            emb = tk.embed_sum(tabs_d, ids[f].view(16, 1), ovs[f].view(1, H))
+            qtalk.qtalk_decode(tk.ctx, 0, emb, lg_t, cp_in[0])
+            tk.argmax(lg_t, suppress_begin=V - 1024, keep_id=EOS, out=ids[f + 1, 0:1])
+            cp.embed_sum(tabs_d[0:1], ids[f + 1, 0:1].view(1, 1), out=cp_in[1:2])
+            cp.select_head(0)
+            qtalk.qtalk_prefill(cp.ctx, 0, cp_in, 2, lgs[0])
+            cp.argmax(lgs[0], out=ids[f + 1, 1:2])
+            for j in range(1, 15):
+                e = cp.embed_sum(tabs_d[j:j + 1], ids[f + 1, j:j + 1].view(1, 1))
+                cp.select_head(j)
+                qtalk.qtalk_decode(cp.ctx, 0, e, lgs[j])
+                cp.argmax(lgs[j], out=ids[f + 1, j + 1:j + 2])
+        outs.append((lg_t, cp_in, lgs))
+    return outs
+
+
+def test_fused_frame_step_equals_separate_kernels():
+    # the same three frames through qtalk_decode_step (gather and pick inside
+    # the persistent decode, no other kernel) and through separate gather,
+    # decode and pick kernels: every id and every logit bit for bit
+    import torch
+    ts = workload("talker_28l_t128_d1024")
+    tw = weights_for("talker_28l_t128_d1024", 2)
+    cs = workload("code_predictor_5l")
+    cw = weights_for("code_predictor_5l")
+    tabs, tabs_d = _tables_dev(ts)
+    pre = prefill_embeddings(ts, 16)
+    ovs = [dev(overlay_row(ts, f)) for f in range(3)]
+    res = []
+    for fused in (False, True):
+        tk, cp = _talker(ts, tw), _talker(cs, cw)
+        tk.prefill(0, dev(pre))
+        ids = torch.zeros((4, 16), dtype=torch.int32, device="cuda")
+        ids[0] = torch.arange(16, dtype=torch.int32) * 37
+        outs = _frame_loop(tk, cp, tabs_d, ovs, ids, 3, fused)
+        tk.sync()
+        cp.sync()
+        # the Talker's logits, its hidden state (the code predictor's first
+        # row) and the 15 code logits; the fused path gathers the second row
+        # inside the kernel, so cp_in[1] is not compared
+        res.append((ids.cpu().numpy(), [(host(lg), host(ci[0]), host(lc)) for lg, ci, lc in outs]))
+        say(f"fused={fused} ids {res[-1][0][1:, :6].tolist()}")
+        tk.close()
+        cp.close()
+    assert np.array_equal(res[0][0], res[1][0])
+    for a, b in zip(res[0][1], res[1][1]):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_fused_frame_step_reports_an_id_outside_its_table():
+    import torch
+    from qwen3_tts_talker_amd import QtalkError, qtalk
+    from qwen3_tts_talker_amd.qtalk import make_gather
+    ts = workload("talker_28l_t128_d1024")
+    tk = _talker(ts, weights_for("talker_28l_t128_d1024", 2))
+    tabs, tabs_d = _tables_dev(ts)
+    tk.prefill(0, dev(prefill_embeddings(ts, 8)))
+    ids = torch.arange(16, dtype=torch.int32, device="cuda") * 3
+    ids[5] = tabs[5].shape[0]                  # one past table 5
+    lg = torch.empty(ts.vocab, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qtalk.qtalk_decode_step(tk.ctx, 0, None, make_gather(tabs_d, ids), lg, None, out_id=out)
+    assert tk.kv_len(0) == 9
+    with pytest.raises(QtalkError) as err:
+        tk.sync()
+    say(f"  sync: {err.value}")
+    assert np.isnan(lg.cpu().numpy()).all()
+    assert tk.kv_len(0) == 8                   # the step's position is dropped
+    tk.sync()                                  # reported once, then cleared
+    with pytest.raises(QtalkError) as err:     # both emb and a gather
+        qtalk.qtalk_decode_step(tk.ctx, 0, lg, make_gather(tabs_d, ids), lg)
+    assert err.value.status == -1
+    tk.close()
+
+
 @pytest.mark.parametrize("n,T", [(16, 128), (7, 100), (3, 1000), (5, 3)])
 def test_prefill_batch_matches_oracle(n, T):
     # 16 x 128: one matrix-core pass of 2048 rows; 7 x 100: ragged tiles;
