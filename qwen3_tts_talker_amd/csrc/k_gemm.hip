@@ -319,18 +319,23 @@ constexpr int SK_KC = 128;             // K values per chunk
 constexpr int SK_LD = SK_KC + 8;       // bf16 per LDS row
 constexpr int SK_WAVE = 2 * 32 * SK_LD;  // bf16 per wave region (A rows, then B rows)
 
-template <int EPI>
+// SPLIT: block z of the grid's third dimension takes the z-th of gridDim.z
+// equal K ranges and writes its partial tile to work[z] (EPI_ADD only; the
+// fused reduce adds the splits, the residual and the next RMSNorm)
+template <int EPI, bool SPLIT = false>
 __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];  // nw * SK_WAVE; also the wave tiles at the end
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
   const int M = a.M;
-  const int nch = a.K / SK_KC;
+  const int nch = a.K / SK_KC / gridDim.z;  // chunks of this block's K range
+  const int kofs = blockIdx.z * nch * SK_KC;
   bf16_t* W = lds + wave * SK_WAVE;
   // staging: instruction i covers rows 4i .. 4i+3, lane l row 4i + l/16,
   // columns 8 (l % 16) .. +7 of the chunk
-  const int sr = lane >> 4, sc = (lane & 15) * 8;
-  const bf16_t* Bg = a.B + (size_t)(n0 + sr) * a.K + sc;
+  const int sr = lane >> 4, sc = (lane & 15) * 8;  // sc: column inside the chunk (LDS and global)
+  const bf16_t* Ag = a.A + kofs + sc;
+  const bf16_t* Bg = a.B + (size_t)(n0 + sr) * a.K + kofs + sc;
   const size_t bstep = (size_t)4 * a.K;
   const int arow_max = M - 1 - m0;  // last valid row of the tile (rows past it: not stored)
   bf16x8_t ra[8], rb[8];  // vector types: the arrays stay in registers
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = min(4 * i + sr, arow_max);
-      ra[i] = *reinterpret_cast<const bf16x8_t*>(a.A + (size_t)(m0 + r) * a.lda + sc + ch * SK_KC);
+      ra[i] = *reinterpret_cast<const bf16x8_t*>(Ag + (size_t)(m0 + r) * a.lda + ch * SK_KC);
       rb[i] = *reinterpret_cast<const bf16x8_t*>(Bg + i * bstep + ch * SK_KC);
     }
   }
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = min(4 * i + sr, arow_max);
-        ra[i] = *reinterpret_cast<const bf16x8_t*>(a.A + (size_t)(m0 + r) * a.lda + sc + nx * SK_KC);
+        ra[i] = *reinterpret_cast<const bf16x8_t*>(Ag + (size_t)(m0 + r) * a.lda + nx * SK_KC);
         rb[i] = *reinterpret_cast<const bf16x8_t*>(Bg + i * bstep + nx * SK_KC);
       }
     }
@@ -392,6 +397,10 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
       continue;
     }
     if (row >= M) continue;
+    if (SPLIT) {
+      a.work[((size_t)blockIdx.z * M + row) * a.N + n0 + col] = v;
+      continue;
+    }
     float* c = reinterpret_cast<float*>(a.C) + (size_t)row * a.ldc + n0 + col;
     if (EPI == EPI_STORE) *c = v;
     else *c += v;
@@ -549,6 +558,25 @@ static int dma_splits(const GemmArgs& a) {
 
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,
                           hipStream_t st) {
+  if (skinny_ok(a) && a.N % 4 == 0 && a.N <= 1024) {
+    // few rows: a narrow output (o_proj, down: N / 32 = 32 tiles) would
+    // leave most CUs idle, so K is split over up to 8 blocks per tile and
+    // the splits meet in the fused reduce, which also adds the residual and
+    // forms the next RMSNorm's bf16 rows
+    const int nch = a.K / SK_KC, tiles = (a.N / 32) * ((a.M + 31) / 32);
+    int ks = 1;
+    while (ks * 2 <= SPLITK_MAX && tiles * ks * 2 <= 256 && nch % (ks * 2) == 0 && nch / (ks * 2) >= 2 &&
+           (size_t)(ks * 2) * a.M * a.N <= a.work_elems)
+      ks *= 2;
+    if (ks > 1) {
+      int nw = 8;
+      while ((nch / ks) % nw) --nw;
+      hipLaunchKernelGGL((k_gemm_skinny<EPI_ADD, true>), dim3(a.N / 32, (a.M + 31) / 32, ks), dim3(64 * nw),
+                         nw * SK_WAVE * sizeof(bf16_t), st, a);
+      hipLaunchKernelGGL(k_splitk_reduce_add_norm, dim3(a.M), dim3(256), 0, st, a, ks, g, eps, hn, ldh);
+      return;
+    }
+  }
   if (a.M >= 512 && a.N % 4 == 0 && a.N <= 1024) {
     const int ks = dma_splits(a);
     if (ks > 1 && ks <= SPLITK_MAX) {
