@@ -643,7 +643,7 @@ void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
 
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* x, int ldx, int K,
                                                       const float* g, float eps, bf16_t* out,
-                                                      int ldo) {
+                                                      int ldo, float* out32, int ld32) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const float* xr = x + (size_t)t * ldx;
@@ -657,16 +657,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* x, int ldx, i
   for (int k = tid * 4; k < K; k += 1024) {
     const float4 v = *reinterpret_cast<const float4*>(xr + k);
     const float4 gg = *reinterpret_cast<const float4*>(g + k);
+    const float4 y = make_float4(v.x * inv * gg.x, v.y * inv * gg.y, v.z * inv * gg.z, v.w * inv * gg.w);
     uint2 o;
-    o.x = f32_to_bf16(v.x * inv * gg.x) | (f32_to_bf16(v.y * inv * gg.y) << 16);
-    o.y = f32_to_bf16(v.z * inv * gg.z) | (f32_to_bf16(v.w * inv * gg.w) << 16);
+    o.x = f32_to_bf16(y.x) | (f32_to_bf16(y.y) << 16);
+    o.y = f32_to_bf16(y.z) | (f32_to_bf16(y.w) << 16);
     *reinterpret_cast<uint2*>(out + (size_t)t * ldo + k) = o;
+    if (out32) *reinterpret_cast<float4*>(out32 + (size_t)t * ld32 + k) = y;
   }
 }
 
 void launch_rmsnorm_bf16(const float* x, int ldx, int T, int K, const float* g, float eps,
-                         bf16_t* out, int ldo, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(T), dim3(256), 0, st, x, ldx, K, g, eps, out, ldo);
+                         bf16_t* out, int ldo, hipStream_t st, float* out32, int ld32) {
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(T), dim3(256), 0, st, x, ldx, K, g, eps, out, ldo, out32, ld32);
 }
 
 }  // namespace qtalk

@@ -125,9 +125,10 @@ bool gemm_shape_ok(int M, int N, int K);
 // shapes the skinny (<= 128-row) product takes: N % 32 == 0, K % 128 == 0
 bool skinny_shape_ok(int N, int K);
 
-// out[t][k] = bf16(RMSNorm(x[t]) * g)
+// out[t][k] = bf16(RMSNorm(x[t]) * g); also the float32 values to out32 when set
 void launch_rmsnorm_bf16(const float* x, int ldx, int T, int K, const float* g,
-                         float eps, bf16_t* out, int ldo, hipStream_t st);
+                         float eps, bf16_t* out, int ldo, hipStream_t st, float* out32 = nullptr,
+                         int ld32 = 0);
 
 // cos/sin table [cap][half], angle pos * theta^(-2i/hd), float64 math
 void launch_rope_table(float2* tab, int cap, int head_dim, double theta,

@@ -598,8 +598,17 @@ struct Fwd {
         if (mfma && nb >= BATCH_MFMA_MIN) layer_rows_mfma(l, rows, l > 0);
         else layer_gemv(l, rows);
       }
-      head(c->x, nb, logits + (size_t)b0 * g.vocab,
-           hidden_out ? hidden_out + (size_t)b0 * g.hidden : nullptr);
+      float* hid = hidden_out ? hidden_out + (size_t)b0 * g.hidden : nullptr;
+      if (mfma && nb >= BATCH_MFMA_MIN && skinny_shape_ok(g.vocab, g.hidden)) {
+        // the head on the matrix cores too (bf16 normed rows, as the layers'
+        // projections): the weights are read once for all rows
+        launch_rmsnorm_bf16(c->x, g.hidden, nb, g.hidden, c->g_final, g.rms_eps, c->hn, g.hidden, st, hid,
+                            g.hidden);
+        gemm(c->hn, g.hidden, head_w(), nb, g.vocab, g.hidden, logits + (size_t)b0 * g.vocab, g.vocab,
+             EPI_STORE);
+      } else {
+        head(c->x, nb, logits + (size_t)b0 * g.vocab, hid);
+      }
     }
     return QTALK_OK;
   }
