@@ -521,8 +521,11 @@ def test_long_context_28_layers_32k_persistent_matches_per_step(monkeypatch):
     # which walks 1025-1032 keys per chunk block here, against the per-step
     # decode kernels on the same cache contents; every logit finite (the f32
     # sums of squares carry the 3e4 channels).  The oracle cannot form this
-    # model's 28 layers at 32k positions in test time: parity unpinned at
-    # this size (the one-layer 32k tests pin the attention there)
+    # model's 28 layers of 32k positions in test time, so the last decode
+    # step is checked against the oracle walked one layer at a time over the
+    # caches the device holds for the earlier positions (read back): the
+    # step itself is pinned; the 32k caches are pinned by the one-layer 32k
+    # tests
     name = "talker_28l_ctx32k_outlier"
     shape = workload(name)
     w = weights_for(name)
@@ -542,13 +545,52 @@ def test_long_context_28_layers_32k_persistent_matches_per_step(monkeypatch):
         assert tk.kv_len(0) == shape.prefill_len
     assert np.array_equal(last[0], last[1])  # same prefill kernels on both
     worst = 0.0
+    # the last step's input row is N(0, 1) without outlier channels, so that
+    # its logits carry the attention over the 32k cached positions
+    last_row = np.random.default_rng(1234).standard_normal(shape.hidden).astype(np.float32)
     for k in range(shape.decode_steps):
-        e = dev(step_embedding(shape, k))
+        row = step_embedding(shape, k) if k + 1 < shape.decode_steps else last_row
+        e = dev(row)
         a, b = host(tks[0].decode(0, e)), host(tks[1].decode(0, e))
         worst = max(worst, rel_err(a, b))
         assert argmax_ok(a, b)
     say(f"  persistent vs per-step decode at 32k: rel diff max {worst:.2e}")
     assert worst <= TOL_BF16
+    tks[0].sync()
+    # the last step (position pos) of the persistent decode against the
+    # oracle: layer l takes the device's K/V of positions < pos, appends its
+    # own K/V row for pos and attends; its output feeds layer l + 1.  A second
+    # walk with o_proj = 0 in every layer gives the attention's share of the
+    # logits, against which the error is also measured.
+    tk = tks[0]
+    pos = tk.kv_len(0) - 1
+    x = last_row[None].astype(np.float64)
+    x0 = x.copy()
+    worst_kv = 0.0
+    for l in range(shape.n_layers):
+        lw = w["layers"][l]
+        one = TalkerOracle(shape, {"layers": [lw], "g_final": w["g_final"], "w_head": w["w_head"]})
+        off = TalkerOracle(shape, {"layers": [dict(lw, wo=np.zeros_like(lw["wo"]))],
+                                   "g_final": w["g_final"], "w_head": w["w_head"]})
+        kd, vd = host(tk.kv_read(0, l, 0)), host(tk.kv_read(0, l, 1))
+        for o in (one, off):
+            o._reserve(0, pos + 1)
+            o.kc[0][0, :, :pos] = kd[:, :pos]
+            o.vc[0][0, :, :pos] = vd[:, :pos]
+            o.cur_len[0] = pos
+        x = one.layer(0, x, 0, pos)
+        x0 = off.layer(0, x0, 0, pos)
+        worst_kv = max(worst_kv, rel_err(kd[:, pos], one.kc[0][0, :, pos]),
+                       rel_err(vd[:, pos], one.vc[0][0, :, pos]))
+        del kd, vd, off
+    ref, ref0 = one.head(x)[0][0], one.head(x0)[0][0]
+    err = rel_err(a, ref)
+    att = rel_err(ref0, ref)
+    say(f"  last step at position {pos} vs the oracle over the device caches: rel err {err:.2e} "
+        f"(the attention's share of the logits {att:.2e}), new K/V rows {worst_kv:.2e}")
+    assert err <= TOL_BF16 and worst_kv <= TOL_BF16
+    assert err <= 0.1 * att
+    assert argmax_ok(a, ref)
     for tk in tks:
         tk.close()
 

@@ -160,6 +160,40 @@ def test_prefill_equals_prefill_then_decode(kv):
                                        rtol=1e-11, atol=1e-12)
 
 
+def test_layer_walk_over_a_stored_cache_reproduces_the_decode():
+    # the harness of the 28-layer 32k GPU check: one decode step formed
+    # layer by layer by one-layer oracles, each handed the stored K/V of the
+    # earlier positions, equals the full oracle's decode step (logits and
+    # the new K/V rows); a cache entry perturbed in the hand-over changes it
+    shape = small_shape(kv_dtype="f16", n_layers=3)
+    w = scaled_weights(shape)
+    emb = prefill_embeddings(shape, 21)
+    full = TalkerOracle(shape, w)
+    full.prefill(0, emb[:20])
+    ref, _ = full.decode(0, emb[20])
+    pos = 20
+
+    def walk(perturb=None):
+        x = emb[20][None].astype(np.float64)
+        for l in range(shape.n_layers):
+            one = TalkerOracle(shape, {"layers": [w["layers"][l]], "g_final": w["g_final"],
+                                       "w_head": w["w_head"]})
+            one._reserve(0, pos + 1)
+            one.kc[0][0, :, :pos] = full.kv(0, l, 0)[:, :pos]
+            one.vc[0][0, :, :pos] = full.kv(0, l, 1)[:, :pos]
+            if perturb == l:
+                one.vc[0][0, 1, 3] += 0.25
+            one.cur_len[0] = pos
+            x = one.layer(0, x, 0, pos)
+            if perturb is None:
+                np.testing.assert_array_equal(one.kc[0][0, :, pos], full.kv(0, l, 0)[:, pos])
+                np.testing.assert_array_equal(one.vc[0][0, :, pos], full.kv(0, l, 1)[:, pos])
+        return one.head(x)[0][0]
+
+    np.testing.assert_allclose(walk(), ref, rtol=1e-13, atol=1e-13)
+    assert np.max(np.abs(walk(perturb=1) - ref)) > 1e-4 * np.max(np.abs(ref))
+
+
 # -- the q8 cache: earlier positions quantised, the call's own rows fresh -------
 
 def _q8_round_trip(t):
