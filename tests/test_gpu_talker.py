@@ -356,6 +356,33 @@ def test_batched_ragged_decode_16_sequences():
     assert max(errs) <= TOL_BF16
     assert all(argmax_ok(outs[k][s], ref[len(pre[s]) + k])
                for k in range(steps))
+    # every sequence's last step against the oracle walked one layer at a
+    # time over the device's K/V of its earlier positions (read back); the
+    # oracle appends and attends each new row itself
+    last = np.stack([step_embedding(shape, steps - 1, seq=q) for q in seqs]).astype(np.float64)
+    pos = [tk.kv_len(q) - 1 for q in seqs]
+    xs = [last[q][None] for q in seqs]
+    worst_kv = 0.0
+    for l in range(shape.n_layers):
+        one = TalkerOracle(shape, {"layers": [w["layers"][l]], "g_final": w["g_final"],
+                                   "w_head": w["w_head"]})
+        for q in seqs:
+            kd, vd = host(tk.kv_read(q, l, 0)), host(tk.kv_read(q, l, 1))
+            one._reserve(q, pos[q] + 1)
+            one.kc[q][0, :, :pos[q]] = kd[:, :pos[q]]
+            one.vc[q][0, :, :pos[q]] = vd[:, :pos[q]]
+            one.cur_len[q] = pos[q]
+            xs[q] = one.layer(0, xs[q], q, pos[q])
+            worst_kv = max(worst_kv, rel_err(kd[:, pos[q]], one.kc[q][0, :, pos[q]]),
+                           rel_err(vd[:, pos[q]], one.vc[q][0, :, pos[q]]))
+        del one
+    head = TalkerOracle(shape, {"layers": [w["layers"][0]], "g_final": w["g_final"],
+                                "w_head": w["w_head"]})
+    walk = [rel_err(outs[-1][q], head.head(xs[q])[0][0]) for q in seqs]
+    say(f"  last batched step, all 16 sequences vs the oracle over the device caches: "
+        f"rel err max {max(walk):.2e}, new K/V rows {worst_kv:.2e}")
+    assert max(walk) <= TOL_BF16 and worst_kv <= TOL_BF16
+    assert all(argmax_ok(outs[-1][q], head.head(xs[q])[0][0]) for q in seqs)
 
 
 def test_batched_ragged_decode_16_sequences_every_row():
