@@ -195,8 +195,13 @@ qtalk_status qtalk_decode_noalloc(qtalk_ctx *ctx, int32_t seq, const float *emb,
 
 /* Batched decode: one position for each of n distinct sequences seqs[0..n)
  * (a HOST array), emb [n][hidden], logits [n][vocab], hidden_out [n][hidden]
- * (nullable).  Row i is exactly the single-sequence decode of seqs[i]; the
- * sequences may have different lengths.  ("qwentts.cpp
+ * (nullable).  Row i is the single-sequence decode of seqs[i]; the sequences
+ * may have different lengths.  Below 8 rows the rows go through the
+ * per-step decode kernels (float32 activations, the same results as
+ * single-sequence decodes on those kernels); from 8 rows the projections
+ * (the codec head included) run on the matrix cores with activations
+ * rounded to bf16, so results differ from single decodes at that rounding.
+ * ("qwentts.cpp
  * src/talker-forward.h", talker_forward_decode and
  * talker_layer_forward_batch.)  Errors: QTALK_E_INVAL (n < 1, n > max_seqs,
  * repeated or out-of-range id), QTALK_E_OVERFLOW if any sequence is full;
