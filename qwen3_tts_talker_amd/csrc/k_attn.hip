@@ -518,6 +518,13 @@ __global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
   const int ns = a.n_splits, HD = a.head_dim;
   const size_t base = (size_t)(t * a.n_heads + h) * ns;
   const float* ml = a.part_ml + base * 2;
+  const float* po = a.part_o + base * HD + d;
+  // the first PF splits' values are requested before the weights, so the
+  // two reads overlap
+  constexpr int PF = 16;
+  float pv[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) pv[i] = i < ns ? po[(size_t)i * HD] : 0.f;
   if (d < 64) {  // one wave forms the weights
     float M = -INFINITY;
     for (int c = d; c < ns; c += 64) M = fmaxf(M, ml[2 * c]);
@@ -533,9 +540,11 @@ __global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
     for (int c = d; c < ns; c += 64) s_w[c] /= L;
   }
   __syncthreads();
-  const float* po = a.part_o + base * HD + d;
   float o = 0.f;
-  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (i < ns) o = fmaf(s_w[i], pv[i], o);
+  int c = PF;
   for (; c + 8 <= ns; c += 8) {
     float v[8];
 #pragma unroll
