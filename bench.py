@@ -32,8 +32,16 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def kv_row_bytes(s) -> int:
+    """Bytes of one cached K or V row of one head: float16 / float32 values,
+    or Q8_0 (head_dim codes, then a float16 scale per 32 values)."""
+    if s.kv_dtype == "q8":
+        return s.head_dim + s.head_dim // 16
+    return s.head_dim * (2 if s.kv_dtype == "f16" else 4)
+
+
 def kv_bytes_per_position(s) -> int:
-    return s.n_layers * 2 * s.n_kv_heads * s.head_dim * (2 if s.kv_dtype == "f16" else 4)
+    return s.n_layers * 2 * s.n_kv_heads * kv_row_bytes(s)
 
 
 def weight_bytes(s) -> int:
@@ -123,16 +131,17 @@ def cpu_baseline(shape, weights, emb, steps_emb, n_steps: int):
     }
 
 
-def batched_decode(n_steps: int, warmup: int = 4) -> dict:
+def batched_decode(n_steps: int, warmup: int = 4, kv_dtype: str = "f16") -> dict:
     """Batched decode of 16 independent utterances on the 28-layer Talker
     (its own seeded weights): KV lengths drawn uniformly from 512..4096, each
     sequence filled by a prefill and 2048-row extends, then one token per
     sequence and step (qtalk_decode_batch).  Algorithmic bytes per step:
-    every weight once plus K and V of every attended position."""
+    every weight once plus K and V of every attended position (in the cache
+    type: float16, or Q8_0 rows)."""
     import torch
     from qwen3_tts_talker_amd import Talker
     from synth import batch_lengths, make_weights, prefill_embeddings, step_embedding, workload
-    shape = workload("talker_28l_batch16_ragged")
+    shape = workload("talker_28l_batch16_ragged").with_(kv_dtype=kv_dtype)
     tk = Talker(shape, make_weights(shape))
     lens = [int(x) for x in batch_lengths(shape)]
     for s, L in enumerate(lens):
@@ -157,12 +166,49 @@ def batched_decode(n_steps: int, warmup: int = 4) -> dict:
     us = e0.elapsed_time(e1) * 1e3 / n_steps
     ctx = [L + warmup for L in lens]  # context of the first timed step
     kv_pos = sum(c + 1 for c in ctx) + len(seqs) * (n_steps - 1) / 2
-    nbytes = 887_095_296 + 114_688 * kv_pos
+    nbytes = weight_bytes(shape) + kv_bytes_per_position(shape) * kv_pos
     tk.close()
-    return {"workload": "talker_28l_batch16_ragged", "seqs": len(seqs), "kv_len_range": [min(lens), max(lens)],
+    return {"workload": "talker_28l_batch16_ragged", "kv_cache": kv_dtype, "seqs": len(seqs),
+            "kv_len_range": [min(lens), max(lens)],
             "steps": n_steps, "step_us": round(us, 1), "tok_s": round(len(seqs) * 1e6 / us, 1),
             "bytes_per_step": int(nbytes), "achieved_gbs": round(nbytes / us / 1e3, 1),
             "hbm_frac": round(nbytes / us / 1e3 / 8000.0, 4)}
+
+
+def q8_decode(n_steps: int, warmup: int = 8) -> dict:
+    """The headline workload (28 layers, 1920-row prefill, batch-1 decode)
+    with the 8-bit cache: decode tok/s and the HBM fraction of its
+    algorithmic bytes (every weight once, Q8_0 K/V rows of every attended
+    position, the new position written)."""
+    import torch
+    from qwen3_tts_talker_amd import Talker
+    from synth import make_weights, prefill_embeddings, step_embedding, workload
+    shape = workload("talker_28l_kv2k").with_(kv_dtype="q8")
+    T = shape.prefill_len
+    tk = Talker(shape, make_weights(shape))
+    emb = torch.from_numpy(prefill_embeddings(shape, T)).cuda()
+    steps = [torch.from_numpy(step_embedding(shape, k)).cuda() for k in range(n_steps)]
+    tk.prefill(0, emb)
+    for k in range(warmup):
+        tk.decode(0, steps[k % n_steps])
+    tk.sync()
+    tk.kv_rewind(0, T)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for k in range(n_steps):
+        tk.decode(0, steps[k])
+    e1.record(st)
+    torch.cuda.synchronize()
+    tk.sync()
+    assert tk.kv_len(0) == T + n_steps
+    us = e0.elapsed_time(e1) * 1e3 / n_steps
+    nbytes = sum(decode_bytes(shape, T + k + 1) for k in range(n_steps)) / n_steps
+    tk.close()
+    return {"workload": "talker_28l_kv2k", "kv_cache": "q8", "steps": n_steps,
+            "decode_ctx": [T + 1, T + n_steps], "step_us": round(us, 1),
+            "tok_s": round(1e6 / us, 1), "bytes_per_step": int(nbytes),
+            "achieved_gbs": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def long_context(n_steps: int, warmup: int = 4) -> dict:
@@ -436,6 +482,9 @@ def main(argv=None):
     ap.add_argument("--long-context", type=int, default=256,
                     help="decode steps of the 32k long-context leg after its 16 x 2048-row "
                          "prefill (0: skip the leg)")
+    ap.add_argument("--q8", type=int, default=64,
+                    help="decode steps of the 8-bit-cache legs (batch-1 headline workload and the "
+                         "16-utterance batch; 0: skip)")
     ap.add_argument("--cp-frames", type=int, default=20,
                     help="code predictor frames timed after the Talker (0: skip)")
     ap.add_argument("--pmc-calibration-mib", type=int, default=0,
@@ -562,6 +611,9 @@ def main(argv=None):
         out["decode_batch"] = batched_decode(args.batch_decode)
     if args.long_context > 0:
         out["long_context"] = long_context(args.long_context)
+    if args.q8 > 0:
+        out["kv_q8"] = {"decode": q8_decode(args.q8),
+                        "decode_batch": batched_decode(max(8, args.q8 // 4), kv_dtype="q8")}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights, emb_h, steps_h, args.cpu_steps)
     print(json.dumps(out), flush=True)

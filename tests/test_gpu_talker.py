@@ -214,18 +214,26 @@ def test_batched_decode_equals_serial(monkeypatch, fused):
         _batched_equals_serial(lens, fused)
 
 
-def _batched_equals_serial(lens, fused):
+def test_q8_batched_decode_equals_serial_and_oracle():
+    # the 8-bit cache through the batched decode: five rows (matrix-vector
+    # path) and eleven (matrix cores), each row's earlier positions read
+    # dequantised and its own new row as computed
+    for lens in ([3, 40, 17, 90, 1], [3, 40, 17, 90, 1, 64, 33, 2, 120, 7, 55]):
+        _batched_equals_serial(lens, True, kv_dtype="q8")
+
+
+def _batched_equals_serial(lens, fused, kv_dtype="f16"):
     # fewer than 8 rows: the matrix-vector kernels, the same per-row
     # arithmetic as serial decode (bitwise on the per-step path); 8 or more:
     # the matrix-core projections (bf16 activations), checked against serial
     # decode and the oracle at the bf16 bar
     n = len(lens)
-    shape = workload("talker_1l_t128").with_(n_seqs=n, cap=256)
+    shape = workload("talker_1l_t128").with_(n_seqs=n, cap=256, kv_dtype=kv_dtype)
     w = weights_for("talker_1l_t128")
     a = _talker(shape, w)
     b = _talker(shape, w)
     orc = TalkerOracle(shape, w)
-    say(f"[case] batched vs serial decode, {n} sequences, fused={fused}")
+    say(f"[case] batched vs serial decode, {n} sequences, fused={fused}, cache {kv_dtype}")
     for s, m in enumerate(lens):
         e = prefill_embeddings(shape, m, seq=s)
         a.prefill(s, dev(e))
