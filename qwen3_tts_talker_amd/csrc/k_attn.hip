@@ -315,33 +315,51 @@ struct KvRaw<float, N> {
   }
 };
 template <int N>
-struct KvRaw<q8_t, N> {  // N codes of one 32-value block and its scale
-  typedef signed char vec __attribute__((ext_vector_type(N)));
-  vec c;
+struct KvRaw<q8_t, N> {  // N (4, 8 or 16) codes of one 32-value block and its scale
+  // loads of at most 8 bytes: Q8_0 rows are 136 bytes, so 8-byte aligned
+  static constexpr int W = N < 8 ? N : 8;
+  typedef signed char vec __attribute__((ext_vector_type(W)));
+  vec c[N / W];
   f16_t sc;
   __device__ __forceinline__ void load(const char* row, int hd, int d) {
-    c = *reinterpret_cast<const vec*>(row + d);
+#pragma unroll
+    for (int i = 0; i < N / W; ++i) c[i] = *reinterpret_cast<const vec*>(row + d + W * i);
     sc = *reinterpret_cast<const f16_t*>(row + hd + (d >> 5) * 2);
   }
   __device__ __forceinline__ void get(float* f) const {
     const float s = (float)sc;
 #pragma unroll
-    for (int i = 0; i < N; ++i) f[i] = (float)c[i] * s;
+    for (int i = 0; i < N; ++i) f[i] = (float)c[i / W][i % W] * s;
   }
 };
+// sum over each aligned group of 8 lanes, in every lane of the group
+// (lanes i and 7 - i, then quad swaps)
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  return v;
+}
 
 template <int HD, int G, typename KVT, int OUT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
-  constexpr int DPL = HD / 16;
-  constexpr int U = 4;          // keys per slot and tile
-  constexpr int TILE = 16 * U;  // keys per tile
   constexpr bool Q8 = std::is_same<KVT, q8_t>::value;
+  // lanes per key row: 16 for float rows (8 values of 16 bytes per lane at
+  // head_dim 128); 8 for Q8_0 rows, so that a lane takes 16 codes (two
+  // 8-byte loads) and the one scale of their 32-value block (up to two query
+  // heads per KV head: more would not fit the registers)
+  constexpr int LPR = Q8 && G <= 2 ? 8 : 16;
+  constexpr int SPW = 64 / LPR;     // slots per wave
+  constexpr int DPL = HD / LPR;
+  constexpr int U = 16 / SPW;       // keys per slot and tile
+  constexpr int TILE = 4 * SPW * U;  // keys per tile (64)
+  static_assert(TILE == 64, "lane layout");
   __shared__ __attribute__((aligned(16))) float s_acc[4][G][HD];
   __shared__ float s_m[4][G], s_l[4][G];
 
   const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = lane >> 4, sub = lane & 15;
+  const int slot = lane / LPR, sub = lane % LPR;
   const int nq = a.n_heads, nkv = a.n_kv_heads;
   const int seq = row_seq(a.rows, t), pos = row_pos(a.rows, t);
   const int k_begin = c * a.keys_per_split;
@@ -388,12 +406,12 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   }
 
-  const int kofs = 4 * wave + slot;
+  const int kofs = SPW * wave + slot;
   KvRaw<KVT, DPL> kr[U], vr[U];
   auto load_tile = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = min(kb + 16 * u + kofs, k_end - 1);
+      const int j = min(kb + 4 * SPW * u + kofs, k_end - 1);
       kr[u].load(Kp + (size_t)j * RB, HD, sub * DPL);
       vr[u].load(Vp + (size_t)j * RB, HD, sub * DPL);
     }
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     if (Q8 && kb + TILE > fresh) {  // rows of this call: as computed
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = min(kb + 16 * u + kofs, k_end - 1);
+        const int j = min(kb + 4 * SPW * u + kofs, k_end - 1);
         if (j >= fresh) {
           const size_t r = (size_t)(t - pos + j) * a.ldq;
 #pragma unroll
@@ -424,13 +442,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = kb + 16 * u + kofs < k_end;
+      const bool ok = kb + 4 * SPW * u + kofs < k_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) d = fmaf(qr[h][e], kf[u][e], d);
-        d = row16_sum(d);
+        d = LPR == 16 ? row16_sum(d) : group8_sum(d);
         sc[u][h] = ok ? d : -INFINITY;
       }
     }
@@ -462,12 +480,15 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   // (slots are the wave's 16-lane rows: swaps across 16 and 32 lanes)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mw4 = half_xor16_max(half_xor32_max(m[h]));
+    // (Q8_0: 8 slots per wave, lanes l and l ^ 8 of each 16-lane row first)
+    const float m8 = LPR == 16 ? m[h] : fmaxf(m[h], dpp_mov<0x128>(m[h]));
+    const float mw4 = half_xor16_max(half_xor32_max(m8));
     const float scl = __builtin_amdgcn_exp2f(m[h] - mw4);
-    const float lw = xor_sum4(l[h] * scl);
+    auto slot_sum = [&](float v) { return xor_sum4(LPR == 16 ? v : v + dpp_mov<0x128>(v)); };
+    const float lw = slot_sum(l[h] * scl);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = xor_sum4(acc[h][e] * scl);
-    if (lane < 16) {
+    for (int e = 0; e < DPL; ++e) acc[h][e] = slot_sum(acc[h][e] * scl);
+    if (lane < LPR) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) s_acc[wave][h][sub * DPL + e] = acc[h][e];
     }
