@@ -290,6 +290,9 @@ void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
 
 template <typename KVT, int N>
 struct KvRaw;
+// get(f): the lane's N values, up to scale(): the factor that turns them
+// into the cached values (1 for float rows; the block scale for Q8_0 codes,
+// applied once to a dot product or a softmax weight instead of to every value)
 template <int N>
 struct KvRaw<f16_t, N> {
   typedef _Float16 vec __attribute__((ext_vector_type(N)));
@@ -301,6 +304,7 @@ struct KvRaw<f16_t, N> {
 #pragma unroll
     for (int i = 0; i < N; ++i) f[i] = (float)v[i];
   }
+  __device__ __forceinline__ float scale() const { return 1.f; }
 };
 template <int N>
 struct KvRaw<float, N> {
@@ -313,7 +317,36 @@ struct KvRaw<float, N> {
 #pragma unroll
     for (int i = 0; i < N; ++i) f[i] = v[i];
   }
+  __device__ __forceinline__ float scale() const { return 1.f; }
 };
+// signed byte k of w as a float in one instruction (SDWA byte select with
+// sign extension)
+template <int K>
+__device__ __forceinline__ float i8_to_f32(uint32_t w);
+template <>
+__device__ __forceinline__ float i8_to_f32<0>(uint32_t w) {
+  float r;
+  asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+  return r;
+}
+template <>
+__device__ __forceinline__ float i8_to_f32<1>(uint32_t w) {
+  float r;
+  asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  return r;
+}
+template <>
+__device__ __forceinline__ float i8_to_f32<2>(uint32_t w) {
+  float r;
+  asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  return r;
+}
+template <>
+__device__ __forceinline__ float i8_to_f32<3>(uint32_t w) {
+  float r;
+  asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
 template <int N>
 struct KvRaw<q8_t, N> {  // N (4, 8 or 16) codes of one 32-value block and its scale
   // loads of at most 8 bytes: Q8_0 rows are 136 bytes, so 8-byte aligned
@@ -326,11 +359,22 @@ struct KvRaw<q8_t, N> {  // N (4, 8 or 16) codes of one 32-value block and its s
     for (int i = 0; i < N / W; ++i) c[i] = *reinterpret_cast<const vec*>(row + d + W * i);
     sc = *reinterpret_cast<const f16_t*>(row + hd + (d >> 5) * 2);
   }
+  // the codes as floats (the scale stays apart)
   __device__ __forceinline__ void get(float* f) const {
-    const float s = (float)sc;
 #pragma unroll
-    for (int i = 0; i < N; ++i) f[i] = (float)c[i / W][i % W] * s;
+    for (int i = 0; i < N / W; ++i) {
+#pragma unroll
+      for (int j = 0; j < W / 4; ++j) {
+        uint32_t w;
+        __builtin_memcpy(&w, reinterpret_cast<const char*>(&c[i]) + 4 * j, 4);
+        f[W * i + 4 * j] = i8_to_f32<0>(w);
+        f[W * i + 4 * j + 1] = i8_to_f32<1>(w);
+        f[W * i + 4 * j + 2] = i8_to_f32<2>(w);
+        f[W * i + 4 * j + 3] = i8_to_f32<3>(w);
+      }
+    }
   }
+  __device__ __forceinline__ float scale() const { return (float)sc; }
 };
 // sum over each aligned group of 8 lanes, in every lane of the group
 // (lanes i and 7 - i, then quad swaps)
@@ -418,11 +462,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   };
   load_tile(k_begin);
   for (int kb = k_begin; kb < k_end; kb += TILE) {
-    float kf[U][DPL], vf[U][DPL];
+    float kf[U][DPL], vf[U][DPL], ks[U], vs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       kr[u].get(kf[u]);
       vr[u].get(vf[u]);
+      ks[u] = kr[u].scale();
+      vs[u] = vr[u].scale();
     }
     load_tile(kb + TILE < k_end ? kb + TILE : kb);  // next tile (the last one reloads itself)
     if (Q8 && kb + TILE > fresh) {  // rows of this call: as computed
@@ -436,6 +482,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
             kf[u][e] = Kf[r + e];
             vf[u][e] = Vf[r + e];
           }
+          ks[u] = vs[u] = 1.f;
         }
       }
     }
@@ -448,6 +495,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) d = fmaf(qr[h][e], kf[u][e], d);
+        d *= ks[u];  // a lane's values share one Q8_0 block scale
         d = LPR == 16 ? row16_sum(d) : group8_sum(d);
         sc[u][h] = ok ? d : -INFINITY;
       }
@@ -465,11 +513,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
         ps += p[u];
       }
       l[h] = fmaf(l[h], alpha, ps);
+      float pv[U];  // softmax weight times the value rows' scale
+#pragma unroll
+      for (int u = 0; u < U; ++u) pv[u] = p[u] * vs[u];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         float v = acc[h][e] * alpha;
 #pragma unroll
-        for (int u = 0; u < U; ++u) v = fmaf(p[u], vf[u][e], v);
+        for (int u = 0; u < U; ++u) v = fmaf(pv[u], vf[u][e], v);
         acc[h][e] = v;
       }
       m[h] = mx;
