@@ -395,9 +395,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   constexpr int LPR = Q8 && G <= 2 ? 8 : 16;
   constexpr int SPW = 64 / LPR;     // slots per wave
   constexpr int DPL = HD / LPR;
-  constexpr int U = 16 / SPW;       // keys per slot and tile
-  constexpr int TILE = 4 * SPW * U;  // keys per tile (64)
-  static_assert(TILE == 64, "lane layout");
+  constexpr int U = LPR == 8 ? 1 : 16 / SPW;  // keys per slot and tile
+  constexpr int TILE = 4 * SPW * U;           // keys per tile (64; 32 for Q8_0 rows)
   __shared__ __attribute__((aligned(16))) float s_acc[4][G][HD];
   __shared__ float s_m[4][G], s_l[4][G];
 
