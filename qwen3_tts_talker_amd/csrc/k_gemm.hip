@@ -273,6 +273,44 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
 #undef QD_COMPUTE
 
   // epilogue: register r of lane l is C[row (r/4)*8 + (l/32)*4 + r%4][col l%32]
+  if constexpr (EPI == EPI_SWIGLU && !SPLIT) {
+    // SwiGLU: columns 0..15 of each 32-column fragment are gate rows of the
+    // weight, 16..31 the matching up rows.  v_permlane16_swap of registers
+    // 2p and 2p + 1 (rows r and r + 1) swaps the odd 16-lane rows of the
+    // first with the even rows of the second, which leaves every lane the
+    // gate and the up value of one output: lanes 16..31 of each half take
+    // row r + 1.  The bf16 tile is staged in the A stages (free once every
+    // wave has read the last one) and leaves in 16-byte row chunks.
+    constexpr int OC = BN / 2, OLD = OC + 8;  // output columns, LDS row stride
+    static_assert(BM * OLD <= NS * BM * BK && OC % 8 == 0, "output tile staging");
+    bf16_t* const os = &As[0][0];
+    __syncthreads();
+    const int odd = (lane >> 4) & 1, c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int rb = wm * WTM + i * 32 + (lane >> 5) * 4 + odd;
+        const int oc = (wn * WTN + j * 32) / 2 + c16;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][2 * p]),
+                                                           __float_as_uint(acc[i][j][2 * p + 1]), false, false);
+          const int row = rb + (p >> 1) * 8 + (p & 1) * 2;
+          os[row * OLD + oc] = (bf16_t)f32_to_bf16(silu_f(__uint_as_float(sw[0])) * __uint_as_float(sw[1]));
+        }
+      }
+    __syncthreads();
+    constexpr int CH = OC / 8;  // 16-byte chunks per output row
+    bf16_t* const cb = reinterpret_cast<bf16_t*>(a.C) + n0 / 2;
+    for (int q = tid; q < BM * CH; q += 512) {
+      const int row = q / CH, ch = q % CH;
+      if (m0 + row < M)
+        *reinterpret_cast<uint4*>(cb + (size_t)(m0 + row) * a.ldc + ch * 8) =
+            *reinterpret_cast<const uint4*>(os + row * OLD + ch * 8);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int rbase = m0 + wm * WTM + i * 32 + (lane >> 5) * 4;
@@ -284,14 +322,6 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
       for (int r = 0; r < 16; ++r) {
         const int row = rbase + (r >> 2) * 8 + (r & 3);
         const float v = acc[i][j][r];
-        if (EPI == EPI_SWIGLU && !SPLIT) {
-          // columns cbase..+15 are gate rows, cbase+16..+31 the matching up rows
-          const float u = __shfl_xor(v, 16);
-          if (fr < 16 && row < M)
-            reinterpret_cast<bf16_t*>(a.C)[(size_t)row * a.ldc + cbase / 2 + fr] =
-                (bf16_t)f32_to_bf16(silu_f(v) * u);
-          continue;
-        }
         if (row >= M) continue;
         if (SPLIT) a.work[((size_t)blockIdx.z * M + row) * a.N + col] = v;
         else if (EPI == EPI_STORE) reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = v;
@@ -601,7 +631,9 @@ void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {
     }
     return;
   }
-  if (a.M >= 512) {
+  // the 256-row tiles' SwiGLU epilogue writes 16-byte chunks of output rows
+  const bool vec_out = epi != EPI_SWIGLU || (a.ldc % 8 == 0 && ((uintptr_t)a.C & 15) == 0);
+  if (a.M >= 512 && vec_out) {
     // 256-row tiles.  The gate|up projection takes 192-column blocks when
     // that gives the grid whole rounds of 256 CUs (6144 wide at M = 2048);
     // otherwise 128 columns, splitting K while the doubled grid still fits
