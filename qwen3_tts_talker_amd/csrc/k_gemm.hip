@@ -184,8 +184,25 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int kbeg = blockIdx.z * k_per_split;
+  // Blocks are dealt round-robin over the 8 XCDs (block i to XCD i % 8).
+  // Split-K grids take logical tile i / 8 + (i % 8) * (grid / 8), so each
+  // XCD runs a run of consecutive logical tiles (column tiles fastest): the
+  // column tiles of a few row tiles in one K range, which share their A
+  // tiles in that XCD's L2 (the hardware order would give an XCD one column
+  // tile and every row tile and K range, and no A tile twice).
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (SPLIT) {
+    const int nx = gridDim.x, nxy = nx * gridDim.y, total = nxy * gridDim.z;
+    if (total % 8 == 0) {
+      const int lin = blockIdx.x + nx * (blockIdx.y + gridDim.y * blockIdx.z);
+      const int lg = (lin & 7) * (total >> 3) + (lin >> 3);
+      bz = lg / nxy;
+      by = (lg - bz * nxy) / nx;
+      bx = lg - bz * nxy - by * nx;
+    }
+  }
+  const int n0 = bx * BN, m0 = by * BM;
+  const int kbeg = bz * k_per_split;
   const int nkt = k_per_split / BK;
   const int M = a.M, K = a.K;
 
@@ -323,7 +340,7 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
         const int row = rbase + (r >> 2) * 8 + (r & 3);
         const float v = acc[i][j][r];
         if (row >= M) continue;
-        if (SPLIT) a.work[((size_t)blockIdx.z * M + row) * a.N + col] = v;
+        if (SPLIT) a.work[((size_t)bz * M + row) * a.N + col] = v;
         else if (EPI == EPI_STORE) reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = v;
         else reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] += v;
       }
