@@ -154,30 +154,38 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a, int k_per_split) 
 }
 
 // Large-M variant with direct-to-LDS loads: 256 x BN block tile over 8 waves
-// (4 x 2, a 64 x BN/2 tile each, 32x32x16 MFMA), BK 64.  Global tiles go
-// straight into LDS with global_load_lds_dwordx4 (no register staging, no
-// LDS store instructions); NS LDS stages, loads issued NS - 1 tiles ahead,
-// one barrier per K tile.  LDS rows are 128 bytes unpadded; 16-byte chunk c
-// of row r sits in slot c ^ (r & 7), which the loads produce by giving lane
-// l of an 8-row instruction row l / 8 and chunk (l % 8) ^ (l / 8), and which
-// makes the operand reads (8 consecutive rows, one chunk) conflict-free.
-// BN = 192 gives the 6144-wide gate|up projection exactly 256 tiles at
-// M = 2048 (two stages fit LDS there, three at BN = 128).
+// (4 x 2, a 64 x BN/2 tile each, 32x32x16 MFMA), K tiles of BK.  Global
+// tiles go straight into LDS with global_load_lds_dwordx4 (no register
+// staging, no LDS store instructions) into NS stages, NS - 1 tiles in flight
+// while one is read.  LDS rows (BK bf16) are unpadded; 16-byte chunk c of
+// row r sits in slot c ^ ((r / RB) % CPR), RB rows per 256 bytes, CPR chunks
+// per row.  The LDS serves a 16-byte read of 16 lanes per clock from its 64
+// banks, and an operand read gives 16 lanes 16 consecutive rows of one
+// chunk, which this layout spreads over all 64 banks.  The loads produce it
+// by giving lane l of the instruction that starts at row R (a multiple of
+// RPI = 64 / CPR rows) row R + l / CPR and chunk (l % CPR) ^ (((R + l / CPR)
+// / RB) % CPR).  BN = 192 gives the 6144-wide gate|up projection exactly 256
+// tiles at M = 2048.  (32-deep tiles with five or six stages measured 4-8%
+// slower at 1920 rows: the copy is bound by L2 bandwidth, not by the bytes
+// in flight.)
 
 template <int BN>
 struct DmaCfg {
-  static constexpr int NS = BN == 128 ? 3 : 2;          // LDS stages
-  static constexpr int A_LD = 4, B_LD = BN / 64;        // 1 KiB loads per wave and K tile
-  static constexpr int LPT = A_LD + B_LD;
+  static constexpr int BK = 64;
+  static constexpr int NS = BN == 128 ? 3 : 2;  // LDS stages: 144 or 112 KiB
 };
 
 template <int BN, int EPI, bool SPLIT>
 __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
-  constexpr int BM = 256, BK = 64;
-  constexpr int NS = DmaCfg<BN>::NS, A_LD = DmaCfg<BN>::A_LD, B_LD = DmaCfg<BN>::B_LD;
-  constexpr int LPT = DmaCfg<BN>::LPT;
+  constexpr int BM = 256, BK = DmaCfg<BN>::BK, NS = DmaCfg<BN>::NS;
+  constexpr int CPR = BK / 8, RPI = 64 / CPR, RB = 128 / BK;
+  constexpr int KS = BK / 16;                 // MFMA k-steps per tile
+  constexpr int JA = BM / RPI / 8;            // A load instructions per wave and tile
+  constexpr int NB = BN / RPI;                // B load instructions per tile
+  constexpr int JB = (NB + 7) / 8;            // ... per wave, at most
   constexpr int WTM = BM / 4, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(KS % 2 == 0 && (BM / RPI) % 8 == 0, "tile split");
   __shared__ __attribute__((aligned(1024))) bf16_t As[NS][BM * BK];
   __shared__ __attribute__((aligned(1024))) bf16_t Bs[NS][BN * BK];
 
@@ -206,23 +214,38 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
   const int nkt = k_per_split / BK;
   const int M = a.M, K = a.K;
 
-  // this lane's source rows (A rows past M re-read row M - 1; never stored)
-  const int lr = lane >> 3, lc = ((lane & 7) ^ (lane >> 3)) * 8;
-  const bf16_t* ag[A_LD];
-  const bf16_t* bg[B_LD];
+  // this wave's load instructions: A rows (wave + 8 j) * RPI for j < JA, then
+  // B rows (wave + 8 j) * RPI; the last B slot only for waves below NB % 8
+  // (A rows past M re-read row M - 1; never stored)
+  const bool bx_last = (NB % 8 == 0) || wave < NB % 8;
+  const bf16_t* ag[JA];
+  const bf16_t* bg[JB];
+  auto src_chunk = [&](int R) { return ((lane % CPR) ^ (((R + lane / CPR) / RB) % CPR)) * 8; };
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j)
-    ag[j] = a.A + (size_t)min(m0 + (wave * A_LD + j) * 8 + lr, M - 1) * a.lda + kbeg + lc;
+  for (int j = 0; j < JA; ++j) {
+    const int R = (wave + 8 * j) * RPI;
+    ag[j] = a.A + (size_t)min(m0 + R + lane / CPR, M - 1) * a.lda + kbeg + src_chunk(R);
+  }
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) bg[j] = a.B + (size_t)(n0 + (wave * B_LD + j) * 8 + lr) * K + kbeg + lc;
+  for (int j = 0; j < JB; ++j) {
+    const int R = (j == JB - 1 && !bx_last ? 0 : wave + 8 * j) * RPI;  // unused slot: any valid row
+    bg[j] = a.B + (size_t)(n0 + R + lane / CPR) * K + kbeg + src_chunk(R);
+  }
+  const int lpt = JA + (NB / 8) + (NB % 8 != 0 && bx_last ? 1 : 0);  // loads per wave and tile
 
-#define QD_ISSUE(KT, S)                                                                            \
-  do {                                                                                             \
-    const int kt_ = (KT), s_ = (S);                                                                \
-    _Pragma("unroll") for (int j = 0; j < A_LD; ++j)                                               \
-        lds_load16(ag[j] + kt_ * BK, &As[s_][(wave * A_LD + j) * 8 * BK]);                       \
-    _Pragma("unroll") for (int j = 0; j < B_LD; ++j)                                               \
-        lds_load16(bg[j] + kt_ * BK, &Bs[s_][(wave * B_LD + j) * 8 * BK]);                       \
+#define QD_ISSUE(KT, S)                                                                           \
+  do {                                                                                            \
+    const int kt_ = (KT), s_ = (S);                                                               \
+    _Pragma("unroll") for (int j = 0; j < JA; ++j)                                                \
+        lds_load16(ag[j] + kt_ * BK, &As[s_][(wave + 8 * j) * RPI * BK]);                         \
+    _Pragma("unroll") for (int j = 0; j < JB; ++j) if (j < JB - 1 || bx_last)                      \
+        lds_load16(bg[j] + kt_ * BK, &Bs[s_][(wave + 8 * j) * RPI * BK]);                         \
+  } while (0)
+  // wait until this wave has at most T tiles of loads outstanding (loads retire in order)
+#define QD_WAIT_TILES(T)                                                                          \
+  do {                                                                                            \
+    if (lpt == JA + NB / 8) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((T) * (JA + NB / 8)) : "memory"); \
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((T) * (JA + NB / 8 + 1)) : "memory");           \
   } while (0)
 
   f32x16_t acc[TM][TN];
@@ -231,63 +254,77 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
-  // operand reads: row (l % 32) of each 32-row fragment, chunk 2 s + l / 32.
+  // operand reads: row (l % 32) of each 32-row fragment, chunk 2 s + l / 32
+  // (fragments start at multiples of 32 rows, so the slot is a function of l).
   // They are inline asm: the compiler would otherwise wait for every
   // outstanding direct-to-LDS load (tiles in flight included) before the
   // first read.  The statements after the wait name the fragments it guards,
-  // so no MFMA is scheduled above it.  The reads of step ks + 1 go out while
-  // the MFMAs of step ks run; a register they refill was last read by an
-  // MFMA already issued (MFMAs take their A/B operands at issue).
-  const int fr = lane & 31, fh = lane >> 5, fx = lane & 7;
+  // so no MFMA is scheduled above it.  The reads of the next k-step go out
+  // while the MFMAs of this one run; a register they refill was last read by
+  // an MFMA already issued (MFMAs take their A/B operands at issue).
+  const int fr = lane & 31, fh = lane >> 5, fx = (fr / RB) % CPR;
   const uint32_t a_off = (uint32_t)(uintptr_t)(As[0] + (wm * WTM + fr) * BK);
   const uint32_t b_off = (uint32_t)(uintptr_t)(Bs[0] + (wn * WTN + fr) * BK);
-  constexpr int NF = TM + TN;  // fragments per K step: A 0..TM-1, then B
-#define QD_READ(X, KS)                                                                        \
+  constexpr int NF = TM + TN;  // fragments per k-step: A 0..TM-1, then B
+#define QD_READ(X, S, KS_)                                                                    \
   do {                                                                                        \
-    const uint32_t slot_ = (((2 * (KS) + fh) ^ fx) * 16);                                     \
+    const uint32_t ab_ = a_off + (S) * (BM * BK * 2), bb_ = b_off + (S) * (BN * BK * 2);      \
+    const uint32_t slot_ = (((2 * (KS_) + fh) ^ fx) * 16);                                    \
     _Pragma("unroll") for (int q = 0; q < NF; ++q) {                                          \
-      const uint32_t addr_ = (q < TM ? ab + q * 32 * BK * 2 : bb + (q - TM) * 32 * BK * 2) + slot_; \
+      const uint32_t addr_ = (q < TM ? ab_ + q * 32 * BK * 2 : bb_ + (q - TM) * 32 * BK * 2) + slot_; \
       asm volatile("ds_read_b128 %0, %1" : "=v"(X[q]) : "v"(addr_));                         \
     }                                                                                         \
   } while (0)
-#define QD_COMPUTE(S)                                                                         \
-  do {                                                                                        \
-    const uint32_t ab = a_off + (S) * (BM * BK * 2), bb = b_off + (S) * (BN * BK * 2);        \
-    bf16x8_t f0[NF], f1[NF];                                                                  \
-    QD_READ(f0, 0);                                                                           \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                  \
-      bf16x8_t* x = (ks & 1) ? f1 : f0;                                                       \
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                      \
-      _Pragma("unroll") for (int q = 0; q < NF; ++q) asm volatile("" : "+v"(x[q]));           \
-      if (ks + 1 < BK / 16) {                                                                 \
-        if (ks & 1) QD_READ(f0, ks + 1);                                                      \
-        else QD_READ(f1, ks + 1);                                                             \
-      }                                                                                       \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                          \
-          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                          \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], x[TM + j], acc[i][j], 0, 0, 0);   \
-    }                                                                                         \
-  } while (0)
 
-  // The barrier is the raw instruction: __syncthreads() would also wait for
-  // every outstanding direct-to-LDS load (the tiles in flight).  Each wave
-  // first waits for its own loads of the tile about to be read; the asm
-  // statements keep the compiler from moving memory accesses across.
+  // Pipeline.  The prologue requests tiles 0 .. NS-1 (one per stage).  In
+  // tile kt, the last k-step's fragments are read before its MFMAs are
+  // issued; at that point the wave waits for its loads of tile kt + 1, and
+  // the raw barrier (not __syncthreads, which would also wait for the loads
+  // in flight) makes every wave's part of tile kt + 1 visible and tells that
+  // tile kt's stage has been read by all waves: tile kt + NS goes there, the
+  // first fragments of tile kt + 1 are read, and only then do the last
+  // MFMAs of tile kt issue, so they cover the barrier and the first reads.
+  bf16x8_t f0[NF], f1[NF];
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 0; s < NS; ++s)
     if (s < nkt) QD_ISSUE(s, s);
+  if (nkt >= NS) QD_WAIT_TILES(NS - 1);
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  QD_READ(f0, 0, 0);
+  int st = 0;  // stage of tile kt
   for (int kt = 0; kt < nkt; ++kt) {
-    if (NS == 3 && kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NS - 1 < nkt) QD_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);
-    QD_COMPUTE(kt % NS);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t* x = (ks & 1) ? f1 : f0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < NF; ++q) asm volatile("" : "+v"(x[q]));
+      if (ks + 1 < KS) {
+        if (ks & 1) QD_READ(f0, st, ks + 1);
+        else QD_READ(f1, st, ks + 1);
+      } else if (kt + 1 < nkt) {
+        if (kt + NS - 1 < nkt) QD_WAIT_TILES(NS - 2);
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + NS < nkt) QD_ISSUE(kt + NS, st);
+        const int nst = st + 1 == NS ? 0 : st + 1;
+        QD_READ(f0, nst, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], x[TM + j], acc[i][j], 0, 0, 0);
+    }
+    st = st + 1 == NS ? 0 : st + 1;
   }
 
 #undef QD_ISSUE
+#undef QD_WAIT_TILES
 #undef QD_READ
-#undef QD_COMPUTE
 
   // epilogue: register r of lane l is C[row (r/4)*8 + (l/32)*4 + r%4][col l%32]
   if constexpr (EPI == EPI_SWIGLU && !SPLIT) {
