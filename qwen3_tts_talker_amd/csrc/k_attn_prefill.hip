@@ -69,14 +69,21 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   constexpr int NLI = KT / RPI / NWV;       // load instructions per wave, tile and operand
   static_assert((HD == 128 || HD == 64) && KT % (RPI * NWV) == 0, "staging split");
   // two tile buffers (tile kt in buffer kt & 1), each K rows then V rows,
-  // key-major, 16-byte chunk c of key row k stored in slot c ^ (k % CPR); the
-  // q fragments pass through buffer 1 before the key loop
+  // key-major, 16-byte chunk c of key row k stored in slot c ^ swz(k).  At
+  // head_dim 128 (256-byte rows, one row per pass over the 64 banks) swz
+  // rotates the low four key bits, (k % 4) * 4 + (k / 4) % 4: the K reads
+  // (16 lanes, 16 consecutive keys, one chunk) and the transposing V reads
+  // (32 lanes, 4 consecutive keys, 4 aligned chunks) then both fall on 16
+  // distinct 16-byte bank groups (k % 16 alone gave the V reads four-way
+  // conflicts).  At head_dim 64 swz(k) = k % 8.  The q fragments pass
+  // through buffer 1 before the key loop
   constexpr int TILE = 2 * KT * HD;  // halfs per buffer
   constexpr int LDS_HALFS = 2 * TILE;
   static_assert(G * NKS * 64 * 8 <= TILE, "q fragments fit one buffer");
   __shared__ __attribute__((aligned(1024))) f16_t lds[LDS_HALFS];
   f16_t* const qlds = lds + TILE;
 
+  auto swz = [](int k) { return CPR == 16 ? ((k & 3) << 2) | ((k >> 2) & 3) : (k & (CPR - 1)); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nkv = a.n_kv_heads;
   const int nqb = (a.T + PB - 1) / PB;
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   do {                                                                                    \
     _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                     \
       const int r0_ = RPI * (wave * NLI + i), key_ = r0_ + srow;                          \
-      const size_t g_ = (size_t)min((KT_) * KT + key_, kend - 1) * HD + (sslot ^ (key_ & (CPR - 1))) * 8; \
+      const size_t g_ = (size_t)min((KT_) * KT + key_, kend - 1) * HD + (sslot ^ swz(key_)) * 8; \
       f16_t* const l_ = lds + (BUF) * TILE + r0_ * HD;                                    \
       lds_load16(Kg + g_, l_);                                                            \
       lds_load16(Vg + g_, l_ + KT * HD);                                                  \
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
     f16x8_t kf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const uint32_t a_ = kb + (uint32_t)(krow * HD + (((2 * ks + h) ^ (krow & (CPR - 1))) * 8)) * 2;
+      const uint32_t a_ = kb + (uint32_t)(krow * HD + (((2 * ks + h) ^ swz(krow)) * 8)) * 2;
       asm volatile("ds_read_b128 %0, %1" : "=v"(kf[ks]) : "v"(a_));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int key = kh * 32 + sk * 16 + vkey + hf * 4, dim = mt * 32 + vdim;
-          const uint32_t a_ = vb + (uint32_t)(key * HD + (((dim >> 3) ^ (key & (CPR - 1))) << 3) + (dim & 7)) * 2;
+          const uint32_t a_ = vb + (uint32_t)(key * HD + (((dim >> 3) ^ swz(key)) << 3) + (dim & 7)) * 2;
           asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[sk][mt][hf]) : "v"(a_));
         }
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
