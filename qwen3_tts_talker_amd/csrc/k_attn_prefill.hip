@@ -34,9 +34,6 @@
 namespace qtalk {
 namespace pa {
 
-constexpr int NWV = 4;        // waves per block
-constexpr int NT = NWV * 64;  // threads per block
-constexpr int KT = 64;        // keys per tile
 constexpr int PB = 32;        // positions per block
 constexpr int G = 2;          // query heads per KV head
 
@@ -59,9 +56,14 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int HD>
-__global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
+// NKQ key groups per block: waves (query head, key group), 32 keys of every
+// tile per wave, tiles of 32 NKQ keys.  NKQ = 2: 4 waves, two blocks per CU;
+// NKQ = 4: 8 waves (two per SIMD on one work item), one block per CU.
+template <int HD, int NKQ>
+__global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_prefill(PrefillAttnArgs a) {
   using namespace pa;
+  constexpr int NWV = G * NKQ;              // waves per block
+  constexpr int KT = 32 * NKQ;              // keys per tile
   constexpr int NKS = HD / 16;              // k-steps of the score product
   constexpr int NMT = HD / 32;              // hd tiles of the value product
   constexpr int CPR = HD / 8;               // 16-byte chunks per key row
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   // (longest with shortest) and every CU gets about the same number of key
   // tiles; otherwise plain longest first.
   const int nb = nqb * nkv, b = blockIdx.x;
-  const int r = (b < a.ncu || nb > 2 * a.ncu) ? b : nb - 1 - (b - a.ncu);
+  const int r = (NKQ != 2 || b < a.ncu || nb > 2 * a.ncu) ? b : nb - 1 - (b - a.ncu);
   const int g = r % nkv;
   const int qb = nqb - 1 - r / nkv;
   const int P0 = a.p0 + qb * PB;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
   const int kend = P1;                      // keys [0, kend)
   const int nkt = (kend + KT - 1) / KT;
 
-  const int hh = wave >> 1, kh = wave & 1;  // query head of the group, key half
+  const int hh = wave / NKQ, kh = wave % NKQ;  // query head of the group, key group
   const int hq = g * G + hh;
   const int last = P1 - 1;
   const int n = lane & 31, h = lane >> 5;
@@ -308,14 +310,14 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
 #undef QA_ISSUE
   __syncthreads();
 
-  // merge the two key halves of each query head through LDS (the tiles are
-  // no longer needed): the key-half-1 wave hands over (m, l, O), the key-half-0
-  // wave combines and writes
-  float* xs = reinterpret_cast<float*>(lds);  // [G][64 lanes][NMT*16 + 2]
+  // merge the key groups of each query head through LDS (the tiles are no
+  // longer needed): the other groups hand over (m, l, O), the group-0 wave
+  // combines and writes
+  float* xs = reinterpret_cast<float*>(lds);  // [G][NKQ-1][64 lanes][NMT*16 + 2]
   constexpr int XS = NMT * 16 + 2;
-  static_assert((size_t)G * 64 * XS * 4 <= sizeof(f16_t) * LDS_HALFS, "merge buffer");
-  float* mine = xs + ((size_t)hh * 64 + lane) * XS;
-  if (kh == 1) {
+  static_assert((size_t)G * (NKQ - 1) * 64 * XS * 4 <= sizeof(f16_t) * LDS_HALFS, "merge buffer");
+  if (kh != 0) {
+    float* mine = xs + ((size_t)(hh * (NKQ - 1) + kh - 1) * 64 + lane) * XS;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -324,12 +326,23 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
     mine[NMT * 16 + 1] = l_run;
   }
   __syncthreads();
-  if (kh == 1 || posn >= P1) return;
-  const float m1 = mine[NMT * 16], l1 = mine[NMT * 16 + 1];
-  const float M = fmaxf(m_run, m1);  // finite: key 0 is visible to every row
+  if (kh != 0 || posn >= P1) return;
+  const float* part[NKQ - 1];
+  float M = m_run;  // finite: key 0 is visible to every row
+#pragma unroll
+  for (int j = 0; j < NKQ - 1; ++j) {
+    part[j] = xs + ((size_t)(hh * (NKQ - 1) + j) * 64 + lane) * XS;
+    M = fmaxf(M, part[j][NMT * 16]);
+  }
   const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-  const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
-  const float l = l_run * a0 + l1 * a1;
+  float aj[NKQ - 1];
+  float l = l_run * a0;
+#pragma unroll
+  for (int j = 0; j < NKQ - 1; ++j) {
+    const float mj = part[j][NMT * 16];
+    aj[j] = mj == -INFINITY ? 0.f : exp2f(mj - M);
+    l += part[j][NMT * 16 + 1] * aj[j];
+  }
   const float inv = 1.0f / xor32_sum(l);
   bf16_t* orow = orows + (size_t)(posn - a.p0) * a.ldo + (size_t)hq * HD;
 #pragma unroll
@@ -339,8 +352,12 @@ __global__ __launch_bounds__(pa::NT, 2) void k_attn_prefill(PrefillAttnArgs a) {
       const int d = mt * 32 + rg * 8 + h * 4;
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[j] = (o[mt][rg * 4 + j] * a0 + mine[mt * 16 + rg * 4 + j] * a1) * inv;
+      for (int j = 0; j < 4; ++j) {
+        float acc = o[mt][rg * 4 + j] * a0;
+#pragma unroll
+        for (int p = 0; p < NKQ - 1; ++p) acc += part[p][mt * 16 + rg * 4 + j] * aj[p];
+        v[j] = acc * inv;
+      }
       uint2 w;
       w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
       w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
@@ -355,8 +372,14 @@ bool attn_prefill_supported(int head_dim, int group) {
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st) {
   const int nqb = (a.T + pa::PB - 1) / pa::PB;
   const dim3 grid(nqb * a.n_kv_heads, a.nbatch > 1 ? a.nbatch : 1);
-  if (a.head_dim == 128) hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(pa::NT), 0, st, a);
-  else hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(pa::NT), 0, st, a);
+  // a causal triangle from position 0 whose longest blocks walk many key
+  // tiles: four key groups per block, two waves per SIMD on each item, so the
+  // longest items finish sooner.  (Over uniformly long rows, chunks at an
+  // offset, two blocks of two groups per CU measured faster.)
+  const bool wide = a.head_dim == 128 && a.nbatch <= 1 && a.p0 == 0 && a.T >= 512;
+  if (wide) hipLaunchKernelGGL((k_attn_prefill<128, 4>), grid, dim3(64 * pa::G * 4), 0, st, a);
+  else if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_prefill<128, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_prefill<64, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
 }
 
 }  // namespace qtalk
