@@ -276,15 +276,17 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
     }                                                                                         \
   } while (0)
 
-  // Pipeline.  The prologue requests tiles 0 .. NS-1 (one per stage).  In
-  // tile kt, the last k-step's fragments are read before its MFMAs are
-  // issued; at that point the wave waits for its loads of tile kt + 1, and
-  // the raw barrier (not __syncthreads, which would also wait for the loads
-  // in flight) makes every wave's part of tile kt + 1 visible and tells that
-  // tile kt's stage has been read by all waves: tile kt + NS goes there, the
-  // first fragments of tile kt + 1 are read, and only then do the last
-  // MFMAs of tile kt issue, so they cover the barrier and the first reads.
-  bf16x8_t f0[NF], f1[NF];
+  // Pipeline.  The prologue requests tiles 0 .. NS-1 (one per stage).
+  // Operand reads run two k-steps ahead, one fragment set per k-step of the
+  // tile (KS = 4 sets).  At k-step 2 of tile kt every read of tile kt has
+  // been issued; the wave waits for all of them and for its loads of tile
+  // kt + 1, and the raw barrier (not __syncthreads, which would also wait
+  // for the loads in flight) makes every wave's part of tile kt + 1 visible
+  // and tells that tile kt's stage has been read by all waves: tile kt + NS
+  // goes there, and the reads of tile kt + 1's k-steps 0 and 1 are issued
+  // under tile kt's last two steps of MFMAs.
+  static_assert(KS == 4, "four k-steps per tile");
+  bf16x8_t fb[KS][NF];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nkt) QD_ISSUE(s, s);
@@ -292,35 +294,49 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  QD_READ(f0, 0, 0);
+  QD_READ(fb[0], 0, 0);
+  QD_READ(fb[1], 0, 1);
+#define QD_MFMA(X)                                                                            \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                            \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                            \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(X[i], X[TM + j], acc[i][j], 0, 0, 0);     \
+  } while (0)
+#define QD_FENCE(X) _Pragma("unroll") for (int q = 0; q < NF; ++q) asm volatile("" : "+v"(X[q]))
   int st = 0;  // stage of tile kt
   for (int kt = 0; kt < nkt; ++kt) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t* x = (ks & 1) ? f1 : f0;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < NF; ++q) asm volatile("" : "+v"(x[q]));
-      if (ks + 1 < KS) {
-        if (ks & 1) QD_READ(f0, st, ks + 1);
-        else QD_READ(f1, st, ks + 1);
-      } else if (kt + 1 < nkt) {
-        if (kt + NS - 1 < nkt) QD_WAIT_TILES(NS - 2);
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (kt + NS < nkt) QD_ISSUE(kt + NS, st);
-        const int nst = st + 1 == NS ? 0 : st + 1;
-        QD_READ(f0, nst, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[i], x[TM + j], acc[i][j], 0, 0, 0);
+    const int nst = st + 1 == NS ? 0 : st + 1;
+    // k-step 0: its reads done, those of step 1 may be outstanding (LDS
+    // reads retire in order)
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NF) : "memory");
+    QD_FENCE(fb[0]);
+    QD_READ(fb[2], st, 2);
+    QD_MFMA(fb[0]);
+    // k-step 1
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NF) : "memory");
+    QD_FENCE(fb[1]);
+    QD_READ(fb[3], st, 3);
+    QD_MFMA(fb[1]);
+    // k-step 2: every read of tile kt done
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    QD_FENCE(fb[2]);
+    QD_FENCE(fb[3]);
+    if (kt + 1 < nkt) {
+      if (kt + NS - 1 < nkt) QD_WAIT_TILES(NS - 2);
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NS < nkt) QD_ISSUE(kt + NS, st);
+      QD_READ(fb[0], nst, 0);
     }
-    st = st + 1 == NS ? 0 : st + 1;
+    QD_MFMA(fb[2]);
+    // k-step 3
+    if (kt + 1 < nkt) QD_READ(fb[1], nst, 1);
+    QD_MFMA(fb[3]);
+    st = nst;
   }
+#undef QD_MFMA
+#undef QD_FENCE
 
 #undef QD_ISSUE
 #undef QD_WAIT_TILES
