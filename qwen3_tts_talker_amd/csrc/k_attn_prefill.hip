@@ -70,23 +70,26 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   constexpr int RPI = 64 / CPR;             // key rows per 1 KiB load instruction
   constexpr int NLI = KT / RPI / NWV;       // load instructions per wave, tile and operand
   static_assert((HD == 128 || HD == 64) && KT % (RPI * NWV) == 0, "staging split");
-  // two tile buffers (tile kt in buffer kt & 1), each K rows then V rows,
-  // key-major, 16-byte chunk c of key row k stored in slot c ^ swz(k).  At
+  // two tile buffers (tile kt in buffer kt & 1): the two K tiles, then the
+  // two V tiles, so that a buffer is one immediate offset (KT * HD halfs)
+  // away from the other; rows key-major, 16-byte chunk c of key row k stored
+  // in slot c ^ swz(k).  At
   // head_dim 128 (256-byte rows, one row per pass over the 64 banks) swz
   // rotates the low four key bits, (k % 4) * 4 + (k / 4) % 4: the K reads
   // (16 lanes, 16 consecutive keys, one chunk) and the transposing V reads
   // (32 lanes, 4 consecutive keys, 4 aligned chunks) then both fall on 16
   // distinct 16-byte bank groups (k % 16 alone gave the V reads four-way
   // conflicts).  At head_dim 64 swz(k) = k % 8.  The q fragments pass
-  // through buffer 1 before the key loop
+  // through the K tile of buffer 1 before the key loop
   constexpr int TILE = 2 * KT * HD;  // halfs per buffer
   constexpr int LDS_HALFS = 2 * TILE;
-  static_assert(G * NKS * 64 * 8 <= TILE, "q fragments fit one buffer");
   __shared__ __attribute__((aligned(1024))) f16_t lds[LDS_HALFS];
-  f16_t* const qlds = lds + TILE;
+  f16_t* const qlds = lds + KT * HD;  // K tile of buffer 1
+  static_assert(G * NKS * 64 * 8 <= KT * HD, "q fragments fit one K tile");
 
   auto swz = [](int k) { return CPR == 16 ? ((k & 3) << 2) | ((k >> 2) & 3) : (k & (CPR - 1)); };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int nkv = a.n_kv_heads;
   const int nqb = (a.T + PB - 1) / PB;
   // work item r (0 = longest: the last 32 positions) of this block.  Blocks b
@@ -170,14 +173,34 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // swizzled.  Rows are clamped to the block's last key (always in bounds;
   // keys past it are masked in the scores, and their P is 0 against finite V).
   const int srow = lane / CPR, sslot = lane % CPR;
+  // byte offset of this lane's 16 bytes in load instruction i, from the
+  // tile's first row (a tile wholly before the block's last key is read
+  // from a uniform base plus these; a tile that reaches past it clamps rows)
+  uint32_t goff[NLI];
+#pragma unroll
+  for (int i = 0; i < NLI; ++i) {
+    const int key_ = RPI * (wave * NLI + i) + srow;
+    goff[i] = (uint32_t)(key_ * HD + (sslot ^ swz(key_)) * 8) * 2;
+  }
 #define QA_ISSUE(KT_, BUF)                                                                \
   do {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                     \
-      const int r0_ = RPI * (wave * NLI + i), key_ = r0_ + srow;                          \
-      const size_t g_ = (size_t)min((KT_) * KT + key_, kend - 1) * HD + (sslot ^ swz(key_)) * 8; \
-      f16_t* const l_ = lds + (BUF) * TILE + r0_ * HD;                                    \
-      lds_load16(Kg + g_, l_);                                                            \
-      lds_load16(Vg + g_, l_ + KT * HD);                                                  \
+    if (((KT_) + 1) * KT <= kend) {                                                       \
+      const char* kt_k_ = reinterpret_cast<const char*>(Kg + (size_t)(KT_) * KT * HD);    \
+      const char* kt_v_ = reinterpret_cast<const char*>(Vg + (size_t)(KT_) * KT * HD);    \
+      asm volatile("" : "+s"(kt_k_), "+s"(kt_v_));                                        \
+      _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                   \
+        f16_t* const l_ = lds + (BUF) * KT * HD + RPI * (wave * NLI + i) * HD;            \
+        lds_load16(kt_k_ + goff[i], l_);                                                  \
+        lds_load16(kt_v_ + goff[i], l_ + 2 * KT * HD);                                    \
+      }                                                                                   \
+    } else {                                                                              \
+      _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                   \
+        const int r0_ = RPI * (wave * NLI + i), key_ = r0_ + srow;                        \
+        const size_t g_ = (size_t)min((KT_) * KT + key_, kend - 1) * HD + (sslot ^ swz(key_)) * 8; \
+        f16_t* const l_ = lds + (BUF) * KT * HD + r0_ * HD;                               \
+        lds_load16(Kg + g_, l_);                                                          \
+        lds_load16(Vg + g_, l_ + 2 * KT * HD);                                            \
+      }                                                                                   \
     }                                                                                     \
   } while (0)
 
@@ -202,17 +225,29 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // this lane's V source: key (gq >> 1) * 8 + (rq >> 2) of the 16-key step,
   // dims (gq & 1) * 16 + (rq & 3) * 4 of the 32-dim tile
   const int vkey = (gq >> 1) * 8 + (rq >> 2), vdim = (gq & 1) * 16 + (rq & 3) * 4;
+  // this lane's operand addresses in buffer 0, formed once (buffer 1 is the
+  // immediate offset KT * HD * 2 bytes further)
+  uint32_t koff[NKS], voff[2][NMT][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    koff[ks] = lds_base + (uint32_t)(krow * HD + (((2 * ks + h) ^ swz(krow)) * 8)) * 2;
+#pragma unroll
+  for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int key = kh * 32 + sk * 16 + vkey + hf * 4, dim = mt * 32 + vdim;
+        voff[sk][mt][hf] = lds_base + (uint32_t)(2 * KT * HD + key * HD + (((dim >> 3) ^ swz(key)) << 3) + (dim & 7)) * 2;
+      }
 
-  auto compute = [&](int kt) {
+  auto compute = [&](int kt, auto bufc) {
+    constexpr uint32_t BOFF = decltype(bufc)::value * KT * HD * 2;  // buffer byte offset
     const int kbase = kt * KT + kh * 32;  // this wave's first key
     if (kbase > last) return;
-    const uint32_t kb = lds_base + (uint32_t)((kt & 1) * TILE) * 2;
     f16x8_t kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const uint32_t a_ = kb + (uint32_t)(krow * HD + (((2 * ks + h) ^ swz(krow)) * 8)) * 2;
-      asm volatile("ds_read_b128 %0, %1" : "=v"(kf[ks]) : "v"(a_));
-    }
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[ks]) : "v"(koff[ks]), "n"(BOFF));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kf[ks]));
@@ -239,17 +274,13 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
     // V^T fragments of both 16-key steps, all 4 hd tiles
     typedef short s16x4_t __attribute__((ext_vector_type(4)));
     s16x4_t vr[2][NMT][2];
-    const uint32_t vb = kb + (uint32_t)(KT * HD) * 2;
 #pragma unroll
     for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int key = kh * 32 + sk * 16 + vkey + hf * 4, dim = mt * 32 + vdim;
-          const uint32_t a_ = vb + (uint32_t)(key * HD + (((dim >> 3) ^ swz(key)) << 3) + (dim & 7)) * 2;
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[sk][mt][hf]) : "v"(a_));
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vr[sk][mt][hf]) : "v"(voff[sk][mt][hf]), "n"(BOFF));
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
@@ -296,16 +327,23 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // for loads just issued) makes every wave's part of tile kt visible and
   // frees the other buffer, whose next tile is requested before the products.
   QA_ISSUE(0, 0);
-  __syncthreads();  // q fragments (buffer 1) written
+  __syncthreads();  // q fragments (K tile of buffer 1) written
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
-  for (int kt = 0; kt < nkt; ++kt) {
+  // two tiles per iteration, so that each names its buffer as a constant
+  for (int kt = 0; kt < nkt; kt += 2) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 1 < nkt) QA_ISSUE(kt + 1, (kt + 1) & 1);
-    compute(kt);
+    if (kt + 1 < nkt) QA_ISSUE(kt + 1, 1);
+    compute(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 >= nkt) break;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nkt) QA_ISSUE(kt + 2, 0);
+    compute(kt + 1, std::integral_constant<int, 1>{});
   }
 #undef QA_ISSUE
   __syncthreads();
