@@ -120,6 +120,10 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   const size_t head_off = (size_t)(seq * nkv + g) * a.cap * HD;
   const f16_t* Kg = a.kc + head_off;
   const f16_t* Vg = a.vc + head_off;
+  // buffer resources over this KV head's rows (whole tiles are read through
+  // them: a scalar tile offset and a constant lane offset per instruction)
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(Kg, a.cap * HD * 2);
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(Vg, a.cap * HD * 2);
 
   // q (B operand of the score product): row posn, hd ks*16 + h*8 + e.  The
   // lane pair (n, n + 32) holds the whole head, and the RoPE partner d + 64 of
@@ -185,13 +189,11 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
 #define QA_ISSUE(KT_, BUF)                                                                \
   do {                                                                                    \
     if (((KT_) + 1) * KT <= kend) {                                                       \
-      const char* kt_k_ = reinterpret_cast<const char*>(Kg + (size_t)(KT_) * KT * HD);    \
-      const char* kt_v_ = reinterpret_cast<const char*>(Vg + (size_t)(KT_) * KT * HD);    \
-      asm volatile("" : "+s"(kt_k_), "+s"(kt_v_));                                        \
+      const uint32_t soff_ = (uint32_t)(KT_) * KT * HD * 2;                               \
       _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                   \
         f16_t* const l_ = lds + (BUF) * KT * HD + RPI * (wave * NLI + i) * HD;            \
-        lds_load16(kt_k_ + goff[i], l_);                                                  \
-        lds_load16(kt_v_ + goff[i], l_ + 2 * KT * HD);                                    \
+        lds_load16_buf(krs, goff[i], soff_, l_);                                          \
+        lds_load16_buf(vrs, goff[i], soff_, l_ + 2 * KT * HD);                            \
       }                                                                                   \
     } else {                                                                              \
       _Pragma("unroll") for (int i = 0; i < NLI; ++i) {                                   \
