@@ -35,6 +35,7 @@ namespace qtalk {
 namespace pa {
 
 constexpr int PB = 32;        // positions per block
+constexpr float LAZY = 8.f;   // online softmax: headroom of the running maximum (log2 units)
 constexpr int G = 2;          // query heads per KV head
 
 // key (0..31) held by score-tile row m: m = a*8 + h*4 + b -> (a>>1)*16 + h*8 + (a&1)*4 + b
@@ -271,8 +272,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
     for (int r = 0; r < 4; ++r) t8[r] = fmaxf(t8[r], t8[r + 4]);
     float mx = fmaxf(fmaxf(t8[0], t8[2]), fmaxf(t8[1], t8[3]));
     mx = xor32_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new == -INFINITY) return;  // no key of this half is visible to any row yet
+    if (__all(mx == -INFINITY)) return;  // no key of this group is visible to any row
     // V^T fragments of both 16-key steps, all 4 hd tiles
     typedef short s16x4_t __attribute__((ext_vector_type(4)));
     s16x4_t vr[2][NMT][2];
@@ -283,18 +283,28 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
           asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vr[sk][mt][hf]) : "v"(voff[sk][mt][hf]), "n"(BOFF));
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    // lazy rescaling: the reference m_run moves only when a row's maximum
+    // passes it by more than LAZY (log2 units), so P <= 2^LAZY (exact in
+    // float16 up to its rounding) and the O/l rescale, once the maxima have
+    // settled, almost never runs; the final 1/l and the merge of the key
+    // groups use the same reference, so the result is the softmax itself
+    float alpha = 1.f;
+    if (__any(mx > m_run + LAZY)) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;  // a row with no visible key yet: P = 0
     float psum = 0.f;
     f16x8_t pf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] - m_new);  // masked: exp2(-inf) = 0
+      const float p = __builtin_amdgcn_exp2f(s[r] - mref);  // masked: exp2(-inf) = 0
       psum += p;
       pf[r >> 3][r & 7] = (f16_t)p;
     }
     l_run = l_run * alpha + psum;
-    if (!__all(alpha == 1.0f)) {  // once the running max settles this is skipped
+    if (!__all(alpha == 1.0f)) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
