@@ -381,6 +381,35 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
     }
     return;
   }
+  if constexpr (EPI == EPI_STORE && !SPLIT && BN == 128) {
+    if (a.vcache != nullptr && n0 >= a.vcol) {
+      // a V head (128 columns): float16 rows staged in the free A stages,
+      // then 16-byte chunks of the 256-byte cache rows at positions vpos0 +
+      // row (the same round to nearest as the append kernel)
+      constexpr int OLD = 128 + 8;  // LDS row stride (halfs)
+      static_assert(BM * OLD * 2 <= NS * BM * BK * 2, "V tile staging");
+      f16_t* const os = reinterpret_cast<f16_t*>(&As[0][0]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * WTM + i * 32 + (lane >> 5) * 4 + (r >> 2) * 8 + (r & 3);
+            os[row * OLD + wn * WTN + j * 32 + fr] = (f16_t)acc[i][j][r];
+          }
+      __syncthreads();
+      f16_t* const dst = a.vcache + ((size_t)((n0 - a.vcol) / 128) * a.vcap + a.vpos0 + m0) * 128;
+      for (int q = tid; q < BM * 16; q += 512) {
+        const int row = q >> 4, ch = q & 15;
+        if (m0 + row < M)
+          *reinterpret_cast<uint4*>(dst + (size_t)row * 128 + ch * 8) =
+              *reinterpret_cast<const uint4*>(os + row * OLD + ch * 8);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int rbase = m0 + wm * WTM + i * 32 + (lane >> 5) * 4;
@@ -689,6 +718,13 @@ void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int
   }
   launch_gemm(EPI_ADD, a, st);
   launch_rmsnorm_bf16(reinterpret_cast<const float*>(a.C), a.ldc, a.M, a.N, g, eps, hn, ldh, st);
+}
+
+bool gemm_writes_v(const GemmArgs& a) {
+  // the path launch_gemm takes for EPI_STORE at M >= 512: 128-column DMA
+  // tiles, split over K only when the grid is short of 256 blocks
+  return a.vcache != nullptr && a.M >= 512 && a.N % 128 == 0 && a.vcol % 128 == 0 && a.vcol < a.N &&
+         dma_splits(a) == 1;
 }
 
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {

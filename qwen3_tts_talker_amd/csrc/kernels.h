@@ -45,6 +45,7 @@ struct QkArgs {
   int cap;
   int skip_q;  // 1: leave q as is (the matrix-core attention norms and ropes it)
   RowMeta rows;
+  int k_only = 0;  // 1: V is already in the cache (written by the projection)
 };
 // KV cache storage: float32, float16, or Q8_0 rows (head_dim int8 codes then
 // head_dim / 32 float16 scales)
@@ -115,8 +116,17 @@ struct GemmArgs {
   int ldc;
   float* work;  // split-K partials [ksplit][M][N]
   size_t work_elems;
+  // EPI_STORE: columns from vcol on are V rows of head_dim 128 that go as
+  // float16 to one sequence's cache, vcache[((col - vcol) / 128) * vcap +
+  // vpos0 + row][col % 128], instead of to C (see gemm_writes_v)
+  f16_t* vcache = nullptr;
+  int vcol = 0, vcap = 0, vpos0 = 0;
 };
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
+// whether launch_gemm(EPI_STORE, a) writes a's V columns to vcache (the
+// 256-row matrix-core product with whole 128-column tiles and no K split);
+// otherwise the caller appends V itself
+bool gemm_writes_v(const GemmArgs& a);
 // C += A * B^T (C = the f32 residual stream [M][N]), then hn = bf16(RMSNorm(C) * g)
 // row by row; split-K partials are reduced in the same pass as the norm.
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,

@@ -219,7 +219,7 @@ struct Fwd {
     return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_rows() * c->kv_rb;
   }
 
-  void qk_append(int l, const RowMeta& rows, bool skip_q = false) {
+  void qk_append(int l, const RowMeta& rows, bool skip_q = false, bool k_only = false) {
     QkArgs q{};
     q.qkv = c->qkv;
     q.ldqkv = c->qkv_dim;
@@ -235,6 +235,7 @@ struct Fwd {
     q.cap = g.max_seq_len;
     q.skip_q = skip_q ? 1 : 0;
     q.rows = rows;
+    q.k_only = k_only ? 1 : 0;
     launch_qk_rope_append(c->kv, q, st);
   }
 
@@ -316,14 +317,28 @@ struct Fwd {
     bf16_t* att_b = reinterpret_cast<bf16_t*>(c->att);
     bf16_t* act_b = reinterpret_cast<bf16_t*>(c->act);
     if (!normed) launch_rmsnorm_bf16(c->x, H, T, H, L.g_in, g.rms_eps, c->hn, H, st);
-    gemm(c->hn, H, L.wqkv, T, c->qkv_dim, H, c->qkv, c->qkv_dim, EPI_STORE);
     const bool sup = attn_prefill_supported(g.head_dim, g.n_heads / g.n_kv_heads);
     // a Q8 cache reaches the matrix cores through a float16 copy of the
     // sequence's positions 0 .. p0+T-1 (one sequence at a time): earlier
     // positions dequantised, this chunk's rows as computed
     const bool q8_mfma = c->kv == KV_Q8 && c->kv16 && sup && rows.uniform == 1;
     const bool mfma_attn = (c->kv == KV_F16 && sup) || q8_mfma;
-    qk_append(l, rows, mfma_attn);
+    // one sequence, float16 cache, head_dim 128: the projection writes V
+    // straight into the cache where its tiling allows, and the append kernel
+    // then forms K only
+    GemmArgs qa{c->hn, H, reinterpret_cast<const bf16_t*>(L.wqkv), T, c->qkv_dim, H, c->qkv, c->qkv_dim,
+                c->work, WORK_ELEMS};
+    if (c->kv == KV_F16 && mfma_attn && g.head_dim == 128 && rows.uniform == 1) {
+      qa.vcache = reinterpret_cast<f16_t*>(kv_layer(c->vc, l)) +
+                  (size_t)rows.seq0 * g.n_kv_heads * g.max_seq_len * g.head_dim;
+      qa.vcol = c->q_dim + c->kv_dim;
+      qa.vcap = g.max_seq_len;
+      qa.vpos0 = rows.p0;
+    }
+    const bool v_done = gemm_writes_v(qa);
+    if (!v_done) qa.vcache = nullptr;
+    launch_gemm(EPI_STORE, qa, st);
+    qk_append(l, rows, mfma_attn, v_done);
     if (mfma_attn) {
       PrefillAttnArgs p{};
       p.q = c->qkv;
