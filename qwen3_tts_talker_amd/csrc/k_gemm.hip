@@ -382,6 +382,73 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
     return;
   }
   if constexpr (EPI == EPI_STORE && !SPLIT && BN == 128) {
+    if (a.kcache != nullptr && n0 >= a.kcol && n0 < a.vcol) {
+      // a K head (128 columns): float32 rows staged in the free A stages,
+      // 128 rows at a time; 16 lanes per row, lane i holding dims 4i .. 4i+3
+      // and their RoPE partners 64 + 4i .. (the arithmetic of the append
+      // kernel: per-head RMSNorm with g_k, NEOX rotation, float16)
+      constexpr int FLD = 128 + 4;  // LDS row stride (floats)
+      static_assert(128 * FLD * 4 <= NS * BM * BK * 2, "K tile staging");
+      float* const fs = reinterpret_cast<float*>(&As[0][0]);
+      const int i4 = (tid & 15) * 4;
+      const float4 g1 = *reinterpret_cast<const float4*>(a.g_k + i4);
+      const float4 g2 = *reinterpret_cast<const float4*>(a.g_k + 64 + i4);
+      // rotations of every row this thread forms (8 passes of 32 rows),
+      // requested before the staging so that they have landed by then
+      float4 cr[8][2];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int pos = a.vpos0 + min(m0 + p * 32 + (tid >> 4), M - 1);
+        cr[p][0] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4);
+        cr[p][1] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4 + 2);
+      }
+      f16_t* const kdst = a.kcache + ((size_t)((n0 - a.kcol) / 128) * a.vcap + a.vpos0 + m0) * 128;
+      typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // LDS free: the last K stage read, or the previous half formed
+        if ((wm >> 1) == half) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = (wm & 1) * WTM + i * 32 + (lane >> 5) * 4 + (r >> 2) * 8 + (r & 3);
+                fs[row * FLD + wn * WTN + j * 32 + fr] = acc[i][j][r];
+              }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int rr = pp * 32 + (tid >> 4);  // row within this half
+          const int row = half * 128 + rr;
+          float4 x1 = *reinterpret_cast<const float4*>(fs + rr * FLD + i4);
+          float4 x2 = *reinterpret_cast<const float4*>(fs + rr * FLD + 64 + i4);
+          float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
+          ss += x2.x * x2.x + x2.y * x2.y + x2.z * x2.z + x2.w * x2.w;
+          ss = row16_sum(ss);
+          const float inv = rsqrtf(ss / 128.0f + a.eps);
+          const float a1[4] = {x1.x * inv * g1.x, x1.y * inv * g1.y, x1.z * inv * g1.z, x1.w * inv * g1.w};
+          const float a2[4] = {x2.x * inv * g2.x, x2.y * inv * g2.y, x2.z * inv * g2.z, x2.w * inv * g2.w};
+          const float4 c01 = cr[half * 4 + pp][0], c23 = cr[half * 4 + pp][1];
+          const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+          float y1[4], y2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y1[e] = a1[e] * c[e] - a2[e] * sn[e];
+            y2[e] = a2[e] * c[e] + a1[e] * sn[e];
+          }
+          if (m0 + row < M) {
+            const f16x4_t o1 = {(f16_t)y1[0], (f16_t)y1[1], (f16_t)y1[2], (f16_t)y1[3]};
+            const f16x4_t o2 = {(f16_t)y2[0], (f16_t)y2[1], (f16_t)y2[2], (f16_t)y2[3]};
+            *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + i4) = o1;
+            *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + 64 + i4) = o2;
+          }
+        }
+      }
+      return;
+    }
     if (a.vcache != nullptr && n0 >= a.vcol) {
       // a V head (128 columns): float16 rows staged in the free A stages,
       // then 16-byte chunks of the 256-byte cache rows at positions vpos0 +
@@ -720,11 +787,11 @@ void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int
   launch_rmsnorm_bf16(reinterpret_cast<const float*>(a.C), a.ldc, a.M, a.N, g, eps, hn, ldh, st);
 }
 
-bool gemm_writes_v(const GemmArgs& a) {
+bool gemm_writes_kv(const GemmArgs& a) {
   // the path launch_gemm takes for EPI_STORE at M >= 512: 128-column DMA
   // tiles, split over K only when the grid is short of 256 blocks
-  return a.vcache != nullptr && a.M >= 512 && a.N % 128 == 0 && a.vcol % 128 == 0 && a.vcol < a.N &&
-         dma_splits(a) == 1;
+  return a.kcache != nullptr && a.vcache != nullptr && a.M >= 512 && a.N % 128 == 0 && a.kcol % 128 == 0 &&
+         a.vcol % 128 == 0 && a.kcol < a.vcol && a.vcol < a.N && dma_splits(a) == 1;
 }
 
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {

@@ -116,17 +116,24 @@ struct GemmArgs {
   int ldc;
   float* work;  // split-K partials [ksplit][M][N]
   size_t work_elems;
-  // EPI_STORE: columns from vcol on are V rows of head_dim 128 that go as
-  // float16 to one sequence's cache, vcache[((col - vcol) / 128) * vcap +
-  // vpos0 + row][col % 128], instead of to C (see gemm_writes_v)
+  // EPI_STORE, the Q|K|V projection of one sequence (head_dim 128): columns
+  // kcol .. vcol-1 are K rows, which get the per-head RMSNorm (gain g_k),
+  // NEOX RoPE at position vpos0 + row (table rope [cap][64]) and go as
+  // float16 to kcache; columns from vcol on are V rows, which go as float16
+  // to vcache; head (col - kcol or vcol) / 128, cache row head * vcap +
+  // vpos0 + row.  Neither goes to C (see gemm_writes_kv).
+  f16_t* kcache = nullptr;
   f16_t* vcache = nullptr;
-  int vcol = 0, vcap = 0, vpos0 = 0;
+  int kcol = 0, vcol = 0, vcap = 0, vpos0 = 0;
+  const float* g_k = nullptr;
+  const float2* rope = nullptr;
+  float eps = 0.f;
 };
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
-// whether launch_gemm(EPI_STORE, a) writes a's V columns to vcache (the
-// 256-row matrix-core product with whole 128-column tiles and no K split);
-// otherwise the caller appends V itself
-bool gemm_writes_v(const GemmArgs& a);
+// whether launch_gemm(EPI_STORE, a) writes a's K and V columns to the cache
+// (the 256-row matrix-core product with whole 128-column tiles and no K
+// split); otherwise the caller appends them itself
+bool gemm_writes_kv(const GemmArgs& a);
 // C += A * B^T (C = the f32 residual stream [M][N]), then hn = bf16(RMSNorm(C) * g)
 // row by row; split-K partials are reduced in the same pass as the norm.
 void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int ldh,

@@ -323,22 +323,27 @@ struct Fwd {
     // positions dequantised, this chunk's rows as computed
     const bool q8_mfma = c->kv == KV_Q8 && c->kv16 && sup && rows.uniform == 1;
     const bool mfma_attn = (c->kv == KV_F16 && sup) || q8_mfma;
-    // one sequence, float16 cache, head_dim 128: the projection writes V
-    // straight into the cache where its tiling allows, and the append kernel
-    // then forms K only
+    // one sequence, float16 cache, head_dim 128: the projection forms K
+    // (norm, RoPE) and V in its epilogue and writes them straight into the
+    // cache where its tiling allows; otherwise the append kernel does
     GemmArgs qa{c->hn, H, reinterpret_cast<const bf16_t*>(L.wqkv), T, c->qkv_dim, H, c->qkv, c->qkv_dim,
                 c->work, WORK_ELEMS};
     if (c->kv == KV_F16 && mfma_attn && g.head_dim == 128 && rows.uniform == 1) {
-      qa.vcache = reinterpret_cast<f16_t*>(kv_layer(c->vc, l)) +
-                  (size_t)rows.seq0 * g.n_kv_heads * g.max_seq_len * g.head_dim;
+      const size_t seq_off = (size_t)rows.seq0 * g.n_kv_heads * g.max_seq_len * g.head_dim;
+      qa.kcache = reinterpret_cast<f16_t*>(kv_layer(c->kc, l)) + seq_off;
+      qa.vcache = reinterpret_cast<f16_t*>(kv_layer(c->vc, l)) + seq_off;
+      qa.kcol = c->q_dim;
       qa.vcol = c->q_dim + c->kv_dim;
       qa.vcap = g.max_seq_len;
       qa.vpos0 = rows.p0;
+      qa.g_k = L.g_k;
+      qa.rope = c->rope;
+      qa.eps = g.rms_eps;
     }
-    const bool v_done = gemm_writes_v(qa);
-    if (!v_done) qa.vcache = nullptr;
+    const bool kv_done = gemm_writes_kv(qa);
+    if (!kv_done) qa.kcache = qa.vcache = nullptr;
     launch_gemm(EPI_STORE, qa, st);
-    qk_append(l, rows, mfma_attn, v_done);
+    if (!kv_done) qk_append(l, rows, mfma_attn);
     if (mfma_attn) {
       PrefillAttnArgs p{};
       p.q = c->qkv;
