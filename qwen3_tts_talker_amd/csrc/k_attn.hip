@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "kv_row.h"
 
 namespace qtalk {
 
@@ -238,21 +239,7 @@ __global__ __launch_bounds__(256) void k_kv_append_f16_128(QkArgs a) {
     const float4 g2 = *reinterpret_cast<const float4*>(a.g_k + 64 + 4 * i);
     const float4 c01 = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + 4 * i);
     const float4 c23 = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + 4 * i + 2);
-    float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
-    ss += x2.x * x2.x + x2.y * x2.y + x2.z * x2.z + x2.w * x2.w;
-    ss = row16_sum(ss);
-    const float inv = rsqrtf(ss / 128.0f + a.eps);
-    const float a1[4] = {x1.x * inv * g1.x, x1.y * inv * g1.y, x1.z * inv * g1.z, x1.w * inv * g1.w};
-    const float a2[4] = {x2.x * inv * g2.x, x2.y * inv * g2.y, x2.z * inv * g2.z, x2.w * inv * g2.w};
-    const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
-    float y1[4], y2[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y1[e] = a1[e] * c[e] - a2[e] * sn[e];
-      y2[e] = a2[e] * c[e] + a1[e] * sn[e];
-    }
-    x1 = make_float4(y1[0], y1[1], y1[2], y1[3]);
-    x2 = make_float4(y2[0], y2[1], y2[2], y2[3]);
+    k_row_norm_rope(x1, x2, g1, g2, c01, c23, a.eps);
   }
   f16_t* row = reinterpret_cast<f16_t*>(is_k ? a.kc : a.vc) + ((size_t)(seq * nkv + kvh) * a.cap + pos) * 128;
   typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;

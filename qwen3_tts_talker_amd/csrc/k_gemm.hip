@@ -11,6 +11,7 @@
 // K over blockIdx.z into a float32 workspace that a second kernel sums in a
 // fixed order (deterministic), applying the epilogue there.
 #include "kernels.h"
+#include "kv_row.h"
 #include "lds_dma.h"
 
 namespace qtalk {
@@ -425,23 +426,10 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
           const int row = half * 128 + rr;
           float4 x1 = *reinterpret_cast<const float4*>(fs + rr * FLD + i4);
           float4 x2 = *reinterpret_cast<const float4*>(fs + rr * FLD + 64 + i4);
-          float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
-          ss += x2.x * x2.x + x2.y * x2.y + x2.z * x2.z + x2.w * x2.w;
-          ss = row16_sum(ss);
-          const float inv = rsqrtf(ss / 128.0f + a.eps);
-          const float a1[4] = {x1.x * inv * g1.x, x1.y * inv * g1.y, x1.z * inv * g1.z, x1.w * inv * g1.w};
-          const float a2[4] = {x2.x * inv * g2.x, x2.y * inv * g2.y, x2.z * inv * g2.z, x2.w * inv * g2.w};
-          const float4 c01 = cr[half * 4 + pp][0], c23 = cr[half * 4 + pp][1];
-          const float c[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
-          float y1[4], y2[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y1[e] = a1[e] * c[e] - a2[e] * sn[e];
-            y2[e] = a2[e] * c[e] + a1[e] * sn[e];
-          }
+          k_row_norm_rope(x1, x2, g1, g2, cr[half * 4 + pp][0], cr[half * 4 + pp][1], a.eps);
           if (m0 + row < M) {
-            const f16x4_t o1 = {(f16_t)y1[0], (f16_t)y1[1], (f16_t)y1[2], (f16_t)y1[3]};
-            const f16x4_t o2 = {(f16_t)y2[0], (f16_t)y2[1], (f16_t)y2[2], (f16_t)y2[3]};
+            const f16x4_t o1 = {(f16_t)x1.x, (f16_t)x1.y, (f16_t)x1.z, (f16_t)x1.w};
+            const f16x4_t o2 = {(f16_t)x2.x, (f16_t)x2.y, (f16_t)x2.z, (f16_t)x2.w};
             *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + i4) = o1;
             *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + 64 + i4) = o2;
           }

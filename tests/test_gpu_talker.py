@@ -205,6 +205,33 @@ def test_chunked_extend_equals_one_shot():
     assert rel_err(lb, lo) <= TOL_BF16
 
 
+def test_projection_epilogue_cache_rows_equal_append_kernel_bitwise():
+    # A one-sequence matrix-core prefill of more than 1024 rows writes K
+    # (RMSNorm, RoPE) and V into the cache from the Q|K|V product's
+    # epilogue; stacked sequences go through the append kernel.  Layer 0's
+    # cache rows depend only on their own input row and position, so
+    # positions 0..599 of a 1200-row prefill equal those of a 600-row
+    # sequence of a stacked batch bit for bit.
+    shape = workload("talker_1l_t128").with_(n_seqs=3)
+    w = weights_for("talker_1l_t128")
+    e0 = prefill_embeddings(shape, 600, seq=0)
+    e1 = prefill_embeddings(shape, 600, seq=1)
+    tk = _talker(shape, w)
+    say("stacked 2 x 600 (append kernel), one 1200-row sequence (projection epilogue)")
+    tk.prefill_batch([0, 1], dev(np.stack([e0, e1])))
+    tk.prefill(2, dev(np.concatenate([e0, e1])))
+    tk.sync()
+    diff = []
+    for which in (0, 1):
+        a = host(tk.kv_read(0, 0, which))
+        b = host(tk.kv_read(2, 0, which))[:, :600]
+        assert np.isfinite(a).all()
+        diff.append((int((a != b).sum()), float(np.abs(a - b).max())))
+    say(f"differing values (K, V): {diff}")
+    assert diff == [(0, 0.0), (0, 0.0)]
+    tk.close()
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_batched_decode_equals_serial(monkeypatch, fused):
     # five sequences (matrix-vector path), then eleven (matrix-core path)
