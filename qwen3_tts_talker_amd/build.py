@@ -26,7 +26,11 @@ FLAGS = [
 # per-source extras: the persistent decode spends its time in short polling
 # loops, whose speed measured sensitive to where they fall in the
 # instruction stream; 64-byte loop alignment makes it independent of that
-SOURCE_FLAGS = {"k_decode_fused.hip": ["-falign-loops=64"]}
+# the prefill attention produces no NaN (masked scores are -inf, every
+# difference of infinities is guarded), so its maxima need no NaN-quieting
+# canonicalisation of the score registers (about 15 fewer vector
+# instructions per 32-key tile)
+SOURCE_FLAGS = {"k_decode_fused.hip": ["-falign-loops=64"], "k_attn_prefill.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):

@@ -295,15 +295,20 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
       m_run = m_new;
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;  // a row with no visible key yet: P = 0
-    float psum = 0.f;
     f16x8_t pf[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] - mref);  // masked: exp2(-inf) = 0
-      psum += p;
-      pf[r >> 3][r & 7] = (f16_t)p;
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (f16_t)__builtin_amdgcn_exp2f(s[r] - mref);  // masked: exp2(-inf) = 0
+    // l sums the float16 weights the value product uses, two per dot2
+    // instruction (float32 accumulation), in two chains
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ps0 = __builtin_amdgcn_fdot2(h2_t{pf[0][2 * q], pf[0][2 * q + 1]}, one2, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(h2_t{pf[1][2 * q], pf[1][2 * q + 1]}, one2, ps1, false);
     }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + (ps0 + ps1);
     if (!__all(alpha == 1.0f)) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
