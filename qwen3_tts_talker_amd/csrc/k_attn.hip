@@ -224,7 +224,7 @@ static void launch_qk_hd(KvKind kv, const QkArgs& a, const dim3& grid, hipStream
 // go out before its two 8-byte stores.  Units: row t, head hh < n_kv (K,
 // RMSNorm + RoPE) or the V head hh - n_kv (as is).
 __global__ __launch_bounds__(256) void k_kv_append_f16_128(QkArgs a) {
-  const int nkv = a.n_kv_heads, nh = a.k_only ? nkv : 2 * nkv;  // k_only: K heads only
+  const int nkv = a.n_kv_heads, nh = 2 * nkv;
   const int unit = blockIdx.x * 16 + (threadIdx.x >> 4), i = threadIdx.x & 15;
   if (unit >= a.rows.n * nh) return;  // whole 16-lane groups: only row16 reductions below
   const int t = unit / nh, hh = unit % nh;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_kv_append_f16_128(QkArgs a) {
 
 void launch_qk_rope_append(KvKind kv, QkArgs a, hipStream_t st) {
   if (kv == KV_F16 && a.skip_q && a.head_dim == 128) {
-    const int nh = a.k_only ? a.n_kv_heads : 2 * a.n_kv_heads;
+    const int nh = 2 * a.n_kv_heads;
     hipLaunchKernelGGL(k_kv_append_f16_128, dim3((a.rows.n * nh + 15) / 16), dim3(256), 0, st, a);
     return;
   }

@@ -383,6 +383,26 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
     return;
   }
   if constexpr (EPI == EPI_STORE && !SPLIT && BN == 128) {
+    // Row r's position, and the element offset (head 0) of its cache row:
+    // one sequence, base0 + r * 128; stacked sequences, formed for the 8
+    // rows i * 32 + tid / 16 this thread stores before any store (a load
+    // issued after a store waits for it), with the sequence index (r + 1/2)
+    // / kv_per taken in float32 (exact for the row counts a product holds)
+    // instead of an integer division
+    const int per = a.kv_per;
+    const float inv_per = per > 0 ? 1.0f / (float)per : 0.f;
+    auto kv_seq = [&](int r) { return per > 0 ? (int)(((float)r + 0.5f) * inv_per) : 0; };
+    auto kv_pos = [&](int r) { return a.vpos0 + r - kv_seq(r) * per; };
+    const size_t base0 = (size_t)a.kv_seqs[0] * a.kv_seq_stride + (size_t)(a.vpos0 + m0) * 128;
+    size_t roff[8];
+    if (per > 0 && a.kcache != nullptr && n0 >= a.kcol) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = min(m0 + i * 32 + (tid >> 4), M - 1);
+        const int z = kv_seq(r);
+        roff[i] = (size_t)a.kv_seqs[z] * a.kv_seq_stride + (size_t)(a.vpos0 + r - z * per) * 128;
+      }
+    }
     if (a.kcache != nullptr && n0 >= a.kcol && n0 < a.vcol) {
       // a K head (128 columns): float32 rows staged in the free A stages,
       // 128 rows at a time; 16 lanes per row, lane i holding dims 4i .. 4i+3
@@ -399,11 +419,11 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
       float4 cr[8][2];
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const int pos = a.vpos0 + min(m0 + p * 32 + (tid >> 4), M - 1);
+        const int pos = kv_pos(min(m0 + p * 32 + (tid >> 4), M - 1));
         cr[p][0] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4);
         cr[p][1] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4 + 2);
       }
-      f16_t* const kdst = a.kcache + ((size_t)((n0 - a.kcol) / 128) * a.vcap + a.vpos0 + m0) * 128;
+      f16_t* const khead = a.kcache + (size_t)((n0 - a.kcol) / 128) * a.vcap * 128;
       typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -428,10 +448,11 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
           float4 x2 = *reinterpret_cast<const float4*>(fs + rr * FLD + 64 + i4);
           k_row_norm_rope(x1, x2, g1, g2, cr[half * 4 + pp][0], cr[half * 4 + pp][1], a.eps);
           if (m0 + row < M) {
+            f16_t* const kdst = khead + (per > 0 ? roff[half * 4 + pp] : base0 + (size_t)row * 128);
             const f16x4_t o1 = {(f16_t)x1.x, (f16_t)x1.y, (f16_t)x1.z, (f16_t)x1.w};
             const f16x4_t o2 = {(f16_t)x2.x, (f16_t)x2.y, (f16_t)x2.z, (f16_t)x2.w};
-            *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + i4) = o1;
-            *reinterpret_cast<f16x4_t*>(kdst + (size_t)row * 128 + 64 + i4) = o2;
+            *reinterpret_cast<f16x4_t*>(kdst + i4) = o1;
+            *reinterpret_cast<f16x4_t*>(kdst + 64 + i4) = o2;
           }
         }
       }
@@ -439,8 +460,8 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
     }
     if (a.vcache != nullptr && n0 >= a.vcol) {
       // a V head (128 columns): float16 rows staged in the free A stages,
-      // then 16-byte chunks of the 256-byte cache rows at positions vpos0 +
-      // row (the same round to nearest as the append kernel)
+      // then 16-byte chunks of the 256-byte cache rows (the same round to
+      // nearest as the append kernel)
       constexpr int OLD = 128 + 8;  // LDS row stride (halfs)
       static_assert(BM * OLD * 2 <= NS * BM * BK * 2, "V tile staging");
       f16_t* const os = reinterpret_cast<f16_t*>(&As[0][0]);
@@ -455,11 +476,13 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
             os[row * OLD + wn * WTN + j * 32 + fr] = (f16_t)acc[i][j][r];
           }
       __syncthreads();
-      f16_t* const dst = a.vcache + ((size_t)((n0 - a.vcol) / 128) * a.vcap + a.vpos0 + m0) * 128;
-      for (int q = tid; q < BM * 16; q += 512) {
-        const int row = q >> 4, ch = q & 15;
+      f16_t* const vhead = a.vcache + (size_t)((n0 - a.vcol) / 128) * a.vcap * 128;
+      static_assert(BM * 16 == 8 * 512, "8 rows per thread");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = i * 32 + (tid >> 4), ch = tid & 15;
         if (m0 + row < M)
-          *reinterpret_cast<uint4*>(dst + (size_t)row * 128 + ch * 8) =
+          *reinterpret_cast<uint4*>(vhead + (per > 0 ? roff[i] : base0 + (size_t)row * 128) + ch * 8) =
               *reinterpret_cast<const uint4*>(os + row * OLD + ch * 8);
       }
       return;
@@ -778,8 +801,11 @@ void launch_gemm_add_norm(GemmArgs a, const float* g, float eps, bf16_t* hn, int
 bool gemm_writes_kv(const GemmArgs& a) {
   // the path launch_gemm takes for EPI_STORE at M >= 512: 128-column DMA
   // tiles, split over K only when the grid is short of 256 blocks
+  // (stacked sequences: whole sequences, at most MAX_ROWS of them, and few
+  // enough rows for the float32 sequence index to be exact)
+  const bool rows_ok = a.kv_per == 0 || (a.M % a.kv_per == 0 && a.M / a.kv_per <= MAX_ROWS && a.M < (1 << 22));
   return a.kcache != nullptr && a.vcache != nullptr && a.M >= 512 && a.N % 128 == 0 && a.kcol % 128 == 0 &&
-         a.vcol % 128 == 0 && a.kcol < a.vcol && a.vcol < a.N && dma_splits(a) == 1;
+         a.vcol % 128 == 0 && a.kcol < a.vcol && a.vcol < a.N && rows_ok && dma_splits(a) == 1;
 }
 
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st) {

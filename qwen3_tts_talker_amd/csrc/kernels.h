@@ -45,7 +45,6 @@ struct QkArgs {
   int cap;
   int skip_q;  // 1: leave q as is (the matrix-core attention norms and ropes it)
   RowMeta rows;
-  int k_only = 0;  // 1: V is already in the cache (written by the projection)
 };
 // KV cache storage: float32, float16, or Q8_0 rows (head_dim int8 codes then
 // head_dim / 32 float16 scales)
@@ -118,13 +117,19 @@ struct GemmArgs {
   size_t work_elems;
   // EPI_STORE, the Q|K|V projection of one sequence (head_dim 128): columns
   // kcol .. vcol-1 are K rows, which get the per-head RMSNorm (gain g_k),
-  // NEOX RoPE at position vpos0 + row (table rope [cap][64]) and go as
+  // NEOX RoPE at the row's position (table rope [cap][64]) and go as
   // float16 to kcache; columns from vcol on are V rows, which go as float16
-  // to vcache; head (col - kcol or vcol) / 128, cache row head * vcap +
-  // vpos0 + row.  Neither goes to C (see gemm_writes_kv).
+  // to vcache.  Row r belongs to sequence kv_seqs[r / kv_per] at position
+  // vpos0 + r % kv_per (kv_per = 0: sequence kv_seqs[0], position vpos0 +
+  // r); its cache row for head (col - kcol or vcol) / 128 is element
+  // seq * kv_seq_stride + (head * vcap + position) * 128 of the layer's
+  // cache.  Neither goes to C (see gemm_writes_kv).
   f16_t* kcache = nullptr;
   f16_t* vcache = nullptr;
   int kcol = 0, vcol = 0, vcap = 0, vpos0 = 0;
+  size_t kv_seq_stride = 0;
+  int kv_per = 0;
+  int kv_seqs[MAX_ROWS] = {};
   const float* g_k = nullptr;
   const float2* rope = nullptr;
   float eps = 0.f;

@@ -219,7 +219,7 @@ struct Fwd {
     return reinterpret_cast<char*>(base) + (size_t)l * c->layer_kv_rows() * c->kv_rb;
   }
 
-  void qk_append(int l, const RowMeta& rows, bool skip_q = false, bool k_only = false) {
+  void qk_append(int l, const RowMeta& rows, bool skip_q = false) {
     QkArgs q{};
     q.qkv = c->qkv;
     q.ldqkv = c->qkv_dim;
@@ -235,7 +235,6 @@ struct Fwd {
     q.cap = g.max_seq_len;
     q.skip_q = skip_q ? 1 : 0;
     q.rows = rows;
-    q.k_only = k_only ? 1 : 0;
     launch_qk_rope_append(c->kv, q, st);
   }
 
@@ -323,15 +322,22 @@ struct Fwd {
     // positions dequantised, this chunk's rows as computed
     const bool q8_mfma = c->kv == KV_Q8 && c->kv16 && sup && rows.uniform == 1;
     const bool mfma_attn = (c->kv == KV_F16 && sup) || q8_mfma;
-    // one sequence, float16 cache, head_dim 128: the projection forms K
-    // (norm, RoPE) and V in its epilogue and writes them straight into the
-    // cache where its tiling allows; otherwise the append kernel does
+    // one sequence or stacked sequences, float16 cache, head_dim 128: the
+    // projection forms K (norm, RoPE) and V in its epilogue and writes them
+    // straight into the cache where its tiling allows; otherwise the append
+    // kernel does
     GemmArgs qa{c->hn, H, reinterpret_cast<const bf16_t*>(L.wqkv), T, c->qkv_dim, H, c->qkv, c->qkv_dim,
                 c->work, WORK_ELEMS};
-    if (c->kv == KV_F16 && mfma_attn && g.head_dim == 128 && rows.uniform == 1) {
-      const size_t seq_off = (size_t)rows.seq0 * g.n_kv_heads * g.max_seq_len * g.head_dim;
-      qa.kcache = reinterpret_cast<f16_t*>(kv_layer(c->kc, l)) + seq_off;
-      qa.vcache = reinterpret_cast<f16_t*>(kv_layer(c->vc, l)) + seq_off;
+    if (c->kv == KV_F16 && mfma_attn && g.head_dim == 128 && (rows.uniform == 1 || rows.uniform == 2)) {
+      qa.kcache = reinterpret_cast<f16_t*>(kv_layer(c->kc, l));
+      qa.vcache = reinterpret_cast<f16_t*>(kv_layer(c->vc, l));
+      qa.kv_seq_stride = (size_t)g.n_kv_heads * g.max_seq_len * g.head_dim;
+      if (rows.uniform == 2) {
+        qa.kv_per = rows.per;
+        for (int z = 0; z < T / rows.per; ++z) qa.kv_seqs[z] = rows.seq[z];
+      } else {
+        qa.kv_seqs[0] = rows.seq0;
+      }
       qa.kcol = c->q_dim;
       qa.vcol = c->q_dim + c->kv_dim;
       qa.vcap = g.max_seq_len;
