@@ -7,8 +7,10 @@
 // "transcribe.cpp src/causal_lm/causal_lm.cpp", block_prefill: query head h
 // reads KV head h / (n_heads / n_kv_heads)).  The rows' own K/V were
 // appended to the cache before this kernel runs, so keys are read back in
-// their cache precision.  q arrives raw from the QKV projection; its QK-norm
-// and RoPE are applied here, on the fragment each lane already holds.
+// their cache precision.  q arrives either prepared by the QKV projection's
+// epilogue (q16: normed, rotated, scaled, float16, read straight into the
+// fragments) or raw in float32, and then its QK-norm and RoPE are applied
+// here, on the fragment each lane already holds.
 //
 // Work split (two query heads per KV head): a block owns one KV head g and
 // 32 consecutive positions; its 4 waves are (query head of the group) x (key
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // hd d < 64 sits in the same lane at ks + NKS/2.  The key-half-0 wave of a
   // query head prepares the fragments and hands them to its partner through
   // LDS; both keep them in registers for the whole key loop.
-  if (kh == 0) {
+  if (kh == 0 && !a.q16) {
     const int t = min(posn - a.p0, a.T - 1);
     const int pr = min(posn, a.p0 + a.T - 1);
     const float* qp = qrows + (size_t)t * a.ldq + (size_t)hq * HD + h * 8;
@@ -344,10 +346,18 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // for loads just issued) makes every wave's part of tile kt visible and
   // frees the other buffer, whose next tile is requested before the products.
   QA_ISSUE(0, 0);
-  __syncthreads();  // q fragments (K tile of buffer 1) written
+  if (a.q16) {  // prepared by the projection: each wave loads its own fragments
+    const int t = min(posn - a.p0, a.T - 1);
+    const f16_t* qp = reinterpret_cast<const f16_t*>(qrows) + (size_t)t * 2 * a.ldq + (size_t)hq * HD + h * 8;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const f16x8_t*>(qp + ks * 16);
+  }
+  __syncthreads();  // q fragments (K tile of buffer 1) written
+  if (!a.q16) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
+  }
   // two tiles per iteration, so that each names its buffer as a constant
   for (int kt = 0; kt < nkt; kt += 2) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");

@@ -403,17 +403,21 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
         roff[i] = (size_t)a.kv_seqs[z] * a.kv_seq_stride + (size_t)(a.vpos0 + r - z * per) * 128;
       }
     }
-    if (a.kcache != nullptr && n0 >= a.kcol && n0 < a.vcol) {
-      // a K head (128 columns): float32 rows staged in the free A stages,
-      // 128 rows at a time; 16 lanes per row, lane i holding dims 4i .. 4i+3
-      // and their RoPE partners 64 + 4i .. (the arithmetic of the append
-      // kernel: per-head RMSNorm with g_k, NEOX rotation, float16)
+    if (a.kcache != nullptr && n0 < a.vcol) {
+      // a q or K head (128 columns): float32 rows staged in the free A
+      // stages, 128 rows at a time; 16 lanes per row, lane i holding dims
+      // 4i .. 4i+3 and their RoPE partners 64 + 4i .. (the arithmetic of the
+      // append kernel: per-head RMSNorm, NEOX rotation; q then times the
+      // score scale), float16 to the cache (K) or in place into C (q)
+      const bool is_q = n0 < a.kcol;
+      const float* const gain = is_q ? a.g_q : a.g_k;
+      const float scale = is_q ? a.qscale : 1.0f;
       constexpr int FLD = 128 + 4;  // LDS row stride (floats)
       static_assert(128 * FLD * 4 <= NS * BM * BK * 2, "K tile staging");
       float* const fs = reinterpret_cast<float*>(&As[0][0]);
       const int i4 = (tid & 15) * 4;
-      const float4 g1 = *reinterpret_cast<const float4*>(a.g_k + i4);
-      const float4 g2 = *reinterpret_cast<const float4*>(a.g_k + 64 + i4);
+      const float4 g1 = *reinterpret_cast<const float4*>(gain + i4);
+      const float4 g2 = *reinterpret_cast<const float4*>(gain + 64 + i4);
       // rotations of every row this thread forms (8 passes of 32 rows),
       // requested before the staging so that they have landed by then
       float4 cr[8][2];
@@ -423,7 +427,8 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
         cr[p][0] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4);
         cr[p][1] = *reinterpret_cast<const float4*>(a.rope + (size_t)pos * 64 + i4 + 2);
       }
-      f16_t* const khead = a.kcache + (size_t)((n0 - a.kcol) / 128) * a.vcap * 128;
+      f16_t* const khead = a.kcache + (size_t)((is_q ? 0 : n0 - a.kcol) / 128) * a.vcap * 128;
+      f16_t* const qhead = reinterpret_cast<f16_t*>(reinterpret_cast<float*>(a.C) + (size_t)m0 * a.ldc) + n0;
       typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -447,8 +452,13 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
           float4 x1 = *reinterpret_cast<const float4*>(fs + rr * FLD + i4);
           float4 x2 = *reinterpret_cast<const float4*>(fs + rr * FLD + 64 + i4);
           k_row_norm_rope(x1, x2, g1, g2, cr[half * 4 + pp][0], cr[half * 4 + pp][1], a.eps);
+          if (is_q) {  // an exact product for K (scale 1)
+            x1.x *= scale; x1.y *= scale; x1.z *= scale; x1.w *= scale;
+            x2.x *= scale; x2.y *= scale; x2.z *= scale; x2.w *= scale;
+          }
           if (m0 + row < M) {
-            f16_t* const kdst = khead + (per > 0 ? roff[half * 4 + pp] : base0 + (size_t)row * 128);
+            f16_t* const kdst = is_q ? qhead + (size_t)row * a.ldc * 2
+                                     : khead + (per > 0 ? roff[half * 4 + pp] : base0 + (size_t)row * 128);
             const f16x4_t o1 = {(f16_t)x1.x, (f16_t)x1.y, (f16_t)x1.z, (f16_t)x1.w};
             const f16x4_t o2 = {(f16_t)x2.x, (f16_t)x2.y, (f16_t)x2.z, (f16_t)x2.w};
             *reinterpret_cast<f16x4_t*>(kdst + i4) = o1;

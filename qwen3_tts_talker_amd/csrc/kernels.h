@@ -94,6 +94,9 @@ struct PrefillAttnArgs {
   int n_heads, n_kv_heads, head_dim, cap;
   int seq, p0, T;
   float qscale;  // log2(e) / sqrt(head_dim)
+  // 1: q arrives normed, rotated and scaled, float16 (row t's head h at halfs
+  // t * 2 * ldq + h * head_dim); 0: raw float32 as above
+  int q16;
   bf16_t* out;   // row t at out + t*ldo
   int ldo;
   int ncu;  // compute units (block placement only)
@@ -115,8 +118,11 @@ struct GemmArgs {
   int ldc;
   float* work;  // split-K partials [ksplit][M][N]
   size_t work_elems;
-  // EPI_STORE, the Q|K|V projection of one sequence (head_dim 128): columns
-  // kcol .. vcol-1 are K rows, which get the per-head RMSNorm (gain g_k),
+  // EPI_STORE, the Q|K|V projection (head_dim 128): columns 0 .. kcol-1
+  // are q rows, which get the per-head RMSNorm (gain g_q), NEOX RoPE and the
+  // score scale qscale and go as float16 into C in place (row r's head h at
+  // halfs h * 128 of the row: the first kcol halfs of its ldc floats);
+  // columns kcol .. vcol-1 are K rows, which get the per-head RMSNorm (gain g_k),
   // NEOX RoPE at the row's position (table rope [cap][64]) and go as
   // float16 to kcache; columns from vcol on are V rows, which go as float16
   // to vcache.  Row r belongs to sequence kv_seqs[r / kv_per] at position
@@ -131,8 +137,9 @@ struct GemmArgs {
   int kv_per = 0;
   int kv_seqs[MAX_ROWS] = {};
   const float* g_k = nullptr;
+  const float* g_q = nullptr;
   const float2* rope = nullptr;
-  float eps = 0.f;
+  float eps = 0.f, qscale = 0.f;
 };
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
 // whether launch_gemm(EPI_STORE, a) writes a's K and V columns to the cache

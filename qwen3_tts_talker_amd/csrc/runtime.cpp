@@ -310,6 +310,9 @@ struct Fwd {
   // c->hn holds RMSNorm(x) * g_in when `normed` (the previous layer's down
   // projection produced it); on return it holds the next layer's input norm
   // unless this is the last layer.
+  // q's score scale: log2(e) / sqrt(head_dim) (softmax in exp2 units)
+  float attn_qscale() const { return 1.4426950408889634f / sqrtf((float)g.head_dim); }
+
   void layer_mfma(int l, const RowMeta& rows, bool normed) {
     const LayerDev& L = c->layers[l];
     const int T = rows.n, H = g.hidden, I = g.intermediate;
@@ -343,8 +346,10 @@ struct Fwd {
       qa.vcap = g.max_seq_len;
       qa.vpos0 = rows.p0;
       qa.g_k = L.g_k;
+      qa.g_q = L.g_q;
       qa.rope = c->rope;
       qa.eps = g.rms_eps;
+      qa.qscale = attn_qscale();
     }
     const bool kv_done = gemm_writes_kv(qa);
     if (!kv_done) qa.kcache = qa.vcache = nullptr;
@@ -383,7 +388,8 @@ struct Fwd {
         p.seq = rows.seq[0];
       }
       if (q8_mfma) p.seq = 0;  // the float16 copy holds this sequence only
-      p.qscale = 1.4426950408889634f / sqrtf((float)g.head_dim);
+      p.qscale = attn_qscale();
+      p.q16 = kv_done ? 1 : 0;
       p.out = att_b;
       p.ldo = c->q_dim;
       p.ncu = c->ncu;
