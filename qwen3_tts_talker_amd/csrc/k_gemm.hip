@@ -413,7 +413,7 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
       const float* const gain = is_q ? a.g_q : a.g_k;
       const float scale = is_q ? a.qscale : 1.0f;
       constexpr int FLD = 128 + 4;  // LDS row stride (floats)
-      static_assert(128 * FLD * 4 <= NS * BM * BK * 2, "K tile staging");
+      static_assert(128 * FLD * 4 <= NS * BM * BK * 2, "q/K tile staging");
       float* const fs = reinterpret_cast<float*>(&As[0][0]);
       const int i4 = (tid & 15) * 4;
       const float4 g1 = *reinterpret_cast<const float4*>(gain + i4);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(512) void k_gemm_dma(GemmArgs a, int k_per_split) {
           float4 x1 = *reinterpret_cast<const float4*>(fs + rr * FLD + i4);
           float4 x2 = *reinterpret_cast<const float4*>(fs + rr * FLD + 64 + i4);
           k_row_norm_rope(x1, x2, g1, g2, cr[half * 4 + pp][0], cr[half * 4 + pp][1], a.eps);
-          if (is_q) {  // an exact product for K (scale 1)
+          if (is_q) {  // q: the score scale
             x1.x *= scale; x1.y *= scale; x1.z *= scale; x1.w *= scale;
             x2.x *= scale; x2.y *= scale; x2.z *= scale; x2.w *= scale;
           }
