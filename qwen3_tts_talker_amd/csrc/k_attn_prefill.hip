@@ -437,13 +437,11 @@ bool attn_prefill_supported(int head_dim, int group) {
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st) {
   const int nqb = (a.T + pa::PB - 1) / pa::PB;
   const dim3 grid(nqb * a.n_kv_heads, a.nbatch > 1 ? a.nbatch : 1);
-  // a causal triangle from position 0 whose longest blocks walk many key
-  // tiles: four key groups per block, two waves per SIMD on each item, so the
-  // longest items finish sooner.  (Over uniformly long rows, chunks at an
-  // offset, two blocks of two groups per CU measured faster.)
-  const bool wide = a.head_dim == 128 && a.nbatch <= 1 && a.p0 == 0 && a.T >= 512;
-  if (wide) hipLaunchKernelGGL((k_attn_prefill<128, 4>), grid, dim3(64 * pa::G * 4), 0, st, a);
-  else if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_prefill<128, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
+  // two key groups per block, two blocks per CU (four key groups on one
+  // item, one block per CU, finished a causal triangle from position 0
+  // sooner while q was prepared here; with q from the projection's epilogue
+  // two groups are faster there too)
+  if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_prefill<128, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
   else hipLaunchKernelGGL((k_attn_prefill<64, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
 }
 
