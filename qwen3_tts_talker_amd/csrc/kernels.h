@@ -129,7 +129,8 @@ struct GemmArgs {
   // vpos0 + r % kv_per (kv_per = 0: sequence kv_seqs[0], position vpos0 +
   // r); its cache row for head (col - kcol or vcol) / 128 is element
   // seq * kv_seq_stride + (head * vcap + position) * 128 of the layer's
-  // cache.  Neither goes to C (see gemm_writes_kv).
+  // cache; K and V do not go to C.  All of this applies when
+  // gemm_writes_kv(a) holds; otherwise C receives every column in float32.
   f16_t* kcache = nullptr;
   f16_t* vcache = nullptr;
   int kcol = 0, vcol = 0, vcap = 0, vpos0 = 0;
@@ -142,9 +143,10 @@ struct GemmArgs {
   float eps = 0.f, qscale = 0.f;
 };
 void launch_gemm(Epilogue epi, GemmArgs a, hipStream_t st);
-// whether launch_gemm(EPI_STORE, a) writes a's K and V columns to the cache
-// (the 256-row matrix-core product with whole 128-column tiles and no K
-// split); otherwise the caller appends them itself
+// whether launch_gemm(EPI_STORE, a) forms q, K and V in its epilogue (q as
+// float16 into C, K and V into the cache): the 256-row matrix-core product
+// with whole 128-column tiles and no K split; otherwise C holds the raw
+// float32 product and the caller appends K and V itself
 bool gemm_writes_kv(const GemmArgs& a);
 // C += A * B^T (C = the f32 residual stream [M][N]), then hn = bf16(RMSNorm(C) * g)
 // row by row; split-K partials are reduced in the same pass as the norm.
