@@ -213,6 +213,8 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  float mref = 0.f;            // the scores' reference: m_run once finite
+  f32x16_t cin = f32x16_t{};   // -mref in every register: the score accumulator's start
 
   // A-operand row of the score product held by this lane: key tau(n) of this
   // wave's 32-key half
@@ -256,9 +258,12 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kf[ks]));
-    f32x16_t s = f32x16_t{};
+    // the row's current reference enters as the accumulator's start (cin,
+    // kept in registers and rebuilt only when the reference moves), so s
+    // holds the scores minus mref (log2 units; mref 0 while the row has none)
+    f32x16_t s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[0], qf[0], cin, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s, 0, 0, 0);
+    for (int ks = 1; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s, 0, 0, 0);
     // causal mask (key <= position) where the half reaches the block's rows
     if (kbase + 31 > P0) {
 #pragma unroll
@@ -290,16 +295,27 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
     // float16 up to its rounding) and the O/l rescale, once the maxima have
     // settled, almost never runs; the final 1/l and the merge of the key
     // groups use the same reference, so the result is the softmax itself
+    // (mx is relative to mref; a row without a reference yet takes any
+    // visible key's maximum)
     float alpha = 1.f;
-    if (__any(mx > m_run + LAZY)) {
-      const float m_new = fmaxf(m_run, mx);
+    if (__any(m_run == -INFINITY ? mx > -INFINITY : mx > LAZY)) {
+      const float m_new = fmaxf(m_run, mx + mref);
       alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      // scores relative to the new reference (a row with no visible key
+      // yet keeps reference 0: its P is 0 either way)
+      const float mref_new = m_new == -INFINITY ? 0.f : m_new;
+      const float shift = mref_new - mref;
+      mref = mref_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] -= shift;
+        cin[r] = -mref;
+      }
     }
-    const float mref = m_run == -INFINITY ? 0.f : m_run;  // a row with no visible key yet: P = 0
     f16x8_t pf[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (f16_t)__builtin_amdgcn_exp2f(s[r] - mref);  // masked: exp2(-inf) = 0
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (f16_t)__builtin_amdgcn_exp2f(s[r]);  // masked: exp2(-inf) = 0
     // l sums the float16 weights the value product uses, two per dot2
     // instruction (float32 accumulation), in two chains
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
