@@ -214,6 +214,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   float mref = 0.f;            // the scores' reference: m_run once finite
+  float thr = -INFINITY;       // a row maximum (relative to mref) past this moves the reference
   f32x16_t cin = f32x16_t{};   // -mref in every register: the score accumulator's start
 
   // A-operand row of the score product held by this lane: key tau(n) of this
@@ -295,23 +296,28 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
     // float16 up to its rounding) and the O/l rescale, once the maxima have
     // settled, almost never runs; the final 1/l and the merge of the key
     // groups use the same reference, so the result is the softmax itself
-    // (mx is relative to mref; a row without a reference yet takes any
-    // visible key's maximum)
-    float alpha = 1.f;
-    if (__any(m_run == -INFINITY ? mx > -INFINITY : mx > LAZY)) {
+    // (mx is relative to mref; thr is -inf while the row has no reference,
+    // so any visible key sets one, then LAZY)
+    if (__any(mx > thr)) {
       const float m_new = fmaxf(m_run, mx + mref);
-      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       // scores relative to the new reference (a row with no visible key
-      // yet keeps reference 0: its P is 0 either way)
+      // yet keeps reference 0: its P is 0 either way); O and l rescaled
       const float mref_new = m_new == -INFINITY ? 0.f : m_new;
       const float shift = mref_new - mref;
       mref = mref_new;
+      thr = m_new == -INFINITY ? -INFINITY : LAZY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] -= shift;
         cin[r] = -mref;
       }
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
     }
     f16x8_t pf[2];
 #pragma unroll
@@ -326,13 +332,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
       ps0 = __builtin_amdgcn_fdot2(h2_t{pf[0][2 * q], pf[0][2 * q + 1]}, one2, ps0, false);
       ps1 = __builtin_amdgcn_fdot2(h2_t{pf[1][2 * q], pf[1][2 * q + 1]}, one2, ps1, false);
     }
-    l_run = l_run * alpha + (ps0 + ps1);
-    if (!__all(alpha == 1.0f)) {
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
-    }
+    l_run += ps0 + ps1;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int sk = 0; sk < 2; ++sk)
