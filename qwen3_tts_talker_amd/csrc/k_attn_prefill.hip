@@ -13,12 +13,16 @@
 // here, on the fragment each lane already holds.
 //
 // Work split (two query heads per KV head): a block owns one KV head g and
-// 32 consecutive positions; its 4 waves are (query head of the group) x (key
-// half), so one staging of a 64-key K/V tile in LDS serves both query heads,
-// and each wave runs the MFMAs of one 32-key half of every tile with its own
-// online softmax.  The two halves are merged (log-sum-exp) at the end.  Small
-// blocks (480 of them at 2048 rows) spread the causal triangle over all CUs
-// two blocks deep, longest first.
+// 32 or 64 consecutive positions; its waves are (query head of the group) x
+// (32-row half of the positions) x (key half), so one staging of a 64-key
+// K/V tile in LDS serves both query heads and all the block's rows, and each
+// wave runs the MFMAs of one 32-key half of every tile with its own online
+// softmax.  The two key halves are merged (log-sum-exp) at the end.  Blocks
+// of 32 positions (4 waves, 480 blocks at 2048 rows) spread a causal
+// triangle over all CUs two blocks deep, longest first; blocks of 64
+// positions (8 waves, one block per CU) stage each K/V byte for twice the
+// query rows, which pays where the blocks' key ranges are of similar length
+// (a chunk far into the context).
 //
 // Per wave and tile (flash-attention order, softmax state in float32):
 //   S^T[key][row] = K . Q^T   v_mfma_f32_32x32x16_f16, A = K rows, B = q
@@ -36,7 +40,7 @@
 namespace qtalk {
 namespace pa {
 
-constexpr int PB = 32;        // positions per block
+constexpr int PR = 32;        // positions per row half (one MFMA tile of query rows)
 constexpr float LAZY = 8.f;   // online softmax: headroom of the running maximum (log2 units)
 constexpr int G = 2;          // query heads per KV head
 
@@ -59,13 +63,15 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// NKQ key groups per block: waves (query head, key group), 32 keys of every
-// tile per wave, tiles of 32 NKQ keys.  NKQ = 2: 4 waves, two blocks per CU;
-// NKQ = 4: 8 waves (two per SIMD on one work item), one block per CU.
-template <int HD, int NKQ>
-__global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_prefill(PrefillAttnArgs a) {
+// NKQ key groups per block, NR row halves of 32 positions: waves (query
+// head, row half, key group), 32 keys of every tile per wave, tiles of 32 NKQ
+// keys.  NKQ = 2, NR = 1: 4 waves, two blocks per CU; NKQ = 2, NR = 2: 8
+// waves, one block per CU.  Either way two waves share a SIMD.
+template <int HD, int NKQ, int NR>
+__global__ __launch_bounds__(64 * pa::G * NKQ * NR, NKQ * NR == 2 ? 2 : 1) void k_attn_prefill(PrefillAttnArgs a) {
   using namespace pa;
-  constexpr int NWV = G * NKQ;              // waves per block
+  constexpr int PB = PR * NR;               // positions per block
+  constexpr int NWV = G * NR * NKQ;         // waves per block
   constexpr int KT = 32 * NKQ;              // keys per tile
   constexpr int NKS = HD / 16;              // k-steps of the score product
   constexpr int NMT = HD / 32;              // hd tiles of the value product
@@ -82,13 +88,16 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // (16 lanes, 16 consecutive keys, one chunk) and the transposing V reads
   // (32 lanes, 4 consecutive keys, 4 aligned chunks) then both fall on 16
   // distinct 16-byte bank groups (k % 16 alone gave the V reads four-way
-  // conflicts).  At head_dim 64 swz(k) = k % 8.  The q fragments pass
-  // through the K tile of buffer 1 before the key loop
+  // conflicts).  At head_dim 64 swz(k) = k % 8.  With one row half the q
+  // fragments pass through the K tile of buffer 1 before the key loop; the
+  // key-group merge at the end reuses the tiles' space
   constexpr int TILE = 2 * KT * HD;  // halfs per buffer
-  constexpr int LDS_HALFS = 2 * TILE;
+  constexpr int XS = HD / 32 * 16 + 2;                    // merge record: O, m, l of one lane
+  constexpr int MERGE_HALFS = G * NR * (NKQ - 1) * 64 * XS * 2;
+  constexpr int LDS_HALFS = 2 * TILE > MERGE_HALFS ? 2 * TILE : MERGE_HALFS;
   __shared__ __attribute__((aligned(1024))) f16_t lds[LDS_HALFS];
   f16_t* const qlds = lds + KT * HD;  // K tile of buffer 1
-  static_assert(G * NKS * 64 * 8 <= KT * HD, "q fragments fit one K tile");
+  static_assert(NR != 1 || G * NKS * 64 * 8 <= KT * HD, "q fragments fit one K tile");
 
   auto swz = [](int k) { return CPR == 16 ? ((k & 3) << 2) | ((k >> 2) & 3) : (k & (CPR - 1)); };
   const int tid = threadIdx.x, lane = tid & 63;
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // (longest with shortest) and every CU gets about the same number of key
   // tiles; otherwise plain longest first.
   const int nb = nqb * nkv, b = blockIdx.x;
-  const int r = (NKQ != 2 || b < a.ncu || nb > 2 * a.ncu) ? b : nb - 1 - (b - a.ncu);
+  const int r = (NKQ * NR != 2 || b < a.ncu || nb > 2 * a.ncu) ? b : nb - 1 - (b - a.ncu);
   const int g = r % nkv;
   const int qb = nqb - 1 - r / nkv;
   const int P0 = a.p0 + qb * PB;
@@ -109,11 +118,13 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   const int kend = P1;                      // keys [0, kend)
   const int nkt = (kend + KT - 1) / KT;
 
-  const int hh = wave / NKQ, kh = wave % NKQ;  // query head of the group, key group
+  // query head of the group, row half, key group
+  const int hh = wave / (NKQ * NR), rh = (wave / NKQ) % NR, kh = wave % NKQ;
   const int hq = g * G + hh;
-  const int last = P1 - 1;
+  const int R0 = P0 + rh * PR;              // this wave's first position
+  const int last = min(R0 + PR, P1) - 1;    // its last key (below R0 when the half is past the end)
   const int n = lane & 31, h = lane >> 5;
-  const int posn = P0 + n;
+  const int posn = R0 + n;
 
   // batched prefill: this block's sequence and its rows of q and out
   const int bz = blockIdx.y;
@@ -132,8 +143,10 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // lane pair (n, n + 32) holds the whole head, and the RoPE partner d + 64 of
   // hd d < 64 sits in the same lane at ks + NKS/2.  The key-half-0 wave of a
   // query head prepares the fragments and hands them to its partner through
-  // LDS; both keep them in registers for the whole key loop.
-  if (kh == 0 && !a.q16) {
+  // LDS (with two row halves, every wave prepares its own); all keep them in
+  // registers for the whole key loop.
+  f16x8_t qf[NKS];
+  if ((NR == 2 || kh == 0) && !a.q16) {
     const int t = min(posn - a.p0, a.T - 1);
     const int pr = min(posn, a.p0 + a.T - 1);
     const float* qp = qrows + (size_t)t * a.ldq + (size_t)hq * HD + h * 8;
@@ -169,7 +182,8 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
       f16x8_t f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = (f16_t)qv[ks][e];
-      *reinterpret_cast<f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]) = f;
+      if (NR == 2) qf[ks] = f;
+      else *reinterpret_cast<f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]) = f;
     }
   }
 
@@ -220,7 +234,6 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // A-operand row of the score product held by this lane: key tau(n) of this
   // wave's 32-key half
   const int krow = kh * 32 + tau(n);
-  f16x8_t qf[NKS];
   // operand reads are inline asm with explicit waits: the compiler would wait
   // for every outstanding direct-to-LDS load (the next tile's) before a read.
   // K fragment of step ks: row krow, chunk 2 ks + h (swizzled).  V^T fragment
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
 #pragma unroll
     for (int ks = 1; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s, 0, 0, 0);
     // causal mask (key <= position) where the half reaches the block's rows
-    if (kbase + 31 > P0) {
+    if (kbase + 31 > R0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kbase + (r >> 3) * 16 + h * 8 + ((r >> 2) & 1) * 4 + (r & 3);
@@ -368,11 +381,13 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const f16x8_t*>(qp + ks * 16);
   }
-  __syncthreads();  // q fragments (K tile of buffer 1) written
-  if (!a.q16) {
+  if constexpr (NR == 1) {
+    __syncthreads();  // q fragments (K tile of buffer 1) written
+    if (!a.q16) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[ks] = *reinterpret_cast<const f16x8_t*>(&qlds[((hh * NKS + ks) * 64 + lane) * 8]);
+    }
   }
   // two tiles per iteration, so that each names its buffer as a constant
   for (int kt = 0; kt < nkt; kt += 2) {
@@ -394,11 +409,11 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   // merge the key groups of each query head through LDS (the tiles are no
   // longer needed): the other groups hand over (m, l, O), the group-0 wave
   // combines and writes
-  float* xs = reinterpret_cast<float*>(lds);  // [G][NKQ-1][64 lanes][NMT*16 + 2]
-  constexpr int XS = NMT * 16 + 2;
-  static_assert((size_t)G * (NKQ - 1) * 64 * XS * 4 <= sizeof(f16_t) * LDS_HALFS, "merge buffer");
+  float* xs = reinterpret_cast<float*>(lds);  // [G][NR][NKQ-1][64 lanes][NMT*16 + 2]
+  static_assert(XS == NMT * 16 + 2 && (size_t)G * NR * (NKQ - 1) * 64 * XS * 4 <= sizeof(f16_t) * LDS_HALFS,
+                "merge buffer");
   if (kh != 0) {
-    float* mine = xs + ((size_t)(hh * (NKQ - 1) + kh - 1) * 64 + lane) * XS;
+    float* mine = xs + ((size_t)((hh * NR + rh) * (NKQ - 1) + kh - 1) * 64 + lane) * XS;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -412,7 +427,7 @@ __global__ __launch_bounds__(64 * pa::G * NKQ, NKQ == 2 ? 2 : 1) void k_attn_pre
   float M = m_run;  // finite: key 0 is visible to every row
 #pragma unroll
   for (int j = 0; j < NKQ - 1; ++j) {
-    part[j] = xs + ((size_t)(hh * (NKQ - 1) + j) * 64 + lane) * XS;
+    part[j] = xs + ((size_t)((hh * NR + rh) * (NKQ - 1) + j) * 64 + lane) * XS;
     M = fmaxf(M, part[j][NMT * 16]);
   }
   const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
@@ -450,15 +465,32 @@ bool attn_prefill_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && group == pa::G;
 }
 
+int attn_prefill_rows_per_block(const PrefillAttnArgs& a) {
+  if (a.head_dim != 128 || a.rows_per_block == 32) return 32;
+  if (a.rows_per_block == 64) return 64;
+  // 64 positions per block halve the K/V staging per flop but give every CU
+  // one block, so the longest block sets the time: taken where the chunk
+  // starts at least its own length into the context (the key ranges of its
+  // blocks then differ by at most a factor of two) and the grid fills the
+  // chip
+  const int nb = (a.T + 63) / 64 * a.n_kv_heads * (a.nbatch > 1 ? a.nbatch : 1);
+  return (a.p0 >= a.T && nb >= a.ncu) ? 64 : 32;
+}
+
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st) {
-  const int nqb = (a.T + pa::PB - 1) / pa::PB;
+  const int pb = attn_prefill_rows_per_block(a);
+  const int nqb = (a.T + pb - 1) / pb;
   const dim3 grid(nqb * a.n_kv_heads, a.nbatch > 1 ? a.nbatch : 1);
-  // two key groups per block, two blocks per CU (four key groups on one
-  // item, one block per CU, finished a causal triangle from position 0
-  // sooner while q was prepared here; with q from the projection's epilogue
-  // two groups are faster there too)
-  if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_prefill<128, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
-  else hipLaunchKernelGGL((k_attn_prefill<64, 2>), grid, dim3(64 * pa::G * 2), 0, st, a);
+  // two key groups per block (four key groups on one item, one block per
+  // CU, finished a causal triangle from position 0 sooner while q was
+  // prepared here; with q from the projection's epilogue two groups are
+  // faster there too)
+  if (a.head_dim == 128 && pb == 64)
+    hipLaunchKernelGGL((k_attn_prefill<128, 2, 2>), grid, dim3(64 * pa::G * 2 * 2), 0, st, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((k_attn_prefill<128, 2, 1>), grid, dim3(64 * pa::G * 2), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn_prefill<64, 2, 1>), grid, dim3(64 * pa::G * 2), 0, st, a);
 }
 
 }  // namespace qtalk

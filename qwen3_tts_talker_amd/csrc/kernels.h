@@ -97,6 +97,9 @@ struct PrefillAttnArgs {
   // 1: q arrives normed, rotated and scaled, float16 (row t's head h at halfs
   // t * 2 * ldq + h * head_dim); 0: raw float32 as above
   int q16;
+  // positions per block: 32, 64 (head_dim 128 only), or 0 to let the
+  // launcher pick from the chunk's offset and the grid size
+  int rows_per_block;
   bf16_t* out;   // row t at out + t*ldo
   int ldo;
   int ncu;  // compute units (block placement only)
@@ -107,6 +110,7 @@ struct PrefillAttnArgs {
 };
 bool attn_prefill_supported(int head_dim, int group);
 void launch_attn_prefill(const PrefillAttnArgs& a, hipStream_t st);
+int attn_prefill_rows_per_block(const PrefillAttnArgs& a);
 
 // C = A[M][K] (bf16) * B[N][K]^T (bf16) on MFMA, float32 accumulation.
 struct GemmArgs {

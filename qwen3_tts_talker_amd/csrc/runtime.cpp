@@ -89,6 +89,7 @@ struct qtalk_ctx {
   int dev = 0;
   hipEvent_t chain_ev = nullptr;  // marks another context's stream (DecodeChain)
   int ncu = 256;  // compute units of the device (placement heuristics only)
+  int attn_rows = 0;  // prefill attention positions per block (0: the launcher picks)
   // QKV -> attention -> merge exchanges of the persistent decode inside each
   // XCD (needs the dispatcher's block b -> XCD b % 8 placement, checked at
   // create and by every launch); QTALK_XCD_LOCAL=0 turns it off
@@ -393,6 +394,7 @@ struct Fwd {
       p.out = att_b;
       p.ldo = c->q_dim;
       p.ncu = c->ncu;
+      p.rows_per_block = c->attn_rows;
       launch_attn_prefill(p, st);
     } else {
       AttnArgs a = attn_args(l, rows);
@@ -724,6 +726,7 @@ qtalk_status qtalk_create(const qtalk_config* config, const qtalk_weights* w, vo
   const char* env = getenv("QTALK_FUSED_DECODE");
   const char* env_coop = getenv("QTALK_COOPERATIVE");
   c->coop = env_coop && env_coop[0] == '1';
+  if (const char* env_rows = getenv("QTALK_ATTN_ROWS")) c->attn_rows = atoi(env_rows) == 64 ? 64 : atoi(env_rows) == 32 ? 32 : 0;
   {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&

@@ -111,14 +111,22 @@ def test_talker_28_layers_prefill128_decode1024():
                     kv_layers=[0, 13, 27])
 
 
-def test_prefill_attention_many_tiles_ragged_extend_to_capacity():
+@pytest.mark.parametrize("rows", ["auto", "64"])
+def test_prefill_attention_many_tiles_ragged_extend_to_capacity(monkeypatch, rows):
     # two real-shape layers: layer 1's cache depends on layer 0's attention
     # output at every row, so comparing it checks every row of the matrix-core
     # prefill attention; 700 and 1348 rows leave ragged 64-key tiles and
-    # 64-position blocks, the extend starts at p0 = 700 and ends at the cap
+    # ragged position blocks, the extend starts at p0 = 700 and ends at the
+    # cap.  rows = 64 forces blocks of 64 positions (picked by the launcher
+    # only for chunks far into the context) on both calls: the 700-row
+    # prefill prepares q in the kernel, the 1348-row extend reads it from the
+    # projection's epilogue, and its last block has a row half wholly past
+    # the end
+    if rows != "auto":
+        monkeypatch.setenv("QTALK_ATTN_ROWS", rows)
     shape = workload("talker_1l_t128")
     w = weights_for("talker_1l_t128", 2)
-    say("[case] 2 real-shape layers: prefill 700, extend 1348 (to cap 2048)")
+    say(f"[case] 2 real-shape layers: prefill 700, extend 1348 (to cap 2048), rows {rows}")
     emb = prefill_embeddings(shape, 2048)
     orc = TalkerOracle(shape, w)
     lo1, ho1 = orc.prefill(0, emb[:700])
@@ -1151,12 +1159,16 @@ def test_fused_frame_step_reports_an_id_outside_its_table():
     tk.close()
 
 
-@pytest.mark.parametrize("n,T", [(16, 128), (7, 100), (3, 1000), (5, 3)])
-def test_prefill_batch_matches_oracle(n, T):
-    # 16 x 128: one matrix-core pass of 2048 rows; 7 x 100: ragged tiles;
+@pytest.mark.parametrize("n,T,rows", [(16, 128, "auto"), (7, 100, "auto"), (7, 100, "64"),
+                                      (3, 1000, "auto"), (5, 3, "auto")])
+def test_prefill_batch_matches_oracle(monkeypatch, n, T, rows):
+    # 16 x 128: one matrix-core pass of 2048 rows; 7 x 100: ragged tiles (and
+    # once with attention blocks of 64 positions forced);
     # 3 x 1000: two passes (2 + 1 sequences); 5 x 3: the matrix-vector path.
     # Sequence ids are listed out of order; a decode after the batch checks
     # that each cache is usable.
+    if rows != "auto":
+        monkeypatch.setenv("QTALK_ATTN_ROWS", rows)
     base = workload("talker_28l_t128_d1024")
     shape = base.with_(n_seqs=16, cap=2048)
     w = weights_for("talker_28l_t128_d1024", 2)
@@ -1164,7 +1176,7 @@ def test_prefill_batch_matches_oracle(n, T):
     orc = TalkerOracle(shape, w)
     seqs = [(5 * b + 3) % 16 for b in range(n)]
     embs = np.stack([prefill_embeddings(shape, T, seq=s) for s in seqs])
-    say(f"prefill_batch n={n} T={T}")
+    say(f"prefill_batch n={n} T={T} rows={rows}")
     lg, hd = tk.prefill_batch(seqs, dev(embs), hidden=True)
     ol, oh = orc.prefill_batch(seqs, embs)
     tk.sync()
